@@ -1,0 +1,194 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE: the reference rule of the "Effort"
+ * approximate vector-matrix multiply, written out step by step.
+ *
+ * Only tests/, the smoke check and the benchmark's CPU-baseline leg may load
+ * this file's library.  It is independent of the GPU library: no shared code,
+ * headers, tables or helpers.  Single-threaded, brute force, double-precision
+ * sums; build with -O2 -ffp-contract=off and without fast-math so that every
+ * fp32 product below is one IEEE round-to-nearest-even multiply and fp16
+ * subnormals are kept.
+ *
+ * Sources (web pages; cited by title and passage):
+ *  [HN] "Show HN: Speeding up LLM inference 2x times (possibly)", Hacker News
+ *       thread (Gopher archive and the forum repost of the post text).
+ *  [HT] hntin item 40095016, the author's reply on algorithmic complexity.
+ *
+ * Parity pins for every function are in tests/test_oracle_pins.py; each
+ * function below is pinned there against brute force, closed forms, invariants
+ * or a library routine.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+   exponent 0: subnormal f * 2^-24; exponent 31: inf/NaN; else (1024+f) * 2^(e-25). */
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1F;
+  int f = h & 0x3FF;
+  double mag;
+  if (e == 0)
+    mag = ldexp((double)f, -24);
+  else if (e == 31)
+    mag = f ? NAN : INFINITY;
+  else
+    mag = ldexp((double)(1024 + f), e - 25);
+  return sign ? -mag : mag;
+}
+
+/* splitmix64 output function (Steele, Lea, Flood 2014) of state x. */
+uint64_t oracle_pair_hash(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+/* |w| as fp32.  The magnitude of a binary16 value is its bit pattern with the
+   sign cleared; the conversion to fp32 is exact. */
+static float magnitude_f32(uint16_t h) { return (float)oracle_f16_to_f64((uint16_t)(h & 0x7FFF)); }
+
+static int cmp_u16_desc(const void* a, const void* b) {
+  uint16_t x = *(const uint16_t*)a, y = *(const uint16_t*)b;
+  return (x < y) - (x > y);
+}
+
+static int cmp_f32_desc(const void* a, const void* b) {
+  float x = *(const float*)a, y = *(const float*)b;
+  return (x < y) - (x > y);
+}
+
+/* Step "get_probes" of the precompute in the [HN] pseudocode (gcy's quote).
+   The pages give only the name; the reading used here: each stored row is
+   sorted by |w| descending (the author's reply to bigcat12345678: all entries
+   kept, ordered from the highest absolute value down) and cut into P rank
+   segments (the reply to marmaduke: each row split into 16 parts).  probe k is
+   the magnitude at rank ceil((k+1) n / P), i.e. the smallest magnitude of
+   segment k.  For finite fp16 the unsigned order of (bits & 0x7FFF) is the
+   order of magnitudes, so the sort is done on those keys. */
+int oracle_probes(const uint16_t* W, int64_t m, int64_t n, int32_t P, float* probes) {
+  if (!W || !probes || m <= 0 || n <= 0 || P < 1 || P > n) return 1;
+  uint16_t* keys = (uint16_t*)malloc((size_t)n * sizeof(uint16_t));
+  if (!keys) return 1;
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t j = 0; j < n; ++j) keys[j] = (uint16_t)(W[i * n + j] & 0x7FFF);
+    qsort(keys, (size_t)n, sizeof(uint16_t), cmp_u16_desc);
+    for (int32_t k = 0; k < P; ++k) {
+      int64_t rank = ((int64_t)(k + 1) * n + P - 1) / P; /* ceil((k+1) n / P), 1-based */
+      probes[i * P + k] = (float)oracle_f16_to_f64(keys[rank - 1]);
+    }
+  }
+  free(keys);
+  return 0;
+}
+
+/* "cutoff_chart = v * probes" in the [HN] pseudocode.  Ranking is by magnitude
+   (the method keeps the largest |v_i * W_ij|), so the chart holds |v_i| times
+   each probe, one fp32 multiply each. */
+int oracle_chart(const float* v, const float* probes, int64_t m, int32_t P, float* chart) {
+  if (!v || !probes || !chart || m <= 0 || P < 1) return 1;
+  for (int64_t i = 0; i < m; ++i) {
+    float av = fabsf(v[i]);
+    for (int32_t k = 0; k < P; ++k) chart[i * P + k] = av * probes[i * P + k];
+  }
+  return 0;
+}
+
+/* "cutoff = topK(cutoff_chart, effort)" in the [HN] pseudocode: effort is the
+   fraction of the chart that lies at or above the cutoff.  K rounds up so the
+   kept fraction never falls below effort; the cutoff is the K-th largest chart
+   value (a value, so ties need no rule).  A full descending sort stands in for
+   a selection. */
+int oracle_cutoff(const float* chart, int64_t N, float effort, int64_t* K, float* cutoff,
+                  int64_t* Kprime) {
+  if (!chart || N <= 0 || !(effort > 0.0f) || !(effort <= 1.0f)) return 1;
+  double kd = ceil((double)effort * (double)N);
+  int64_t k = (int64_t)kd;
+  if (k < 1) k = 1;
+  if (k > N) k = N;
+  float* s = (float*)malloc((size_t)N * sizeof(float));
+  if (!s) return 1;
+  memcpy(s, chart, (size_t)N * sizeof(float));
+  qsort(s, (size_t)N, sizeof(float), cmp_f32_desc);
+  float c = s[k - 1];
+  free(s);
+  int64_t kp = 0;
+  for (int64_t t = 0; t < N; ++t) kp += (chart[t] >= c);
+  if (K) *K = k;
+  if (cutoff) *cutoff = c;
+  if (Kprime) *Kprime = kp;
+  return 0;
+}
+
+/* bucketMul of the [HN] pseudocode, done without buckets: every product whose
+   fp32 magnitude reaches the cutoff is kept (O(effort * inDim * outDim)
+   multiplications in the real method, [HT]); kept products are scattered into
+   the output ("multiply it by 256, and add it into the output vector at the 3rd
+   row", the passage bigcat12345678 quotes).  Here all m*n pairs are swept. */
+int oracle_keep_sum(const uint16_t* W, int64_t m, int64_t n, const float* v, float cutoff,
+                    double* y_double, int64_t* row_kept, uint64_t* fingerprint, uint8_t* mask,
+                    int64_t* total_kept) {
+  if (!W || !v || !y_double || m <= 0 || n <= 0) return 1;
+  for (int64_t j = 0; j < n; ++j) y_double[j] = 0.0;
+  uint64_t fp = 0;
+  int64_t total = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    float av = fabsf(v[i]);
+    double vi = (double)v[i];
+    int64_t cnt = 0;
+    for (int64_t j = 0; j < n; ++j) {
+      uint16_t h = W[i * n + j];
+      float p = av * magnitude_f32(h);
+      int keep = (p >= cutoff);
+      if (mask) mask[i * n + j] = (uint8_t)keep;
+      if (keep) {
+        y_double[j] += vi * oracle_f16_to_f64(h);
+        fp += oracle_pair_hash((uint64_t)(i * n + j));
+        ++cnt;
+      }
+    }
+    if (row_kept) row_kept[i] = cnt;
+    total += cnt;
+  }
+  if (fingerprint) *fingerprint = fp;
+  if (total_kept) *total_kept = total;
+  return 0;
+}
+
+int oracle_run(const uint16_t* W, int64_t m, int64_t n, const float* probes, int32_t P,
+               const float* v, float effort, float* cutoff, int64_t* K, int64_t* Kprime,
+               double* y_double, int64_t* row_kept, int64_t* row_chart_kept,
+               uint64_t* fingerprint, uint8_t* mask, int64_t* total_kept) {
+  if (!W || !probes || !v || !y_double || m <= 0 || n <= 0 || P < 1 || P > n) return 1;
+  int64_t N = m * P;
+  float* chart = (float*)malloc((size_t)N * sizeof(float));
+  if (!chart) return 1;
+  int rc = oracle_chart(v, probes, m, P, chart);
+  float c = 0.0f;
+  if (!rc) rc = oracle_cutoff(chart, N, effort, K, &c, Kprime);
+  if (!rc && row_chart_kept) {
+    for (int64_t i = 0; i < m; ++i) {
+      int64_t cnt = 0;
+      for (int32_t k = 0; k < P; ++k) cnt += (chart[i * P + k] >= c);
+      row_chart_kept[i] = cnt;
+    }
+  }
+  free(chart);
+  if (rc) return rc;
+  if (cutoff) *cutoff = c;
+  return oracle_keep_sum(W, m, n, v, c, y_double, row_kept, fingerprint, mask, total_kept);
+}
+
+int oracle_dense(const uint16_t* W, int64_t m, int64_t n, const float* v, double* y_double) {
+  if (!W || !v || !y_double || m <= 0 || n <= 0) return 1;
+  for (int64_t j = 0; j < n; ++j) y_double[j] = 0.0;
+  for (int64_t i = 0; i < m; ++i) {
+    double vi = (double)v[i];
+    for (int64_t j = 0; j < n; ++j) y_double[j] += vi * oracle_f16_to_f64(W[i * n + j]);
+  }
+  return 0;
+}

@@ -1,0 +1,367 @@
+// api.cpp -- C ABI of libeffort: argument validation, workspace carving and
+// kernel launches.  Every check happens before the first enqueue.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "effort.h"
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace effort {
+int prepare_host(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t groups, void* layout,
+                 uint64_t layout_bytes, effort_desc* desc_out);
+uint64_t blob_checksum(const void* blob, uint64_t total);
+}  // namespace effort
+
+using namespace effort;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // device property cache (immutable per device)
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (dev < kMaxDevices) g_cu_count[dev] = cus;
+  return cus;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_desc(const effort_desc* d, Geometry* g) {
+  if (!d) return EFFORT_EINVAL;
+  if (d->magic != EFFORT_MAGIC || d->version != EFFORT_VERSION) return EFFORT_ECORRUPT;
+  if (d->desc_check != desc_check_of(*d)) return EFFORT_ECORRUPT;
+  if (!geometry_from_desc(d, g)) return EFFORT_ECORRUPT;
+  return EFFORT_OK;
+}
+
+bool effort_ok(float e) { return e > 0.0f && e <= 1.0f; }  // false for NaN
+
+uint32_t k_of(float effort, int64_t N) {
+  double k = ceil((double)effort * (double)N);
+  if (k < 1.0) k = 1.0;
+  if (k > (double)N) k = (double)N;
+  return (uint32_t)k;
+}
+
+struct DebugOut {
+  float* cutoff;
+  int64_t* K;
+  int32_t* row_kept;
+  uint64_t* fingerprint;
+  uint8_t* mask;
+};
+
+// One vector: select, dispatch, bucketMul on `s`.
+int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
+            uint8_t* ws, hipStream_t s, const DebugOut* dbg, hipEvent_t const* ev) {
+  const WsLayout w = ws_layout(g);
+  uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + w.ctrl);
+  uint32_t* result = reinterpret_cast<uint32_t*>(ws + w.result);
+  uint32_t* rowctr = reinterpret_cast<uint32_t*>(ws + w.rowctr);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist);
+  float* chart = reinterpret_cast<float*>(ws + w.chart);
+  uint32_t* thresh = reinterpret_cast<uint32_t*>(ws + w.thresh);
+  uint32_t* runlen = reinterpret_cast<uint32_t*>(ws + w.runlen);
+  const uint16_t* probes = reinterpret_cast<const uint16_t*>(layout + g.off_probes);
+  const uint32_t* counts = reinterpret_cast<const uint32_t*>(layout + g.off_counts);
+  const uint32_t* entries = reinterpret_cast<const uint32_t*>(layout + g.off_entries);
+  hipError_t e;
+
+  if (dbg) {
+    if (dbg->row_kept && (e = launch_zero_bytes(dbg->row_kept, (uint64_t)g.m * 4, s)) != hipSuccess)
+      return EFFORT_EHIP;
+    if (dbg->fingerprint && (e = launch_zero_bytes(dbg->fingerprint, 8, s)) != hipSuccess)
+      return EFFORT_EHIP;
+    if (dbg->mask && (e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)) != hipSuccess)
+      return EFFORT_EHIP;
+  }
+
+  if (ev && ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return EFFORT_EHIP;
+  SelectArgs sa;
+  sa.v = v;
+  sa.probes = probes;
+  sa.m = g.m;
+  sa.P = g.P;
+  sa.K = k_of(effort, g.m * (int64_t)g.P);
+  sa.done = ctrl;
+  sa.hist = hist;
+  sa.chart = chart;
+  sa.result = result;
+  sa.y = y;
+  sa.n = g.n;
+  sa.rows_per_block = g.P >= 1024 ? 1 : 1024 / g.P;
+  if ((e = launch_select(sa, s)) != hipSuccess) return EFFORT_EHIP;
+
+  if (ev && ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return EFFORT_EHIP;
+  DispatchArgs da;
+  da.v = v;
+  da.probes = probes;
+  da.counts = counts;
+  da.result = result;
+  da.thresh = thresh;
+  da.runlen = runlen;
+  da.rowctr = rowctr;
+  da.row_chart_kept = nullptr;
+  da.m = g.m;
+  da.P = g.P;
+  da.G = g.G;
+  if ((e = launch_dispatch(da, s)) != hipSuccess) return EFFORT_EHIP;
+
+  if (ev && ev[2] && hipEventRecord(ev[2], s) != hipSuccess) return EFFORT_EHIP;
+  MulArgs ma;
+  ma.v = v;
+  ma.entries = entries;
+  ma.thresh = thresh;
+  ma.runlen = runlen;
+  ma.rowctr = rowctr;
+  ma.y = y;
+  ma.m = g.m;
+  ma.n = g.n;
+  ma.row_stride = g.row_stride;
+  ma.G = g.G;
+  ma.TW = g.TW;
+  ma.row_kept = dbg ? dbg->row_kept : nullptr;
+  ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
+  ma.mask = dbg ? dbg->mask : nullptr;
+  const bool record = dbg && (dbg->row_kept || dbg->fingerprint || dbg->mask);
+  int bpg = (2 * cu_count() + g.G - 1) / g.G;
+  if ((int64_t)bpg > g.m) bpg = (int)g.m;
+  if (bpg < 1) bpg = 1;
+  if ((e = launch_bucketmul(ma, record, bpg, s)) != hipSuccess) return EFFORT_EHIP;
+  if (ev && ev[3] && hipEventRecord(ev[3], s) != hipSuccess) return EFFORT_EHIP;
+
+  if (dbg && (dbg->cutoff || dbg->K) &&
+      launch_debug_result(result, dbg->cutoff, dbg->K, s) != hipSuccess)
+    return EFFORT_EHIP;
+  return EFFORT_OK;
+}
+
+int matvec_common(const effort_desc* desc, const void* layout_dev, const float* v_dev, int32_t batch,
+                  float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream,
+                  const DebugOut* dbg, void* const* events) {
+  Geometry g;
+  int rc = check_desc(desc, &g);
+  if (rc) return rc;
+  if (!layout_dev || !v_dev || !y_dev || !ws_dev) return EFFORT_EINVAL;
+  if (!aligned(layout_dev, 256) || !aligned(ws_dev, 256) || !aligned(v_dev, 4) || !aligned(y_dev, 4))
+    return EFFORT_EINVAL;
+  if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
+  if (!effort_ok(effort)) return EFFORT_EINVAL;
+  const WsLayout w = ws_layout(g);
+  if (ws_bytes < w.slice * (uint64_t)batch) return EFFORT_ENOSPACE;
+  if (dbg) {
+    if (dbg->K && !aligned(dbg->K, 8)) return EFFORT_EINVAL;
+    if (dbg->fingerprint && !aligned(dbg->fingerprint, 8)) return EFFORT_EINVAL;
+    if (dbg->row_kept && !aligned(dbg->row_kept, 4)) return EFFORT_EINVAL;
+    if (dbg->cutoff && !aligned(dbg->cutoff, 4)) return EFFORT_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* layout = static_cast<const uint8_t*>(layout_dev);
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  for (int32_t b = 0; b < batch; ++b) {
+    rc = run_one(g, layout, v_dev + (int64_t)b * g.m, effort, y_dev + (int64_t)b * g.n,
+                 ws + (uint64_t)b * w.slice, s, dbg, reinterpret_cast<hipEvent_t const*>(events));
+    if (rc) return rc;
+  }
+  return EFFORT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* effort_strerror(int status) {
+  switch (status) {
+    case EFFORT_OK: return "ok";
+    case EFFORT_EINVAL: return "invalid argument";
+    case EFFORT_ENOSPACE: return "buffer too small";
+    case EFFORT_EHIP: return "HIP error";
+    case EFFORT_EUNSUPPORTED: return "unsupported";
+    case EFFORT_ECORRUPT: return "corrupt descriptor or layout";
+    default: return "unknown status";
+  }
+}
+
+int32_t effort_default_groups(int64_t out_dim) { return default_groups(out_dim); }
+
+int effort_layout_bytes_ex(int64_t in_dim, int64_t out_dim, int32_t P, int32_t groups, uint64_t* bytes) {
+  if (!bytes) return EFFORT_EINVAL;
+  Geometry g;
+  int rc = make_geometry(in_dim, out_dim, P, groups, &g);
+  if (rc) return rc;
+  *bytes = g.total;
+  return EFFORT_OK;
+}
+
+int effort_layout_bytes(int64_t in_dim, int64_t out_dim, int32_t P, uint64_t* bytes) {
+  return effort_layout_bytes_ex(in_dim, out_dim, P, 0, bytes);
+}
+
+int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* bytes) {
+  if (!bytes) return EFFORT_EINVAL;
+  Geometry g;
+  int rc = check_desc(desc, &g);
+  if (rc) return rc;
+  if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
+  *bytes = ws_layout(g).slice * (uint64_t)batch;
+  return EFFORT_OK;
+}
+
+int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream) {
+  if (!ws_dev || !aligned(ws_dev, 256)) return EFFORT_EINVAL;
+  return launch_zero_bytes(ws_dev, ws_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EFFORT_OK
+             : EFFORT_EHIP;
+}
+
+int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                           int32_t groups, void* layout_host, uint64_t layout_bytes,
+                           effort_desc* desc_out) {
+  return prepare_host(w_fp16, in_dim, out_dim, P, groups, layout_host, layout_bytes, desc_out);
+}
+
+int effort_prepare_host(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                        void* layout_host, uint64_t layout_bytes, effort_desc* desc_out) {
+  return prepare_host(w_fp16, in_dim, out_dim, P, 0, layout_host, layout_bytes, desc_out);
+}
+
+int effort_prepare(const uint16_t* w_fp16_host, int64_t in_dim, int64_t out_dim, int32_t P,
+                   void* layout_dev, uint64_t layout_bytes, effort_desc* desc_out, void* stream) {
+  if (!w_fp16_host || !layout_dev || !desc_out || !aligned(layout_dev, 256)) return EFFORT_EINVAL;
+  Geometry g;
+  int rc = make_geometry(in_dim, out_dim, P, 0, &g);
+  if (rc) return rc;
+  if (layout_bytes < g.total) return EFFORT_ENOSPACE;
+  void* tmp = aligned_alloc(256, (size_t)g.total);
+  if (!tmp) return EFFORT_ENOSPACE;
+  rc = prepare_host(w_fp16_host, in_dim, out_dim, P, 0, tmp, g.total, desc_out);
+  if (!rc) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(layout_dev, tmp, (size_t)g.total, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      rc = EFFORT_EHIP;
+  }
+  free(tmp);
+  return rc;
+}
+
+int effort_layout_check(const effort_desc* desc, const void* layout_host) {
+  Geometry g;
+  int rc = check_desc(desc, &g);
+  if (rc) return rc;
+  if (!layout_host || !aligned(layout_host, 8)) return EFFORT_EINVAL;
+  if (memcmp(layout_host, desc, sizeof *desc) != 0) return EFFORT_ECORRUPT;
+  if (blob_checksum(layout_host, g.total) != desc->checksum) return EFFORT_ECORRUPT;
+  return EFFORT_OK;
+}
+
+int effort_matvec(const effort_desc* desc, const void* layout_dev, const float* v_dev, float effort,
+                  float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream) {
+  return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws_dev, ws_bytes, stream, nullptr,
+                       nullptr);
+}
+
+int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                          int32_t batch, float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
+                          void* stream) {
+  return matvec_common(desc, layout_dev, v_dev, batch, effort, y_dev, ws_dev, ws_bytes, stream,
+                       nullptr, nullptr);
+}
+
+int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                        float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
+                        float* cutoff_dev, int64_t* K_dev, int32_t* row_kept_dev,
+                        uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, void* stream) {
+  DebugOut d{cutoff_dev, K_dev, row_kept_dev, fingerprint_dev, kept_mask_dev};
+  return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws_dev, ws_bytes, stream, &d,
+                       nullptr);
+}
+
+int effort_matvec_timed(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                        float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream,
+                        void* const* events) {
+  return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws_dev, ws_bytes, stream, nullptr,
+                       events);
+}
+
+int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_t out_dim,
+               float* y_dev, void* stream) {
+  if (!w_dev || !v_dev || !y_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
+  if (!aligned(w_dev, 2) || !aligned(v_dev, 4) || !aligned(y_dev, 4)) return EFFORT_EINVAL;
+  const int64_t strips = (out_dim + 63) / 64;
+  const int cus = cu_count();
+  int rs = 1;
+  if (strips < cus) {
+    int64_t want = (2 * cus + strips - 1) / strips;
+    int64_t cap = (in_dim + 255) / 256;
+    rs = (int)(want < cap ? want : cap);
+    if (rs < 1) rs = 1;
+  }
+  return launch_dense_gemv(w_dev, v_dev, in_dim, out_dim, y_dev, 8, rs,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EFFORT_OK
+             : EFFORT_EHIP;
+}
+
+int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, int64_t in_dim,
+                     int64_t out_dim, float* y_dev, void* stream) {
+  if (!w_dev || !v_dev || !y_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
+  if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
+  if (!aligned(w_dev, 2) || !aligned(v_dev, 4) || !aligned(y_dev, 4)) return EFFORT_EINVAL;
+  return launch_dense_gemm_small(w_dev, v_dev, batch, in_dim, out_dim, y_dev,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EFFORT_OK
+             : EFFORT_EHIP;
+}
+
+int effort_silu_mul(const float* h1_dev, const float* h3_dev, int64_t n, float* out_dev, void* stream) {
+  if (!h1_dev || !h3_dev || !out_dev || n < 1) return EFFORT_EINVAL;
+  if (!aligned(h1_dev, 4) || !aligned(h3_dev, 4) || !aligned(out_dev, 4)) return EFFORT_EINVAL;
+  return launch_silu_mul(h1_dev, h3_dev, n, out_dev, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EFFORT_OK
+             : EFFORT_EHIP;
+}
+
+int effort_event_create(void** event_out) {
+  if (!event_out) return EFFORT_EINVAL;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return EFFORT_EHIP;
+  *event_out = e;
+  return EFFORT_OK;
+}
+
+int effort_event_record(void* event, void* stream) {
+  if (!event) return EFFORT_EINVAL;
+  return hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EFFORT_OK
+             : EFFORT_EHIP;
+}
+
+int effort_event_elapsed_ms(void* start, void* end, float* ms_out) {
+  if (!start || !end || !ms_out) return EFFORT_EINVAL;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(end)) != hipSuccess) return EFFORT_EHIP;
+  return hipEventElapsedTime(ms_out, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end)) ==
+                 hipSuccess
+             ? EFFORT_OK
+             : EFFORT_EHIP;
+}
+
+int effort_event_destroy(void* event) {
+  if (!event) return EFFORT_EINVAL;
+  return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? EFFORT_OK : EFFORT_EHIP;
+}
+
+int effort_stream_synchronize(void* stream) {
+  return hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess ? EFFORT_OK : EFFORT_EHIP;
+}
+
+}  // extern "C"

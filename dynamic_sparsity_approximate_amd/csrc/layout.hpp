@@ -1,0 +1,125 @@
+// layout.hpp -- geometry of the prepared weight layout and of the workspace.
+//
+// Layout blob (all offsets 256-byte aligned):
+//   [0, 256)        copy of the effort_desc
+//   probes          u16 [m][P]      fp16 magnitude bits at ranks ceil((k+1) n / P)
+//   counts          u32 [m][P][G]   cumulative entries of group g in rank segments 0..k
+//   entries         u32 [m][G*TW]   per row, per group, the group's entries in rank
+//                                   order: low 16 bits = fp16 value bits, high 16
+//                                   bits = column index inside the group
+//
+// Rank order is |w| descending, ties by column ascending.  Segment k of a row is
+// ranks (ceil(k n / P), ceil((k+1) n / P)]; its smallest magnitude is probe k.
+// Because a group's entries are stored in rank order, the entries of one row and
+// group that can pass the keep test form a prefix of its run, and the counts
+// table bounds that prefix by whole segments.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "effort.h"
+
+namespace effort {
+
+constexpr uint64_t kAlign = 256;
+constexpr int32_t kTargetGroupWidth = 2048;
+
+inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+struct Geometry {
+  int64_t m = 0, n = 0;
+  int32_t P = 0, G = 0, TW = 0;
+  int64_t row_stride = 0;
+  uint64_t off_probes = 0, off_counts = 0, off_entries = 0, total = 0;
+};
+
+inline int32_t default_groups(int64_t n) {
+  if (n < 1) return 1;
+  int64_t g = (n + kTargetGroupWidth - 1) / kTargetGroupWidth;
+  return (int32_t)(g < 1 ? 1 : g);
+}
+
+// Fills g from (m, n, P, groups).  groups = 0 picks the default.  The group
+// width is ceil(n / groups) rounded up to 64 columns, and the effective group
+// count is ceil(n / width), so no group is empty.
+inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geometry* g) {
+  if (m < 1 || n < 1 || P < 1 || (int64_t)P > n || groups < 0) return EFFORT_EINVAL;
+  if (m > (1ll << 31) - 1 || n > (1ll << 31) - 1) return EFFORT_EUNSUPPORTED;
+  if ((int64_t)m * P > (1ll << 31) - 1) return EFFORT_EUNSUPPORTED;  // chart size fits u32 counts
+  if (groups == 0) groups = default_groups(n);
+  int64_t tw = (n + groups - 1) / groups;
+  tw = (int64_t)align_up((uint64_t)tw, 64);
+  if (tw > EFFORT_MAX_GROUP_WIDTH) return EFFORT_EUNSUPPORTED;
+  int64_t G = (n + tw - 1) / tw;
+  g->m = m;
+  g->n = n;
+  g->P = P;
+  g->G = (int32_t)G;
+  g->TW = (int32_t)tw;
+  g->row_stride = G * tw;
+  g->off_probes = kAlign;
+  g->off_counts = align_up(g->off_probes + (uint64_t)m * P * 2, kAlign);
+  g->off_entries = align_up(g->off_counts + (uint64_t)m * P * G * 4, kAlign);
+  g->total = align_up(g->off_entries + (uint64_t)m * g->row_stride * 4, kAlign);
+  return EFFORT_OK;
+}
+
+// Workspace of one vector (offsets in bytes from the vector's slice start).
+//   ctrl     u32[64]      [0] done counter of the cutoff kernel
+//   result   u32[8]       [0] cutoff bits, [1] K', [2] K
+//   rowctr   u32[G]       per-group row counters of the multiply
+//   hist     u32[2048]    first-digit histogram of the chart
+//   chart    f32[m*P]
+//   thresh   u32[m]       per-row fp16 magnitude threshold
+//   runlen   u32[G][m]    per (group, row) entries to read
+struct WsLayout {
+  uint64_t ctrl, result, rowctr, hist, chart, thresh, runlen, slice;
+};
+
+inline WsLayout ws_layout(const Geometry& g) {
+  WsLayout w;
+  w.ctrl = 0;
+  w.result = 256;
+  w.rowctr = 512;
+  w.hist = align_up(w.rowctr + (uint64_t)g.G * 4, kAlign);
+  w.chart = align_up(w.hist + 2048 * 4, kAlign);
+  w.thresh = align_up(w.chart + (uint64_t)g.m * g.P * 4, kAlign);
+  w.runlen = align_up(w.thresh + (uint64_t)g.m * 4, kAlign);
+  w.slice = align_up(w.runlen + (uint64_t)g.G * g.m * 4, kAlign);
+  return w;
+}
+
+// FNV-1a-64 over 8-byte little-endian words.
+inline uint64_t fnv1a64_words(const uint64_t* p, uint64_t nwords, uint64_t h = 0xCBF29CE484222325ull) {
+  for (uint64_t i = 0; i < nwords; ++i) {
+    h ^= p[i];
+    h *= 0x100000001B3ull;
+  }
+  return h;
+}
+
+inline uint64_t desc_check_of(const effort_desc& d) {
+  effort_desc c = d;
+  c.desc_check = 0;
+  // hash every byte of the struct before desc_check (padding is zeroed by the writer)
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(&c);
+  uint64_t h = 0xCBF29CE484222325ull;
+  for (size_t i = 0; i < offsetof(effort_desc, desc_check); ++i) {
+    h ^= p[i];
+    h *= 0x100000001B3ull;
+  }
+  return h;
+}
+
+inline bool geometry_from_desc(const effort_desc* d, Geometry* g) {
+  Geometry x;
+  if (make_geometry(d->in_dim, d->out_dim, d->probes_per_row, d->groups, &x) != EFFORT_OK) return false;
+  if (x.G != d->groups || x.TW != d->group_width || x.row_stride != d->row_stride ||
+      x.off_probes != d->off_probes || x.off_counts != d->off_counts ||
+      x.off_entries != d->off_entries || x.total != d->total_bytes || d->index_bytes != 2)
+    return false;
+  *g = x;
+  return true;
+}
+
+}  // namespace effort

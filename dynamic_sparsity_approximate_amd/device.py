@@ -1,0 +1,87 @@
+"""A prepared matrix resident in HBM with its own workspace (torch owns the memory)."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+
+
+class EffortMatrix:
+    """Layout of one fp16 matrix W[in][out] on a device, ready for effort_matvec.
+
+    The host converter runs once; the blob is copied to device memory once; each
+    call then reads only the device copy.  `batch` sizes the workspace.
+    """
+
+    def __init__(self, w_fp16, P: int = 16, groups: int = 0, device="cuda", batch: int = 1):
+        import torch
+
+        self.desc, blob = B.effort_prepare_host(w_fp16, P, groups)
+        self.in_dim = int(self.desc.in_dim)
+        self.out_dim = int(self.desc.out_dim)
+        self.P = int(self.desc.probes_per_row)
+        self.groups = int(self.desc.groups)
+        self.layout_bytes = int(self.desc.total_bytes)
+        self.layout = torch.from_numpy(blob).to(device)
+        self.batch = batch
+        self.ws_bytes = B.effort_workspace_bytes(self.desc, batch)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    @classmethod
+    def from_blob(cls, desc, layout_dev, batch: int = 1):
+        """Wrap an existing device copy of a prepared blob (shares `layout_dev`)."""
+        import torch
+
+        self = cls.__new__(cls)
+        self.desc = desc
+        self.in_dim, self.out_dim = int(desc.in_dim), int(desc.out_dim)
+        self.P, self.groups = int(desc.probes_per_row), int(desc.groups)
+        self.layout_bytes = int(desc.total_bytes)
+        self.layout = layout_dev
+        self.batch = batch
+        self.ws_bytes = B.effort_workspace_bytes(desc, batch)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=layout_dev.device)
+        return self
+
+    def matvec(self, v, effort: float, y=None, stream=None):
+        import torch
+
+        if y is None:
+            y = torch.empty(self.out_dim, dtype=torch.float32, device=v.device)
+        B.effort_matvec(self.desc, self.layout, v, effort, y, self.ws, self.ws_bytes, stream)
+        return y
+
+    def matvec_batched(self, v, effort: float, y=None, stream=None):
+        import torch
+
+        b = v.shape[0]
+        if y is None:
+            y = torch.empty((b, self.out_dim), dtype=torch.float32, device=v.device)
+        B.effort_matvec_batched(self.desc, self.layout, v, b, effort, y, self.ws, self.ws_bytes, stream)
+        return y
+
+    def matvec_debug(self, v, effort: float, with_mask: bool = True, stream=None) -> dict:
+        import torch
+
+        dev = v.device
+        y = torch.empty(self.out_dim, dtype=torch.float32, device=dev)
+        cutoff = torch.empty(1, dtype=torch.float32, device=dev)
+        K = torch.empty(2, dtype=torch.int64, device=dev)
+        row_kept = torch.empty(self.in_dim, dtype=torch.int32, device=dev)
+        fp = torch.empty(1, dtype=torch.int64, device=dev)
+        mask = (torch.empty((self.in_dim, self.out_dim), dtype=torch.uint8, device=dev)
+                if with_mask else None)
+        B.effort_matvec_debug(self.desc, self.layout, v, effort, y, self.ws, self.ws_bytes, cutoff, K,
+                              row_kept, fp, mask, stream)
+        torch.cuda.synchronize(dev)
+        out = {
+            "y": y.cpu().numpy(),
+            "cutoff": cutoff.cpu().numpy()[0],
+            "K": int(K[0].item()),
+            "Kprime": int(K[1].item()),
+            "row_kept": row_kept.cpu().numpy().astype(np.int64),
+            "fingerprint": int(fp.cpu().numpy().view(np.uint64)[0]),
+            "mask": mask.cpu().numpy() if mask is not None else None,
+        }
+        out["total_kept"] = int(out["row_kept"].sum())
+        return out

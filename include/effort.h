@@ -1,0 +1,189 @@
+/*
+ * effort.h -- C ABI of the MI355X (gfx950) implementation of the "Effort"
+ * approximate vector-matrix multiply ("bucketMul").
+ *
+ * Method (web pages, cited by title and passage):
+ *  [HN] "Show HN: Speeding up LLM inference 2x times (possibly)", Hacker News
+ *       thread: the quoted pseudocode precompute(W) / approxMul(v, ...) in the
+ *       exchange with gcy; the sorted (index, value) row storage in the author's
+ *       reply to bigcat12345678; the 16-part row split of bucketMul in the reply
+ *       to marmaduke; effort as a per-call knob "in real time" in the post text.
+ *  [HT] hntin item 40095016: cost O(effort*inDim*outDim) multiplications,
+ *       O(inDim) dispatch, O(inDim log inDim) cutoff.
+ *
+ * y = v . W computed from only the products whose magnitude reaches a cutoff:
+ *   W      fp16 [in_dim][out_dim], row i multiplies v_i (the stored matrix is
+ *          the transposed weight, "W = W.T" in the precompute of [HN]).
+ *   probes per row, P magnitudes at ranks ceil((k+1) out_dim / P) of the row
+ *          sorted by |w| descending.
+ *   K      min(N, max(1, ceil(effort * N))) in double, N = in_dim * P.
+ *   cutoff K-th largest of fl32(|v_i| * probe_i[k]) ("topK(cutoff_chart, effort)").
+ *   kept   (i, j) with fl32(|v_i| * |W_ij|) >= cutoff.
+ *   y_j    sum of v_i * W_ij over kept (i, j), accumulated in fp32.
+ *
+ * Conventions for every function:
+ *  - returns int: EFFORT_OK (0) or an error code; effort_strerror() names it.
+ *  - pointers are plain host or device pointers as stated per argument; the
+ *    caller owns all memory.  The library never allocates device memory and
+ *    keeps no global mutable state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
+ *    work is stream-ordered and asynchronous unless stated otherwise.
+ *  - every argument is validated on the host before anything is enqueued, so
+ *    EINVAL / ENOSPACE / ECORRUPT leave the stream untouched.
+ *  - device pointers must be 16-byte aligned; the layout 256-byte aligned.
+ */
+#ifndef EFFORT_H
+#define EFFORT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  EFFORT_OK = 0,
+  EFFORT_EINVAL = 1,      /* null / misaligned pointer, bad size, effort not in (0,1], non-finite W */
+  EFFORT_ENOSPACE = 2,    /* a caller buffer (layout, workspace) is too small */
+  EFFORT_EHIP = 3,        /* a HIP call or kernel launch failed */
+  EFFORT_EUNSUPPORTED = 4,/* valid request this build does not handle (e.g. group too wide) */
+  EFFORT_ECORRUPT = 5     /* descriptor or layout header fails its magic/version/checksum */
+};
+
+#define EFFORT_MAGIC 0x4F464645u /* "EFFO" little-endian */
+#define EFFORT_VERSION 1u
+#define EFFORT_MAX_GROUP_WIDTH 8192 /* output columns per group (fp32 LDS tile of 32 KiB) */
+#define EFFORT_MAX_BATCH 16
+
+/* Host-side descriptor of a prepared layout; filled by effort_prepare*, passed
+   by pointer to the multiply.  Plain old data; a copy is stored at the start of
+   the layout blob. */
+typedef struct effort_desc {
+  uint32_t magic, version;
+  int64_t in_dim, out_dim;    /* m, n */
+  int32_t probes_per_row;     /* P, 1 <= P <= n */
+  int32_t groups;             /* G: output-column groups */
+  int32_t group_width;        /* TW: columns per group, multiple of 64; last group may be narrower */
+  int32_t index_bytes;        /* bytes of the in-group column index of an entry (2) */
+  int64_t row_stride;         /* entries per stored row = G * TW */
+  uint64_t off_probes;        /* byte offsets inside the layout */
+  uint64_t off_counts;
+  uint64_t off_entries;
+  uint64_t total_bytes;
+  uint64_t checksum;          /* FNV-1a-64 over the blob's 8-byte words after the header */
+  uint64_t desc_check;        /* FNV-1a-64 over all fields above */
+} effort_desc;
+
+/* Name of a status code (static string). */
+const char* effort_strerror(int status);
+
+/* ---------------------------------------------------------------- sizing (host only, no HIP calls) */
+
+/* Default number of output-column groups for out_dim columns. */
+int32_t effort_default_groups(int64_t out_dim);
+
+/* Bytes of the layout of an in_dim x out_dim matrix with P probes per row and
+   `groups` output groups (0 = effort_default_groups(out_dim)).
+   EINVAL: in_dim < 1, out_dim < 1, P not in [1, out_dim], bytes NULL.
+   EUNSUPPORTED: the resulting group width exceeds EFFORT_MAX_GROUP_WIDTH. */
+int effort_layout_bytes(int64_t in_dim, int64_t out_dim, int32_t P, uint64_t* bytes);
+int effort_layout_bytes_ex(int64_t in_dim, int64_t out_dim, int32_t P, int32_t groups,
+                           uint64_t* bytes);
+
+/* Device workspace for one call of effort_matvec* with `batch` vectors
+   (1 <= batch <= EFFORT_MAX_BATCH).  The workspace must be zero-filled before
+   its first use (effort_workspace_init); every call leaves it ready for the
+   next.  One workspace serves one call at a time. */
+int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* bytes);
+
+/* Zero-fill `ws_bytes` of device memory at ws_dev (stream-ordered). */
+int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- offline converter ("precompute" of [HN]) */
+
+/* Host fp16 bits W[in_dim][out_dim] (y = v . W) -> host layout blob.
+   Per row: entries sorted by |w| descending (ties: column ascending), grouped by
+   output-column group; each entry is (fp16 value, 16-bit column index within
+   its group); P probes (fp16 magnitudes); per (row, probe segment, group) the
+   cumulative entry count.  layout_host: host memory of >= layout_bytes bytes,
+   8-byte aligned.  desc_out: host.  EINVAL also for non-finite W. */
+int effort_prepare_host(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                        void* layout_host, uint64_t layout_bytes, effort_desc* desc_out);
+int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                           int32_t groups, void* layout_host, uint64_t layout_bytes,
+                           effort_desc* desc_out);
+
+/* Same, then copies the blob into caller-owned device memory layout_dev on
+   `stream`.  Uses a temporary host buffer and synchronizes `stream` before
+   returning. */
+int effort_prepare(const uint16_t* w_fp16_host, int64_t in_dim, int64_t out_dim, int32_t P,
+                   void* layout_dev, uint64_t layout_bytes, effort_desc* desc_out, void* stream);
+
+/* Checks a host layout blob against its descriptor (magic, version,
+   descriptor check, blob checksum).  ECORRUPT on mismatch. */
+int effort_layout_check(const effort_desc* desc, const void* layout_host);
+
+/* ---------------------------------------------------------------- hot path ("approxMul" of [HN]) */
+
+/* y_dev[out_dim] = approximate v_dev[in_dim] . W at the given effort.
+   layout_dev: device copy of the prepared blob.  v_dev: device fp32.  y_dev:
+   device fp32, overwritten (zeroed by the call).  ws_dev: device workspace of
+   >= effort_workspace_bytes(desc, 1) bytes.  effort in (0, 1], else EINVAL.
+   v must be finite (precondition, not checked). */
+int effort_matvec(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                  float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* `batch` independent vectors v_dev[batch][in_dim] -> y_dev[batch][out_dim],
+   each with its own K, cutoff and kept set.  ws >= effort_workspace_bytes(desc, batch). */
+int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                          int32_t batch, float effort, float* y_dev, void* ws_dev,
+                          uint64_t ws_bytes, void* stream);
+
+/* effort_matvec plus parity outputs (all device pointers; each may be NULL):
+   cutoff_dev[1]        cutoff value;
+   K_dev[2]             K and K' = #{chart >= cutoff};
+   row_kept_dev[in_dim] kept products per row;
+   fingerprint_dev[1]   sum over kept (i,j) of splitmix64-output(i*out_dim+j), mod 2^64;
+   kept_mask_dev        uint8 [in_dim][out_dim], 1 where kept.
+   Same kernels as effort_matvec with the recording switched on; untimed. */
+int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                        float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
+                        float* cutoff_dev, int64_t* K_dev, int32_t* row_kept_dev,
+                        uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, void* stream);
+
+/* effort_matvec that also records hipEvent_t events[0..3] (each may be NULL) on
+   `stream`: before the cutoff kernel, before the dispatch kernel, before the
+   bucketMul kernel, after it.  For measurement. */
+int effort_matvec_timed(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                        float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
+                        void* stream, void* const* events);
+
+/* ---------------------------------------------------------------- comparators and glue */
+
+/* Dense y_dev[out_dim] = v_dev[in_dim] . W, W fp16 [in_dim][out_dim] row-major on
+   the device, fp32 accumulation.  The dense matvec the approximate one is
+   measured against ([HN]: the author's comparison with a dense matmul). */
+int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_t out_dim,
+               float* y_dev, void* stream);
+
+/* Dense y_dev[batch][out_dim] = v_dev[batch][in_dim] . W, 1 <= batch <= EFFORT_MAX_BATCH. */
+int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, int64_t in_dim,
+                     int64_t out_dim, float* y_dev, void* stream);
+
+/* out[i] = silu(h1[i]) * h3[i], silu(x) = x / (1 + exp(-x)): the gate of a
+   gated feed-forward block between its approximate matvecs. */
+int effort_silu_mul(const float* h1_dev, const float* h3_dev, int64_t n, float* out_dev,
+                    void* stream);
+
+/* ---------------------------------------------------------------- measurement helpers */
+
+int effort_event_create(void** event_out);            /* hipEvent_t with timing */
+int effort_event_record(void* event, void* stream);
+int effort_event_elapsed_ms(void* start, void* end, float* ms_out); /* waits for `end` */
+int effort_event_destroy(void* event);
+int effort_stream_synchronize(void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EFFORT_H */

@@ -1,0 +1,268 @@
+"""Host-side tests of libeffort: exported symbols, validation, and the layout.
+
+No GPU is needed: sizing, the converter and every argument check run before
+any HIP call.  The layout checks decode the prepared blob with numpy and
+compare it with the input matrix and with the oracle's probes and kept sets.
+"""
+import ctypes
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "dynamic_sparsity_approximate_amd", "libeffort.so")
+if not os.path.exists(LIB):
+    subprocess.check_call([sys.executable, "-m", "dynamic_sparsity_approximate_amd.build"], cwd=ROOT)
+
+import dynamic_sparsity_approximate_amd as E  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from dynamic_sparsity_approximate_amd import binding as B  # noqa: E402
+
+
+def rand_case(m, n, seed, tag="abi"):
+    W = synth.weights(m, n, seed=seed, stream=synth.stream_id(tag, "W", m, n))
+    v = synth.activations(m, seed=seed, stream=synth.stream_id(tag, "v", m))
+    return W, v
+
+
+def decode(desc, blob):
+    m, n, P, G, TW = desc.in_dim, desc.out_dim, desc.probes_per_row, desc.groups, desc.group_width
+    pr = blob[desc.off_probes: desc.off_probes + m * P * 2].view(np.uint16).reshape(m, P)
+    cnt = blob[desc.off_counts: desc.off_counts + m * P * G * 4].view(np.uint32).reshape(m, P, G)
+    ent = blob[desc.off_entries: desc.off_entries + m * desc.row_stride * 4].view(np.uint32)
+    return pr, cnt, ent.reshape(m, desc.row_stride)
+
+
+# ---------------------------------------------------------------- symbols
+
+def test_library_exports_every_declared_function():
+    names = B.header_functions()
+    assert len(names) >= 20
+    lib = ctypes.CDLL(LIB)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_names_codes():
+    assert E.effort_strerror(0) == "ok"
+    assert "invalid" in E.effort_strerror(1)
+    assert E.effort_strerror(99) == "unknown status"
+
+
+# ---------------------------------------------------------------- sizing
+
+def test_layout_bytes_and_groups():
+    assert E.effort_default_groups(14336) == 7
+    assert E.effort_default_groups(1024) == 1
+    assert E.effort_default_groups(32000) == 16
+    m, n, P = 4096, 14336, 16
+    nb = E.effort_layout_bytes(m, n, P)
+    # entries dominate: 4 bytes per weight, plus probes and counts
+    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 7
+    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 7 + 4 * 256
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 10, 1, 0), B.EFFORT_EINVAL), ((10, 0, 1, 0), B.EFFORT_EINVAL),
+    ((10, 10, 0, 0), B.EFFORT_EINVAL), ((10, 10, 11, 0), B.EFFORT_EINVAL),
+    ((10, 10, 1, -1), B.EFFORT_EINVAL), ((10, 100000, 1, 1), B.EFFORT_EUNSUPPORTED),
+    ((2**31, 8, 1, 0), B.EFFORT_EUNSUPPORTED),
+])
+def test_layout_bytes_rejects(args, code):
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_layout_bytes_ex(*args)
+    assert ei.value.code == code
+
+
+def test_group_geometry_covers_columns():
+    for n, g in [(100, 8), (1000, 3), (14336, 8), (641, 2), (64, 64), (8192, 1)]:
+        W, _ = rand_case(2, n, seed=1)
+        d, _ = E.effort_prepare_host(W, 1, g)
+        assert d.group_width % 64 == 0
+        assert (d.groups - 1) * d.group_width < n <= d.groups * d.group_width
+        assert d.row_stride == d.groups * d.group_width
+
+
+# ---------------------------------------------------------------- converter
+
+@pytest.mark.parametrize("m,n,P,G", [(5, 37, 3, 0), (9, 300, 16, 3), (4, 64, 64, 1), (3, 130, 7, 3),
+                                     (16, 256, 16, 0), (1, 1, 1, 0)])
+def test_layout_roundtrip_and_order(m, n, P, G):
+    W, _ = rand_case(m, n, seed=m + n + P)
+    if m > 2:
+        W[1, ::3] = W[1, 0]  # ties
+        W[2, : n // 2] = 0   # zeros
+    d, blob = E.effort_prepare_host(W, P, G)
+    E.effort_layout_check(d, blob)
+    pr, cnt, ent = decode(d, blob)
+    TW = d.group_width
+    # probes are the oracle's order statistics
+    ref = oracle.probes(W, P)
+    assert np.array_equal(pr.view(np.float16).astype(np.float32), ref)
+    for i in range(m):
+        # whole-row rank of each column: |w| descending, column ascending
+        keys = (W[i] & 0x7FFF).astype(np.int64)
+        order = np.lexsort((np.arange(n), -keys))
+        rank = np.empty(n, np.int64)
+        rank[order] = np.arange(1, n + 1)
+        seen = np.zeros(n, bool)
+        for g in range(d.groups):
+            width = min(TW, n - g * TW)
+            run = ent[i, g * TW: g * TW + width]
+            vals = (run & 0xFFFF).astype(np.uint16)
+            cols = g * TW + (run >> 16).astype(np.int64)
+            assert np.all((run >> 16) < width)
+            assert np.array_equal(vals, W[i, cols])         # values round-trip
+            assert not seen[cols].any()
+            seen[cols] = True
+            assert np.all(np.diff(rank[cols]) > 0)          # rank order inside the group
+            for k in range(P):
+                Rk = -(-(k + 1) * n // P)
+                assert cnt[i, k, g] == np.sum(rank[cols] <= Rk)
+            assert np.all(ent[i, g * TW + width: (g + 1) * TW] == 0)  # padding
+        assert seen.all()
+
+
+def test_converter_rejects_nonfinite_and_small_buffer():
+    W, _ = rand_case(4, 8, seed=2)
+    W[1, 3] = 0x7C00  # +inf
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_prepare_host(W, 2)
+    assert ei.value.code == B.EFFORT_EINVAL
+    W[1, 3] = 0xFE00  # NaN
+    with pytest.raises(E.EffortError):
+        E.effort_prepare_host(W, 2)
+    W[1, 3] = 0
+    d = E.effort_desc()
+    small = np.zeros(64, np.uint64)
+    rc = B.lib().effort_prepare_host(W.ctypes.data, 4, 8, 2, small.ctypes.data, 512, ctypes.byref(d))
+    assert rc == B.EFFORT_ENOSPACE
+
+
+def test_layout_check_detects_corruption():
+    W, _ = rand_case(8, 40, seed=3)
+    d, blob = E.effort_prepare_host(W, 4)
+    bad = blob.copy()
+    bad[d.off_entries + 17] ^= 1
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_layout_check(d, bad)
+    assert ei.value.code == B.EFFORT_ECORRUPT
+    d2 = d.copy()
+    d2.magic ^= 1
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_layout_check(d2, blob)
+    assert ei.value.code == B.EFFORT_ECORRUPT
+    d3 = d.copy()
+    d3.out_dim += 1  # descriptor check fails
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_layout_check(d3, blob)
+    assert ei.value.code == B.EFFORT_ECORRUPT
+
+
+# ---------------------------------------------------------------- layout walk against the oracle
+
+def _threshold(av, cutoff):
+    """Smallest fp16 magnitude key k with fl32(av * k) >= cutoff (0x7C00: none), by bisection."""
+    keys = np.arange(0x7C00, dtype=np.uint16)
+    mags = keys.view(np.float16).astype(np.float32)
+    ok = (np.float32(av) * mags) >= np.float32(cutoff)
+    idx = np.nonzero(ok)[0]
+    return int(idx[0]) if idx.size else 0x7C00
+
+
+@pytest.mark.parametrize("m,n,P,G,effort", [(64, 300, 16, 3, 0.25), (32, 128, 4, 2, 0.6),
+                                            (48, 200, 200, 1, 0.1), (20, 70, 1, 2, 0.5)])
+def test_run_prefix_contains_exactly_the_kept_entries(m, n, P, G, effort):
+    """The (row, group) read length the multiply uses covers every kept entry,
+    and the keep test on the key equals the oracle's product test."""
+    W, v = rand_case(m, n, seed=P)
+    d, blob = E.effort_prepare_host(W, P, G)
+    pr, cnt, ent = decode(d, blob)
+    ref = oracle.run(W, oracle.probes(W, P), v, effort, mask=True)
+    TW = d.group_width
+    for i in range(m):
+        t = _threshold(abs(v[i]), ref["cutoff"])
+        q = int(np.sum(pr[i] >= t))
+        assert q == ref["row_chart_kept"][i]
+        for g in range(d.groups):
+            width = min(TW, n - g * TW)
+            L = int(cnt[i, min(q, P - 1), g])
+            run = ent[i, g * TW: g * TW + width]
+            keep = (run & 0x7FFF) >= t
+            cols = g * TW + (run >> 16).astype(np.int64)
+            assert np.array_equal(keep, ref["mask"][i, cols].astype(bool))
+            assert not keep[L:].any()
+            # kept entries form a prefix of the run
+            assert np.all(keep[: keep.sum()])
+
+
+# ---------------------------------------------------------------- matvec validation (no HIP call is reached)
+
+def _desc_and_blob():
+    W, _ = rand_case(16, 64, seed=4)
+    return E.effort_prepare_host(W, 4)
+
+
+FAKE = 1 << 40  # 256-aligned fake device address: never dereferenced, validation fails first
+
+
+@pytest.mark.parametrize("effort", [0.0, -1.0, 1.5, float("nan"), float("inf")])
+def test_matvec_rejects_effort(effort):
+    d, _ = _desc_and_blob()
+    ws = E.effort_workspace_bytes(d, 1)
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_matvec(d, FAKE, FAKE, effort, FAKE, FAKE, ws)
+    assert ei.value.code == B.EFFORT_EINVAL
+
+
+def test_matvec_rejects_bad_buffers_and_descriptors():
+    d, _ = _desc_and_blob()
+    ws = E.effort_workspace_bytes(d, 1)
+    cases = [
+        (dict(layout=None), B.EFFORT_EINVAL),
+        (dict(v=None), B.EFFORT_EINVAL),
+        (dict(y=None), B.EFFORT_EINVAL),
+        (dict(ws=None), B.EFFORT_EINVAL),
+        (dict(layout=FAKE + 16), B.EFFORT_EINVAL),
+        (dict(ws=FAKE + 8), B.EFFORT_EINVAL),
+        (dict(v=FAKE + 2), B.EFFORT_EINVAL),
+        (dict(ws_bytes=ws - 1), B.EFFORT_ENOSPACE),
+    ]
+    for over, code in cases:
+        a = dict(layout=FAKE, v=FAKE, y=FAKE, ws=FAKE, ws_bytes=ws)
+        a.update(over)
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_matvec(d, a["layout"], a["v"], 0.25, a["y"], a["ws"], a["ws_bytes"])
+        assert ei.value.code == code, over
+    for field in ("magic", "version", "groups", "desc_check", "off_entries"):
+        d2 = d.copy()
+        setattr(d2, field, getattr(d2, field) + 1)
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_matvec(d2, FAKE, FAKE, 0.25, FAKE, FAKE, ws)
+        assert ei.value.code == B.EFFORT_ECORRUPT, field
+    for batch in (0, 17):
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_matvec_batched(d, FAKE, FAKE, batch, 0.25, FAKE, FAKE, ws * 17)
+        assert ei.value.code == B.EFFORT_EINVAL
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_matvec_batched(d, FAKE, FAKE, 4, 0.25, FAKE, FAKE, 4 * ws - 1)
+    assert ei.value.code == B.EFFORT_ENOSPACE
+    assert E.effort_workspace_bytes(d, 4) == 4 * ws
+    with pytest.raises(E.EffortError):
+        E.effort_workspace_bytes(d, 0)
+
+
+def test_dense_and_glue_validation():
+    for args in [(None, FAKE, 4, 4, FAKE), (FAKE, FAKE, 0, 4, FAKE), (FAKE, FAKE, 4, 0, FAKE),
+                 (FAKE + 1, FAKE, 4, 4, FAKE)]:
+        with pytest.raises(E.EffortError) as ei:
+            E.dense_gemv(*args)
+        assert ei.value.code == B.EFFORT_EINVAL
+    with pytest.raises(E.EffortError):
+        E.dense_gemm_small(FAKE, FAKE, 17, 4, 4, FAKE)
+    with pytest.raises(E.EffortError):
+        E.effort_silu_mul(FAKE, FAKE, 0, FAKE)

@@ -1,0 +1,231 @@
+"""GPU parity: libeffort against the oracle on the same seeded inputs.
+
+Contract checked on every case:
+  * cutoff bit-equal (uint32 pattern), K and K' equal;
+  * kept set equal: per-row kept counts and the 64-bit order-free fingerprint,
+    plus the full uint8 mask where the case says so;
+  * y within rel-L2 <= 1e-3 of the oracle's double-precision sums (the GPU
+    accumulates in fp32 with atomics in no fixed order); if the oracle's y is
+    exactly zero, |y_gpu| <= 1e-30.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_TOL = 1e-3
+
+torch = pytest.importorskip("torch")
+import dynamic_sparsity_approximate_amd as E  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(y, ref):
+    ref = np.asarray(ref, np.float64)
+    y = np.asarray(y, np.float64)
+    nr = np.linalg.norm(ref)
+    if nr == 0.0:
+        return 0.0 if np.max(np.abs(y), initial=0.0) <= 1e-30 else np.inf
+    return float(np.linalg.norm(y - ref) / nr)
+
+
+def check(got, ref, with_mask=True, where=""):
+    assert np.float32(got["cutoff"]).view(np.uint32) == np.float32(ref["cutoff"]).view(np.uint32), \
+        (where, got["cutoff"], ref["cutoff"])
+    assert got["K"] == ref["K"] and got["Kprime"] == ref["Kprime"], where
+    assert np.array_equal(got["row_kept"], ref["row_kept"]), where
+    assert got["fingerprint"] == ref["fingerprint"], where
+    if with_mask:
+        assert np.array_equal(got["mask"], ref["mask"]), where
+    err = rel_l2(got["y"], ref["y"])
+    assert err <= REL_L2_TOL, (where, err)
+    return err
+
+
+def case(m, n, seed, tag):
+    W = synth.weights(m, n, seed=seed, stream=synth.stream_id(tag, "W", m, n))
+    v = synth.activations(m, seed=seed, stream=synth.stream_id(tag, "v", m))
+    return W, v
+
+
+def run_pair(W, v, P, effort, groups=0, with_mask=True, where=""):
+    d = dev()
+    M = E.EffortMatrix(W, P=P, groups=groups, device=d)
+    vt = torch.from_numpy(np.ascontiguousarray(v)).to(d)
+    got = M.matvec_debug(vt, effort, with_mask=with_mask)
+    ref = oracle.run(W, oracle.probes(W, P), v, effort, mask=with_mask)
+    return check(got, ref, with_mask, where)
+
+
+# ---------------------------------------------------------------- small cases (full mask)
+
+def test_hand_example():
+    import json
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    W = np.array(g["W"], dtype=np.float16).view(np.uint16)
+    v = np.array(g["v"], dtype=np.float32)
+    M = E.EffortMatrix(W, P=g["P"], device=dev())
+    vt = torch.from_numpy(v).to(dev())
+    for c in g["cases"]:
+        got = M.matvec_debug(vt, c["effort"])
+        assert float(got["cutoff"]) == c["cutoff"]
+        assert got["K"] == c["K"] and got["Kprime"] == c["Kprime"]
+        assert got["mask"].tolist() == c["mask"]
+        assert np.allclose(got["y"], c["y"], rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("P", [16, 1, 256])
+@pytest.mark.parametrize("effort", [1.0, 0.5, 0.25])
+def test_config0(P, effort):
+    """256 x 256, W ~ N(0, 0.02) fp16, v ~ 0.5 Student-t(3), seed 0."""
+    W = synth.matrix("config0", 256, 256, seed=0)
+    v = synth.vector("config0", 256, seed=0)
+    say("config0 P=%d effort=%g" % (P, effort))
+    run_pair(W, v, P, effort, where="config0")
+
+
+@pytest.mark.parametrize("m,n,P,G", [(300, 1000, 16, 0), (1, 1, 1, 0), (7, 65, 3, 2),
+                                     (513, 2049, 16, 3), (64, 8192, 8, 1), (100, 100, 100, 0),
+                                     (2, 5000, 5, 0), (1000, 3, 2, 0), (257, 300, 16, 5)])
+@pytest.mark.parametrize("effort", [0.05, 0.3, 1.0])
+def test_ragged_shapes(m, n, P, G, effort):
+    W, v = case(m, n, seed=m + n, tag="ragged")
+    say("ragged m=%d n=%d P=%d G=%d effort=%g" % (m, n, P, G, effort))
+    run_pair(W, v, P, effort, groups=G, where="ragged")
+
+
+def test_degenerate_inputs():
+    d = dev()
+    # zero vector: cutoff 0 keeps everything, y = 0
+    W, v = case(64, 200, seed=1, tag="degen")
+    run_pair(W, np.zeros(64, np.float32), 8, 0.25, where="zero v")
+    # equal magnitudes everywhere: whole rows tie
+    We = np.full((32, 96), np.float16(0.5).view(np.uint16), np.uint16)
+    We[::3] |= 0x8000
+    run_pair(We, np.linspace(-2, 2, 32).astype(np.float32), 4, 0.3, where="ties")
+    # fp16 subnormal and zero weights
+    Ws = W.copy()
+    Ws[:, ::2] &= 0x83FF
+    Ws[:, 1::7] = 0
+    run_pair(Ws, v, 8, 0.4, where="subnormal")
+    # one dominant activation, tiny effort (K = 1)
+    v2 = v.copy() * 1e-3
+    v2[5] = 40.0
+    run_pair(W, v2, 8, 1e-7, where="K=1")
+    # activations that are exactly zero in some rows
+    v3 = v.copy()
+    v3[::2] = 0.0
+    run_pair(W, v3, 16, 0.5, where="zero rows")
+    del d
+
+
+def test_repeat_calls_and_workspace_reuse():
+    W, v = case(512, 3000, seed=3, tag="repeat")
+    M = E.EffortMatrix(W, P=16, device=dev())
+    vt = torch.from_numpy(v).to(dev())
+    a = M.matvec_debug(vt, 0.25)
+    b = M.matvec_debug(vt, 1.0)
+    c = M.matvec_debug(vt, 0.25)
+    assert np.float32(a["cutoff"]) == np.float32(c["cutoff"])
+    assert np.array_equal(a["mask"], c["mask"]) and a["fingerprint"] == c["fingerprint"]
+    assert b["total_kept"] == W.size
+    assert rel_l2(a["y"], c["y"]) < 1e-6
+    # the timed entry point (no recording) gives the same y
+    y = M.matvec(vt, 0.25)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), a["y"]) < 1e-6
+
+
+def test_batched_matches_single_vectors():
+    d = dev()
+    W = synth.matrix("batched", 1024, 2048, seed=0)
+    M = E.EffortMatrix(W, P=16, device=d, batch=5)
+    V = np.stack([synth.vector("batched", 1024, seed=s) for s in range(5)])
+    Y = M.matvec_batched(torch.from_numpy(V).to(d), 0.25)
+    torch.cuda.synchronize()
+    pr = oracle.probes(W, 16)
+    for b in range(5):
+        ref = oracle.run(W, pr, V[b], 0.25)
+        assert rel_l2(Y[b].cpu().numpy(), ref["y"]) <= REL_L2_TOL
+
+
+# ---------------------------------------------------------------- comparators and glue
+
+@pytest.mark.parametrize("m,n", [(256, 256), (4096, 1024), (300, 1001), (1, 8), (77, 4100)])
+def test_dense_gemv(m, n):
+    d = dev()
+    W, v = case(m, n, seed=7, tag="dense")
+    Wt = torch.from_numpy(W.view(np.int16)).to(d)
+    y = torch.empty(n, dtype=torch.float32, device=d)
+    E.dense_gemv(Wt, torch.from_numpy(v).to(d), m, n, y)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), oracle.dense(W, v)) <= 1e-5
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 5, 16])
+def test_dense_gemm_small(b):
+    d = dev()
+    m, n = 512, 1100
+    W = synth.matrix("gemm", m, n, seed=0)
+    V = np.stack([synth.vector("gemm", m, seed=s) for s in range(b)])
+    Y = torch.empty((b, n), dtype=torch.float32, device=d)
+    E.dense_gemm_small(torch.from_numpy(W.view(np.int16)).to(d), torch.from_numpy(V).to(d), b, m, n, Y)
+    torch.cuda.synchronize()
+    for i in range(b):
+        assert rel_l2(Y[i].cpu().numpy(), oracle.dense(W, V[i])) <= 1e-5
+
+
+def test_silu_mul():
+    d = dev()
+    h1 = synth.activations(10000, seed=1, stream=5) * 4
+    h3 = synth.activations(10000, seed=2, stream=6)
+    out = torch.empty(10000, dtype=torch.float32, device=d)
+    E.effort_silu_mul(torch.from_numpy(h1).to(d), torch.from_numpy(h3).to(d), 10000, out)
+    torch.cuda.synchronize()
+    assert rel_l2(out.cpu().numpy(), oracle.silu_mul(h1, h3)) <= 1e-6
+
+
+# ---------------------------------------------------------------- Mistral-7B-shaped matrices
+
+SHAPES = [(4096, 4096), (4096, 1024), (4096, 14336), (14336, 4096)]
+_probe_cache = {}
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_mistral_shapes(shape):
+    """Full-size matrices in the configuration the benchmark times (P = 16,
+    default groups): every effort of the sweep, full mask on seed 0, counts and
+    fingerprint on seed 1."""
+    d = dev()
+    m, n = shape
+    W = synth.matrix("config1", m, n, seed=0)
+    say("shape %dx%d: oracle probes" % (m, n))
+    pr = oracle.probes(W, 16)
+    M = E.EffortMatrix(W, P=16, device=d)
+    for seed in (0, 1):
+        v = synth.vector("config1", m, seed=seed)
+        vt = torch.from_numpy(v).to(d)
+        for effort in (1.0, 0.5, 0.25, 0.125):
+            with_mask = seed == 0
+            say("shape %dx%d seed %d effort %g" % (m, n, seed, effort))
+            got = M.matvec_debug(vt, effort, with_mask=with_mask)
+            ref = oracle.run(W, pr, v, effort, mask=with_mask)
+            err = check(got, ref, with_mask, where="%dx%d/%d/%g" % (m, n, seed, effort))
+            say("  ok kept=%.4f relL2=%.2e" % (ref["total_kept"] / W.size, err))

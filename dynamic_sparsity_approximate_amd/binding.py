@@ -26,7 +26,10 @@ EFFORT_MAX_GROUP_WIDTH = 8192
 class EffortError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__("%s: %s (status %d)" % (where, effort_strerror(code), code))
+        msg = "%s: %s (status %d)" % (where, effort_strerror(code), code)
+        if code == EFFORT_EHIP:
+            msg += ": " + effort_last_hip_error()
+        super().__init__(msg)
 
 
 class effort_desc(ctypes.Structure):
@@ -48,13 +51,22 @@ class effort_desc(ctypes.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libeffort.so is not built (python -m dynamic_sparsity_approximate_amd.build)")
+    raise ImportError("libeffort.so is not built (python dynamic_sparsity_approximate_amd/build.py)")
+# One HIP runtime per process: torch ships its own libamdhip64 (soname
+# libamdhip64.so.7, loaded by the file name libamdhip64.so).  Loading torch first
+# lets libeffort's dependency on libamdhip64.so.7 resolve to that same copy;
+# loading libeffort first would bring in a second runtime that sees no device.
+try:
+    import torch  # noqa: F401
+except ImportError:  # C-only use: the system runtime is the only one
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 _p, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
 _D = ctypes.POINTER(effort_desc)
 _PROTOS = {
     "effort_strerror": ([ctypes.c_int], ctypes.c_char_p),
+    "effort_last_hip_error": ([], ctypes.c_char_p),
     "effort_default_groups": ([_i64], _i32),
     "effort_layout_bytes": ([_i64, _i64, _i32, ctypes.POINTER(_u64)], ctypes.c_int),
     "effort_layout_bytes_ex": ([_i64, _i64, _i32, _i32, ctypes.POINTER(_u64)], ctypes.c_int),
@@ -125,6 +137,10 @@ def _check(rc: int, where: str):
 
 def effort_strerror(status: int) -> str:
     return _lib.effort_strerror(status).decode()
+
+
+def effort_last_hip_error() -> str:
+    return _lib.effort_last_hip_error().decode()
 
 
 def effort_default_groups(out_dim: int) -> int:

@@ -1,6 +1,6 @@
 """Build libeffort.so (HIP for gfx950 + host C++) in-tree with hipcc.
 
-    python -m dynamic_sparsity_approximate_amd.build
+    python dynamic_sparsity_approximate_amd/build.py
 """
 from __future__ import annotations
 

@@ -20,6 +20,14 @@ using namespace effort;
 namespace {
 
 constexpr int kMaxDevices = 64;
+thread_local hipError_t t_last_hip_error = hipSuccess;  // what effort_last_hip_error() reports
+
+// Records a failed HIP status for effort_last_hip_error().
+bool hip_failed(hipError_t e) {
+  if (e == hipSuccess) return false;
+  t_last_hip_error = e;
+  return true;
+}
 int g_cu_count[kMaxDevices];  // device property cache (immutable per device)
 
 int cu_count() {
@@ -32,6 +40,8 @@ int cu_count() {
   if (dev < kMaxDevices) g_cu_count[dev] = cus;
   return cus;
 }
+
+int status_of(hipError_t e) { return hip_failed(e) ? EFFORT_EHIP : EFFORT_OK; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -77,15 +87,15 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   hipError_t e;
 
   if (dbg) {
-    if (dbg->row_kept && (e = launch_zero_bytes(dbg->row_kept, (uint64_t)g.m * 4, s)) != hipSuccess)
+    if (dbg->row_kept && hip_failed(e = launch_zero_bytes(dbg->row_kept, (uint64_t)g.m * 4, s)))
       return EFFORT_EHIP;
-    if (dbg->fingerprint && (e = launch_zero_bytes(dbg->fingerprint, 8, s)) != hipSuccess)
+    if (dbg->fingerprint && hip_failed(e = launch_zero_bytes(dbg->fingerprint, 8, s)))
       return EFFORT_EHIP;
-    if (dbg->mask && (e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)) != hipSuccess)
+    if (dbg->mask && hip_failed(e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)))
       return EFFORT_EHIP;
   }
 
-  if (ev && ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return EFFORT_EHIP;
+  if (ev && ev[0] && hip_failed(hipEventRecord(ev[0], s))) return EFFORT_EHIP;
   SelectArgs sa;
   sa.v = v;
   sa.probes = probes;
@@ -99,9 +109,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   sa.y = y;
   sa.n = g.n;
   sa.rows_per_block = g.P >= 1024 ? 1 : 1024 / g.P;
-  if ((e = launch_select(sa, s)) != hipSuccess) return EFFORT_EHIP;
+  if (hip_failed(e = launch_select(sa, s))) return EFFORT_EHIP;
 
-  if (ev && ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return EFFORT_EHIP;
+  if (ev && ev[1] && hip_failed(hipEventRecord(ev[1], s))) return EFFORT_EHIP;
   DispatchArgs da;
   da.v = v;
   da.probes = probes;
@@ -114,9 +124,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   da.m = g.m;
   da.P = g.P;
   da.G = g.G;
-  if ((e = launch_dispatch(da, s)) != hipSuccess) return EFFORT_EHIP;
+  if (hip_failed(e = launch_dispatch(da, s))) return EFFORT_EHIP;
 
-  if (ev && ev[2] && hipEventRecord(ev[2], s) != hipSuccess) return EFFORT_EHIP;
+  if (ev && ev[2] && hip_failed(hipEventRecord(ev[2], s))) return EFFORT_EHIP;
   MulArgs ma;
   ma.v = v;
   ma.entries = entries;
@@ -136,11 +146,11 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   int bpg = (2 * cu_count() + g.G - 1) / g.G;
   if ((int64_t)bpg > g.m) bpg = (int)g.m;
   if (bpg < 1) bpg = 1;
-  if ((e = launch_bucketmul(ma, record, bpg, s)) != hipSuccess) return EFFORT_EHIP;
-  if (ev && ev[3] && hipEventRecord(ev[3], s) != hipSuccess) return EFFORT_EHIP;
+  if (hip_failed(e = launch_bucketmul(ma, record, bpg, s))) return EFFORT_EHIP;
+  if (ev && ev[3] && hip_failed(hipEventRecord(ev[3], s))) return EFFORT_EHIP;
 
   if (dbg && (dbg->cutoff || dbg->K) &&
-      launch_debug_result(result, dbg->cutoff, dbg->K, s) != hipSuccess)
+      hip_failed(launch_debug_result(result, dbg->cutoff, dbg->K, s)))
     return EFFORT_EHIP;
   return EFFORT_OK;
 }
@@ -178,6 +188,8 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
 }  // namespace
 
 extern "C" {
+
+const char* effort_last_hip_error(void) { return hipGetErrorName(t_last_hip_error); }
 
 const char* effort_strerror(int status) {
   switch (status) {
@@ -218,9 +230,7 @@ int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* byt
 
 int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream) {
   if (!ws_dev || !aligned(ws_dev, 256)) return EFFORT_EINVAL;
-  return launch_zero_bytes(ws_dev, ws_bytes, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? EFFORT_OK
-             : EFFORT_EHIP;
+  return status_of(launch_zero_bytes(ws_dev, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
@@ -246,8 +256,8 @@ int effort_prepare(const uint16_t* w_fp16_host, int64_t in_dim, int64_t out_dim,
   rc = prepare_host(w_fp16_host, in_dim, out_dim, P, 0, tmp, g.total, desc_out);
   if (!rc) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(layout_dev, tmp, (size_t)g.total, hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess)
+    if (hip_failed(hipMemcpyAsync(layout_dev, tmp, (size_t)g.total, hipMemcpyHostToDevice, s)) ||
+        hip_failed(hipStreamSynchronize(s)))
       rc = EFFORT_EHIP;
   }
   free(tmp);
@@ -306,10 +316,8 @@ int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_
     rs = (int)(want < cap ? want : cap);
     if (rs < 1) rs = 1;
   }
-  return launch_dense_gemv(w_dev, v_dev, in_dim, out_dim, y_dev, 8, rs,
-                           static_cast<hipStream_t>(stream)) == hipSuccess
-             ? EFFORT_OK
-             : EFFORT_EHIP;
+  return status_of(launch_dense_gemv(w_dev, v_dev, in_dim, out_dim, y_dev, 8, rs,
+                           static_cast<hipStream_t>(stream)));
 }
 
 int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, int64_t in_dim,
@@ -317,51 +325,42 @@ int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, i
   if (!w_dev || !v_dev || !y_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
   if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
   if (!aligned(w_dev, 2) || !aligned(v_dev, 4) || !aligned(y_dev, 4)) return EFFORT_EINVAL;
-  return launch_dense_gemm_small(w_dev, v_dev, batch, in_dim, out_dim, y_dev,
-                                 static_cast<hipStream_t>(stream)) == hipSuccess
-             ? EFFORT_OK
-             : EFFORT_EHIP;
+  return status_of(launch_dense_gemm_small(w_dev, v_dev, batch, in_dim, out_dim, y_dev,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int effort_silu_mul(const float* h1_dev, const float* h3_dev, int64_t n, float* out_dev, void* stream) {
   if (!h1_dev || !h3_dev || !out_dev || n < 1) return EFFORT_EINVAL;
   if (!aligned(h1_dev, 4) || !aligned(h3_dev, 4) || !aligned(out_dev, 4)) return EFFORT_EINVAL;
-  return launch_silu_mul(h1_dev, h3_dev, n, out_dev, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? EFFORT_OK
-             : EFFORT_EHIP;
+  return status_of(launch_silu_mul(h1_dev, h3_dev, n, out_dev, static_cast<hipStream_t>(stream)));
 }
 
 int effort_event_create(void** event_out) {
   if (!event_out) return EFFORT_EINVAL;
   hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return EFFORT_EHIP;
+  if (hip_failed(hipEventCreate(&e))) return EFFORT_EHIP;
   *event_out = e;
   return EFFORT_OK;
 }
 
 int effort_event_record(void* event, void* stream) {
   if (!event) return EFFORT_EINVAL;
-  return hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)) == hipSuccess
-             ? EFFORT_OK
-             : EFFORT_EHIP;
+  return status_of(hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)));
 }
 
 int effort_event_elapsed_ms(void* start, void* end, float* ms_out) {
   if (!start || !end || !ms_out) return EFFORT_EINVAL;
-  if (hipEventSynchronize(static_cast<hipEvent_t>(end)) != hipSuccess) return EFFORT_EHIP;
-  return hipEventElapsedTime(ms_out, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end)) ==
-                 hipSuccess
-             ? EFFORT_OK
-             : EFFORT_EHIP;
+  if (hip_failed(hipEventSynchronize(static_cast<hipEvent_t>(end)))) return EFFORT_EHIP;
+  return status_of(hipEventElapsedTime(ms_out, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end)));
 }
 
 int effort_event_destroy(void* event) {
   if (!event) return EFFORT_EINVAL;
-  return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? EFFORT_OK : EFFORT_EHIP;
+  return status_of(hipEventDestroy(static_cast<hipEvent_t>(event)));
 }
 
 int effort_stream_synchronize(void* stream) {
-  return hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess ? EFFORT_OK : EFFORT_EHIP;
+  return status_of(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

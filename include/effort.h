@@ -77,6 +77,10 @@ typedef struct effort_desc {
 /* Name of a status code (static string). */
 const char* effort_strerror(int status);
 
+/* Name of the last failed HIP status seen by a call of this library on the
+   calling thread ("hipSuccess" if none); explains an EFFORT_EHIP. */
+const char* effort_last_hip_error(void);
+
 /* ---------------------------------------------------------------- sizing (host only, no HIP calls) */
 
 /* Default number of output-column groups for out_dim columns. */

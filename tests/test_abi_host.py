@@ -15,7 +15,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "dynamic_sparsity_approximate_amd", "libeffort.so")
 if not os.path.exists(LIB):
-    subprocess.check_call([sys.executable, "-m", "dynamic_sparsity_approximate_amd.build"], cwd=ROOT)
+    subprocess.check_call([sys.executable, os.path.join(ROOT, "dynamic_sparsity_approximate_amd", "build.py")],
+                          cwd=ROOT)
 
 import dynamic_sparsity_approximate_amd as E  # noqa: E402
 import oracle  # noqa: E402

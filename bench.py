@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark: Effort approximate matvec on one MI355X.
+
+Workload: W 4096 x 14336 fp16 (in x out, Mistral-7B w1/w3 shape) ~ N(0, 0.02),
+v ~ 0.5 Student-t(3) fp32, effort 0.25, batch 1, P = 16 probes per row,
+seeded synthetic data.  A step is one effort_matvec call: cutoff kernel,
+dispatch kernel and the bucketMul stream with its flush.
+
+Timing:
+  * every timed loop cycles over R distinct device copies of the layout (and R
+    vectors), R chosen so a cycle touches >= 1 GiB, so the 256 MB last-level
+    cache cannot serve repeats; the dense comparator cycles over its own copies;
+  * the calls of one cycle are captured once in a HIP graph and the graph is
+    replayed; hipEvents on the replay stream bracket the timed region;
+  * the bucketMul kernel's own duration comes from hipEvents recorded around
+    it (effort_matvec_timed) in eager calls queued behind graph replays.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/matvec + HBM GB/s at effort 0.25, 4096×14336 fp16; speedup vs dense GEMV"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COUNTERS = os.path.join(ROOT, "profiles", "counters_bucketmul_4096x14336_e0.25.txt")
+KERNEL_SRC = os.path.join(ROOT, "dynamic_sparsity_approximate_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--m", type=int, default=4096)
+    ap.add_argument("--n", type=int, default=14336)
+    ap.add_argument("--effort", type=float, default=0.25)
+    ap.add_argument("--P", type=int, default=16)
+    ap.add_argument("--groups", type=int, default=0)
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["full", "effort", "dense", "copy"], default="full",
+                    help="effort/dense: time only that path (for profiler runs); copy: plain "
+                         "1 GiB device copies for counter calibration")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernels_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_counters():
+    """HBM traffic of the bucketMul kernel from the committed rocprofv3 --pmc summary,
+    or None if it is missing or was taken on a different kernels.hip."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernels_sha256") != kernels_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def host_info():
+    info = {"nproc": os.cpu_count()}
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return info
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, g, reps):
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b), (time.perf_counter() - t0) * 1e3
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dynamic_sparsity_approximate_amd as E
+    import synth
+
+    dev = torch.device("cuda:0")
+    m, n, P, effort = args.m, args.n, args.P, args.effort
+    GiB = float(1 << 30)
+
+    if args.mode == "copy":
+        x = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_per_copy": 1 << 30, "copies": 5}))
+        return
+
+    log("generating W %dx%d and converting" % (m, n))
+    W = synth.matrix("config1", m, n, seed=0)
+    t0 = time.perf_counter()
+    M = E.EffortMatrix(W, P=P, groups=args.groups, device=dev)
+    log("layout %.1f MB, G=%d, prepare %.1fs" % (M.layout_bytes / 1e6, M.groups, time.perf_counter() - t0))
+
+    # kept counts of the vectors (parity-path run, untimed)
+    v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
+    kept0 = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
+    call_bytes = 4.0 * kept0
+    R = max(2, int(math.ceil(args.rotate_gib * GiB / call_bytes)))
+    Rd = max(2, int(math.ceil(args.rotate_gib * GiB / (2.0 * m * n))))
+    log("rotation: %d layouts (%.0f MB read per call), %d dense copies" % (R, call_bytes / 1e6, Rd))
+
+    result = {}
+    if args.mode in ("full", "effort"):
+        layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
+        vs = [torch.from_numpy(synth.vector("config1", m, seed=r)).to(dev) for r in range(R)]
+        ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+        kept = []
+        for r in range(R):
+            Mr = E.EffortMatrix.from_blob(M.desc, layouts[r])
+            kept.append(Mr.matvec_debug(vs[r], effort, with_mask=False)["total_kept"])
+        kept_mean = float(np.mean(kept))
+        ws, wsb = M.ws, M.ws_bytes
+
+        def cycle():
+            for r in range(R):
+                E.effort_matvec(M.desc, layouts[r], vs[r], effort, ys[r], ws, wsb)
+
+        for _ in range(3):  # eager warm-up (and JIT of code objects)
+            cycle()
+        torch.cuda.synchronize()
+        g = capture(torch, cycle)
+        wreps = max(1, args.warmup // R)
+        time_replays(torch, g, wreps)
+        reps = max(1, int(math.ceil(args.steps / R)))
+        steps = reps * R
+        log("timing %d steps" % steps)
+        ms, host_ms = time_replays(torch, g, reps)
+        us_per = ms * 1e3 / steps
+
+        # per-stage durations: events around each kernel of R eager calls.  A few
+        # graph replays go first so the GPU is busy while the host enqueues the
+        # eager calls; the eager calls then run back to back.
+        evs = [[E.effort_event_create() for _ in range(4)] for _ in range(R)]
+        head = max(1, int(math.ceil(3000.0 / max(us_per * R, 1.0))))
+        sel, dsp, mul = [], [], []
+        treps = max(1, min(reps, 50))
+        for _ in range(treps):
+            for _ in range(head):
+                g.replay()
+            for r in range(R):
+                E.effort_matvec_timed(M.desc, layouts[r], vs[r], effort, ys[r], ws, wsb, evs[r])
+            torch.cuda.synchronize()
+            for r in range(R):
+                e = evs[r]
+                sel.append(E.effort_event_elapsed_ms(e[0], e[1]))
+                dsp.append(E.effort_event_elapsed_ms(e[1], e[2]))
+                mul.append(E.effort_event_elapsed_ms(e[2], e[3]))
+        mul_us = statistics.mean(mul) * 1e3
+        alg_mul = 4.0 * kept_mean + 4.0 * m + 4.0 * n
+        alg_step = 4.0 * kept_mean + 2.0 * m * P + 4.0 * m + 4.0 * n
+        achieved = alg_mul / (mul_us * 1e-6) / 1e9
+        traffic = read_counters()
+        result.update({
+            "us_per_matvec": us_per,
+            "ms_per_step": ms / steps,
+            "steps": steps,
+            "host_ms": host_ms,
+            "kept_fraction": kept_mean / (m * n),
+            "hbm_gbs": alg_step / (us_per * 1e-6) / 1e9,
+            "stages_us": {"select": statistics.mean(sel) * 1e3, "dispatch": statistics.mean(dsp) * 1e3,
+                          "bucketmul": mul_us},
+            "roofline": {"bound": "hbm", "kernel": "k_bucketmul", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": traffic, "alg_bytes": alg_mul, "kernel_us": mul_us},
+            "rotation": R, "groups": M.groups,
+        })
+        for e in sum(evs, []):
+            E.effort_event_destroy(e)
+        del layouts
+
+    if args.mode in ("full", "dense"):
+        Wd0 = torch.from_numpy(W.view(np.int16)).to(dev)
+        Wds = [Wd0] + [Wd0.clone() for _ in range(Rd - 1)]
+        vds = [torch.from_numpy(synth.vector("config1", m, seed=r)).to(dev) for r in range(Rd)]
+        yds = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(Rd)]
+
+        def dcycle():
+            for r in range(Rd):
+                E.dense_gemv(Wds[r], vds[r], m, n, yds[r])
+
+        for _ in range(3):
+            dcycle()
+        gd = capture(torch, dcycle)
+        time_replays(torch, gd, max(1, args.warmup // Rd))
+        dreps = max(1, int(math.ceil(args.steps / Rd)))
+        dms, _ = time_replays(torch, gd, dreps)
+        dense_us = dms * 1e3 / (dreps * Rd)
+        result["dense_us"] = dense_us
+        result["dense_gbs"] = 2.0 * m * n / (dense_us * 1e-6) / 1e9
+        if "us_per_matvec" in result:
+            result["speedup_vs_dense"] = dense_us / result["us_per_matvec"]
+
+    cpu = None
+    if args.mode == "full" and not args.no_cpu_baseline:
+        import oracle
+
+        log("cpu baseline: oracle probes (untimed precompute)")
+        pr = oracle.probes(W, P)
+        times = []
+        t_end = time.perf_counter() + args.cpu_seconds
+        s = 0
+        while (time.perf_counter() < t_end or len(times) < 3) and s < 100:
+            v = synth.vector("config1", m, seed=s)
+            t = time.perf_counter()
+            oracle.run(W, pr, v, effort)
+            times.append(time.perf_counter() - t)
+            s += 1
+        cpu = {"value": statistics.median(times) * 1e6, "unit": "µs/matvec", "cores": 1,
+               "kind": "oracle",
+               "sample": "oracle.run (single-threaded C, brute-force keep test over all %dx%d "
+                         "products) on %d seeded vectors of the same workload, probes precomputed; "
+                         "median" % (m, n, len(times))}
+        cpu.update(host_info())
+
+    if args.mode == "full":
+        out = {
+            "metric": METRIC, "value": result["us_per_matvec"], "unit": "µs/matvec",
+            "n_gpus": 1, "steps": result["steps"], "warmup": args.warmup,
+            "ms_per_step": result["ms_per_step"], "higher_is_better": False, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32 (fp16 weights)", "data": "synthetic",
+            "config": {"workload": "effort matvec %dx%d fp16, effort %g, batch 1" % (m, n, effort),
+                       "in_dim": m, "out_dim": n, "effort": effort, "P": P,
+                       "groups": result["groups"], "rotation_copies": result["rotation"]},
+            "hbm_gbs": result["hbm_gbs"], "kept_fraction": result["kept_fraction"],
+            "dense_us": result["dense_us"], "dense_gbs": result["dense_gbs"],
+            "speedup_vs_dense": result["speedup_vs_dense"], "stages_us": result["stages_us"],
+            "roofline": result["roofline"], "cpu_baseline": cpu,
+        }
+    else:
+        out = dict(result, mode=args.mode)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -40,7 +40,8 @@ class effort_desc(ctypes.Structure):
         ("group_width", ctypes.c_int32), ("index_bytes", ctypes.c_int32),
         ("row_stride", ctypes.c_int64),
         ("off_probes", ctypes.c_uint64), ("off_counts", ctypes.c_uint64),
-        ("off_entries", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+        ("off_entries", ctypes.c_uint64), ("off_rowmax", ctypes.c_uint64),
+        ("total_bytes", ctypes.c_uint64),
         ("checksum", ctypes.c_uint64), ("desc_check", ctypes.c_uint64),
     ]
 

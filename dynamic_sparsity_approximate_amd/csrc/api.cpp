@@ -43,6 +43,11 @@ int cu_count() {
 
 int status_of(hipError_t e) { return hip_failed(e) ? EFFORT_EHIP : EFFORT_OK; }
 
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int check_desc(const effort_desc* d, Geometry* g) {
@@ -76,11 +81,11 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   const WsLayout w = ws_layout(g);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + w.ctrl);
   uint32_t* result = reinterpret_cast<uint32_t*>(ws + w.result);
-  uint32_t* rowctr = reinterpret_cast<uint32_t*>(ws + w.rowctr);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist);
-  float* chart = reinterpret_cast<float*>(ws + w.chart);
+  uint32_t* boff = reinterpret_cast<uint32_t*>(ws + w.boff);
+  float* sorted = reinterpret_cast<float*>(ws + w.sorted);
   uint32_t* thresh = reinterpret_cast<uint32_t*>(ws + w.thresh);
   uint32_t* runlen = reinterpret_cast<uint32_t*>(ws + w.runlen);
+  uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + w.bsum);
   const uint16_t* probes = reinterpret_cast<const uint16_t*>(layout + g.off_probes);
   const uint32_t* counts = reinterpret_cast<const uint32_t*>(layout + g.off_counts);
   const uint32_t* entries = reinterpret_cast<const uint32_t*>(layout + g.off_entries);
@@ -101,14 +106,14 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   sa.probes = probes;
   sa.m = g.m;
   sa.P = g.P;
-  sa.K = k_of(effort, g.m * (int64_t)g.P);
+  sa.N = g.m * (int64_t)g.P;
+  sa.K = k_of(effort, sa.N);
   sa.done = ctrl;
-  sa.hist = hist;
-  sa.chart = chart;
+  sa.boff = boff;
+  sa.sorted = sorted;
   sa.result = result;
   sa.y = y;
   sa.n = g.n;
-  sa.rows_per_block = g.P >= 1024 ? 1 : 1024 / g.P;
   if (hip_failed(e = launch_select(sa, s))) return EFFORT_EHIP;
 
   if (ev && ev[1] && hip_failed(hipEventRecord(ev[1], s))) return EFFORT_EHIP;
@@ -116,10 +121,11 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   da.v = v;
   da.probes = probes;
   da.counts = counts;
+  da.rowmax = reinterpret_cast<const uint16_t*>(layout + g.off_rowmax);
   da.result = result;
   da.thresh = thresh;
   da.runlen = runlen;
-  da.rowctr = rowctr;
+  da.bsum = bsum;
   da.row_chart_kept = nullptr;
   da.m = g.m;
   da.P = g.P;
@@ -132,19 +138,19 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   ma.entries = entries;
   ma.thresh = thresh;
   ma.runlen = runlen;
-  ma.rowctr = rowctr;
+  ma.bsum = bsum;
   ma.y = y;
   ma.m = g.m;
   ma.n = g.n;
   ma.row_stride = g.row_stride;
   ma.G = g.G;
   ma.TW = g.TW;
+  ma.nbd = (int32_t)((g.m + kDspRows - 1) / kDspRows);
   ma.row_kept = dbg ? dbg->row_kept : nullptr;
   ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
   ma.mask = dbg ? dbg->mask : nullptr;
   const bool record = dbg && (dbg->row_kept || dbg->fingerprint || dbg->mask);
-  int bpg = (2 * cu_count() + g.G - 1) / g.G;
-  if ((int64_t)bpg > g.m) bpg = (int)g.m;
+  int bpg = (cu_count() + g.G - 1) / g.G;
   if (bpg < 1) bpg = 1;
   if (hip_failed(e = launch_bucketmul(ma, record, bpg, s))) return EFFORT_EHIP;
   if (ev && ev[3] && hip_failed(hipEventRecord(ev[3], s))) return EFFORT_EHIP;
@@ -299,6 +305,7 @@ int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const f
 int effort_matvec_timed(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                         float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream,
                         void* const* events) {
+  if (stream_capturing(static_cast<hipStream_t>(stream))) return EFFORT_EUNSUPPORTED;
   return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws_dev, ws_bytes, stream, nullptr,
                        events);
 }

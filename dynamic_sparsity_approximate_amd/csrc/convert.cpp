@@ -26,6 +26,7 @@ static void convert_rows(const uint16_t* W, const Geometry& g, uint8_t* blob, in
   uint16_t* probes = reinterpret_cast<uint16_t*>(blob + g.off_probes);
   uint32_t* counts = reinterpret_cast<uint32_t*>(blob + g.off_counts);
   uint32_t* entries = reinterpret_cast<uint32_t*>(blob + g.off_entries);
+  uint16_t* rowmax = reinterpret_cast<uint16_t*>(blob + g.off_rowmax);
   std::vector<uint64_t> order((size_t)n);
   std::vector<uint32_t> seg_cnt((size_t)P * G);
   std::vector<int64_t> fill((size_t)G);
@@ -35,6 +36,7 @@ static void convert_rows(const uint16_t* W, const Geometry& g, uint8_t* blob, in
     for (int64_t j = 0; j < n; ++j)
       order[j] = ((uint64_t)(0x7FFFu - (row[j] & 0x7FFFu)) << 32) | (uint64_t)j;
     std::sort(order.begin(), order.end());
+    rowmax[i] = (uint16_t)(row[order[0] & 0xFFFFFFFFu] & 0x7FFFu);
     std::fill(seg_cnt.begin(), seg_cnt.end(), 0u);
     std::fill(fill.begin(), fill.end(), 0);
     uint32_t* row_entries = entries + i * g.row_stride;
@@ -79,6 +81,7 @@ static int fill_desc(const Geometry& g, effort_desc* d) {
   d->off_probes = g.off_probes;
   d->off_counts = g.off_counts;
   d->off_entries = g.off_entries;
+  d->off_rowmax = g.off_rowmax;
   d->total_bytes = g.total;
   return EFFORT_OK;
 }

@@ -98,35 +98,79 @@ __device__ void find_from_top(const uint32_t* h, int nb, uint32_t K, uint32_t* t
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 // ---------------------------------------------------------------- cutoff
 
 constexpr int SEL_T = 1024;
-constexpr uint32_t CAND_CAP = 12288;
+constexpr int SEL_PER = SEL_VALS / SEL_T;
+constexpr uint32_t CAND_CAP = 10240;
+
+// Visits every candidate value (chart entries whose exponent field is `ebin`),
+// from LDS when they were gathered there, else from the blocks' sorted slices.
+template <typename F>
+__device__ void for_each_candidate(bool in_lds, const float* cand, uint32_t ncand,
+                                   const SelectArgs& a, uint32_t ebin, int nblocks, F f) {
+  if (in_lds) {
+    for (uint32_t p = threadIdx.x; p < ncand; p += SEL_T) f(__float_as_uint(cand[p]));
+  } else {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int b = wid; b < nblocks; b += SEL_T / 64) {
+      const uint32_t s = a.boff[(size_t)b * (SEL_BINS + 1) + ebin];
+      const uint32_t e = a.boff[(size_t)b * (SEL_BINS + 1) + ebin + 1];
+      const float* src = a.sorted + (size_t)b * SEL_VALS;
+      for (uint32_t p = s + lane; p < e; p += 64) f(__float_as_uint(src[p]));
+    }
+  }
+}
 
 __global__ __launch_bounds__(SEL_T) void k_select(SelectArgs a) {
-  __shared__ uint32_t h[2048];
+  __shared__ uint32_t hist[4096];
+  __shared__ float cand[CAND_CAP];
   __shared__ uint32_t tmp[SEL_T / 64 + 1];
   __shared__ uint32_t sres[8];
-  __shared__ uint32_t cand[CAND_CAP];
   const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * SEL_VALS;
 
   for (int64_t j = (int64_t)blockIdx.x * SEL_T + tid; j < a.n; j += (int64_t)gridDim.x * SEL_T)
     a.y[j] = 0.0f;
-  for (int b = tid; b < 2048; b += SEL_T) h[b] = 0u;
-  __syncthreads();
 
-  // first digit (bits 30..20; bit 31 is the sign, always 0 here) of this block's chart slice
-  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
-  const int64_t r1 = r0 + a.rows_per_block < a.m ? r0 + a.rows_per_block : a.m;
-  for (int64_t e = r0 * a.P + tid; e < r1 * a.P; e += SEL_T) {
-    const int64_t i = e / a.P;
-    const float c = __fmul_rn(fabsf(a.v[i]), h2f(a.probes[e]));
-    a.chart[e] = c;
-    atomicAdd(&h[__float_as_uint(c) >> 20], 1u);
+  // -- every block: chart slice, histogram of the exponent field, slice ordered by bin
+  for (int b = tid; b < 2 * SEL_BINS; b += SEL_T) hist[b] = 0u;
+  __syncthreads();
+  float c[SEL_PER];
+  uint32_t bin[SEL_PER];
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) {
+    const int64_t e = base + tid + j * SEL_T;
+    bin[j] = 0xFFFFFFFFu;
+    if (e < a.N) {
+      c[j] = __fmul_rn(fabsf(a.v[e / a.P]), h2f(a.probes[e]));
+      bin[j] = __float_as_uint(c[j]) >> 23;
+      atomicAdd(&hist[bin[j]], 1u);
+    }
   }
   __syncthreads();
-  for (int b = tid; b < 2048; b += SEL_T)
-    if (h[b]) atomicAdd(&a.hist[b], h[b]);
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<SEL_T>(tid < SEL_BINS ? hist[tid] : 0u, tmp, &tot);
+  uint32_t* boff = a.boff + (size_t)blockIdx.x * (SEL_BINS + 1);
+  if (tid < SEL_BINS) {
+    hist[SEL_BINS + tid] = ex;
+    boff[tid] = ex;
+  }
+  if (tid == 0) boff[SEL_BINS] = tot;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j)
+    if (bin[j] != 0xFFFFFFFFu) cand[atomicAdd(&hist[SEL_BINS + bin[j]], 1u)] = c[j];
+  __syncthreads();
+  for (uint32_t p = tid; p < tot; p += SEL_T) a.sorted[base + p] = cand[p];
   __threadfence();
   __syncthreads();
   if (tid == 0) sres[7] = (atomicAdd(a.done, 1u) == gridDim.x - 1) ? 1u : 0u;
@@ -134,209 +178,407 @@ __global__ __launch_bounds__(SEL_T) void k_select(SelectArgs a) {
   if (sres[7] == 0u) return;
   __threadfence();
 
-  // ---- last block: finish the selection over all m*P chart values
-  for (int b = tid; b < 2048; b += SEL_T)
-    h[b] = __hip_atomic_load(&a.hist[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // -- last block: exponent bin of the K-th largest, then its 23 mantissa bits
+  const int nb = (int)gridDim.x;
+  {
+    const int bn = tid & (SEL_BINS - 1);
+    uint32_t part = 0;
+    for (int b = tid / SEL_BINS; b < nb; b += SEL_T / SEL_BINS) {
+      const uint32_t* bo = a.boff + (size_t)b * (SEL_BINS + 1);
+      part += bo[bn + 1] - bo[bn];
+    }
+    hist[tid] = part;
+  }
   __syncthreads();
-  find_from_top<SEL_T>(h, 2048, a.K, tmp, sres);
-  const uint32_t b1 = sres[0] & 2047u, above1 = sres[1];
-  const uint32_t K1 = a.K - above1;
-  const uint32_t n1 = h[b1];
+  uint32_t tb = 0;
+  if (tid < SEL_BINS) tb = hist[tid] + hist[tid + 256] + hist[tid + 512] + hist[tid + 768];
+  __syncthreads();
+  if (tid < SEL_BINS) hist[tid] = tb;
+  __syncthreads();
+  find_from_top<SEL_T>(hist, SEL_BINS, a.K, tmp, sres);
+  const uint32_t ebin = sres[0] & (SEL_BINS - 1), above0 = sres[1];
+  const uint32_t K1 = a.K - above0;
+  const uint32_t ncand = hist[ebin];
   __syncthreads();
 
-  for (int b = tid; b < 1024; b += SEL_T) h[b] = 0u;
-  if (tid == 0) sres[6] = 0u;
-  __syncthreads();
-  const int64_t N = a.m * (int64_t)a.P;
-  const bool use_cand = n1 <= CAND_CAP;
-  for (int64_t e = tid; e < N; e += SEL_T) {
-    const uint32_t bits = __float_as_uint(a.chart[e]);
-    if ((bits >> 20) == b1) {
-      atomicAdd(&h[(bits >> 10) & 1023u], 1u);
-      if (use_cand) {
-        const uint32_t pos = atomicAdd(&sres[6], 1u);
-        if (pos < CAND_CAP) cand[pos] = bits;
+  // gather the candidates into LDS when they fit
+  const bool in_lds = ncand <= CAND_CAP;
+  if (in_lds) {
+    uint32_t* rs = hist;          // run start inside the block's slice
+    uint32_t* rc = hist + 1024;   // run length
+    uint32_t* ro = hist + 2048;   // destination offset
+    uint32_t run_base = 0;
+    for (int b0 = 0; b0 < nb; b0 += SEL_T) {
+      const int b = b0 + tid;
+      uint32_t s = 0, cnt = 0;
+      if (b < nb) {
+        const uint32_t* bo = a.boff + (size_t)b * (SEL_BINS + 1);
+        s = bo[ebin];
+        cnt = bo[ebin + 1] - s;
       }
+      uint32_t chunk_tot;
+      const uint32_t off = block_excl_scan<SEL_T>(cnt, tmp, &chunk_tot);
+      rs[tid] = s;
+      rc[tid] = cnt;
+      ro[tid] = off;
+      __syncthreads();
+      const int wid = tid >> 6, lane = tid & 63;
+      const int nrun = nb - b0 < SEL_T ? nb - b0 : SEL_T;
+      for (int r = wid; r < nrun; r += SEL_T / 64) {
+        const float* src = a.sorted + (size_t)(b0 + r) * SEL_VALS + rs[r];
+        for (uint32_t p = lane; p < rc[r]; p += 64) cand[run_base + ro[r] + p] = src[p];
+      }
+      run_base += chunk_tot;
+      __syncthreads();
     }
   }
+
+  // mantissa bits 22..11
+  for (int b = tid; b < 4096; b += SEL_T) hist[b] = 0u;
   __syncthreads();
-  find_from_top<SEL_T>(h, 1024, K1, tmp, sres);
-  const uint32_t b2 = sres[0] & 1023u, above2 = sres[1];
-  const uint32_t K2 = K1 - above2;
+  for_each_candidate(in_lds, cand, ncand, a, ebin, nb,
+                     [&](uint32_t bits) { atomicAdd(&hist[(bits >> 11) & 4095u], 1u); });
+  __syncthreads();
+  find_from_top<SEL_T>(hist, 4096, K1, tmp, sres);
+  const uint32_t dA = sres[0] & 4095u, aboveA = sres[1];
+  const uint32_t K2 = K1 - aboveA;
   __syncthreads();
 
-  for (int b = tid; b < 1024; b += SEL_T) h[b] = 0u;
+  // mantissa bits 10..0
+  for (int b = tid; b < 2048; b += SEL_T) hist[b] = 0u;
   __syncthreads();
-  const uint32_t pre = (b1 << 10) | b2;
-  if (use_cand) {
-    for (uint32_t e = tid; e < n1 && e < CAND_CAP; e += SEL_T) {
-      const uint32_t bits = cand[e];
-      if ((bits >> 10) == pre) atomicAdd(&h[bits & 1023u], 1u);
-    }
-  } else {
-    for (int64_t e = tid; e < N; e += SEL_T) {
-      const uint32_t bits = __float_as_uint(a.chart[e]);
-      if ((bits >> 10) == pre) atomicAdd(&h[bits & 1023u], 1u);
-    }
-  }
+  for_each_candidate(in_lds, cand, ncand, a, ebin, nb, [&](uint32_t bits) {
+    if (((bits >> 11) & 4095u) == dA) atomicAdd(&hist[bits & 2047u], 1u);
+  });
   __syncthreads();
-  find_from_top<SEL_T>(h, 1024, K2, tmp, sres);
-  const uint32_t b3 = sres[0] & 1023u, above3 = sres[1];
+  find_from_top<SEL_T>(hist, 2048, K2, tmp, sres);
+  const uint32_t dB = sres[0] & 2047u, aboveB = sres[1];
   if (tid == 0) {
-    a.result[0] = (pre << 10) | b3;
-    a.result[1] = above1 + above2 + above3 + h[b3];
+    a.result[0] = (ebin << 23) | (dA << 11) | dB;
+    a.result[1] = above0 + aboveA + aboveB + hist[dB];
     a.result[2] = a.K;
     *a.done = 0u;
   }
-  for (int b = tid; b < 2048; b += SEL_T) a.hist[b] = 0u;
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const int64_t blocks = (a.m + a.rows_per_block - 1) / a.rows_per_block;
+  const int64_t blocks = (a.N + SEL_VALS - 1) / SEL_VALS;
   hipLaunchKernelGGL(k_select, dim3((unsigned)blocks), dim3(SEL_T), 0, s, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- dispatch
 
-constexpr int DSP_T = 256;
-
-__global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
-  if (blockIdx.x == 0)
-    for (int g = threadIdx.x; g < a.G; g += DSP_T) a.rowctr[g] = 0u;
-  const int64_t i = (int64_t)blockIdx.x * DSP_T + threadIdx.x;
-  if (i >= a.m) return;
-  const float c = __uint_as_float(a.result[0]);
-  const float av = fabsf(a.v[i]);
-  // smallest finite fp16 magnitude key whose product with |v_i| reaches the
-  // cutoff (0x7C00 = none); the product is monotone in the key
-  uint32_t lo = 0u, hi = 0x7C00u;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (__fmul_rn(av, h2f(mid)) >= c)
-      hi = mid;
-    else
-      lo = mid + 1u;
+__global__ __launch_bounds__(DSP_ROWS) void k_dispatch(DispatchArgs a) {
+  __shared__ uint32_t red[DSP_ROWS / 64];
+  __shared__ float redf[DSP_ROWS / 64];
+  const int64_t i = (int64_t)blockIdx.x * DSP_ROWS + threadIdx.x;
+  const bool valid = i < a.m;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int G1 = a.G + 1;
+  uint32_t t = 0x7C00u;
+  int32_t q = 0;
+  bool none = true;  // no entry of the row can pass
+  float bound = 0.0f;
+  if (valid) {
+    const float c = __uint_as_float(a.result[0]);
+    const float av = fabsf(a.v[i]);
+    const uint32_t rmax = a.rowmax[i];
+    bound = av * h2f(rmax);
+    // smallest finite fp16 magnitude key whose product with |v_i| reaches the
+    // cutoff (0x7C00 = none); the product is monotone in the key
+    uint32_t lo = 0u, hi = 0x7C00u;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (__fmul_rn(av, h2f(mid)) >= c)
+        hi = mid;
+      else
+        lo = mid + 1u;
+    }
+    t = lo;
+    none = rmax < t;
+    // q = probes (descending keys) at or above the threshold = fully kept
+    // segments; segment q (if any) is the one that is partly kept
+    const uint16_t* pr = a.probes + i * a.P;
+    int32_t qlo = 0, qhi = a.P;
+    while (qlo < qhi) {
+      const int32_t mid = (qlo + qhi) >> 1;
+      if ((uint32_t)pr[mid] >= t)
+        qlo = mid + 1;
+      else
+        qhi = mid;
+    }
+    q = qlo;
+    a.thresh[i] = t;
+    if (a.row_chart_kept) a.row_chart_kept[i] = q;
   }
-  const uint32_t t = lo;
-  // q = number of probes (descending keys) at or above the threshold = number of
-  // fully kept segments; segment q (if any) is the one that is partly kept
-  const uint16_t* pr = a.probes + i * a.P;
-  int32_t qlo = 0, qhi = a.P;
-  while (qlo < qhi) {
-    const int32_t mid = (qlo + qhi) >> 1;
-    if ((uint32_t)pr[mid] >= t)
-      qlo = mid + 1;
-    else
-      qhi = mid;
-  }
-  const int32_t q = qlo;
   const int32_t qc = q < a.P ? q : a.P - 1;
-  const uint32_t* cr = a.counts + ((size_t)i * a.P + qc) * a.G;
-  for (int g = 0; g < a.G; ++g) a.runlen[(size_t)g * a.m + i] = cr[g];
-  a.thresh[i] = t;
-  if (a.row_chart_kept) a.row_chart_kept[i] = q;
+  const uint32_t* cr = a.counts + ((size_t)(valid ? i : 0) * a.P + qc) * a.G;
+  for (int g = 0; g < a.G; ++g) {
+    const uint32_t L = (valid && !none) ? cr[g] : 0u;
+    if (valid) a.runlen[(size_t)g * a.m + i] = L;
+    const uint32_t s = wave_sum(L);
+    if (lane == 0) red[wid] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t tot = 0;
+      for (int w = 0; w < DSP_ROWS / 64; ++w) tot += red[w];
+      a.bsum[(size_t)blockIdx.x * G1 + g] = tot;
+    }
+    __syncthreads();
+  }
+  // bound on |any sum of products| of these rows
+  float bs = bound;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) bs += __shfl_xor(bs, off, 64);
+  if (lane == 0) redf[wid] = bs;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.0f;
+    for (int w = 0; w < DSP_ROWS / 64; ++w) tot += redf[w];
+    a.bsum[(size_t)blockIdx.x * G1 + a.G] = __float_as_uint(tot);
+  }
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
-  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, a);
+  const int64_t blocks = (a.m + DSP_ROWS - 1) / DSP_ROWS;
+  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_ROWS), 0, s, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- bucketMul
 
-constexpr int MUL_T = 512;
+constexpr int MUL_T = 1024;
+constexpr int MUL_W = MUL_T / 64;
+
+// Finds, among `count` non-negative values x[0..count) (x(j) loads one), the
+// index j with prefix(j) <= target < prefix(j) + x[j] and x[j] > 0; returns
+// j and prefix(j).  Wave-uniform; requires target < sum.
+template <typename X>
+__device__ __forceinline__ void wave_locate(uint32_t count, uint32_t target, X x, uint32_t* idx,
+                                            uint32_t* before) {
+  const int lane = threadIdx.x & 63;
+  uint32_t acc = 0;
+  for (uint32_t j0 = 0; j0 < count; j0 += 64) {
+    const uint32_t j = j0 + lane;
+    const uint32_t s = j < count ? x(j) : 0u;
+    const uint32_t inc = wave_incl_scan(s);
+    const uint32_t lo = acc + inc - s;
+    const unsigned long long hit = __ballot(s > 0u && lo <= target && target < lo + s);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      *idx = j0 + (uint32_t)l;
+      *before = __shfl(lo, l, 64);
+      return;
+    }
+    acc += __shfl(inc, 63, 64);
+  }
+  *idx = count;
+  *before = acc;
+}
+
+// Fixed-point accumulation: with B >= |any sum of kept products| and B < 2^eB,
+// scale S = 50 - eB puts every scaled sum below 2^50 in magnitude.  A product
+// w * v * 2^S is exact in double (11 + 24 significant bits); adding 1.5 * 2^52
+// rounds it to an integer held in the low mantissa bits, which are then read
+// as an int64.
+constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
+
+__device__ __forceinline__ int64_t fixed_product(uint32_t w, double vs) {
+  const double d = __builtin_fma((double)h2f(w), vs, kMagic);
+  return (int64_t)(__double_as_longlong(d) - __double_as_longlong(kMagic));
+}
 
 template <bool REC>
 __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ thresh, const uint32_t* __restrict__ runlen,
-    uint32_t* __restrict__ rowctr, float* __restrict__ y, MulArgs a) {
-  extern __shared__ float tile[];
-  const int g = (int)(blockIdx.x % (unsigned)a.G);
+    const uint32_t* __restrict__ bsum, float* __restrict__ y, MulArgs a) {
+  extern __shared__ unsigned long long tile[];
+  const int G = a.G;
+  const int G1 = G + 1;
+  const int g = (int)(blockIdx.x % (unsigned)G);
+  const uint32_t bslot = blockIdx.x / (unsigned)G;
+  const uint32_t bpg = gridDim.x / (unsigned)G;
   const int64_t col0 = (int64_t)g * a.TW;
   const int tw = (int)((int64_t)a.TW < a.n - col0 ? (int64_t)a.TW : a.n - col0);
-  for (int c = threadIdx.x; c < tw; c += MUL_T) tile[c] = 0.0f;
+  for (int c = threadIdx.x; c < tw; c += MUL_T) tile[c] = 0ull;
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t m = (uint32_t)a.m;
+  const uint32_t nbd = (uint32_t)a.nbd;
+  const uint32_t* rl = runlen + (size_t)g * a.m;
+
+  // group total and the fixed-point scale
+  uint32_t T = 0;
+  float B = 0.0f;
+  for (uint32_t b0 = 0; b0 < nbd; b0 += 64) {
+    const uint32_t b = b0 + lane;
+    T += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
+    float bb = b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bb += __shfl_xor(bb, off, 64);
+    B += bb;
+  }
+  int eB = 0;
+  frexpf(B * 1.001f + 1e-38f, &eB);  // B * 1.001 < 2^eB; the margin covers float summation
+  const int S = __builtin_amdgcn_readfirstlane(50 - eB);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  uint32_t* ctr = rowctr + g;
-  const uint32_t* rl = runlen + (size_t)g * a.m;
-  const uint32_t m = (uint32_t)a.m;
-  uint32_t row = 0u;
-  if (lane == 0) row = atomicAdd(ctr, 1u);
-  row = __builtin_amdgcn_readfirstlane(row);
-  while (row < m) {
-    uint32_t nxt = 0u;
-    if (lane == 0) nxt = atomicAdd(ctr, 1u);  // next row, fetched while this one streams
-    const uint32_t L = min(rl[row], (uint32_t)tw);  // never past the group's slot
-    const uint32_t t = thresh[row];
-    const float vi = vvec[row];
-    const uint4* base =
-        reinterpret_cast<const uint4*>(entries + (size_t)row * (size_t)a.row_stride + col0);
-    uint32_t cnt = 0u;
-    uint64_t fp = 0u;
-    for (uint32_t off = (uint32_t)lane * 4u; off < L; off += 1024u) {
-      uint4 e[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t o = off + (uint32_t)u * 256u;
-        e[u] = o < L ? base[o >> 2] : make_uint4(0u, 0u, 0u, 0u);
+  // this wave's share [start, end) of the group's entries, concatenated over rows
+  const uint64_t nslots = (uint64_t)bpg * MUL_W;
+  const uint64_t slot = (uint64_t)bslot * MUL_W + wid;
+  const uint32_t start = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T * slot / nslots));
+  const uint32_t end = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T * (slot + 1) / nslots));
+
+  if (start < end) {
+    uint32_t bstar, before_b;
+    wave_locate(nbd, start, [&](uint32_t b) { return bsum[(size_t)b * G1 + g]; }, &bstar, &before_b);
+    const uint32_t r0 = bstar < nbd ? bstar * DSP_ROWS : m;
+    const uint32_t nr = r0 < m ? (m - r0 < (uint32_t)DSP_ROWS ? m - r0 : (uint32_t)DSP_ROWS) : 0u;
+    uint32_t jrow = 0, before_r = 0;
+    if (nr > 0u)
+      wave_locate(nr, start - before_b, [&](uint32_t j) { return rl[r0 + j]; }, &jrow, &before_r);
+    uint32_t rowb = __builtin_amdgcn_readfirstlane(jrow < nr ? r0 + jrow : m);
+    uint32_t offb = __builtin_amdgcn_readfirstlane(start - before_b - before_r);
+    uint32_t remaining = end - start;
+
+    while (remaining > 0u && rowb < m) {
+      // metadata of up to 64 rows, one per lane
+      const uint32_t r = rowb + (uint32_t)lane;
+      uint32_t Lj = 0u, tj = 0x7C00u;
+      float vj = 0.0f;
+      if (r < m) {
+        Lj = min(rl[r], (uint32_t)tw);
+        tj = thresh[r];
+        vj = vvec[r];
       }
+      const uint32_t aj = lane == 0 ? offb : 0u;
+      const uint32_t lenj = Lj > aj ? Lj - aj : 0u;
+      const uint32_t incl = wave_incl_scan(lenj);
+      const uint32_t excl = incl - lenj;
+      const uint32_t takej = excl >= remaining ? 0u : min(lenj, remaining - excl);
+      const uint32_t batch_take = __builtin_amdgcn_readfirstlane(min(__shfl(incl, 63, 64), remaining));
+      // clamped: only a row whose weights are all zero can exceed it, and its
+      // products stay 0
+      const double vsj = fmin(fmax(ldexp((double)vj, S), -0x1p100), 0x1p100);
+      unsigned long long todo = __ballot(takej > 0u);
+
+      // chunks of <= 1024 entries of one row; the next chunk's loads are in
+      // flight while the current one is processed
+      uint32_t cj = 0, cs0 = 0, cs1 = 0, ce = 0;
+      bool have = false;
+      uint4 cur[4], nxt[4];
+      auto first_of = [&](uint32_t j, uint32_t* s0, uint32_t* e) {
+        *s0 = __builtin_amdgcn_readlane(aj, j);
+        *e = *s0 + __builtin_amdgcn_readlane(takej, j);
+      };
+      auto issue = [&](uint32_t j, uint32_t s0, uint32_t s1, uint4* buf) {
+        const uint4* base = reinterpret_cast<const uint4*>(
+            entries + (size_t)(rowb + j) * (size_t)a.row_stride + col0);
+        const uint32_t o = (s0 & ~3u) + (uint32_t)lane * 4u;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t o = off + (uint32_t)u * 256u;
-        const uint32_t ev[4] = {e[u].x, e[u].y, e[u].z, e[u].w};
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t p = o + (uint32_t)u * 256u;
+          buf[u] = p < s1 ? base[p >> 2] : make_uint4(0u, 0u, 0u, 0u);
+        }
+      };
+      if (todo) {
+        cj = (uint32_t)(__ffsll((long long)todo) - 1);
+        todo &= todo - 1ull;
+        first_of(cj, &cs0, &ce);
+        cs1 = min(ce, (cs0 & ~3u) + 1024u);
+        issue(cj, cs0, cs1, cur);
+        have = true;
+      }
+      while (have) {
+        // next chunk: rest of this row, else the next row with entries
+        uint32_t nj = cj, ns0 = cs1, ne = ce;
+        bool nhave = true;
+        if (cs1 >= ce) {
+          if (todo) {
+            nj = (uint32_t)(__ffsll((long long)todo) - 1);
+            todo &= todo - 1ull;
+            first_of(nj, &ns0, &ne);
+          } else {
+            nhave = false;
+          }
+        }
+        const uint32_t ns1 = min(ne, (ns0 & ~3u) + 1024u);
+        if (nhave) issue(nj, ns0, ns1, nxt);
+
+        // process the current chunk
+        const uint32_t t = __builtin_amdgcn_readlane(tj, cj);
+        const double vs = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(vsj), cj),
+                                           __builtin_amdgcn_readlane(__double2loint(vsj), cj));
+        const uint32_t row = rowb + cj;
+        uint32_t cnt = 0u;
+        uint64_t fp = 0u;
+        const uint32_t o = (cs0 & ~3u) + (uint32_t)lane * 4u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t w = ev[k];
-          if (o + (uint32_t)k < L && (w & 0x7FFFu) >= t) {
-            atomicAdd(&tile[w >> 16], vi * h2f(w));
-            if (REC) {
-              const uint64_t col = (uint64_t)col0 + (w >> 16);
-              const uint64_t flat = (uint64_t)row * (uint64_t)a.n + col;
-              if (a.mask) a.mask[flat] = 1u;
-              fp += pair_hash(flat);
-              ++cnt;
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t p = o + (uint32_t)u * 256u;
+          const uint32_t ev[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) {
+            const uint32_t w = ev[k2];
+            const uint32_t pos = p + (uint32_t)k2;
+            if (pos >= cs0 && pos < cs1 && (w & 0x7FFFu) >= t) {
+              atomicAdd(&tile[w >> 16], (unsigned long long)fixed_product(w, vs));
+              if (REC) {
+                const uint64_t flat = (uint64_t)row * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
+                if (a.mask) a.mask[flat] = 1u;
+                fp += pair_hash(flat);
+                ++cnt;
+              }
             }
           }
         }
+        if (REC) {
+          uint32_t flo = (uint32_t)fp, fhi = (uint32_t)(fp >> 32);
+          for (int sh = 32; sh > 0; sh >>= 1) {
+            cnt += __shfl_xor(cnt, sh, 64);
+            const uint32_t olo = __shfl_xor(flo, sh, 64);
+            const uint32_t ohi = __shfl_xor(fhi, sh, 64);
+            const uint64_t sum = ((uint64_t)fhi << 32 | flo) + ((uint64_t)ohi << 32 | olo);
+            flo = (uint32_t)sum;
+            fhi = (uint32_t)(sum >> 32);
+          }
+          if (lane == 0) {
+            if (cnt && a.row_kept) atomicAdd(&a.row_kept[row], (int32_t)cnt);
+            if (a.fingerprint) atomicAdd(a.fingerprint, ((unsigned long long)fhi << 32) | flo);
+          }
+        }
+        cj = nj;
+        cs0 = ns0;
+        cs1 = ns1;
+        ce = ne;
+        have = nhave;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
       }
+      remaining -= batch_take;
+      rowb += 64u;
+      offb = 0u;
     }
-    if (REC) {
-      uint32_t flo = (uint32_t)fp, fhi = (uint32_t)(fp >> 32);
-      for (int off = 32; off > 0; off >>= 1) {
-        cnt += __shfl_xor(cnt, off, 64);
-        const uint32_t olo = __shfl_xor(flo, off, 64);
-        const uint32_t ohi = __shfl_xor(fhi, off, 64);
-        const uint64_t s = ((uint64_t)fhi << 32 | flo) + ((uint64_t)ohi << 32 | olo);
-        flo = (uint32_t)s;
-        fhi = (uint32_t)(s >> 32);
-      }
-      if (lane == 0) {
-        if (cnt && a.row_kept) atomicAdd(&a.row_kept[row], (int32_t)cnt);
-        if (a.fingerprint) atomicAdd(a.fingerprint, ((unsigned long long)fhi << 32) | flo);
-      }
-    }
-    row = __builtin_amdgcn_readlane(nxt, 0);
   }
   __syncthreads();
+  const double unscale = ldexp(1.0, -S);
   for (int c = threadIdx.x; c < tw; c += MUL_T) {
-    const float s = tile[c];
-    if (s != 0.0f) atomicAdd(&y[col0 + c], s);
+    const long long acc = (long long)tile[c];
+    if (acc != 0) atomicAdd(&y[col0 + c], (float)((double)acc * unscale));
   }
 }
 
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s) {
   const unsigned grid = (unsigned)(a.G * blocks_per_group);
-  const size_t lds = (size_t)a.TW * sizeof(float);
+  const size_t lds = (size_t)a.TW * sizeof(unsigned long long);
   if (record)
     hipLaunchKernelGGL(k_bucketmul<true>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
-                       a.thresh, a.runlen, a.rowctr, a.y, a);
+                       a.thresh, a.runlen, a.bsum, a.y, a);
   else
     hipLaunchKernelGGL(k_bucketmul<false>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
-                       a.thresh, a.runlen, a.rowctr, a.y, a);
+                       a.thresh, a.runlen, a.bsum, a.y, a);
   return hipGetLastError();
 }
 

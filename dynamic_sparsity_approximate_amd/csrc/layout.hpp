@@ -7,6 +7,7 @@
 //   entries         u32 [m][G*TW]   per row, per group, the group's entries in rank
 //                                   order: low 16 bits = fp16 value bits, high 16
 //                                   bits = column index inside the group
+//   rowmax          u16 [m]         largest magnitude key of each row
 //
 // Rank order is |w| descending, ties by column ascending.  Segment k of a row is
 // ranks (ceil(k n / P), ceil((k+1) n / P)]; its smallest magnitude is probe k.
@@ -30,7 +31,7 @@ struct Geometry {
   int64_t m = 0, n = 0;
   int32_t P = 0, G = 0, TW = 0;
   int64_t row_stride = 0;
-  uint64_t off_probes = 0, off_counts = 0, off_entries = 0, total = 0;
+  uint64_t off_probes = 0, off_counts = 0, off_entries = 0, off_rowmax = 0, total = 0;
 };
 
 inline int32_t default_groups(int64_t n) {
@@ -50,6 +51,7 @@ inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geomet
   int64_t tw = (n + groups - 1) / groups;
   tw = (int64_t)align_up((uint64_t)tw, 64);
   if (tw > EFFORT_MAX_GROUP_WIDTH) return EFFORT_EUNSUPPORTED;
+  if ((int64_t)m * tw > (1ll << 32) - 1) return EFFORT_EUNSUPPORTED;  // a group's entries fit u32
   int64_t G = (n + tw - 1) / tw;
   g->m = m;
   g->n = n;
@@ -60,32 +62,41 @@ inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geomet
   g->off_probes = kAlign;
   g->off_counts = align_up(g->off_probes + (uint64_t)m * P * 2, kAlign);
   g->off_entries = align_up(g->off_counts + (uint64_t)m * P * G * 4, kAlign);
-  g->total = align_up(g->off_entries + (uint64_t)m * g->row_stride * 4, kAlign);
+  g->off_rowmax = align_up(g->off_entries + (uint64_t)m * g->row_stride * 4, kAlign);
+  g->total = align_up(g->off_rowmax + (uint64_t)m * 2, kAlign);
   return EFFORT_OK;
 }
 
 // Workspace of one vector (offsets in bytes from the vector's slice start).
-//   ctrl     u32[64]      [0] done counter of the cutoff kernel
-//   result   u32[8]       [0] cutoff bits, [1] K', [2] K
-//   rowctr   u32[G]       per-group row counters of the multiply
-//   hist     u32[2048]    first-digit histogram of the chart
-//   chart    f32[m*P]
-//   thresh   u32[m]       per-row fp16 magnitude threshold
-//   runlen   u32[G][m]    per (group, row) entries to read
+//   ctrl     u32[64]                  [0] done counter of the cutoff kernel
+//   result   u32[8]                   [0] cutoff bits, [1] K', [2] K
+//   boff     u32[SB][257]             per cutoff block: exclusive offsets of its 256 exponent bins
+//   sorted   f32[SB * 4096]           per cutoff block: its chart slice ordered by bin
+//   thresh   u32[m]                   per-row fp16 magnitude threshold
+//   runlen   u32[G][m]                per (group, row) entries to read
+//   bsum     u32[ceil(m/256)][G + 1]  per dispatch block: sum of runlen per group, then
+//                                     (as f32) the sum of |v_i| * rowmax_i over its rows
+// SB = ceil(m * P / 4096).
+constexpr int64_t kSelVals = 4096;
+constexpr int64_t kDspRows = 256;
+
 struct WsLayout {
-  uint64_t ctrl, result, rowctr, hist, chart, thresh, runlen, slice;
+  uint64_t ctrl, result, boff, sorted, thresh, runlen, bsum, slice;
 };
 
 inline WsLayout ws_layout(const Geometry& g) {
+  const uint64_t N = (uint64_t)g.m * g.P;
+  const uint64_t SB = (N + kSelVals - 1) / kSelVals;
+  const uint64_t nbd = ((uint64_t)g.m + kDspRows - 1) / kDspRows;
   WsLayout w;
   w.ctrl = 0;
   w.result = 256;
-  w.rowctr = 512;
-  w.hist = align_up(w.rowctr + (uint64_t)g.G * 4, kAlign);
-  w.chart = align_up(w.hist + 2048 * 4, kAlign);
-  w.thresh = align_up(w.chart + (uint64_t)g.m * g.P * 4, kAlign);
+  w.boff = 512;
+  w.sorted = align_up(w.boff + SB * 257 * 4, kAlign);
+  w.thresh = align_up(w.sorted + SB * kSelVals * 4, kAlign);
   w.runlen = align_up(w.thresh + (uint64_t)g.m * 4, kAlign);
-  w.slice = align_up(w.runlen + (uint64_t)g.G * g.m * 4, kAlign);
+  w.bsum = align_up(w.runlen + (uint64_t)g.G * g.m * 4, kAlign);
+  w.slice = align_up(w.bsum + nbd * (g.G + 1) * 4, kAlign);
   return w;
 }
 
@@ -116,7 +127,8 @@ inline bool geometry_from_desc(const effort_desc* d, Geometry* g) {
   if (make_geometry(d->in_dim, d->out_dim, d->probes_per_row, d->groups, &x) != EFFORT_OK) return false;
   if (x.G != d->groups || x.TW != d->group_width || x.row_stride != d->row_stride ||
       x.off_probes != d->off_probes || x.off_counts != d->off_counts ||
-      x.off_entries != d->off_entries || x.total != d->total_bytes || d->index_bytes != 2)
+      x.off_entries != d->off_entries || x.off_rowmax != d->off_rowmax ||
+      x.total != d->total_bytes || d->index_bytes != 2)
     return false;
   *g = x;
   return true;

@@ -51,7 +51,7 @@ enum {
 };
 
 #define EFFORT_MAGIC 0x4F464645u /* "EFFO" little-endian */
-#define EFFORT_VERSION 1u
+#define EFFORT_VERSION 2u
 #define EFFORT_MAX_GROUP_WIDTH 8192 /* output columns per group (fp32 LDS tile of 32 KiB) */
 #define EFFORT_MAX_BATCH 16
 
@@ -69,6 +69,7 @@ typedef struct effort_desc {
   uint64_t off_probes;        /* byte offsets inside the layout */
   uint64_t off_counts;
   uint64_t off_entries;
+  uint64_t off_rowmax;
   uint64_t total_bytes;
   uint64_t checksum;          /* FNV-1a-64 over the blob's 8-byte words after the header */
   uint64_t desc_check;        /* FNV-1a-64 over all fields above */
@@ -109,7 +110,7 @@ int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream);
    Per row: entries sorted by |w| descending (ties: column ascending), grouped by
    output-column group; each entry is (fp16 value, 16-bit column index within
    its group); P probes (fp16 magnitudes); per (row, probe segment, group) the
-   cumulative entry count.  layout_host: host memory of >= layout_bytes bytes,
+   cumulative entry count; the row's largest magnitude.  layout_host: host memory of >= layout_bytes bytes,
    8-byte aligned.  desc_out: host.  EINVAL also for non-finite W. */
 int effort_prepare_host(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
                         void* layout_host, uint64_t layout_bytes, effort_desc* desc_out);
@@ -157,7 +158,8 @@ int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const f
 
 /* effort_matvec that also records hipEvent_t events[0..3] (each may be NULL) on
    `stream`: before the cutoff kernel, before the dispatch kernel, before the
-   bucketMul kernel, after it.  For measurement. */
+   bucketMul kernel, after it.  For measurement.  EUNSUPPORTED while `stream` is
+   being captured into a graph. */
 int effort_matvec_timed(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                         float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
                         void* stream, void* const* events);

@@ -38,6 +38,10 @@ def decode(desc, blob):
     return pr, cnt, ent.reshape(m, desc.row_stride)
 
 
+def decode_rowmax(desc, blob):
+    return blob[desc.off_rowmax: desc.off_rowmax + desc.in_dim * 2].view(np.uint16)
+
+
 # ---------------------------------------------------------------- symbols
 
 def test_library_exports_every_declared_function():
@@ -63,8 +67,8 @@ def test_layout_bytes_and_groups():
     m, n, P = 4096, 14336, 16
     nb = E.effort_layout_bytes(m, n, P)
     # entries dominate: 4 bytes per weight, plus probes and counts
-    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 7
-    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 7 + 4 * 256
+    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 7 + 2 * m
+    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 7 + 2 * m + 5 * 256
 
 
 @pytest.mark.parametrize("args,code", [
@@ -101,6 +105,7 @@ def test_layout_roundtrip_and_order(m, n, P, G):
     E.effort_layout_check(d, blob)
     pr, cnt, ent = decode(d, blob)
     TW = d.group_width
+    assert np.array_equal(decode_rowmax(d, blob), (W & 0x7FFF).max(axis=1))
     # probes are the oracle's order statistics
     ref = oracle.probes(W, P)
     assert np.array_equal(pr.view(np.float16).astype(np.float32), ref)

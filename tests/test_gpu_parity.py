@@ -229,3 +229,30 @@ def test_mistral_shapes(shape):
             ref = oracle.run(W, pr, v, effort, mask=with_mask)
             err = check(got, ref, with_mask, where="%dx%d/%d/%g" % (m, n, seed, effort))
             say("  ok kept=%.4f relL2=%.2e" % (ref["total_kept"] / W.size, err))
+
+
+def test_graph_replays_match_eager():
+    """Calls captured in a HIP graph give the eager result on every replay
+    (with eager work and synchronizations between replays)."""
+    d = dev()
+    W, v = case(1024, 4096, seed=9, tag="graph")
+    M = E.EffortMatrix(W, P=16, device=d)
+    vt = torch.from_numpy(v).to(d)
+    ref = M.matvec_debug(vt, 0.25)
+    y = torch.empty(4096, dtype=torch.float32, device=d)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            E.effort_matvec(M.desc, M.layout, vt, 0.25, y, M.ws, M.ws_bytes)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert rel_l2(y.cpu().numpy(), ref["y"]) < 1e-6, rep
+        # eager work between replays, on the same workspace
+        other = M.matvec_debug(vt, 0.5 if rep % 2 else 0.25, with_mask=False)
+        assert other["K"] > 0

@@ -79,16 +79,18 @@ struct DebugOut {
 int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
             uint8_t* ws, hipStream_t s, const DebugOut* dbg, hipEvent_t const* ev) {
   const WsLayout w = ws_layout(g);
-  uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + w.ctrl);
   uint32_t* result = reinterpret_cast<uint32_t*>(ws + w.result);
-  uint32_t* boff = reinterpret_cast<uint32_t*>(ws + w.boff);
-  float* sorted = reinterpret_cast<float*>(ws + w.sorted);
-  uint32_t* thresh = reinterpret_cast<uint32_t*>(ws + w.thresh);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist);
+  uint32_t* hist2 = reinterpret_cast<uint32_t*>(ws + w.hist2);
+  uint32_t* cand = reinterpret_cast<uint32_t*>(ws + w.cand);
   uint32_t* runlen = reinterpret_cast<uint32_t*>(ws + w.runlen);
   uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + w.bsum);
   const uint16_t* probes = reinterpret_cast<const uint16_t*>(layout + g.off_probes);
   const uint32_t* counts = reinterpret_cast<const uint32_t*>(layout + g.off_counts);
   const uint32_t* entries = reinterpret_cast<const uint32_t*>(layout + g.off_entries);
+  const uint16_t* rowmax = reinterpret_cast<const uint16_t*>(layout + g.off_rowmax);
+  const int64_t N = g.m * (int64_t)g.P;
+  const uint32_t K = k_of(effort, N);
   hipError_t e;
 
   if (dbg) {
@@ -106,11 +108,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   sa.probes = probes;
   sa.m = g.m;
   sa.P = g.P;
-  sa.N = g.m * (int64_t)g.P;
-  sa.K = k_of(effort, sa.N);
-  sa.done = ctrl;
-  sa.boff = boff;
-  sa.sorted = sorted;
+  sa.N = N;
+  sa.hist = hist;
+  sa.hist2 = hist2;
   sa.result = result;
   sa.y = y;
   sa.n = g.n;
@@ -121,24 +121,30 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   da.v = v;
   da.probes = probes;
   da.counts = counts;
-  da.rowmax = reinterpret_cast<const uint16_t*>(layout + g.off_rowmax);
+  da.rowmax = rowmax;
+  da.hist = hist;
+  da.hist2 = hist2;
+  da.cand = cand;
   da.result = result;
-  da.thresh = thresh;
   da.runlen = runlen;
   da.bsum = bsum;
-  da.row_chart_kept = nullptr;
   da.m = g.m;
   da.P = g.P;
   da.G = g.G;
+  da.G4 = g.G4;
+  da.K = K;
   if (hip_failed(e = launch_dispatch(da, s))) return EFFORT_EHIP;
 
   if (ev && ev[2] && hip_failed(hipEventRecord(ev[2], s))) return EFFORT_EHIP;
   MulArgs ma;
   ma.v = v;
   ma.entries = entries;
-  ma.thresh = thresh;
   ma.runlen = runlen;
   ma.bsum = bsum;
+  ma.hist = hist;
+  ma.hist2 = hist2;
+  ma.cand = cand;
+  ma.result = result;
   ma.y = y;
   ma.m = g.m;
   ma.n = g.n;
@@ -146,6 +152,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   ma.G = g.G;
   ma.TW = g.TW;
   ma.nbd = (int32_t)((g.m + kDspRows - 1) / kDspRows);
+  ma.K = K;
   ma.row_kept = dbg ? dbg->row_kept : nullptr;
   ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
   ma.mask = dbg ? dbg->mask : nullptr;

@@ -56,12 +56,12 @@ static void convert_rows(const uint16_t* W, const Geometry& g, uint8_t* blob, in
       if (r == seg_end) probes[i * P + k] = (uint16_t)(bits & 0x7FFFu);
     }
     // cumulative counts over segments
-    uint32_t* crow = counts + (size_t)i * P * G;
+    uint32_t* crow = counts + (size_t)i * P * g.G4;
     for (int32_t grp = 0; grp < G; ++grp) {
       uint32_t acc = 0;
       for (int32_t kk = 0; kk < P; ++kk) {
         acc += seg_cnt[(size_t)kk * G + grp];
-        crow[(size_t)kk * G + grp] = acc;
+        crow[(size_t)kk * g.G4 + grp] = acc;
       }
     }
   }

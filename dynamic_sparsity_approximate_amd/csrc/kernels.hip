@@ -7,15 +7,16 @@
 // O(inDim), multiply O(effort inDim outDim)).
 //
 // Three kernels per call, all on one stream:
-//   k_select    chart |v_i| * probe_i[k] -> radix select of the K-th largest
-//               (11/10/10-bit digits of the fp32 bit pattern; the last block to
-//               finish the first digit finishes the selection) and zeroing of y.
-//   k_dispatch  per row the smallest fp16 magnitude key that passes the keep
-//               test, and per (group, row) how many rank-ordered entries to read.
-//   k_bucketmul per output-column group an LDS tile of y; waves take rows from a
-//               per-group counter, stream the run prefix with 16-byte loads, keep
-//               entries whose key reaches the threshold, ds_add_f32 v_i * w into
-//               the tile, and finally add the tile to y.
+//   k_chart_hist chart |v_i| * probe_i[k] and a histogram of its top 12 bits;
+//                zeroes y.
+//   k_dispatch   per (group, row) how many rank-ordered entries to read, from the
+//                low edge of the bin holding the K-th largest chart value; one
+//                extra block finishes the exact radix selection of the cutoff.
+//   k_bucketmul  per output-column group an LDS tile of y; each wave streams an
+//                equal share of the group's run prefixes with 16-byte loads,
+//                keeps entries whose key reaches the row threshold (from the
+//                exact cutoff), adds v_i * w as 64-bit fixed point into the tile,
+//                and finally adds the tile to y.
 // No MFMA: the multiply is a bandwidth-bound gather-scatter, not a contraction.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -37,14 +38,43 @@ __device__ __forceinline__ uint64_t pair_hash(uint64_t x) {
   return z ^ (z >> 31);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// Wave-level scans and sums with DPP row shifts (rows of 16 lanes) and
+// readlane for the four row totals; no LDS traffic.
+__device__ __forceinline__ uint32_t row_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
   return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x = row_incl_scan(x);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t add = row == 0 ? 0u : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
+  return x + add;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  x = row_incl_scan(x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 15) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 31) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 47) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 // Exclusive scan over the block (NT threads); tmp holds NT/64 + 1 words.
@@ -98,251 +128,220 @@ __device__ void find_from_top(const uint32_t* h, int nb, uint32_t K, uint32_t* t
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- wave helpers
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 // ---------------------------------------------------------------- cutoff
 
 constexpr int SEL_T = 1024;
-constexpr int SEL_PER = SEL_VALS / SEL_T;
-constexpr uint32_t CAND_CAP = 10240;
-
-// Visits every candidate value (chart entries whose exponent field is `ebin`),
-// from LDS when they were gathered there, else from the blocks' sorted slices.
-template <typename F>
-__device__ void for_each_candidate(bool in_lds, const float* cand, uint32_t ncand,
-                                   const SelectArgs& a, uint32_t ebin, int nblocks, F f) {
-  if (in_lds) {
-    for (uint32_t p = threadIdx.x; p < ncand; p += SEL_T) f(__float_as_uint(cand[p]));
-  } else {
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int b = wid; b < nblocks; b += SEL_T / 64) {
-      const uint32_t s = a.boff[(size_t)b * (SEL_BINS + 1) + ebin];
-      const uint32_t e = a.boff[(size_t)b * (SEL_BINS + 1) + ebin + 1];
-      const float* src = a.sorted + (size_t)b * SEL_VALS;
-      for (uint32_t p = s + lane; p < e; p += 64) f(__float_as_uint(src[p]));
+// The P <= PM probe keys of row i in registers (16-byte loads when P % 8 == 0).
+constexpr int PMAXR = 32;
+template <int PM>
+__device__ __forceinline__ void load_row_keys(const uint16_t* probes, int32_t P, int64_t i,
+                                              uint32_t* key) {
+  const uint16_t* pr = probes + i * P;
+  if ((P & 7) == 0) {
+#pragma unroll
+    for (int c = 0; c < PM / 8; ++c) {
+      uint4 q = make_uint4(0u, 0u, 0u, 0u);
+      if (c * 8 < P) q = *reinterpret_cast<const uint4*>(pr + c * 8);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        key[c * 8 + 2 * j] = w[j] & 0xFFFFu;
+        key[c * 8 + 2 * j + 1] = w[j] >> 16;
+      }
     }
+  } else {
+#pragma unroll
+    for (int k = 0; k < PM; ++k) key[k] = k < P ? (uint32_t)pr[k] : 0u;
   }
 }
 
-__global__ __launch_bounds__(SEL_T) void k_select(SelectArgs a) {
-  __shared__ uint32_t hist[4096];
-  __shared__ float cand[CAND_CAP];
-  __shared__ uint32_t tmp[SEL_T / 64 + 1];
-  __shared__ uint32_t sres[8];
+constexpr int CH_T = 256;  // rows per block of the histogram kernel
+
+__global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
+  __shared__ uint32_t hist[HIST_BINS];
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * SEL_VALS;
-
-  for (int64_t j = (int64_t)blockIdx.x * SEL_T + tid; j < a.n; j += (int64_t)gridDim.x * SEL_T)
+  for (int b = tid; b < HIST_BINS; b += CH_T) hist[b] = 0u;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * CH_T + tid;
+  if (i < a.m) {
+    const float av = fabsf(a.v[i]);
+    if (a.P <= PMAXR) {
+      uint32_t key[PMAXR];
+      load_row_keys<PMAXR>(a.probes, a.P, i, key);
+#pragma unroll
+      for (int k = 0; k < PMAXR; ++k)
+        if (k < a.P) atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(key[k]))) >> HIST_SHIFT], 1u);
+    } else {
+      const uint16_t* pr = a.probes + i * a.P;
+      for (int k = 0; k < a.P; ++k)
+        atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(pr[k]))) >> HIST_SHIFT], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < HIST_BINS; b += CH_T)
+    if (hist[b]) atomicAdd(&a.hist[b], hist[b]);
+  // y is accumulated by the multiply; global stores come last (no barrier waits on them)
+  for (int64_t j = (int64_t)blockIdx.x * CH_T + tid; j < a.n; j += (int64_t)gridDim.x * CH_T)
     a.y[j] = 0.0f;
-
-  // -- every block: chart slice, histogram of the exponent field, slice ordered by bin
-  for (int b = tid; b < 2 * SEL_BINS; b += SEL_T) hist[b] = 0u;
-  __syncthreads();
-  float c[SEL_PER];
-  uint32_t bin[SEL_PER];
-#pragma unroll
-  for (int j = 0; j < SEL_PER; ++j) {
-    const int64_t e = base + tid + j * SEL_T;
-    bin[j] = 0xFFFFFFFFu;
-    if (e < a.N) {
-      c[j] = __fmul_rn(fabsf(a.v[e / a.P]), h2f(a.probes[e]));
-      bin[j] = __float_as_uint(c[j]) >> 23;
-      atomicAdd(&hist[bin[j]], 1u);
-    }
-  }
-  __syncthreads();
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan<SEL_T>(tid < SEL_BINS ? hist[tid] : 0u, tmp, &tot);
-  uint32_t* boff = a.boff + (size_t)blockIdx.x * (SEL_BINS + 1);
-  if (tid < SEL_BINS) {
-    hist[SEL_BINS + tid] = ex;
-    boff[tid] = ex;
-  }
-  if (tid == 0) boff[SEL_BINS] = tot;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < SEL_PER; ++j)
-    if (bin[j] != 0xFFFFFFFFu) cand[atomicAdd(&hist[SEL_BINS + bin[j]], 1u)] = c[j];
-  __syncthreads();
-  for (uint32_t p = tid; p < tot; p += SEL_T) a.sorted[base + p] = cand[p];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sres[7] = (atomicAdd(a.done, 1u) == gridDim.x - 1) ? 1u : 0u;
-  __syncthreads();
-  if (sres[7] == 0u) return;
-  __threadfence();
-
-  // -- last block: exponent bin of the K-th largest, then its 23 mantissa bits
-  const int nb = (int)gridDim.x;
-  {
-    const int bn = tid & (SEL_BINS - 1);
-    uint32_t part = 0;
-    for (int b = tid / SEL_BINS; b < nb; b += SEL_T / SEL_BINS) {
-      const uint32_t* bo = a.boff + (size_t)b * (SEL_BINS + 1);
-      part += bo[bn + 1] - bo[bn];
-    }
-    hist[tid] = part;
-  }
-  __syncthreads();
-  uint32_t tb = 0;
-  if (tid < SEL_BINS) tb = hist[tid] + hist[tid + 256] + hist[tid + 512] + hist[tid + 768];
-  __syncthreads();
-  if (tid < SEL_BINS) hist[tid] = tb;
-  __syncthreads();
-  find_from_top<SEL_T>(hist, SEL_BINS, a.K, tmp, sres);
-  const uint32_t ebin = sres[0] & (SEL_BINS - 1), above0 = sres[1];
-  const uint32_t K1 = a.K - above0;
-  const uint32_t ncand = hist[ebin];
-  __syncthreads();
-
-  // gather the candidates into LDS when they fit
-  const bool in_lds = ncand <= CAND_CAP;
-  if (in_lds) {
-    uint32_t* rs = hist;          // run start inside the block's slice
-    uint32_t* rc = hist + 1024;   // run length
-    uint32_t* ro = hist + 2048;   // destination offset
-    uint32_t run_base = 0;
-    for (int b0 = 0; b0 < nb; b0 += SEL_T) {
-      const int b = b0 + tid;
-      uint32_t s = 0, cnt = 0;
-      if (b < nb) {
-        const uint32_t* bo = a.boff + (size_t)b * (SEL_BINS + 1);
-        s = bo[ebin];
-        cnt = bo[ebin + 1] - s;
-      }
-      uint32_t chunk_tot;
-      const uint32_t off = block_excl_scan<SEL_T>(cnt, tmp, &chunk_tot);
-      rs[tid] = s;
-      rc[tid] = cnt;
-      ro[tid] = off;
-      __syncthreads();
-      const int wid = tid >> 6, lane = tid & 63;
-      const int nrun = nb - b0 < SEL_T ? nb - b0 : SEL_T;
-      for (int r = wid; r < nrun; r += SEL_T / 64) {
-        const float* src = a.sorted + (size_t)(b0 + r) * SEL_VALS + rs[r];
-        for (uint32_t p = lane; p < rc[r]; p += 64) cand[run_base + ro[r] + p] = src[p];
-      }
-      run_base += chunk_tot;
-      __syncthreads();
-    }
-  }
-
-  // mantissa bits 22..11
-  for (int b = tid; b < 4096; b += SEL_T) hist[b] = 0u;
-  __syncthreads();
-  for_each_candidate(in_lds, cand, ncand, a, ebin, nb,
-                     [&](uint32_t bits) { atomicAdd(&hist[(bits >> 11) & 4095u], 1u); });
-  __syncthreads();
-  find_from_top<SEL_T>(hist, 4096, K1, tmp, sres);
-  const uint32_t dA = sres[0] & 4095u, aboveA = sres[1];
-  const uint32_t K2 = K1 - aboveA;
-  __syncthreads();
-
-  // mantissa bits 10..0
-  for (int b = tid; b < 2048; b += SEL_T) hist[b] = 0u;
-  __syncthreads();
-  for_each_candidate(in_lds, cand, ncand, a, ebin, nb, [&](uint32_t bits) {
-    if (((bits >> 11) & 4095u) == dA) atomicAdd(&hist[bits & 2047u], 1u);
-  });
-  __syncthreads();
-  find_from_top<SEL_T>(hist, 2048, K2, tmp, sres);
-  const uint32_t dB = sres[0] & 2047u, aboveB = sres[1];
-  if (tid == 0) {
-    a.result[0] = (ebin << 23) | (dA << 11) | dB;
-    a.result[1] = above0 + aboveA + aboveB + hist[dB];
-    a.result[2] = a.K;
-    *a.done = 0u;
+  if (blockIdx.x == 0) {  // the dispatch accumulates into these
+    for (int b = tid; b < 1024; b += CH_T) a.hist2[b] = 0u;
+    if (tid == 0) a.result[RES_NCAND] = 0u;
   }
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const int64_t blocks = (a.N + SEL_VALS - 1) / SEL_VALS;
-  hipLaunchKernelGGL(k_select, dim3((unsigned)blocks), dim3(SEL_T), 0, s, a);
+  const int64_t blocks = (a.m + CH_T - 1) / CH_T;
+  hipLaunchKernelGGL(k_chart_hist, dim3((unsigned)blocks), dim3(CH_T), 0, s, a);
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- dispatch
+// Smallest finite fp16 magnitude key k with fl32(av * k) >= c (0x7C00: none).
+// The product is monotone in the key, so bisection finds it.
+__device__ __forceinline__ uint32_t key_threshold(float av, float c) {
+  uint32_t lo = 0u, hi = 0x7C00u;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (__fmul_rn(av, h2f(mid)) >= c)
+      hi = mid;
+    else
+      lo = mid + 1u;
+  }
+  return lo;
+}
 
-__global__ __launch_bounds__(DSP_ROWS) void k_dispatch(DispatchArgs a) {
-  __shared__ uint32_t red[DSP_ROWS / 64];
-  __shared__ float redf[DSP_ROWS / 64];
-  const int64_t i = (int64_t)blockIdx.x * DSP_ROWS + threadIdx.x;
+__global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
+  __shared__ uint32_t hist[HIST_BINS];
+  __shared__ uint32_t h2[1024];
+  __shared__ uint32_t tmp[DSP_T / 64 + 1];
+  __shared__ uint32_t sres[8];
+  __shared__ uint32_t red[16 * (DSP_T / 64)];
+  __shared__ float redf[DSP_T / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int64_t i = (int64_t)blockIdx.x * DSP_T + tid;
   const bool valid = i < a.m;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int G1 = a.G + 1;
-  uint32_t t = 0x7C00u;
-  int32_t q = 0;
-  bool none = true;  // no entry of the row can pass
-  float bound = 0.0f;
+  // row data first (independent of the cutoff), then the histogram
+  float av = 0.0f;
+  uint32_t rmax = 0u;
+  uint32_t pk[PMAXR];
   if (valid) {
-    const float c = __uint_as_float(a.result[0]);
-    const float av = fabsf(a.v[i]);
-    const uint32_t rmax = a.rowmax[i];
-    bound = av * h2f(rmax);
-    // smallest finite fp16 magnitude key whose product with |v_i| reaches the
-    // cutoff (0x7C00 = none); the product is monotone in the key
-    uint32_t lo = 0u, hi = 0x7C00u;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (__fmul_rn(av, h2f(mid)) >= c)
-        hi = mid;
-      else
-        lo = mid + 1u;
+    av = fabsf(a.v[i]);
+    rmax = a.rowmax[i];
+    if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, pk);
+  }
+  for (int b = tid; b < HIST_BINS; b += DSP_T) hist[b] = a.hist[b];
+  for (int b = tid; b < 1024; b += DSP_T) h2[b] = 0u;
+  __syncthreads();
+  find_from_top<DSP_T>(hist, HIST_BINS, a.K, tmp, sres);
+  const uint32_t b1 = sres[0] & (HIST_BINS - 1);
+  const uint32_t above1 = sres[1];
+  // the K-th largest chart value lies in bin b1: its low edge bounds the cutoff below
+  const float lo = __uint_as_float(b1 << HIST_SHIFT);
+  const uint32_t t = key_threshold(av, lo);
+  const bool none = !valid || rmax < t;  // no entry of the row can pass
+  int32_t q = 0;
+  uint32_t hits = 0u;  // chart entries of this row in bin b1 (P <= PMAXR)
+  if (valid) {
+    if (a.P <= PMAXR) {
+#pragma unroll
+      for (int k = 0; k < PMAXR; ++k) {
+        if (k < a.P) {
+          q += pk[k] >= t ? 1 : 0;  // probes are descending keys: q = segments kept whole
+          const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pk[k])));
+          if ((bits >> HIST_SHIFT) == b1) {
+            hits |= 1u << k;
+            atomicAdd(&h2[(bits >> 9) & 1023u], 1u);
+          }
+        }
+      }
+    } else {
+      const uint16_t* pr = a.probes + i * a.P;
+      for (int k = 0; k < a.P; ++k) {
+        const uint32_t key = pr[k];
+        q += key >= t ? 1 : 0;
+        const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key)));
+        if ((bits >> HIST_SHIFT) == b1) atomicAdd(&h2[(bits >> 9) & 1023u], 1u);
+      }
     }
-    t = lo;
-    none = rmax < t;
-    // q = probes (descending keys) at or above the threshold = fully kept
-    // segments; segment q (if any) is the one that is partly kept
-    const uint16_t* pr = a.probes + i * a.P;
-    int32_t qlo = 0, qhi = a.P;
-    while (qlo < qhi) {
-      const int32_t mid = (qlo + qhi) >> 1;
-      if ((uint32_t)pr[mid] >= t)
-        qlo = mid + 1;
-      else
-        qhi = mid;
-    }
-    q = qlo;
-    a.thresh[i] = t;
-    if (a.row_chart_kept) a.row_chart_kept[i] = q;
   }
   const int32_t qc = q < a.P ? q : a.P - 1;
-  const uint32_t* cr = a.counts + ((size_t)(valid ? i : 0) * a.P + qc) * a.G;
-  for (int g = 0; g < a.G; ++g) {
-    const uint32_t L = (valid && !none) ? cr[g] : 0u;
-    if (valid) a.runlen[(size_t)g * a.m + i] = L;
-    const uint32_t s = wave_sum(L);
-    if (lane == 0) red[wid] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t tot = 0;
-      for (int w = 0; w < DSP_ROWS / 64; ++w) tot += red[w];
-      a.bsum[(size_t)blockIdx.x * G1 + g] = tot;
-    }
-    __syncthreads();
-  }
-  // bound on |any sum of products| of these rows
-  float bs = bound;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) bs += __shfl_xor(bs, off, 64);
+  const uint32_t* cr = a.counts + ((size_t)(valid ? i : 0) * a.P + qc) * a.G4;
+  constexpr int GCH = 16;  // groups per pass: their counts are loaded before any store
+  constexpr int SUBS = DSP_T / DSP_ROWS;
+  constexpr int WPS = DSP_ROWS / 64;
+  // bound on |any sum of products| of the row
+  const float bs = wave_sum_f(valid ? av * h2f(rmax) : 0.0f);
   if (lane == 0) redf[wid] = bs;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float tot = 0.0f;
-    for (int w = 0; w < DSP_ROWS / 64; ++w) tot += redf[w];
-    a.bsum[(size_t)blockIdx.x * G1 + a.G] = __float_as_uint(tot);
+  for (int g0 = 0; g0 < a.G; g0 += GCH) {
+    uint32_t L[GCH];
+#pragma unroll
+    for (int u4 = 0; u4 < GCH / 4; ++u4) {
+      uint4 c4 = make_uint4(0u, 0u, 0u, 0u);
+      if (!none && g0 + u4 * 4 < a.G) c4 = *reinterpret_cast<const uint4*>(cr + g0 + u4 * 4);
+      L[u4 * 4 + 0] = c4.x;
+      L[u4 * 4 + 1] = c4.y;
+      L[u4 * 4 + 2] = c4.z;
+      L[u4 * 4 + 3] = c4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < GCH; ++u) {
+      if (g0 + u >= a.G) L[u] = 0u;
+      const uint32_t s = wave_sum(L[u]);
+      if (lane == 0) red[u * (DSP_T / 64) + wid] = s;
+    }
+    __syncthreads();  // no global store is outstanding here
+    if (valid)
+#pragma unroll
+      for (int u = 0; u < GCH; ++u)
+        if (g0 + u < a.G) a.runlen[(size_t)(g0 + u) * a.m + i] = L[u];
+    for (int x = tid; x < GCH * SUBS; x += DSP_T) {
+      const int u = x / SUBS, sub = x % SUBS;
+      const int64_t sbt = (int64_t)blockIdx.x * SUBS + sub;
+      if (g0 + u < a.G && sbt * DSP_ROWS < a.m) {
+        uint32_t tot = 0;
+        for (int w = 0; w < WPS; ++w) tot += red[u * (DSP_T / 64) + sub * WPS + w];
+        a.bsum[(size_t)sbt * G1 + g0 + u] = tot;
+      }
+    }
+    if (g0 == 0 && tid < SUBS) {
+      const int64_t sbt = (int64_t)blockIdx.x * SUBS + tid;
+      if (sbt * DSP_ROWS < a.m) {
+        float tot = 0.0f;
+        for (int w = 0; w < WPS; ++w) tot += redf[tid * WPS + w];
+        a.bsum[(size_t)sbt * G1 + a.G] = __float_as_uint(tot);
+      }
+    }
+    if (g0 + GCH < a.G) __syncthreads();  // red[] is reused (more than GCH groups)
+  }
+  // the bin's refinement histogram and its values, for the exact cutoff
+  if (blockIdx.x == 0 && tid == 0) {
+    a.result[RES_BIN] = b1;
+    a.result[RES_ABOVE] = above1;
+  }
+  for (int b = tid; b < 1024; b += DSP_T)
+    if (h2[b]) atomicAdd(&a.hist2[b], h2[b]);
+  if (a.P <= PMAXR) {
+    const uint32_t c = (uint32_t)__popc(hits);
+    const uint32_t incl = wave_incl_scan(c);
+    uint32_t base = 0u;
+    if (lane == 63 && incl) base = atomicAdd(&a.result[RES_NCAND], incl);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + incl - c;
+#pragma unroll
+    for (int k = 0; k < PMAXR; ++k)
+      if ((hits >> k) & 1u) a.cand[base++] = __float_as_uint(__fmul_rn(av, h2f(pk[k])));
+  } else if (valid) {
+    const uint16_t* pr = a.probes + i * a.P;
+    for (int k = 0; k < a.P; ++k) {
+      const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pr[k])));
+      if ((bits >> HIST_SHIFT) == b1) a.cand[atomicAdd(&a.result[RES_NCAND], 1u)] = bits;
+    }
   }
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  const int64_t blocks = (a.m + DSP_ROWS - 1) / DSP_ROWS;
-  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_ROWS), 0, s, a);
+  const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
+  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, a);
   return hipGetLastError();
 }
 
@@ -368,10 +367,10 @@ __device__ __forceinline__ void wave_locate(uint32_t count, uint32_t target, X x
     if (hit) {
       const int l = __ffsll((long long)hit) - 1;
       *idx = j0 + (uint32_t)l;
-      *before = __shfl(lo, l, 64);
+      *before = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
       return;
     }
-    acc += __shfl(inc, 63, 64);
+    acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   }
   *idx = count;
   *before = acc;
@@ -389,12 +388,61 @@ __device__ __forceinline__ int64_t fixed_product(uint32_t w, double vs) {
   return (int64_t)(__double_as_longlong(d) - __double_as_longlong(kMagic));
 }
 
+// Exact cutoff from the bin b1 (and the count of values above it), the 1024-bin
+// histogram of the bin's next 10 bits and the bin's values: two more radix
+// digits.  Every block computes it; all get the same value.
+__device__ uint32_t exact_cutoff(const MulArgs& a, uint32_t* hs, uint32_t* tmp, uint32_t* sres,
+                                 uint32_t* kprime) {
+  const int tid = threadIdx.x;
+  const uint32_t b1 = a.result[RES_BIN], above1 = a.result[RES_ABOVE];
+  const uint32_t nc = a.result[RES_NCAND];
+  for (int b = tid; b < 1024; b += MUL_T) hs[b] = a.hist2[b];
+  __syncthreads();
+  const uint32_t K1 = a.K - above1;
+  find_from_top<MUL_T>(hs, 1024, K1, tmp, sres);
+  const uint32_t b2 = sres[0] & 1023u, above2 = sres[1];
+  const uint32_t K2 = K1 - above2;
+  const uint32_t pre = (b1 << 10) | b2;  // bits 30..9
+  __syncthreads();
+  for (int b = tid; b < 512; b += MUL_T) hs[b] = 0u;
+  __syncthreads();
+  for (uint32_t p0 = 0; p0 < nc; p0 += MUL_T * 4u) {
+    uint32_t bits[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t p = p0 + (uint32_t)u * MUL_T + tid;
+      bits[u] = p < nc ? a.cand[p] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (bits[u] != 0xFFFFFFFFu && (bits[u] >> 9) == pre) atomicAdd(&hs[bits[u] & 511u], 1u);
+  }
+  __syncthreads();
+  find_from_top<MUL_T>(hs, 512, K2, tmp, sres);
+  const uint32_t b3 = sres[0] & 511u, above3 = sres[1];
+  *kprime = above1 + above2 + above3 + hs[b3];
+  __syncthreads();
+  return (pre << 9) | b3;
+}
+
 template <bool REC>
 __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
-    const uint32_t* __restrict__ thresh, const uint32_t* __restrict__ runlen,
-    const uint32_t* __restrict__ bsum, float* __restrict__ y, MulArgs a) {
+    const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
+    const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
   extern __shared__ unsigned long long tile[];
+  __shared__ uint32_t hs[1024];
+  __shared__ uint32_t ctmp[MUL_T / 64 + 1];
+  __shared__ uint32_t csres[8];
+  (void)result;
+  uint32_t kprime;
+  const uint32_t cut_bits = exact_cutoff(a, hs, ctmp, csres, &kprime);
+  const float cutoff = __uint_as_float(cut_bits);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.result[RES_CUTOFF] = cut_bits;
+    a.result[RES_KPRIME] = kprime;
+    a.result[RES_K] = a.K;
+  }
   const int G = a.G;
   const int G1 = G + 1;
   const int g = (int)(blockIdx.x % (unsigned)G);
@@ -415,10 +463,7 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
   for (uint32_t b0 = 0; b0 < nbd; b0 += 64) {
     const uint32_t b = b0 + lane;
     T += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
-    float bb = b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) bb += __shfl_xor(bb, off, 64);
-    B += bb;
+    B += wave_sum_f(b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f);
   }
   int eB = 0;
   frexpf(B * 1.001f + 1e-38f, &eB);  // B * 1.001 < 2^eB; the margin covers float summation
@@ -446,19 +491,20 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     while (remaining > 0u && rowb < m) {
       // metadata of up to 64 rows, one per lane
       const uint32_t r = rowb + (uint32_t)lane;
-      uint32_t Lj = 0u, tj = 0x7C00u;
+      uint32_t Lj = 0u;
       float vj = 0.0f;
       if (r < m) {
         Lj = min(rl[r], (uint32_t)tw);
-        tj = thresh[r];
         vj = vvec[r];
       }
+      const uint32_t tj = Lj ? key_threshold(fabsf(vj), cutoff) : 0x7C00u;
       const uint32_t aj = lane == 0 ? offb : 0u;
       const uint32_t lenj = Lj > aj ? Lj - aj : 0u;
       const uint32_t incl = wave_incl_scan(lenj);
       const uint32_t excl = incl - lenj;
       const uint32_t takej = excl >= remaining ? 0u : min(lenj, remaining - excl);
-      const uint32_t batch_take = __builtin_amdgcn_readfirstlane(min(__shfl(incl, 63, 64), remaining));
+      const uint32_t batch_take =
+          min((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), remaining);
       // clamped: only a row whose weights are all zero can exceed it, and its
       // products stay 0
       const double vsj = fmin(fmax(ldexp((double)vj, S), -0x1p100), 0x1p100);
@@ -568,6 +614,8 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const long long acc = (long long)tile[c];
     if (acc != 0) atomicAdd(&y[col0 + c], (float)((double)acc * unscale));
   }
+  if (blockIdx.x == 0)  // only the dispatch reads it: ready for the next call
+    for (int b = threadIdx.x; b < HIST_BINS; b += MUL_T) a.hist[b] = 0u;
 }
 
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s) {
@@ -575,10 +623,10 @@ hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group,
   const size_t lds = (size_t)a.TW * sizeof(unsigned long long);
   if (record)
     hipLaunchKernelGGL(k_bucketmul<true>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
-                       a.thresh, a.runlen, a.bsum, a.y, a);
+                       a.runlen, a.bsum, a.result, a.y, a);
   else
     hipLaunchKernelGGL(k_bucketmul<false>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
-                       a.thresh, a.runlen, a.bsum, a.y, a);
+                       a.runlen, a.bsum, a.result, a.y, a);
   return hipGetLastError();
 }
 

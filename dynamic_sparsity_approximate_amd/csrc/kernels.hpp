@@ -5,57 +5,70 @@
 
 namespace effort {
 
-// Select: chart = fl32(|v_i| * probe_i[k]); cutoff = K-th largest chart value.
-// Block b owns chart entries [b*SEL_VALS, (b+1)*SEL_VALS).
-constexpr int SEL_VALS = 4096;   // chart values per select block
-constexpr int SEL_BINS = 256;    // first digit: the fp32 exponent field
+// Cutoff, first pass: chart = fl32(|v_i| * probe_i[k]); a histogram of the
+// top 12 bits (exponent + 4 fraction bits) of the chart values, accumulated in
+// a global 4096-bin array; one thread per row.
+constexpr int HIST_BINS = 4096;
+constexpr int HIST_SHIFT = 19;
 struct SelectArgs {
   const float* v;
   const uint16_t* probes;  // [m][P] fp16 magnitude bits
   int64_t m;
   int32_t P;
   int64_t N;         // m * P
-  uint32_t K;
-  uint32_t* done;    // last-block counter (zero on entry, left zero)
-  uint32_t* boff;    // [blocks][SEL_BINS + 1] per-block exclusive bin offsets
-  float* sorted;     // [blocks * SEL_VALS] chart slice of each block, ordered by bin
-  uint32_t* result;  // [0] cutoff bits, [1] K', [2] K
+  uint32_t* hist;    // [HIST_BINS], zero on entry (the multiply clears it)
+  uint32_t* hist2;   // [1024] cleared here for the dispatch
+  uint32_t* result;  // [3] candidate count, cleared here
   float* y;          // zeroed here (the multiply accumulates into it)
   int64_t n;
 };
 
-// Dispatch: per row threshold and per (group, row) read length, plus the sum
-// of the read lengths of each block of DSP_ROWS rows per group.
+// result words of the workspace
+constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN = 4, RES_ABOVE = 5;
+
+// Dispatch: per (group, row) read length from a lower bound of the cutoff (the
+// low edge of the histogram bin b1 that holds the K-th largest chart value),
+// per block of DSP_ROWS rows the sum of the read lengths of each group and the
+// bound sum |v_i| * rowmax_i; the chart values that fall in bin b1 go to a
+// candidate list and a 1024-bin histogram of their next 10 bits.
 constexpr int DSP_ROWS = 256;
+constexpr int DSP_T = 1024;
 struct DispatchArgs {
   const float* v;
   const uint16_t* probes;   // [m][P]
-  const uint32_t* counts;   // [m][P][G]
+  const uint32_t* counts;   // [m][P][G4]
   const uint16_t* rowmax;   // [m] largest magnitude key per row
-  const uint32_t* result;   // cutoff bits
-  uint32_t* thresh;         // [m]
+  const uint32_t* hist;     // [HIST_BINS]
+  uint32_t* hist2;          // [1024], zero on entry
+  uint32_t* cand;           // [m * P] candidate chart values (bit patterns)
+  uint32_t* result;         // RES_NCAND (zero on entry), RES_BIN, RES_ABOVE written here
   uint32_t* runlen;         // [G][m]
   uint32_t* bsum;           // [ceil(m / DSP_ROWS)][G + 1]
-  int32_t* row_chart_kept;  // [m] or null
   int64_t m;
-  int32_t P, G;
+  int32_t P, G, G4;
+  uint32_t K;
 };
 
-// bucketMul: stream each (row, group) run prefix, keep entries whose magnitude
-// reaches the row threshold, scatter v_i * w into an LDS tile of the group's
-// output columns, then add the tile to y.  The entries of a group, concatenated
-// over rows, are split evenly over the group's waves.  The tile holds 64-bit
-// fixed-point sums (integer LDS atomics); the scale comes from the bound
-// sum_i |v_i| * rowmax_i >= |any partial sum|.
+// bucketMul: every block first finishes the exact cutoff (histograms + the
+// candidate list), then streams each (row, group) run prefix, keeps entries
+// whose magnitude reaches the row threshold, scatters v_i * w into an LDS tile
+// of the group's output columns and adds the tile to y.  The entries of a
+// group, concatenated over rows, are split evenly over the group's waves.  The
+// tile holds 64-bit fixed-point sums (integer LDS atomics); the scale comes from
+// the bound sum_i |v_i| * rowmax_i >= |any partial sum|.
 struct MulArgs {
   const float* v;
   const uint32_t* entries;  // [m][row_stride]
-  const uint32_t* thresh;   // [m]
   const uint32_t* runlen;   // [G][m]
   const uint32_t* bsum;     // [nbd][G + 1]
+  uint32_t* hist;           // [HIST_BINS], cleared here for the next call
+  const uint32_t* hist2;    // [1024]
+  const uint32_t* cand;     // candidate chart values
+  uint32_t* result;         // reads RES_NCAND, RES_BIN, RES_ABOVE; writes the cutoff, K', K
   float* y;                 // [n]
   int64_t m, n, row_stride;
   int32_t G, TW, nbd;
+  uint32_t K;
   // parity recording (null in the timed path)
   int32_t* row_kept;
   unsigned long long* fingerprint;

@@ -3,7 +3,9 @@
 // Layout blob (all offsets 256-byte aligned):
 //   [0, 256)        copy of the effort_desc
 //   probes          u16 [m][P]      fp16 magnitude bits at ranks ceil((k+1) n / P)
-//   counts          u32 [m][P][G]   cumulative entries of group g in rank segments 0..k
+//   counts          u32 [m][P][G4]  cumulative entries of group g in rank segments 0..k
+//                                   (G4 = G rounded up to 4, so a (row, segment) slice
+//                                   is 16-byte aligned)
 //   entries         u32 [m][G*TW]   per row, per group, the group's entries in rank
 //                                   order: low 16 bits = fp16 value bits, high 16
 //                                   bits = column index inside the group
@@ -29,7 +31,7 @@ inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 struct Geometry {
   int64_t m = 0, n = 0;
-  int32_t P = 0, G = 0, TW = 0;
+  int32_t P = 0, G = 0, G4 = 0, TW = 0;
   int64_t row_stride = 0;
   uint64_t off_probes = 0, off_counts = 0, off_entries = 0, off_rowmax = 0, total = 0;
 };
@@ -57,44 +59,40 @@ inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geomet
   g->n = n;
   g->P = P;
   g->G = (int32_t)G;
+  g->G4 = (int32_t)((G + 3) / 4 * 4);
   g->TW = (int32_t)tw;
   g->row_stride = G * tw;
   g->off_probes = kAlign;
   g->off_counts = align_up(g->off_probes + (uint64_t)m * P * 2, kAlign);
-  g->off_entries = align_up(g->off_counts + (uint64_t)m * P * G * 4, kAlign);
+  g->off_entries = align_up(g->off_counts + (uint64_t)m * P * g->G4 * 4, kAlign);
   g->off_rowmax = align_up(g->off_entries + (uint64_t)m * g->row_stride * 4, kAlign);
   g->total = align_up(g->off_rowmax + (uint64_t)m * 2, kAlign);
   return EFFORT_OK;
 }
 
 // Workspace of one vector (offsets in bytes from the vector's slice start).
-//   ctrl     u32[64]                  [0] done counter of the cutoff kernel
-//   result   u32[8]                   [0] cutoff bits, [1] K', [2] K
-//   boff     u32[SB][257]             per cutoff block: exclusive offsets of its 256 exponent bins
-//   sorted   f32[SB * 4096]           per cutoff block: its chart slice ordered by bin
-//   thresh   u32[m]                   per-row fp16 magnitude threshold
+//   result   u32[64]                  [0] cutoff bits, [1] K', [2] K, [3] candidates
+//   hist     u32[4096]                histogram of the chart's top 12 bits
+//   hist2    u32[1024]                bits 18..9 of the chart values in the cutoff's bin
+//   cand     u32[m*P]                 those chart values (bit patterns)
 //   runlen   u32[G][m]                per (group, row) entries to read
-//   bsum     u32[ceil(m/256)][G + 1]  per dispatch block: sum of runlen per group, then
-//                                     (as f32) the sum of |v_i| * rowmax_i over its rows
-// SB = ceil(m * P / 4096).
-constexpr int64_t kSelVals = 4096;
+//   bsum     u32[ceil(m/256)][G + 1]  per 256 rows: sum of runlen per group, then
+//                                     (as f32) the sum of |v_i| * rowmax_i
+// result, hist and hist2 are zero on entry and left zero.
 constexpr int64_t kDspRows = 256;
 
 struct WsLayout {
-  uint64_t ctrl, result, boff, sorted, thresh, runlen, bsum, slice;
+  uint64_t result, hist, hist2, cand, runlen, bsum, slice;
 };
 
 inline WsLayout ws_layout(const Geometry& g) {
-  const uint64_t N = (uint64_t)g.m * g.P;
-  const uint64_t SB = (N + kSelVals - 1) / kSelVals;
   const uint64_t nbd = ((uint64_t)g.m + kDspRows - 1) / kDspRows;
   WsLayout w;
-  w.ctrl = 0;
-  w.result = 256;
-  w.boff = 512;
-  w.sorted = align_up(w.boff + SB * 257 * 4, kAlign);
-  w.thresh = align_up(w.sorted + SB * kSelVals * 4, kAlign);
-  w.runlen = align_up(w.thresh + (uint64_t)g.m * 4, kAlign);
+  w.result = 0;
+  w.hist = 256;
+  w.hist2 = w.hist + 4096 * 4;
+  w.cand = align_up(w.hist2 + 1024 * 4, kAlign);
+  w.runlen = align_up(w.cand + (uint64_t)g.m * g.P * 4, kAlign);
   w.bsum = align_up(w.runlen + (uint64_t)g.G * g.m * 4, kAlign);
   w.slice = align_up(w.bsum + nbd * (g.G + 1) * 4, kAlign);
   return w;

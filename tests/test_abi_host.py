@@ -33,7 +33,8 @@ def rand_case(m, n, seed, tag="abi"):
 def decode(desc, blob):
     m, n, P, G, TW = desc.in_dim, desc.out_dim, desc.probes_per_row, desc.groups, desc.group_width
     pr = blob[desc.off_probes: desc.off_probes + m * P * 2].view(np.uint16).reshape(m, P)
-    cnt = blob[desc.off_counts: desc.off_counts + m * P * G * 4].view(np.uint32).reshape(m, P, G)
+    G4 = (G + 3) // 4 * 4
+    cnt = blob[desc.off_counts: desc.off_counts + m * P * G4 * 4].view(np.uint32).reshape(m, P, G4)[:, :, :G]
     ent = blob[desc.off_entries: desc.off_entries + m * desc.row_stride * 4].view(np.uint32)
     return pr, cnt, ent.reshape(m, desc.row_stride)
 
@@ -67,8 +68,8 @@ def test_layout_bytes_and_groups():
     m, n, P = 4096, 14336, 16
     nb = E.effort_layout_bytes(m, n, P)
     # entries dominate: 4 bytes per weight, plus probes and counts
-    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 7 + 2 * m
-    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 7 + 2 * m + 5 * 256
+    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 8 + 2 * m
+    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 8 + 2 * m + 5 * 256
 
 
 @pytest.mark.parametrize("args,code", [

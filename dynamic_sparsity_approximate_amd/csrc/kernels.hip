@@ -358,19 +358,26 @@ __device__ __forceinline__ void wave_locate(uint32_t count, uint32_t target, X x
                                             uint32_t* before) {
   const int lane = threadIdx.x & 63;
   uint32_t acc = 0;
-  for (uint32_t j0 = 0; j0 < count; j0 += 64) {
-    const uint32_t j = j0 + lane;
-    const uint32_t s = j < count ? x(j) : 0u;
-    const uint32_t inc = wave_incl_scan(s);
-    const uint32_t lo = acc + inc - s;
-    const unsigned long long hit = __ballot(s > 0u && lo <= target && target < lo + s);
-    if (hit) {
-      const int l = __ffsll((long long)hit) - 1;
-      *idx = j0 + (uint32_t)l;
-      *before = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
-      return;
+  for (uint32_t j0 = 0; j0 < count; j0 += 256) {
+    uint32_t s[4];  // 256 values loaded together, then scanned in order
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t j = j0 + (uint32_t)u * 64u + (uint32_t)lane;
+      s[u] = j < count ? x(j) : 0u;
     }
-    acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t inc = wave_incl_scan(s[u]);
+      const uint32_t lo = acc + inc - s[u];
+      const unsigned long long hit = __ballot(s[u] > 0u && lo <= target && target < lo + s[u]);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        *idx = j0 + (uint32_t)u * 64u + (uint32_t)l;
+        *before = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
+        return;
+      }
+      acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+    }
   }
   *idx = count;
   *before = acc;
@@ -516,8 +523,8 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
       bool have = false;
       uint4 cur[4], nxt[4];
       auto first_of = [&](uint32_t j, uint32_t* s0, uint32_t* e) {
-        *s0 = __builtin_amdgcn_readlane(aj, j);
-        *e = *s0 + __builtin_amdgcn_readlane(takej, j);
+        *s0 = (uint32_t)__builtin_amdgcn_readlane((int)aj, j);
+        *e = *s0 + (uint32_t)__builtin_amdgcn_readlane((int)takej, j);
       };
       auto issue = [&](uint32_t j, uint32_t s0, uint32_t s1, uint4* buf) {
         const uint4* base = reinterpret_cast<const uint4*>(
@@ -554,7 +561,7 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
         if (nhave) issue(nj, ns0, ns1, nxt);
 
         // process the current chunk
-        const uint32_t t = __builtin_amdgcn_readlane(tj, cj);
+        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tj, cj);
         const double vs = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(vsj), cj),
                                            __builtin_amdgcn_readlane(__double2loint(vsj), cj));
         const uint32_t row = rowb + cj;

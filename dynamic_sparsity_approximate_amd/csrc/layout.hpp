@@ -25,7 +25,7 @@
 namespace effort {
 
 constexpr uint64_t kAlign = 256;
-constexpr int32_t kTargetGroupWidth = 2048;
+constexpr int32_t kTargetGroupWidth = 4096;
 
 inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 

@@ -62,14 +62,15 @@ def test_strerror_names_codes():
 # ---------------------------------------------------------------- sizing
 
 def test_layout_bytes_and_groups():
-    assert E.effort_default_groups(14336) == 7
+    assert E.effort_default_groups(14336) == 4
+    assert E.effort_default_groups(4096) == 1
     assert E.effort_default_groups(1024) == 1
-    assert E.effort_default_groups(32000) == 16
+    assert E.effort_default_groups(32000) == 8
     m, n, P = 4096, 14336, 16
     nb = E.effort_layout_bytes(m, n, P)
-    # entries dominate: 4 bytes per weight, plus probes and counts
-    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 8 + 2 * m
-    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 8 + 2 * m + 5 * 256
+    # entries dominate: 4 bytes per weight, plus probes and counts (4 groups)
+    assert nb >= 4 * m * n + 2 * m * P + 4 * m * P * 4 + 2 * m
+    assert nb < 4 * m * n + 2 * m * P + 4 * m * P * 4 + 2 * m + 5 * 256
 
 
 @pytest.mark.parametrize("args,code", [

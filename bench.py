@@ -12,8 +12,9 @@ Timing:
     cache cannot serve repeats; the dense comparator cycles over its own copies;
   * the calls of one cycle are captured once in a HIP graph and the graph is
     replayed; hipEvents on the replay stream bracket the timed region;
-  * the bucketMul kernel's own duration comes from hipEvents recorded around
-    it (effort_matvec_timed) in eager calls queued behind graph replays.
+  * each kernel's own duration comes from a hipEvent pair that the runtime
+    stamps with that kernel's begin and end (effort_matvec_timed, launched with
+    hipExtLaunchKernelGGL), in eager calls queued behind graph replays.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -191,7 +192,7 @@ def main():
         # per-stage durations: events around each kernel of R eager calls.  A few
         # graph replays go first so the GPU is busy while the host enqueues the
         # eager calls; the eager calls then run back to back.
-        evs = [[E.effort_event_create() for _ in range(4)] for _ in range(R)]
+        evs = [[E.effort_event_create() for _ in range(6)] for _ in range(R)]
         head = max(1, int(math.ceil(3000.0 / max(us_per * R, 1.0))))
         sel, dsp, mul = [], [], []
         treps = max(1, min(reps, 50))
@@ -204,8 +205,8 @@ def main():
             for r in range(R):
                 e = evs[r]
                 sel.append(E.effort_event_elapsed_ms(e[0], e[1]))
-                dsp.append(E.effort_event_elapsed_ms(e[1], e[2]))
-                mul.append(E.effort_event_elapsed_ms(e[2], e[3]))
+                dsp.append(E.effort_event_elapsed_ms(e[2], e[3]))
+                mul.append(E.effort_event_elapsed_ms(e[4], e[5]))
         mul_us = statistics.mean(mul) * 1e3
         alg_mul = 4.0 * kept_mean + 4.0 * m + 4.0 * n
         alg_step = 4.0 * kept_mean + 2.0 * m * P + 4.0 * m + 4.0 * n

@@ -224,7 +224,9 @@ def effort_matvec_debug(desc, layout, v, effort: float, y, ws, ws_bytes: int, cu
 
 
 def effort_matvec_timed(desc, layout, v, effort: float, y, ws, ws_bytes: int, events, stream=None):
-    arr = (_p * 4)(*[e if e else None for e in events])
+    if len(events) != 6:
+        raise ValueError("events: six handles, (start, stop) for select, dispatch, bucketMul")
+    arr = (_p * 6)(*[e if e else None for e in events])
     _check(_lib.effort_matvec_timed(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
                                     _ptr(ws), ws_bytes, _stream(stream), arr), "effort_matvec_timed")
 

@@ -77,7 +77,7 @@ struct DebugOut {
 
 // One vector: select, dispatch, bucketMul on `s`.
 int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
-            uint8_t* ws, hipStream_t s, const DebugOut* dbg, hipEvent_t const* ev) {
+            uint8_t* ws, hipStream_t s, const DebugOut* dbg, const EventPair* ev) {
   const WsLayout w = ws_layout(g);
   uint32_t* result = reinterpret_cast<uint32_t*>(ws + w.result);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist);
@@ -102,7 +102,6 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
       return EFFORT_EHIP;
   }
 
-  if (ev && ev[0] && hip_failed(hipEventRecord(ev[0], s))) return EFFORT_EHIP;
   SelectArgs sa;
   sa.v = v;
   sa.probes = probes;
@@ -114,9 +113,8 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   sa.result = result;
   sa.y = y;
   sa.n = g.n;
-  if (hip_failed(e = launch_select(sa, s))) return EFFORT_EHIP;
+  if (hip_failed(e = launch_select(sa, s, ev ? &ev[0] : nullptr))) return EFFORT_EHIP;
 
-  if (ev && ev[1] && hip_failed(hipEventRecord(ev[1], s))) return EFFORT_EHIP;
   DispatchArgs da;
   da.v = v;
   da.probes = probes;
@@ -133,9 +131,8 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   da.G = g.G;
   da.G4 = g.G4;
   da.K = K;
-  if (hip_failed(e = launch_dispatch(da, s))) return EFFORT_EHIP;
+  if (hip_failed(e = launch_dispatch(da, s, ev ? &ev[1] : nullptr))) return EFFORT_EHIP;
 
-  if (ev && ev[2] && hip_failed(hipEventRecord(ev[2], s))) return EFFORT_EHIP;
   MulArgs ma;
   ma.v = v;
   ma.entries = entries;
@@ -159,8 +156,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   const bool record = dbg && (dbg->row_kept || dbg->fingerprint || dbg->mask);
   int bpg = (cu_count() + g.G - 1) / g.G;
   if (bpg < 1) bpg = 1;
-  if (hip_failed(e = launch_bucketmul(ma, record, bpg, s))) return EFFORT_EHIP;
-  if (ev && ev[3] && hip_failed(hipEventRecord(ev[3], s))) return EFFORT_EHIP;
+  if (hip_failed(e = launch_bucketmul(ma, record, bpg, s, ev ? &ev[2] : nullptr))) return EFFORT_EHIP;
 
   if (dbg && (dbg->cutoff || dbg->K) &&
       hip_failed(launch_debug_result(result, dbg->cutoff, dbg->K, s)))
@@ -187,12 +183,20 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
     if (dbg->row_kept && !aligned(dbg->row_kept, 4)) return EFFORT_EINVAL;
     if (dbg->cutoff && !aligned(dbg->cutoff, 4)) return EFFORT_EINVAL;
   }
+  EventPair ev[3];
+  if (events) {
+    for (int k = 0; k < 3; ++k) {
+      ev[k].start = static_cast<hipEvent_t>(events[2 * k]);
+      ev[k].stop = static_cast<hipEvent_t>(events[2 * k + 1]);
+      if (!ev[k].start != !ev[k].stop) return EFFORT_EINVAL;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* layout = static_cast<const uint8_t*>(layout_dev);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   for (int32_t b = 0; b < batch; ++b) {
     rc = run_one(g, layout, v_dev + (int64_t)b * g.m, effort, y_dev + (int64_t)b * g.n,
-                 ws + (uint64_t)b * w.slice, s, dbg, reinterpret_cast<hipEvent_t const*>(events));
+                 ws + (uint64_t)b * w.slice, s, dbg, events ? ev : nullptr);
     if (rc) return rc;
   }
   return EFFORT_OK;

@@ -19,6 +19,7 @@
 //                and finally adds the tile to y.
 // No MFMA: the multiply is a bandwidth-bound gather-scatter, not a contraction.
 #include <hip/hip_fp16.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -189,9 +190,13 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
   }
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev) {
   const int64_t blocks = (a.m + CH_T - 1) / CH_T;
-  hipLaunchKernelGGL(k_chart_hist, dim3((unsigned)blocks), dim3(CH_T), 0, s, a);
+  if (ev && ev->start)
+    hipExtLaunchKernelGGL(k_chart_hist, dim3((unsigned)blocks), dim3(CH_T), 0, s, ev->start, ev->stop,
+                          0, a);
+  else
+    hipLaunchKernelGGL(k_chart_hist, dim3((unsigned)blocks), dim3(CH_T), 0, s, a);
   return hipGetLastError();
 }
 
@@ -339,9 +344,13 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   }
 }
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev) {
   const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
-  hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, a);
+  if (ev && ev->start)
+    hipExtLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, ev->start, ev->stop,
+                          0, a);
+  else
+    hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, a);
   return hipGetLastError();
 }
 
@@ -625,10 +634,14 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     for (int b = threadIdx.x; b < HIST_BINS; b += MUL_T) a.hist[b] = 0u;
 }
 
-hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s) {
+hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
+                            const EventPair* ev) {
   const unsigned grid = (unsigned)(a.G * blocks_per_group);
   const size_t lds = (size_t)a.TW * sizeof(unsigned long long);
-  if (record)
+  if (ev && ev->start && !record)
+    hipExtLaunchKernelGGL(k_bucketmul<false>, dim3(grid), dim3(MUL_T), (uint32_t)lds, s, ev->start,
+                          ev->stop, 0, a.v, a.entries, a.runlen, a.bsum, a.result, a.y, a);
+  else if (record)
     hipLaunchKernelGGL(k_bucketmul<true>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
                        a.runlen, a.bsum, a.result, a.y, a);
   else

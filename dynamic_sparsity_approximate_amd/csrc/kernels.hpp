@@ -75,9 +75,18 @@ struct MulArgs {
   uint8_t* mask;
 };
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
-hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s);
+// Optional timing: when `start` is set, the kernel is launched with
+// hipExtLaunchKernelGGL and the runtime stamps `start`/`stop` with the kernel's
+// own begin and end.
+struct EventPair {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev = nullptr);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev = nullptr);
+hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
+                            const EventPair* ev = nullptr);
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                              int lanes_per_row, int row_splits, hipStream_t s);
 hipError_t launch_dense_gemm_small(const uint16_t* W, const float* v, int batch, int64_t m,

@@ -156,10 +156,12 @@ int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const f
                         float* cutoff_dev, int64_t* K_dev, int32_t* row_kept_dev,
                         uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, void* stream);
 
-/* effort_matvec that also records hipEvent_t events[0..3] (each may be NULL) on
-   `stream`: before the cutoff kernel, before the dispatch kernel, before the
-   bucketMul kernel, after it.  For measurement.  EUNSUPPORTED while `stream` is
-   being captured into a graph. */
+/* effort_matvec with kernel timing, for measurement.  events[0..5] are hipEvent_t
+   pairs (start, stop) for the cutoff kernel, the dispatch kernel and the
+   bucketMul kernel; the runtime stamps each pair with that kernel's own begin
+   and end (hipExtLaunchKernelGGL).  A pair may be (NULL, NULL) to leave that
+   kernel untimed; a pair with one NULL member is EINVAL.  EUNSUPPORTED while
+   `stream` is being captured into a graph. */
 int effort_matvec_timed(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                         float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
                         void* stream, void* const* events);

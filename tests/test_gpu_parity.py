@@ -256,3 +256,30 @@ def test_graph_replays_match_eager():
         # eager work between replays, on the same workspace
         other = M.matvec_debug(vt, 0.5 if rep % 2 else 0.25, with_mask=False)
         assert other["K"] > 0
+
+
+def test_timed_entry_matches_and_stamps_kernels():
+    """effort_matvec_timed gives the untimed result and a positive duration for
+    each of its three kernels; a half-set event pair is rejected."""
+    d = dev()
+    W, v = case(2048, 4096, seed=11, tag="timed")
+    M = E.EffortMatrix(W, P=16, device=d)
+    vt = torch.from_numpy(v).to(d)
+    ref = M.matvec_debug(vt, 0.25, with_mask=False)
+    y = torch.empty(4096, dtype=torch.float32, device=d)
+    evs = [E.effort_event_create() for _ in range(6)]
+    try:
+        for _ in range(3):
+            E.effort_matvec_timed(M.desc, M.layout, vt, 0.25, y, M.ws, M.ws_bytes, evs)
+            torch.cuda.synchronize()
+            assert rel_l2(y.cpu().numpy(), ref["y"]) < 1e-6
+            for k in range(3):
+                ms = E.effort_event_elapsed_ms(evs[2 * k], evs[2 * k + 1])
+                assert 0.0 < ms < 100.0, (k, ms)
+        with pytest.raises(E.EffortError):
+            E.effort_matvec_timed(M.desc, M.layout, vt, 0.25, y, M.ws, M.ws_bytes,
+                                  [evs[0], None, None, None, None, None])
+    finally:
+        torch.cuda.synchronize()
+        for e in evs:
+            E.effort_event_destroy(e)

@@ -149,6 +149,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   ma.G = g.G;
   ma.TW = g.TW;
   ma.nbd = (int32_t)((g.m + kDspRows - 1) / kDspRows);
+  ma.P = g.P;
   ma.K = K;
   ma.row_kept = dbg ? dbg->row_kept : nullptr;
   ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;

@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "effort.h"
 #include "kernels.hpp"
 
 namespace effort {
@@ -214,11 +215,39 @@ __device__ __forceinline__ uint32_t key_threshold(float av, float c) {
   return lo;
 }
 
+// The same threshold from an estimate: k = fp16(c / av) is within one key of
+// it (the fp32 quotient is far finer than an fp16 step), so checking the exact
+// products at k - 2 .. k + 1 settles it; out-of-range quotients, tiny av and
+// any check that does not bracket the answer fall back to bisection.
+__device__ __forceinline__ uint32_t key_threshold_fast(float av, float c) {
+  if (!(c > 0.0f)) return 0u;
+  const float q = c * __builtin_amdgcn_rcpf(av);
+  if (av >= 0x1p-100f && q <= 65504.0f) {
+    const uint32_t k = (uint32_t)__half_as_ushort(__float2half_rn(q));
+    auto ok = [&](uint32_t key) { return __fmul_rn(av, h2f(key)) >= c; };
+    const bool o1 = k > 0u && ok(k - 1u);
+    const bool o2 = k > 1u && ok(k - 2u);
+    const bool o0 = ok(k);
+    const bool p1 = k + 1u >= 0x7C00u || ok(k + 1u);
+    if (o1 && !o2) return k - 1u;
+    if (!o1 && o0) return k;
+    if (!o0 && p1) return k + 1u;
+  }
+  return key_threshold(av, c);
+}
+
+static_assert(DSP_T == DSP_ROWS, "one dispatch block per block of rows");
+static_assert(HIST_BINS == 16 * DSP_T, "each dispatch thread holds 16 histogram bins");
+
+// One block per DSP_ROWS rows, one thread per row.  Every block finds the bin
+// b1 of the K-th largest chart value from the histogram (16 bins per thread in
+// registers, one block scan).  With lo = the bin's low edge (a lower bound of
+// the cutoff), a row keeps whole the probe segments whose chart value is >= lo
+// (probes are descending, so these are segments 0..q-1), and the read length
+// of (row, group) covers segments 0..min(q, P-1) through the counts table.
 __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
-  __shared__ uint32_t hist[HIST_BINS];
-  __shared__ uint32_t h2[1024];
   __shared__ uint32_t tmp[DSP_T / 64 + 1];
-  __shared__ uint32_t sres[8];
+  __shared__ uint32_t sres[2];
   __shared__ uint32_t red[16 * (DSP_T / 64)];
   __shared__ float redf[DSP_T / 64];
   const int tid = threadIdx.x;
@@ -226,7 +255,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   const int64_t i = (int64_t)blockIdx.x * DSP_T + tid;
   const bool valid = i < a.m;
   const int G1 = a.G + 1;
-  // row data first (independent of the cutoff), then the histogram
+  // row data and this thread's 16 histogram bins, all loads issued together
   float av = 0.0f;
   uint32_t rmax = 0u;
   uint32_t pk[PMAXR];
@@ -235,16 +264,36 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
     rmax = a.rowmax[i];
     if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, pk);
   }
-  for (int b = tid; b < HIST_BINS; b += DSP_T) hist[b] = a.hist[b];
-  for (int b = tid; b < 1024; b += DSP_T) h2[b] = 0u;
+  const int hb = HIST_BINS - 16 * (tid + 1);  // bins hb .. hb + 15, thread 0 holds the top
+  uint32_t h[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 q4 = *reinterpret_cast<const uint4*>(a.hist + hb + 4 * c);
+    h[4 * c] = q4.x;
+    h[4 * c + 1] = q4.y;
+    h[4 * c + 2] = q4.z;
+    h[4 * c + 3] = q4.w;
+  }
+  uint32_t hs = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) hs += h[k];
+  uint32_t tot;
+  uint32_t above = block_excl_scan<DSP_T>(hs, tmp, &tot);
+  if (above < a.K && a.K <= above + hs) {
+#pragma unroll
+    for (int k = 15; k >= 0; --k) {
+      if (above < a.K && a.K <= above + h[k]) {
+        sres[0] = (uint32_t)(hb + k);
+        sres[1] = above;
+      }
+      above += h[k];
+    }
+  }
   __syncthreads();
-  find_from_top<DSP_T>(hist, HIST_BINS, a.K, tmp, sres);
   const uint32_t b1 = sres[0] & (HIST_BINS - 1);
   const uint32_t above1 = sres[1];
-  // the K-th largest chart value lies in bin b1: its low edge bounds the cutoff below
-  const float lo = __uint_as_float(b1 << HIST_SHIFT);
-  const uint32_t t = key_threshold(av, lo);
-  const bool none = !valid || rmax < t;  // no entry of the row can pass
+  const uint32_t lo_bits = b1 << HIST_SHIFT;
+  const bool none = !valid || __float_as_uint(__fmul_rn(av, h2f(rmax))) < lo_bits;
   int32_t q = 0;
   uint32_t hits = 0u;  // chart entries of this row in bin b1 (P <= PMAXR)
   if (valid) {
@@ -252,29 +301,30 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
 #pragma unroll
       for (int k = 0; k < PMAXR; ++k) {
         if (k < a.P) {
-          q += pk[k] >= t ? 1 : 0;  // probes are descending keys: q = segments kept whole
           const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pk[k])));
+          q += bits >= lo_bits ? 1 : 0;
           if ((bits >> HIST_SHIFT) == b1) {
             hits |= 1u << k;
-            atomicAdd(&h2[(bits >> 9) & 1023u], 1u);
+            atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
           }
         }
       }
     } else {
       const uint16_t* pr = a.probes + i * a.P;
       for (int k = 0; k < a.P; ++k) {
-        const uint32_t key = pr[k];
-        q += key >= t ? 1 : 0;
-        const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key)));
-        if ((bits >> HIST_SHIFT) == b1) atomicAdd(&h2[(bits >> 9) & 1023u], 1u);
+        const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pr[k])));
+        q += bits >= lo_bits ? 1 : 0;
+        if ((bits >> HIST_SHIFT) == b1) {
+          atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
+          a.cand[atomicAdd(&a.result[RES_NCAND], 1u)] = bits;
+        }
       }
     }
   }
   const int32_t qc = q < a.P ? q : a.P - 1;
   const uint32_t* cr = a.counts + ((size_t)(valid ? i : 0) * a.P + qc) * a.G4;
   constexpr int GCH = 16;  // groups per pass: their counts are loaded before any store
-  constexpr int SUBS = DSP_T / DSP_ROWS;
-  constexpr int WPS = DSP_ROWS / 64;
+  constexpr int NW = DSP_T / 64;
   // bound on |any sum of products| of the row
   const float bs = wave_sum_f(valid ? av * h2f(rmax) : 0.0f);
   if (lane == 0) redf[wid] = bs;
@@ -293,39 +343,32 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
     for (int u = 0; u < GCH; ++u) {
       if (g0 + u >= a.G) L[u] = 0u;
       const uint32_t s = wave_sum(L[u]);
-      if (lane == 0) red[u * (DSP_T / 64) + wid] = s;
+      if (lane == 0) red[u * NW + wid] = s;
     }
-    __syncthreads();  // no global store is outstanding here
+    __syncthreads();
     if (valid)
 #pragma unroll
       for (int u = 0; u < GCH; ++u)
         if (g0 + u < a.G) a.runlen[(size_t)(g0 + u) * a.m + i] = L[u];
-    for (int x = tid; x < GCH * SUBS; x += DSP_T) {
-      const int u = x / SUBS, sub = x % SUBS;
-      const int64_t sbt = (int64_t)blockIdx.x * SUBS + sub;
-      if (g0 + u < a.G && sbt * DSP_ROWS < a.m) {
-        uint32_t tot = 0;
-        for (int w = 0; w < WPS; ++w) tot += red[u * (DSP_T / 64) + sub * WPS + w];
-        a.bsum[(size_t)sbt * G1 + g0 + u] = tot;
-      }
+    if (tid < GCH && g0 + tid < a.G) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += red[tid * NW + w];
+      a.bsum[(size_t)blockIdx.x * G1 + g0 + tid] = t;
     }
-    if (g0 == 0 && tid < SUBS) {
-      const int64_t sbt = (int64_t)blockIdx.x * SUBS + tid;
-      if (sbt * DSP_ROWS < a.m) {
-        float tot = 0.0f;
-        for (int w = 0; w < WPS; ++w) tot += redf[tid * WPS + w];
-        a.bsum[(size_t)sbt * G1 + a.G] = __float_as_uint(tot);
-      }
+    if (g0 == 0 && tid == 0) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += redf[w];
+      a.bsum[(size_t)blockIdx.x * G1 + a.G] = __float_as_uint(t);
     }
     if (g0 + GCH < a.G) __syncthreads();  // red[] is reused (more than GCH groups)
   }
-  // the bin's refinement histogram and its values, for the exact cutoff
   if (blockIdx.x == 0 && tid == 0) {
     a.result[RES_BIN] = b1;
     a.result[RES_ABOVE] = above1;
   }
-  for (int b = tid; b < 1024; b += DSP_T)
-    if (h2[b]) atomicAdd(&a.hist2[b], h2[b]);
+  // the chart values in bin b1, for the exact cutoff
   if (a.P <= PMAXR) {
     const uint32_t c = (uint32_t)__popc(hits);
     const uint32_t incl = wave_incl_scan(c);
@@ -335,12 +378,6 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
 #pragma unroll
     for (int k = 0; k < PMAXR; ++k)
       if ((hits >> k) & 1u) a.cand[base++] = __float_as_uint(__fmul_rn(av, h2f(pk[k])));
-  } else if (valid) {
-    const uint16_t* pr = a.probes + i * a.P;
-    for (int k = 0; k < a.P; ++k) {
-      const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pr[k])));
-      if ((bits >> HIST_SHIFT) == b1) a.cand[atomicAdd(&a.result[RES_NCAND], 1u)] = bits;
-    }
   }
 }
 
@@ -357,6 +394,16 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair
 // ---------------------------------------------------------------- bucketMul
 
 constexpr int MUL_T = 1024;
+constexpr int CH = 256;  // entries per chunk: one 16-byte quad per lane
+
+struct Chunk {
+  uint32_t j, s0, s1;  // row of the batch, entries [s0, s1) of its run
+  bool valid;
+};
+
+// Word 3 of a raw buffer descriptor on gfx9-family chips: 32-bit data format
+// (a zero format would make every access out of range).
+constexpr int kBufferDword3 = 0x00020000;
 constexpr int MUL_W = MUL_T / 64;
 
 // Finds, among `count` non-negative values x[0..count) (x(j) loads one), the
@@ -404,61 +451,64 @@ __device__ __forceinline__ int64_t fixed_product(uint32_t w, double vs) {
   return (int64_t)(__double_as_longlong(d) - __double_as_longlong(kMagic));
 }
 
-// Exact cutoff from the bin b1 (and the count of values above it), the 1024-bin
-// histogram of the bin's next 10 bits and the bin's values: two more radix
-// digits.  Every block computes it; all get the same value.
-__device__ uint32_t exact_cutoff(const MulArgs& a, uint32_t* hs, uint32_t* tmp, uint32_t* sres,
-                                 uint32_t* kprime) {
-  const int tid = threadIdx.x;
-  const uint32_t b1 = a.result[RES_BIN], above1 = a.result[RES_ABOVE];
-  const uint32_t nc = a.result[RES_NCAND];
-  for (int b = tid; b < 1024; b += MUL_T) hs[b] = a.hist2[b];
-  __syncthreads();
-  const uint32_t K1 = a.K - above1;
-  find_from_top<MUL_T>(hs, 1024, K1, tmp, sres);
-  const uint32_t b2 = sres[0] & 1023u, above2 = sres[1];
-  const uint32_t K2 = K1 - above2;
-  const uint32_t pre = (b1 << 10) | b2;  // bits 30..9
-  __syncthreads();
-  for (int b = tid; b < 512; b += MUL_T) hs[b] = 0u;
-  __syncthreads();
-  for (uint32_t p0 = 0; p0 < nc; p0 += MUL_T * 4u) {
-    uint32_t bits[4];
+// wave_locate over 256 values already in registers: x[u] holds index u * 64 + lane
+// (zero at and beyond `count`).
+__device__ __forceinline__ void wave_locate_regs(const uint32_t* x, uint32_t count, uint32_t target,
+                                                 uint32_t* idx, uint32_t* before) {
+  uint32_t acc = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t p = p0 + (uint32_t)u * MUL_T + tid;
-      bits[u] = p < nc ? a.cand[p] : 0xFFFFFFFFu;
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t inc = wave_incl_scan(x[u]);
+    const uint32_t lo = acc + inc - x[u];
+    const unsigned long long hit = __ballot(x[u] > 0u && lo <= target && target < lo + x[u]);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      *idx = (uint32_t)u * 64u + (uint32_t)l;
+      *before = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
+      return;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (bits[u] != 0xFFFFFFFFu && (bits[u] >> 9) == pre) atomicAdd(&hs[bits[u] & 511u], 1u);
+    acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
   }
-  __syncthreads();
-  find_from_top<MUL_T>(hs, 512, K2, tmp, sres);
-  const uint32_t b3 = sres[0] & 511u, above3 = sres[1];
-  *kprime = above1 + above2 + above3 + hs[b3];
-  __syncthreads();
-  return (pre << 9) | b3;
+  *idx = count;
+  *before = acc;
 }
 
+// Block (g, s) of the grid: group g's LDS tile, share s of its entries.
+//
+// Prologue, three dependent rounds of global loads:
+//   (1) the cutoff's bin, the refinement histogram, the first 4 * MUL_T
+//       candidate chart values, and (wave 0) the per-256-row sums that place
+//       each wave's share, scanned once into LDS;
+//   (2) the run lengths and activations of the 256 rows where each wave's
+//       share starts, in flight while the block finishes the exact cutoff
+//       (bits 18..9 from the refinement histogram, bits 8..0 from the
+//       candidates; every block computes the same value);
+//   (3) the share's first chunks of entries, in flight while each row's fp16
+//       key threshold is derived from the cutoff.
+//
+// Accumulation: with B >= |any sum of kept products| and B * 1.001 < 2^eB,
+// the scale 2^S, S = 30 - eB, keeps every tile sum below 2^30 in magnitude.
+// A kept product is fl32(w * v * 2^S) rounded to an integer (relative error
+// 2^-24 plus half a unit of 2^-S) and added to the column's int32 LDS word;
+// integer adds make the tile independent of order.
 template <bool REC>
 __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
     const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
-  extern __shared__ unsigned long long tile[];
+  static_assert(MUL_T == 1024, "one refinement-histogram bin per thread");
+  __shared__ int32_t tile[EFFORT_MAX_GROUP_WIDTH];
   __shared__ uint32_t hs[1024];
+  __shared__ uint32_t hs3[512];
   __shared__ uint32_t ctmp[MUL_T / 64 + 1];
   __shared__ uint32_t csres[8];
-  (void)result;
-  uint32_t kprime;
-  const uint32_t cut_bits = exact_cutoff(a, hs, ctmp, csres, &kprime);
-  const float cutoff = __uint_as_float(cut_bits);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.result[RES_CUTOFF] = cut_bits;
-    a.result[RES_KPRIME] = kprime;
-    a.result[RES_K] = a.K;
-  }
+  __shared__ uint32_t pfx[256];  // inclusive prefix sums of the group's per-256-row sums
+  __shared__ uint32_t sT;
+  __shared__ int32_t sS;
+  __shared__ uint32_t mrl[MUL_W][DSP_ROWS];  // per wave: run lengths of its first 256 rows
+  __shared__ float mv[MUL_W][DSP_ROWS];      // and their activations
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
   const int G = a.G;
   const int G1 = G + 1;
   const int g = (int)(blockIdx.x % (unsigned)G);
@@ -466,178 +516,326 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
   const uint32_t bpg = gridDim.x / (unsigned)G;
   const int64_t col0 = (int64_t)g * a.TW;
   const int tw = (int)((int64_t)a.TW < a.n - col0 ? (int64_t)a.TW : a.n - col0);
-  for (int c = threadIdx.x; c < tw; c += MUL_T) tile[c] = 0ull;
-
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint32_t m = (uint32_t)a.m;
   const uint32_t nbd = (uint32_t)a.nbd;
   const uint32_t* rl = runlen + (size_t)g * a.m;
 
-  // group total and the fixed-point scale
-  uint32_t T = 0;
-  float B = 0.0f;
-  for (uint32_t b0 = 0; b0 < nbd; b0 += 64) {
-    const uint32_t b = b0 + lane;
-    T += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
-    B += wave_sum_f(b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f);
+  // ---- round 1
+  const uint32_t h2v = a.hist2[tid];
+  const uint32_t b1 = result[RES_BIN], above1 = result[RES_ABOVE], nc = result[RES_NCAND];
+  uint32_t cb[4];  // candidates p < min(m * P, 4 * MUL_T); those at p >= nc are ignored
+  {
+    const uint64_t cap = (uint64_t)a.m * (uint64_t)a.P;
+    const uint32_t ncap = (uint32_t)(cap < 4u * MUL_T ? cap : 4u * MUL_T);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.cand, (short)0, (int)(ncap * 4u), kBufferDword3);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      cb[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u * MUL_T + tid) * 4, 0, 0);
   }
-  int eB = 0;
-  frexpf(B * 1.001f + 1e-38f, &eB);  // B * 1.001 < 2^eB; the margin covers float summation
-  const int S = __builtin_amdgcn_readfirstlane(50 - eB);
+  if (wid == 0) {
+    uint32_t sb[4];
+    float sf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
+      sb[u] = b < nbd ? bsum[(size_t)b * G1 + g] : 0u;
+      sf[u] = b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f;
+    }
+    uint32_t acc = 0;
+    float B = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t inc = wave_incl_scan(sb[u]);
+      pfx[u * 64 + lane] = acc + inc;
+      acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      B += wave_sum_f(sf[u]);
+    }
+    for (uint32_t b0 = 256; b0 < nbd; b0 += 64) {  // more than 256 blocks of rows
+      const uint32_t b = b0 + lane;
+      acc += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
+      B += wave_sum_f(b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f);
+    }
+    if (lane == 0) {
+      int eB = 0;
+      frexpf(B * 1.001f + 1e-38f, &eB);  // the margin covers float summation
+      sT = acc;
+      sS = 30 - eB;
+    }
+  }
+  for (int c = tid; c < tw; c += MUL_T) tile[c] = 0;
+  if (tid < 512) hs3[tid] = 0u;
+  hs[tid] = h2v;
   __syncthreads();
+  const uint32_t T = sT;
+  const int S = sS;
 
   // this wave's share [start, end) of the group's entries, concatenated over rows
   const uint64_t nslots = (uint64_t)bpg * MUL_W;
   const uint64_t slot = (uint64_t)bslot * MUL_W + wid;
   const uint32_t start = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T * slot / nslots));
   const uint32_t end = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T * (slot + 1) / nslots));
+  const bool active = start < end;
 
-  if (start < end) {
-    uint32_t bstar, before_b;
-    wave_locate(nbd, start, [&](uint32_t b) { return bsum[(size_t)b * G1 + g]; }, &bstar, &before_b);
-    const uint32_t r0 = bstar < nbd ? bstar * DSP_ROWS : m;
-    const uint32_t nr = r0 < m ? (m - r0 < (uint32_t)DSP_ROWS ? m - r0 : (uint32_t)DSP_ROWS) : 0u;
+  // the 256-row block where the share starts: first prefix above start
+  uint32_t bstar = nbd, before_b = 0;
+  if (active) {
+    if (nbd <= 256u) {
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
+        const unsigned long long hit = __ballot(b < nbd && pfx[b] > start);
+        if (hit) {
+          bstar = (uint32_t)u * 64u + (uint32_t)(__ffsll((long long)hit) - 1);
+          before_b = bstar > 0u ? pfx[bstar - 1u] : 0u;
+          break;
+        }
+      }
+    } else {
+      wave_locate(nbd, start, [&](uint32_t b) { return bsum[(size_t)b * G1 + g]; }, &bstar, &before_b);
+    }
+  }
+  const uint32_t r0 = bstar < nbd ? bstar * DSP_ROWS : m;
+  const uint32_t nr = r0 < m ? (m - r0 < (uint32_t)DSP_ROWS ? m - r0 : (uint32_t)DSP_ROWS) : 0u;
+
+  // ---- round 2
+  uint32_t lr[4];
+  float lv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t j = (uint32_t)u * 64u + (uint32_t)lane;
+    lr[u] = j < nr ? rl[r0 + j] : 0u;
+    lv[u] = j < nr ? vvec[r0 + j] : 0.0f;
+  }
+  // the exact cutoff, meanwhile
+  const uint32_t K1 = a.K - above1;
+  find_from_top<MUL_T>(hs, 1024, K1, ctmp, csres);
+  const uint32_t b2 = csres[0] & 1023u, above2 = csres[1];
+  const uint32_t K2 = K1 - above2;
+  const uint32_t pre = (b1 << 10) | b2;  // bits 30..9 of the cutoff
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t p = (uint32_t)u * MUL_T + (uint32_t)tid;
+    if (p < nc && (cb[u] >> 9) == pre) atomicAdd(&hs3[cb[u] & 511u], 1u);
+  }
+  for (uint32_t p0 = 4u * MUL_T; p0 < nc; p0 += 4u * MUL_T) {  // more than 4 * MUL_T candidates
+    uint32_t bits[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t p = p0 + (uint32_t)u * MUL_T + (uint32_t)tid;
+      bits[u] = p < nc ? a.cand[p] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t p = p0 + (uint32_t)u * MUL_T + (uint32_t)tid;
+      if (p < nc && (bits[u] >> 9) == pre) atomicAdd(&hs3[bits[u] & 511u], 1u);
+    }
+  }
+  __syncthreads();  // hs3 complete; every thread has read csres
+  find_from_top<MUL_T>(hs3, 512, K2, ctmp, csres);
+  const uint32_t b3 = csres[0] & 511u, above3 = csres[1];
+  const uint32_t cut_bits = (pre << 9) | b3;
+  const float cutoff = __uint_as_float(cut_bits);
+  if (blockIdx.x == 0 && tid == 0) {
+    a.result[RES_CUTOFF] = cut_bits;
+    a.result[RES_KPRIME] = above1 + above2 + above3 + hs3[b3];
+    a.result[RES_K] = a.K;
+  }
+
+  // ---- round 3: the share's first rows, their chunks in flight
+  uint32_t remaining = end - start;
+  uint32_t rowb = m, offb = 0;
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mrl[wid][u * 64 + lane] = lr[u];
+      mv[wid][u * 64 + lane] = lv[u];
+    }
     uint32_t jrow = 0, before_r = 0;
-    if (nr > 0u)
-      wave_locate(nr, start - before_b, [&](uint32_t j) { return rl[r0 + j]; }, &jrow, &before_r);
-    uint32_t rowb = __builtin_amdgcn_readfirstlane(jrow < nr ? r0 + jrow : m);
-    uint32_t offb = __builtin_amdgcn_readfirstlane(start - before_b - before_r);
-    uint32_t remaining = end - start;
+    if (nr > 0u) wave_locate_regs(lr, nr, start - before_b, &jrow, &before_r);
+    rowb = __builtin_amdgcn_readfirstlane(jrow < nr ? r0 + jrow : m);
+    offb = __builtin_amdgcn_readfirstlane(start - before_b - before_r);
+  }
 
-    while (remaining > 0u && rowb < m) {
-      // metadata of up to 64 rows, one per lane
-      const uint32_t r = rowb + (uint32_t)lane;
-      uint32_t Lj = 0u;
-      float vj = 0.0f;
-      if (r < m) {
-        Lj = min(rl[r], (uint32_t)tw);
+  // batch state: up to 64 rows from rowb, one per lane
+  uint32_t Lj = 0u, aj = 0u, takej = 0u, batch_take = 0u;
+  float vj = 0.0f;
+  unsigned long long todo = 0ull;
+  // chunk sequence: row sj of the batch, entries [ss, se) not yet issued
+  uint32_t sj = 0u, ss = 0u, se = 0u;
+
+  auto batch_meta = [&]() {
+    const uint32_t r = rowb + (uint32_t)lane;
+    Lj = 0u;
+    vj = 0.0f;
+    if (r < m) {
+      if (r >= r0 && r - r0 < nr) {
+        Lj = mrl[wid][r - r0];
+        vj = mv[wid][r - r0];
+      } else {
+        Lj = rl[r];
         vj = vvec[r];
       }
-      const uint32_t tj = Lj ? key_threshold(fabsf(vj), cutoff) : 0x7C00u;
-      const uint32_t aj = lane == 0 ? offb : 0u;
-      const uint32_t lenj = Lj > aj ? Lj - aj : 0u;
-      const uint32_t incl = wave_incl_scan(lenj);
-      const uint32_t excl = incl - lenj;
-      const uint32_t takej = excl >= remaining ? 0u : min(lenj, remaining - excl);
-      const uint32_t batch_take =
-          min((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), remaining);
-      // clamped: only a row whose weights are all zero can exceed it, and its
-      // products stay 0
-      const double vsj = fmin(fmax(ldexp((double)vj, S), -0x1p100), 0x1p100);
-      unsigned long long todo = __ballot(takej > 0u);
-
-      // chunks of <= 1024 entries of one row; the next chunk's loads are in
-      // flight while the current one is processed
-      uint32_t cj = 0, cs0 = 0, cs1 = 0, ce = 0;
-      bool have = false;
-      uint4 cur[4], nxt[4];
-      auto first_of = [&](uint32_t j, uint32_t* s0, uint32_t* e) {
-        *s0 = (uint32_t)__builtin_amdgcn_readlane((int)aj, j);
-        *e = *s0 + (uint32_t)__builtin_amdgcn_readlane((int)takej, j);
-      };
-      auto issue = [&](uint32_t j, uint32_t s0, uint32_t s1, uint4* buf) {
-        const uint4* base = reinterpret_cast<const uint4*>(
-            entries + (size_t)(rowb + j) * (size_t)a.row_stride + col0);
-        const uint32_t o = (s0 & ~3u) + (uint32_t)lane * 4u;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t p = o + (uint32_t)u * 256u;
-          buf[u] = p < s1 ? base[p >> 2] : make_uint4(0u, 0u, 0u, 0u);
-        }
-      };
-      if (todo) {
-        cj = (uint32_t)(__ffsll((long long)todo) - 1);
-        todo &= todo - 1ull;
-        first_of(cj, &cs0, &ce);
-        cs1 = min(ce, (cs0 & ~3u) + 1024u);
-        issue(cj, cs0, cs1, cur);
-        have = true;
-      }
-      while (have) {
-        // next chunk: rest of this row, else the next row with entries
-        uint32_t nj = cj, ns0 = cs1, ne = ce;
-        bool nhave = true;
-        if (cs1 >= ce) {
-          if (todo) {
-            nj = (uint32_t)(__ffsll((long long)todo) - 1);
-            todo &= todo - 1ull;
-            first_of(nj, &ns0, &ne);
-          } else {
-            nhave = false;
-          }
-        }
-        const uint32_t ns1 = min(ne, (ns0 & ~3u) + 1024u);
-        if (nhave) issue(nj, ns0, ns1, nxt);
-
-        // process the current chunk
-        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tj, cj);
-        const double vs = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(vsj), cj),
-                                           __builtin_amdgcn_readlane(__double2loint(vsj), cj));
-        const uint32_t row = rowb + cj;
-        uint32_t cnt = 0u;
-        uint64_t fp = 0u;
-        const uint32_t o = (cs0 & ~3u) + (uint32_t)lane * 4u;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t p = o + (uint32_t)u * 256u;
-          const uint32_t ev[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-#pragma unroll
-          for (int k2 = 0; k2 < 4; ++k2) {
-            const uint32_t w = ev[k2];
-            const uint32_t pos = p + (uint32_t)k2;
-            if (pos >= cs0 && pos < cs1 && (w & 0x7FFFu) >= t) {
-              atomicAdd(&tile[w >> 16], (unsigned long long)fixed_product(w, vs));
-              if (REC) {
-                const uint64_t flat = (uint64_t)row * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
-                if (a.mask) a.mask[flat] = 1u;
-                fp += pair_hash(flat);
-                ++cnt;
-              }
-            }
-          }
-        }
-        if (REC) {
-          uint32_t flo = (uint32_t)fp, fhi = (uint32_t)(fp >> 32);
-          for (int sh = 32; sh > 0; sh >>= 1) {
-            cnt += __shfl_xor(cnt, sh, 64);
-            const uint32_t olo = __shfl_xor(flo, sh, 64);
-            const uint32_t ohi = __shfl_xor(fhi, sh, 64);
-            const uint64_t sum = ((uint64_t)fhi << 32 | flo) + ((uint64_t)ohi << 32 | olo);
-            flo = (uint32_t)sum;
-            fhi = (uint32_t)(sum >> 32);
-          }
-          if (lane == 0) {
-            if (cnt && a.row_kept) atomicAdd(&a.row_kept[row], (int32_t)cnt);
-            if (a.fingerprint) atomicAdd(a.fingerprint, ((unsigned long long)fhi << 32) | flo);
-          }
-        }
-        cj = nj;
-        cs0 = ns0;
-        cs1 = ns1;
-        ce = ne;
-        have = nhave;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
-      }
-      remaining -= batch_take;
-      rowb += 64u;
-      offb = 0u;
+      Lj = min(Lj, (uint32_t)tw);
     }
+    aj = lane == 0 ? offb : 0u;
+    const uint32_t lenj = Lj > aj ? Lj - aj : 0u;
+    const uint32_t incl = wave_incl_scan(lenj);
+    const uint32_t excl = incl - lenj;
+    takej = excl >= remaining ? 0u : min(lenj, remaining - excl);
+    batch_take = min((uint32_t)__builtin_amdgcn_readlane((int)incl, 63), remaining);
+    todo = __ballot(takej > 0u);
+    sj = 0u;
+    ss = 0u;
+    se = 0u;
+  };
+  // Next chunk of the batch: <= CH entries of one row, one 16-byte quad per
+  // lane.  Wave-uniform.
+  auto take = [&](Chunk& c) {
+    if (ss >= se && todo) {
+      sj = (uint32_t)(__ffsll((long long)todo) - 1);
+      todo &= todo - 1ull;
+      ss = (uint32_t)__builtin_amdgcn_readlane((int)aj, sj);
+      se = ss + (uint32_t)__builtin_amdgcn_readlane((int)takej, sj);
+    }
+    c.valid = ss < se;
+    c.j = sj;
+    c.s0 = ss;
+    c.s1 = c.valid ? min(se, (ss & ~3u) + (uint32_t)CH) : 0u;
+    ss = c.valid ? c.s1 : ss;
+  };
+  // Loads the chunk's quad for this lane through a buffer descriptor whose
+  // range ends at s1: words past it read as zero without a memory access (the
+  // range is checked per 4-byte word), so every lane issues the load and the
+  // wait counters stay exact.  An empty chunk (s1 = 0) accesses no memory.
+  auto issue = [&](const Chunk& c, uint4& buf) {
+    const uint32_t* base = entries + (size_t)(rowb + c.j) * (size_t)a.row_stride + col0;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(c.s1 * 4u), kBufferDword3);
+    const auto q = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, (int)(((c.s0 & ~3u) + (uint32_t)lane * 4u) * 4u), 0, 0);
+    buf = make_uint4(q[0], q[1], q[2], q[3]);
+  };
+  uint32_t tj = 0x7C00u;
+  float vfj = 0.0f;
+  auto process = [&](const Chunk& c, const uint4& buf) {
+    if (!c.valid) return;
+    const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tj, c.j);
+    const float vf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj), c.j));
+    uint32_t ev[4] = {buf.x, buf.y, buf.z, buf.w};
+    if (!REC) {
+      // Words past s1 are zero.  Words before s0 can only sit in lane 0's
+      // quad of a share's first chunk: they belong to the previous share and
+      // are zeroed here.  A zero word has key 0 and passes only when the
+      // cutoff is 0, where it adds 0.
+      if (c.s0 & 3u) {
+        const uint32_t skip = lane == 0 ? (c.s0 & 3u) : 0u;
+        ev[0] = skip > 0u ? 0u : ev[0];
+        ev[1] = skip > 1u ? 0u : ev[1];
+        ev[2] = skip > 2u ? 0u : ev[2];
+      }
+      const float tf = h2f(t);
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const uint32_t w = ev[k2];
+        const float x = h2f(w);
+        if (fabsf(x) >= tf)  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
+          atomicAdd(&tile[w >> 16], __float2int_rn(__fmul_rn(x, vf)));
+      }
+    } else {
+      const uint32_t row = rowb + c.j;
+      const uint32_t p = (c.s0 & ~3u) + (uint32_t)lane * 4u;
+      uint32_t cnt = 0u;
+      uint64_t fp = 0u;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const uint32_t w = ev[k2];
+        const uint32_t pos = p + (uint32_t)k2;
+        if (pos >= c.s0 && pos < c.s1 && (w & 0x7FFFu) >= t) {
+          atomicAdd(&tile[w >> 16], __float2int_rn(__fmul_rn(h2f(w), vf)));
+          const uint64_t flat = (uint64_t)row * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
+          if (a.mask) a.mask[flat] = 1u;
+          fp += pair_hash(flat);
+          ++cnt;
+        }
+      }
+      uint32_t flo = (uint32_t)fp, fhi = (uint32_t)(fp >> 32);
+      for (int sh = 32; sh > 0; sh >>= 1) {
+        cnt += __shfl_xor(cnt, sh, 64);
+        const uint32_t olo = __shfl_xor(flo, sh, 64);
+        const uint32_t ohi = __shfl_xor(fhi, sh, 64);
+        const uint64_t sum = ((uint64_t)fhi << 32 | flo) + ((uint64_t)ohi << 32 | olo);
+        flo = (uint32_t)sum;
+        fhi = (uint32_t)(sum >> 32);
+      }
+      if (lane == 0) {
+        if (cnt && a.row_kept) atomicAdd(&a.row_kept[row], (int32_t)cnt);
+        if (a.fingerprint) atomicAdd(a.fingerprint, ((unsigned long long)fhi << 32) | flo);
+      }
+    }
+  };
+  auto thresholds = [&]() {
+    tj = Lj ? key_threshold_fast(fabsf(vj), cutoff) : 0x7C00u;
+    // clamped: only a row whose weights are all zero can exceed it, and its
+    // products stay 0
+    vfj = fminf(fmaxf(ldexpf(vj, S), -0x1p100f), 0x1p100f);
+  };
+  // A ring of 8 chunks in flight: a slot is processed, then refilled with the
+  // next chunk, so 7 loads stay outstanding while one is used.
+  Chunk d0, d1, d2, d3, d4, d5, d6, d7;
+  uint4 q0, q1, q2, q3, q4, q5, q6, q7;
+  auto fill = [&]() {
+    take(d0); issue(d0, q0);
+    take(d1); issue(d1, q1);
+    take(d2); issue(d2, q2);
+    take(d3); issue(d3, q3);
+    take(d4); issue(d4, q4);
+    take(d5); issue(d5, q5);
+    take(d6); issue(d6, q6);
+    take(d7); issue(d7, q7);
+  };
+  // unconditional, so that the wait counters stay exact: a wave without a
+  // share (rowb = m, remaining = 0) gets empty chunks that access no memory
+  batch_meta();
+  fill();
+  thresholds();
+
+  // ---- stream
+  while (active && rowb < m) {
+    for (;;) {
+      process(d0, q0); take(d0); issue(d0, q0);
+      process(d1, q1); take(d1); issue(d1, q1);
+      process(d2, q2); take(d2); issue(d2, q2);
+      process(d3, q3); take(d3); issue(d3, q3);
+      process(d4, q4); take(d4); issue(d4, q4);
+      process(d5, q5); take(d5); issue(d5, q5);
+      process(d6, q6); take(d6); issue(d6, q6);
+      process(d7, q7); take(d7); issue(d7, q7);
+      if (!(d0.valid || d1.valid || d2.valid || d3.valid || d4.valid || d5.valid || d6.valid ||
+            d7.valid))
+        break;
+    }
+    remaining -= batch_take;
+    rowb += 64u;
+    offb = 0u;
+    if (remaining == 0u || rowb >= m) break;
+    batch_meta();
+    fill();
+    thresholds();
   }
   __syncthreads();
   const double unscale = ldexp(1.0, -S);
-  for (int c = threadIdx.x; c < tw; c += MUL_T) {
-    const long long acc = (long long)tile[c];
+  for (int c = tid; c < tw; c += MUL_T) {
+    const int32_t acc = tile[c];
     if (acc != 0) atomicAdd(&y[col0 + c], (float)((double)acc * unscale));
   }
   if (blockIdx.x == 0)  // only the dispatch reads it: ready for the next call
-    for (int b = threadIdx.x; b < HIST_BINS; b += MUL_T) a.hist[b] = 0u;
+    for (int b = tid; b < HIST_BINS; b += MUL_T) a.hist[b] = 0u;
 }
 
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
                             const EventPair* ev) {
   const unsigned grid = (unsigned)(a.G * blocks_per_group);
-  const size_t lds = (size_t)a.TW * sizeof(unsigned long long);
+  const size_t lds = 0;
   if (ev && ev->start && !record)
     hipExtLaunchKernelGGL(k_bucketmul<false>, dim3(grid), dim3(MUL_T), (uint32_t)lds, s, ev->start,
                           ev->stop, 0, a.v, a.entries, a.runlen, a.bsum, a.result, a.y, a);

@@ -32,7 +32,7 @@ constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN 
 // bound sum |v_i| * rowmax_i; the chart values that fall in bin b1 go to a
 // candidate list and a 1024-bin histogram of their next 10 bits.
 constexpr int DSP_ROWS = 256;
-constexpr int DSP_T = 1024;
+constexpr int DSP_T = 256;
 struct DispatchArgs {
   const float* v;
   const uint16_t* probes;   // [m][P]
@@ -67,7 +67,7 @@ struct MulArgs {
   uint32_t* result;         // reads RES_NCAND, RES_BIN, RES_ABOVE; writes the cutoff, K', K
   float* y;                 // [n]
   int64_t m, n, row_stride;
-  int32_t G, TW, nbd;
+  int32_t G, TW, nbd, P;
   uint32_t K;
   // parity recording (null in the timed path)
   int32_t* row_kept;

@@ -1,13 +1,16 @@
 """MI355X (gfx950) implementation of the "Effort" approximate vector-matrix multiply.
 
 The compute path is libeffort.so (hand-written HIP kernels behind the C ABI of
-include/effort.h).  This package is its ctypes binding plus a small holder for
-a prepared matrix resident in device memory; PyTorch only supplies device
-memory and streams.
+include/effort.h).  This package is its ctypes binding, a small holder for a
+prepared matrix resident in device memory, and the sequencing of chained calls
+(a decoder stack's matvecs, a mixture-of-experts block); PyTorch only supplies
+device memory and streams.
 """
 from .binding import *  # noqa: F401,F403
 from .binding import EffortError, effort_desc, LIB_PATH  # noqa: F401
+from .chain import LAYER_ROLES, DecodeStep, DenseDecodeStep, MoEFFN, route_top2  # noqa: F401
 from .device import EffortMatrix  # noqa: F401
 
 __all__ = [n for n in dir() if n.startswith(("effort_", "dense_")) or n in
-           ("EffortError", "EffortMatrix", "LIB_PATH")]
+           ("EffortError", "EffortMatrix", "LIB_PATH", "LAYER_ROLES", "DecodeStep",
+            "DenseDecodeStep", "MoEFFN", "route_top2")]

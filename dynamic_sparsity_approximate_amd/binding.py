@@ -84,6 +84,7 @@ _PROTOS = {
     "dense_gemv": ([_p, _p, _i64, _i64, _p, _p], ctypes.c_int),
     "dense_gemm_small": ([_p, _p, _i32, _i64, _i64, _p, _p], ctypes.c_int),
     "effort_silu_mul": ([_p, _p, _i64, _p, _p], ctypes.c_int),
+    "effort_axpby": ([_p, _f32, _p, _f32, _i64, _p, _p], ctypes.c_int),
     "effort_event_create": ([ctypes.POINTER(_p)], ctypes.c_int),
     "effort_event_record": ([_p, _p], ctypes.c_int),
     "effort_event_elapsed_ms": ([_p, _p, ctypes.POINTER(_f32)], ctypes.c_int),
@@ -242,6 +243,10 @@ def dense_gemm_small(w, v, batch: int, in_dim: int, out_dim: int, y, stream=None
 
 def effort_silu_mul(h1, h3, n: int, out, stream=None):
     _check(_lib.effort_silu_mul(_ptr(h1), _ptr(h3), n, _ptr(out), _stream(stream)), "effort_silu_mul")
+
+
+def effort_axpby(a, ga: float, b, gb: float, n: int, out, stream=None):
+    _check(_lib.effort_axpby(_ptr(a), ga, _ptr(b), gb, n, _ptr(out), _stream(stream)), "effort_axpby")
 
 
 def effort_event_create() -> int:

@@ -1,0 +1,135 @@
+"""Chains of approximate matvecs on one stream.
+
+The Effort method is applied per weight matrix with a per-call effort (Show HN
+thread "Speeding up LLM inference 2x times (possibly)": effort is a real-time
+knob; the author runs Mistral and Mixtral through it).  These classes only
+sequence calls into libeffort and own the intermediate buffers; every step of
+the arithmetic, the glue included (silu(h1) * h3, the gated expert sum), runs
+in the library's kernels.  A caller that repeats a chain captures `enqueue`
+into a HIP graph.
+"""
+from __future__ import annotations
+
+import math
+
+from . import binding as B
+
+LAYER_ROLES = ("wq", "wk", "wv", "wo", "w1", "w3", "w2")
+
+
+class DecodeStep:
+    """All matvecs of one decode step of a decoder stack.
+
+    `layers` is a list of dicts role -> EffortMatrix with the roles of
+    LAYER_ROLES; `head` is the output projection.  Per layer l: wq, wk, wv, w1
+    and w3 multiply the layer input x[l]; wo multiplies a[l] (attention, which
+    produces wo's input, is outside this path); w2 multiplies silu(h1) * h3,
+    formed from the approximate outputs h1 = x W1 and h3 = x W3.  The head
+    multiplies `head_in`.  Inputs are device fp32 vectors supplied by the caller.
+    """
+
+    def __init__(self, layers, head, x, a, head_in):
+        import torch
+
+        if len(layers) != len(x) or len(layers) != len(a):
+            raise ValueError("one x and one a vector per layer")
+        self.layers, self.head = layers, head
+        self.x, self.a, self.head_in = x, a, head_in
+        dev = head_in.device
+        self.out = []
+        for L in layers:
+            o = {r: torch.empty(L[r].out_dim, dtype=torch.float32, device=dev) for r in LAYER_ROLES}
+            o["g"] = torch.empty(L["w1"].out_dim, dtype=torch.float32, device=dev)
+            self.out.append(o)
+        self.logits = torch.empty(head.out_dim, dtype=torch.float32, device=dev)
+        self.calls = 7 * len(layers) + 1
+
+    def inputs_of(self, l: int) -> dict:
+        """role -> the device vector that role's matvec multiplies in layer l."""
+        o = self.out[l]
+        return {"wq": self.x[l], "wk": self.x[l], "wv": self.x[l], "wo": self.a[l], "w1": self.x[l],
+                "w3": self.x[l], "w2": o["g"]}
+
+    def enqueue(self, effort: float, stream=None):
+        for l, L in enumerate(self.layers):
+            o, ins = self.out[l], self.inputs_of(l)
+            for r in ("wq", "wk", "wv", "wo", "w1", "w3"):
+                L[r].matvec(ins[r], effort, o[r], stream)
+            B.effort_silu_mul(o["w1"], o["w3"], L["w1"].out_dim, o["g"], stream)
+            L["w2"].matvec(o["g"], effort, o["w2"], stream)
+        self.head.matvec(self.head_in, effort, self.logits, stream)
+
+
+class DenseDecodeStep:
+    """The same chain with the dense fp16 GEMV (weights as device fp16 [in][out])."""
+
+    def __init__(self, layers, head, x, a, head_in):
+        import torch
+
+        self.layers, self.head = layers, head
+        self.x, self.a, self.head_in = x, a, head_in
+        dev = head_in.device
+        self.out = []
+        for L in layers:
+            o = {r: torch.empty(L[r].shape[1], dtype=torch.float32, device=dev) for r in LAYER_ROLES}
+            o["g"] = torch.empty(L["w1"].shape[1], dtype=torch.float32, device=dev)
+            self.out.append(o)
+        self.logits = torch.empty(head.shape[1], dtype=torch.float32, device=dev)
+
+    def enqueue(self, stream=None):
+        for l, L in enumerate(self.layers):
+            o = self.out[l]
+            ins = {"wq": self.x[l], "wk": self.x[l], "wv": self.x[l], "wo": self.a[l],
+                   "w1": self.x[l], "w3": self.x[l]}
+            for r in ("wq", "wk", "wv", "wo", "w1", "w3"):
+                m, n = L[r].shape
+                B.dense_gemv(L[r], ins[r], m, n, o[r], stream)
+            B.effort_silu_mul(o["w1"], o["w3"], L["w1"].shape[1], o["g"], stream)
+            m, n = L["w2"].shape
+            B.dense_gemv(L["w2"], o["g"], m, n, o["w2"], stream)
+        m, n = self.head.shape
+        B.dense_gemv(self.head, self.head_in, m, n, self.logits, stream)
+
+
+def route_top2(logits):
+    """Top-2 experts of a router's logits (ties go to the lower index) and their
+    gates, the softmax over the two chosen logits (computed in double, returned
+    as fp32 values)."""
+    vals = [float(x) for x in logits]
+    order = sorted(range(len(vals)), key=lambda e: (-vals[e], e))
+    e0, e1 = order[0], order[1]
+    z = math.exp(vals[e1] - vals[e0])
+    g0 = 1.0 / (1.0 + z)
+    g1 = z / (1.0 + z)
+    return e0, e1, float(g0), float(g1)
+
+
+class MoEFFN:
+    """A mixture-of-experts feed-forward block: expert e is (w1, w3, w2) as
+    EffortMatrix, y = g0 * FFN_e0(x) + g1 * FFN_e1(x) with FFN(x) =
+    (silu(x W1) * x W3) W2.  Only the two routed experts' layouts are read."""
+
+    def __init__(self, experts, device):
+        import torch
+
+        self.experts = experts  # entries that are never routed to may be None
+        first = next(e for e in experts if e is not None)
+        d_in, d_hid = first[0].in_dim, first[0].out_dim
+        self.d_in, self.d_hid = d_in, d_hid
+        mk = lambda n: torch.empty(n, dtype=torch.float32, device=device)  # noqa: E731
+        self.h1 = [mk(d_hid), mk(d_hid)]
+        self.h3 = [mk(d_hid), mk(d_hid)]
+        self.g = [mk(d_hid), mk(d_hid)]
+        self.o = [mk(d_in), mk(d_in)]
+        self.y = mk(d_in)
+
+    def enqueue(self, x, route, effort: float, stream=None):
+        e0, e1, g0, g1 = route
+        for k, e in enumerate((e0, e1)):
+            w1, w3, w2 = self.experts[e]
+            w1.matvec(x, effort, self.h1[k], stream)
+            w3.matvec(x, effort, self.h3[k], stream)
+            B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], stream)
+            w2.matvec(self.g[k], effort, self.o[k], stream)
+        B.effort_axpby(self.o[0], g0, self.o[1], g1, self.d_in, self.y, stream)
+        return self.y

@@ -354,6 +354,13 @@ int effort_silu_mul(const float* h1_dev, const float* h3_dev, int64_t n, float* 
   return status_of(launch_silu_mul(h1_dev, h3_dev, n, out_dev, static_cast<hipStream_t>(stream)));
 }
 
+int effort_axpby(const float* a_dev, float ga, const float* b_dev, float gb, int64_t n, float* out_dev,
+                 void* stream) {
+  if (!a_dev || !b_dev || !out_dev || n < 1) return EFFORT_EINVAL;
+  if (!aligned(a_dev, 4) || !aligned(b_dev, 4) || !aligned(out_dev, 4)) return EFFORT_EINVAL;
+  return status_of(launch_axpby(a_dev, ga, b_dev, gb, n, out_dev, static_cast<hipStream_t>(stream)));
+}
+
 int effort_event_create(void** event_out) {
   if (!event_out) return EFFORT_EINVAL;
   hipEvent_t e;

@@ -1031,6 +1031,21 @@ hipError_t launch_silu_mul(const float* h1, const float* h3, int64_t n, float* o
   return hipGetLastError();
 }
 
+__global__ void k_axpby(const float* __restrict__ a, float ga, const float* __restrict__ b, float gb,
+                        int64_t n, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = __fadd_rn(__fmul_rn(ga, a[i]), __fmul_rn(gb, b[i]));
+}
+
+hipError_t launch_axpby(const float* a, float ga, const float* b, float gb, int64_t n, float* out,
+                        hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_axpby, dim3((unsigned)blocks), dim3(256), 0, s, a, ga, b, gb, n, out);
+  return hipGetLastError();
+}
+
 __global__ void k_zero_bytes(uint8_t* p, uint64_t bytes, int aligned) {
   const uint64_t nvec = aligned ? bytes / 16 : 0;
   uint4* p16 = reinterpret_cast<uint4*>(p);

@@ -92,6 +92,8 @@ hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64
 hipError_t launch_dense_gemm_small(const uint16_t* W, const float* v, int batch, int64_t m,
                                    int64_t n, float* y, hipStream_t s);
 hipError_t launch_silu_mul(const float* h1, const float* h3, int64_t n, float* out, hipStream_t s);
+hipError_t launch_axpby(const float* a, float ga, const float* b, float gb, int64_t n, float* out,
+                        hipStream_t s);
 hipError_t launch_zero_bytes(void* p, uint64_t bytes, hipStream_t s);
 hipError_t launch_debug_result(const uint32_t* result, float* cutoff, int64_t* K, hipStream_t s);
 

@@ -183,6 +183,12 @@ int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, i
 int effort_silu_mul(const float* h1_dev, const float* h3_dev, int64_t n, float* out_dev,
                     void* stream);
 
+/* out[i] = ga * a[i] + gb * b[i] (two fp32 products, one fp32 sum; out may
+   alias a or b): the gated sum of two experts' outputs in a mixture-of-experts
+   feed-forward block. */
+int effort_axpby(const float* a_dev, float ga, const float* b_dev, float gb, int64_t n,
+                 float* out_dev, void* stream);
+
 /* ---------------------------------------------------------------- measurement helpers */
 
 int effort_event_create(void** event_out);            /* hipEvent_t with timing */

@@ -274,3 +274,8 @@ def test_dense_and_glue_validation():
         E.dense_gemm_small(FAKE, FAKE, 17, 4, 4, FAKE)
     with pytest.raises(E.EffortError):
         E.effort_silu_mul(FAKE, FAKE, 0, FAKE)
+    for args in [(None, 1.0, FAKE, 1.0, 4, FAKE), (FAKE, 1.0, FAKE, 1.0, 0, FAKE),
+                 (FAKE + 2, 1.0, FAKE, 1.0, 4, FAKE)]:
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_axpby(*args)
+        assert ei.value.code == B.EFFORT_EINVAL

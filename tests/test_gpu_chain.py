@@ -1,0 +1,149 @@
+"""GPU parity of chained approximate matvecs: a decode step of a Mistral-7B-shaped
+stack (two layers and the output head) and a Mixtral-shaped mixture-of-experts
+block.  Every matvec is compared with the oracle on the input vector the GPU
+actually used (copied back), so the chain's data flow cannot mask an error;
+the glue kernels are compared with their plain definitions.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import dynamic_sparsity_approximate_amd as E  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+REL_L2_TOL = 1e-3
+DIM, KV, HID, VOCAB = 4096, 1024, 14336, 32000
+SHAPES = {"wq": (DIM, DIM), "wk": (DIM, KV), "wv": (DIM, KV), "wo": (DIM, DIM),
+          "w1": (DIM, HID), "w3": (DIM, HID), "w2": (HID, DIM)}
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(y, ref):
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(np.asarray(y, np.float64) - ref) / np.linalg.norm(ref))
+
+
+def check_matvec(W, v_used, y_gpu, effort, where):
+    ref = oracle.run(W, oracle.probes(W, 16), np.ascontiguousarray(v_used, np.float32), effort)
+    err = rel_l2(y_gpu, ref["y"])
+    assert err <= REL_L2_TOL, (where, err)
+    return err
+
+
+def test_decode_step_two_layers_and_head():
+    d = dev()
+    effort = 0.25
+    Ws, layers = [], []
+    for layer in range(2):
+        WL, L = {}, {}
+        for r in E.LAYER_ROLES:
+            m, n = SHAPES[r]
+            WL[r] = synth.matrix("config2", m, n, seed=0, layer=layer, w=r)
+            L[r] = E.EffortMatrix(WL[r], P=16, device=d)
+        Ws.append(WL)
+        layers.append(L)
+    Wh = synth.matrix("config2", DIM, VOCAB, seed=0, w="head")
+    head = E.EffortMatrix(Wh, P=16, device=d)
+    to = lambda a: torch.from_numpy(a).to(d)  # noqa: E731
+    x = [to(synth.vector("config2/x", DIM, seed=0, layer=l)) for l in range(2)]
+    a = [to(synth.vector("config2/attn", DIM, seed=0, layer=l)) for l in range(2)]
+    hin = to(synth.vector("config2/head_in", DIM, seed=0))
+    step = E.DecodeStep(layers, head, x, a, hin)
+    assert step.calls == 15
+    step.enqueue(effort)
+    torch.cuda.synchronize()
+    eager = [{k: v.cpu().numpy().copy() for k, v in o.items()} for o in step.out]
+    logits = step.logits.cpu().numpy().copy()
+
+    for layer in range(2):
+        ins = {r: t.cpu().numpy() for r, t in step.inputs_of(layer).items()}
+        o = eager[layer]
+        g_ref = oracle.silu_mul(o["w1"], o["w3"])
+        assert rel_l2(o["g"], g_ref) <= 1e-6
+        for r in E.LAYER_ROLES:
+            err = check_matvec(Ws[layer][r], ins[r], o[r], effort, (layer, r))
+            say("layer %d %s rel-L2 %.2e" % (layer, r, err))
+    err = check_matvec(Wh, hin.cpu().numpy(), logits, effort, "head")
+    say("head rel-L2 %.2e" % err)
+
+    # the chain captured in a graph replays to the eager result
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step.enqueue(effort)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        step.logits.fill_(float("nan"))
+        for o in step.out:
+            o["w2"].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert rel_l2(step.logits.cpu().numpy(), logits) < 1e-6, rep
+        for layer in range(2):
+            assert rel_l2(step.out[layer]["w2"].cpu().numpy(), eager[layer]["w2"]) < 1e-6, rep
+
+
+@pytest.mark.parametrize("effort", [0.25, 0.16, 0.12])
+def test_moe_block_two_routed_experts(effort):
+    """Mixtral-shaped block, 8 experts, top-2 routing from seeded logits; only the
+    routed experts are materialized (the others are never read)."""
+    d = dev()
+    token = int(effort * 100)
+    logits = synth.normals(8, seed=token, stream=synth.stream_id("config3/router"))
+    route = E.route_top2(logits)
+    e0, e1, g0, g1 = route
+    say("route", route)
+    experts, Wx = [None] * 8, {}
+    for e in (e0, e1):
+        Wx[e] = (synth.matrix("config3", DIM, HID, seed=0, expert=e, w="w1"),
+                 synth.matrix("config3", DIM, HID, seed=0, expert=e, w="w3"),
+                 synth.matrix("config3", HID, DIM, seed=0, expert=e, w="w2"))
+        experts[e] = tuple(E.EffortMatrix(W, P=16, device=d) for W in Wx[e])
+    moe = E.MoEFFN(experts, d)
+    x = torch.from_numpy(synth.vector("config3/x", DIM, seed=token)).to(d)
+    y = moe.enqueue(x, route, effort)
+    torch.cuda.synchronize()
+    xh = x.cpu().numpy()
+    outs = []
+    for k, e in enumerate((e0, e1)):
+        W1, W3, W2 = Wx[e]
+        h1, h3 = moe.h1[k].cpu().numpy(), moe.h3[k].cpu().numpy()
+        gk, ok = moe.g[k].cpu().numpy(), moe.o[k].cpu().numpy()
+        check_matvec(W1, xh, h1, effort, ("w1", e))
+        check_matvec(W3, xh, h3, effort, ("w3", e))
+        assert rel_l2(gk, oracle.silu_mul(h1, h3)) <= 1e-6
+        check_matvec(W2, gk, ok, effort, ("w2", e))
+        outs.append(ok)
+    y_ref = np.float64(np.float32(g0)) * outs[0] + np.float64(np.float32(g1)) * outs[1]
+    err = rel_l2(y.cpu().numpy(), y_ref)
+    assert err <= 1e-6, err
+    say("moe effort %.2f experts %d,%d ok" % (effort, e0, e1))
+
+
+def test_axpby_matches_definition():
+    d = dev()
+    a = synth.activations(5000, seed=3, stream=11)
+    b = synth.activations(5000, seed=4, stream=12)
+    out = torch.empty(5000, dtype=torch.float32, device=d)
+    E.effort_axpby(torch.from_numpy(a).to(d), 0.625, torch.from_numpy(b).to(d), -1.5, 5000, out)
+    torch.cuda.synchronize()
+    ref = (np.float32(0.625) * a).astype(np.float32) + (np.float32(-1.5) * b).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy(), ref.astype(np.float32))

@@ -52,9 +52,14 @@ def parse():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "effort", "dense", "copy"], default="full",
+    ap.add_argument("--mode", choices=["full", "effort", "dense", "copy", "sweep", "batched",
+                                       "decode", "moe"], default="full",
                     help="effort/dense: time only that path (for profiler runs); copy: plain "
-                         "1 GiB device copies for counter calibration")
+                         "1 GiB device copies for counter calibration; sweep: the four "
+                         "Mistral-7B shapes at efforts 1/.5/.25/.125; batched: b = 1..16 "
+                         "vectors against the dense small GEMM; decode: a whole Mistral-7B-"
+                         "shaped decode step; moe: a Mixtral-shaped expert block")
+    ap.add_argument("--layers", type=int, default=32, help="decode mode: decoder layers")
     return ap.parse_args()
 
 
@@ -145,6 +150,10 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_per_copy": 1 << 30, "copies": 5}))
+        return
+
+    if args.mode in EXTRA_MODES:
+        EXTRA_MODES[args.mode](args, torch, np, E, synth, dev)
         return
 
     log("generating W %dx%d and converting" % (m, n))
@@ -291,6 +300,194 @@ def main():
     else:
         out = dict(result, mode=args.mode)
     print(json.dumps(out))
+
+
+# ---------------------------------------------------------------- other configurations
+# Each prints one JSON line of its own; the headline line above is unchanged.
+
+def graph_time_us(torch, fn, reps, warm=3):
+    """Capture fn() once, replay it `reps` times, return µs per replay."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    g = capture(torch, fn)
+    time_replays(torch, g, warm)
+    ms, _ = time_replays(torch, g, reps)
+    return ms * 1e3 / reps
+
+
+def rotation_copies(call_bytes, rotate_gib=1.0):
+    return max(2, int(math.ceil(rotate_gib * (1 << 30) / max(call_bytes, 1.0))))
+
+
+def run_sweep(args, torch, np, E, synth, dev):
+    """Mistral-7B matrix shapes x efforts {1, .5, .25, .125}: µs/matvec with the
+    same rotation rule as the headline, beside the dense GEMV."""
+    shapes = [(4096, 4096), (4096, 1024), (4096, 14336), (14336, 4096)]
+    rows = []
+    for (m, n) in shapes:
+        W = synth.matrix("config1", m, n, seed=0)
+        M = E.EffortMatrix(W, P=args.P, device=dev)
+        Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+        Rd = rotation_copies(2.0 * m * n)
+        Wds = [Wd] + [Wd.clone() for _ in range(Rd - 1)]
+        vd = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
+        yd = torch.empty(n, dtype=torch.float32, device=dev)
+        dense_us = graph_time_us(torch, lambda: [E.dense_gemv(w, vd, m, n, yd) for w in Wds], 50) / Rd
+        del Wds
+        for effort in (1.0, 0.5, 0.25, 0.125):
+            v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
+            kept = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
+            R = rotation_copies(4.0 * kept)
+            layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
+            vs = [torch.from_numpy(synth.vector("config1", m, seed=r)).to(dev) for r in range(R)]
+            ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
+
+            def cyc():
+                for r in range(R):
+                    E.effort_matvec(M.desc, layouts[r], vs[r], effort, ys[r], M.ws, M.ws_bytes)
+
+            us = graph_time_us(torch, cyc, max(5, 2000 // R)) / R
+            rows.append({"in": m, "out": n, "effort": effort, "us": round(us, 2),
+                         "kept_fraction": round(kept / (m * n), 4),
+                         "alg_GBps": round((4.0 * kept + 2.0 * m * args.P + 4.0 * (m + n)) / us / 1e3, 1),
+                         "dense_us": round(dense_us, 2), "speedup_vs_dense": round(dense_us / us, 3),
+                         "rotation": R})
+            log(json.dumps(rows[-1]))
+            del layouts
+    print(json.dumps({"mode": "sweep", "unit": "µs/matvec", "P": args.P, "points": rows}))
+
+
+def run_batched(args, torch, np, E, synth, dev):
+    """b independent vectors through one matrix, each with its own cutoff, against
+    the dense small GEMM that reads W once for all b."""
+    m, n, effort = args.m, args.n, args.effort
+    W = synth.matrix("config1", m, n, seed=0)
+    M = E.EffortMatrix(W, P=args.P, device=dev, batch=16)
+    Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+    Rd = rotation_copies(2.0 * m * n)
+    Wds = [Wd] + [Wd.clone() for _ in range(Rd - 1)]
+    v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
+    kept = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
+    R = rotation_copies(4.0 * kept)
+    layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
+    rows = []
+    for b in (1, 2, 4, 8, 16):
+        V = torch.from_numpy(np.stack([synth.vector("config4", m, seed=s) for s in range(b)])).to(dev)
+        Y = torch.empty((b, n), dtype=torch.float32, device=dev)
+
+        def cyc():
+            for r in range(R):
+                E.effort_matvec_batched(M.desc, layouts[r], V, b, effort, Y, M.ws, M.ws_bytes)
+
+        us = graph_time_us(torch, cyc, max(5, 400 // R)) / R
+        dense_us = graph_time_us(torch, lambda: [E.dense_gemm_small(w, V, b, m, n, Y) for w in Wds],
+                                 20) / Rd
+        rows.append({"batch": b, "effort_us": round(us, 2), "dense_gemm_us": round(dense_us, 2),
+                     "effort_faster": us < dense_us})
+        log(json.dumps(rows[-1]))
+    cross = next((r["batch"] for r in rows if not r["effort_faster"]), None)
+    print(json.dumps({"mode": "batched", "workload": "%dx%d fp16, effort %g" % (m, n, effort),
+                      "unit": "µs per call (all b vectors)", "points": rows,
+                      "first_batch_where_dense_wins": cross}))
+
+
+MISTRAL = {"dim": 4096, "kv": 1024, "hidden": 14336, "vocab": 32000}
+
+
+def layer_shapes():
+    d, kv, h = MISTRAL["dim"], MISTRAL["kv"], MISTRAL["hidden"]
+    return {"wq": (d, d), "wk": (d, kv), "wv": (d, kv), "wo": (d, d), "w1": (d, h), "w3": (d, h),
+            "w2": (h, d)}
+
+
+def run_decode(args, torch, np, E, synth, dev):
+    """Every matvec of one decode step of a Mistral-7B-shaped stack (random-init
+    fp16 weights, a distinct seeded matrix per layer and role), captured in one
+    graph; per-token latency beside the same chain with the dense GEMV."""
+    effort, L = args.effort, args.layers
+    shapes = layer_shapes()
+    layers, dlayers = [], []
+    t0 = time.perf_counter()
+    weights = 0
+    for l in range(L):
+        EL, DL = {}, {}
+        for r in E.LAYER_ROLES:
+            m, n = shapes[r]
+            W = synth.matrix("config2", m, n, seed=0, layer=l, w=r)
+            EL[r] = E.EffortMatrix(W, P=args.P, device=dev)
+            DL[r] = torch.from_numpy(W.view(np.int16)).to(dev)
+            weights += m * n
+        layers.append(EL)
+        dlayers.append(DL)
+        log("layer %d prepared (%.0fs)" % (l, time.perf_counter() - t0))
+    Wh = synth.matrix("config2", MISTRAL["dim"], MISTRAL["vocab"], seed=0, w="head")
+    head = E.EffortMatrix(Wh, P=args.P, device=dev)
+    dhead = torch.from_numpy(Wh.view(np.int16)).to(dev)
+    weights += Wh.size
+    del Wh
+    to = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    x = [to(synth.vector("config2/x", MISTRAL["dim"], seed=0, layer=l)) for l in range(L)]
+    a = [to(synth.vector("config2/attn", MISTRAL["dim"], seed=0, layer=l)) for l in range(L)]
+    hin = to(synth.vector("config2/head_in", MISTRAL["dim"], seed=0))
+    step = E.DecodeStep(layers, head, x, a, hin)
+    dstep = E.DenseDecodeStep(dlayers, dhead, x, a, hin)
+    us = graph_time_us(torch, lambda: step.enqueue(effort), 20)
+    dus = graph_time_us(torch, lambda: dstep.enqueue(), 20)
+    print(json.dumps({"mode": "decode", "workload": "Mistral-7B-shaped decode step, %d layers + head, "
+                      "effort %g, batch 1" % (L, effort), "matvecs": step.calls,
+                      "weights": weights, "effort_us_per_token": round(us, 1),
+                      "dense_us_per_token": round(dus, 1), "speedup_vs_dense": round(dus / us, 3),
+                      "dense_GBps": round(2.0 * weights / dus / 1e3, 1)}))
+
+
+def run_moe(args, torch, np, E, synth, dev):
+    """A Mixtral-shaped expert block (8 experts of w1/w3 4096x14336 and w2
+    14336x4096), top-2 routing from seeded logits; per-token latency of the two
+    routed experts' six matvecs and the glue, beside the dense equivalent."""
+    d, h = MISTRAL["dim"], MISTRAL["hidden"]
+    experts, dexperts = [], []
+    for e in range(8):
+        Ws = [synth.matrix("config3", d, h, seed=0, expert=e, w="w1"),
+              synth.matrix("config3", d, h, seed=0, expert=e, w="w3"),
+              synth.matrix("config3", h, d, seed=0, expert=e, w="w2")]
+        experts.append(tuple(E.EffortMatrix(W, P=args.P, device=dev) for W in Ws))
+        dexperts.append(tuple(torch.from_numpy(W.view(np.int16)).to(dev) for W in Ws))
+        log("expert %d prepared" % e)
+    moe = E.MoEFFN(experts, dev)
+    tokens = 16
+    xs = [torch.from_numpy(synth.vector("config3/x", d, seed=t)).to(dev) for t in range(tokens)]
+    routes = [E.route_top2(synth.normals(8, seed=t, stream=synth.stream_id("config3/router")))
+              for t in range(tokens)]
+    hbuf = torch.empty(h, dtype=torch.float32, device=dev)
+    h3buf = torch.empty(h, dtype=torch.float32, device=dev)
+    gbuf = torch.empty(h, dtype=torch.float32, device=dev)
+    o = [torch.empty(d, dtype=torch.float32, device=dev) for _ in range(2)]
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+
+    def dense_token(t):
+        e0, e1, g0, g1 = routes[t]
+        for k, e in enumerate((e0, e1)):
+            w1, w3, w2 = dexperts[e]
+            E.dense_gemv(w1, xs[t], d, h, hbuf)
+            E.dense_gemv(w3, xs[t], d, h, h3buf)
+            E.effort_silu_mul(hbuf, h3buf, h, gbuf)
+            E.dense_gemv(w2, gbuf, h, d, o[k])
+        E.effort_axpby(o[0], g0, o[1], g1, d, y)
+
+    dus = graph_time_us(torch, lambda: [dense_token(t) for t in range(tokens)], 10) / tokens
+    points = []
+    for effort in (0.25, 0.16, 0.12):
+        us = graph_time_us(torch, lambda: [moe.enqueue(xs[t], routes[t], effort)
+                                          for t in range(tokens)], 10) / tokens
+        points.append({"effort": effort, "effort_us_per_token": round(us, 1),
+                       "speedup_vs_dense": round(dus / us, 3)})
+        log(json.dumps(points[-1]))
+    print(json.dumps({"mode": "moe", "workload": "Mixtral-shaped expert block, 8 experts, top-2, "
+                      "%d tokens" % tokens, "dense_us_per_token": round(dus, 1), "points": points}))
+
+
+EXTRA_MODES = {"sweep": run_sweep, "batched": run_batched, "decode": run_decode, "moe": run_moe}
 
 
 if __name__ == "__main__":

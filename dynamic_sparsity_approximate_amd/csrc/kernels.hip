@@ -100,36 +100,6 @@ __device__ uint32_t block_excl_scan(uint32_t x, uint32_t* tmp, uint32_t* total) 
   return r;
 }
 
-// h[0..nb) in LDS.  Finds the bin b with above(b) < K <= above(b) + h[b], where
-// above(b) counts the entries of all higher bins; writes out[0] = b,
-// out[1] = above(b).  Requires 1 <= K <= sum(h).
-template <int NT>
-__device__ void find_from_top(const uint32_t* h, int nb, uint32_t K, uint32_t* tmp, uint32_t* out) {
-  const int per = (nb + NT - 1) / NT;
-  if (threadIdx.x == 0) {
-    out[0] = 0u;
-    out[1] = 0u;
-  }
-  uint32_t s = 0;
-  for (int u = 0; u < per; ++u) {
-    const int b = nb - 1 - ((int)threadIdx.x * per + u);
-    if (b >= 0) s += h[b];
-  }
-  uint32_t tot;
-  uint32_t above = block_excl_scan<NT>(s, tmp, &tot);
-  for (int u = 0; u < per; ++u) {
-    const int b = nb - 1 - ((int)threadIdx.x * per + u);
-    if (b < 0) break;
-    const uint32_t c = h[b];
-    if (above < K && K <= above + c) {
-      out[0] = (uint32_t)b;
-      out[1] = above;
-    }
-    above += c;
-  }
-  __syncthreads();
-}
-
 // ---------------------------------------------------------------- cutoff
 
 constexpr int SEL_T = 1024;
@@ -473,16 +443,115 @@ __device__ __forceinline__ void wave_locate_regs(const uint32_t* x, uint32_t cou
   *before = acc;
 }
 
+// The exact cutoff, computed by one wave.  The dispatch found the bin b1 of the
+// K-th largest chart value (bits 30..19) and the count above1 of larger
+// values; the refinement histogram hist2 of the bin's values (bits 18..9)
+// gives the second digit, and the candidate values that share bits 30..9 give
+// the last nine bits through a 512-bin histogram in the wave's own LDS words
+// h3[512].  Radix selection: every step keeps the bin holding the remaining
+// rank, so the result is the K-th largest value itself.  Returns its bit
+// pattern; *kprime = the number of chart values >= it.  Wave-uniform.
+__device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
+                                      const uint32_t* __restrict__ cand, uint32_t ncap, uint32_t nc,
+                                      uint32_t b1, uint32_t above1, uint32_t K, uint32_t* h3,
+                                      uint32_t* kprime) {
+  const int lane = threadIdx.x & 63;
+  // lane l holds refinement bins [1008 - 16 l, 1024 - 16 l): lane 0 the top
+  uint32_t h[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 q = *reinterpret_cast<const uint4*>(hist2 + 1008 - 16 * lane + 4 * c);
+    h[4 * c] = q.x;
+    h[4 * c + 1] = q.y;
+    h[4 * c + 2] = q.z;
+    h[4 * c + 3] = q.w;
+  }
+  // the first 16 * 64 candidates, loaded with the histogram (words past the
+  // list's capacity read as zero; those at p >= nc are ignored)
+  uint32_t cv[16];
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)cand, (short)0, (int)(ncap * 4u), kBufferDword3);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u * 64 + lane) * 4, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h3[k * 64 + lane] = 0u;
+
+  // second digit: the bin holding rank K1 within b1, counted from the top
+  const uint32_t K1 = K - above1;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sum += h[k];
+  uint32_t above = wave_incl_scan(sum) - sum;
+  const unsigned long long hit = __ballot(above < K1 && K1 <= above + sum);
+  const int L = __ffsll((long long)hit) - 1;
+  uint32_t b2 = 0u, above2 = 0u;
+  if (lane == L) {
+#pragma unroll
+    for (int k = 15; k >= 0; --k) {
+      if (above < K1 && K1 <= above + h[k]) {
+        b2 = (uint32_t)(1008 - 16 * lane + k);
+        above2 = above;
+      }
+      above += h[k];
+    }
+  }
+  b2 = (uint32_t)__builtin_amdgcn_readlane((int)b2, L);
+  above2 = (uint32_t)__builtin_amdgcn_readlane((int)above2, L);
+  const uint32_t K2 = K1 - above2;
+  const uint32_t pre = (b1 << 10) | b2;  // bits 30..9 of the cutoff
+
+  // last digit: histogram of the matching candidates' bits 8..0
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const uint32_t p = (uint32_t)(u * 64 + lane);
+    if (p < nc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
+  }
+  for (uint32_t p0 = 16u * 64u; p0 < nc; p0 += 64u) {  // more than 1024 candidates
+    const uint32_t p = p0 + (uint32_t)lane;
+    const uint32_t c = p < nc ? cand[p] : 0u;
+    if (p < nc && (c >> 9) == pre) atomicAdd(&h3[c & 511u], 1u);
+  }
+  // lane l holds bins [504 - 8 l, 512 - 8 l)
+  uint32_t g[8];
+  sum = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    g[k] = h3[504 - 8 * lane + k];
+    sum += g[k];
+  }
+  above = wave_incl_scan(sum) - sum;
+  const unsigned long long hit3 = __ballot(above < K2 && K2 <= above + sum);
+  const int L3 = __ffsll((long long)hit3) - 1;
+  uint32_t b3 = 0u, above3 = 0u, c3 = 0u;
+  if (lane == L3) {
+#pragma unroll
+    for (int k = 7; k >= 0; --k) {
+      if (above < K2 && K2 <= above + g[k]) {
+        b3 = (uint32_t)(504 - 8 * lane + k);
+        above3 = above;
+        c3 = g[k];
+      }
+      above += g[k];
+    }
+  }
+  b3 = (uint32_t)__builtin_amdgcn_readlane((int)b3, L3);
+  above3 = (uint32_t)__builtin_amdgcn_readlane((int)above3, L3);
+  c3 = (uint32_t)__builtin_amdgcn_readlane((int)c3, L3);
+  *kprime = above1 + above2 + above3 + c3;
+  return (pre << 9) | b3;
+}
+
 // Block (g, s) of the grid: group g's LDS tile, share s of its entries.
 //
 // Prologue, three dependent rounds of global loads:
-//   (1) the cutoff's bin, the refinement histogram, the first 4 * MUL_T
-//       candidate chart values, and (wave 0) the per-256-row sums that place
-//       each wave's share, scanned once into LDS;
-//   (2) the run lengths and activations of the 256 rows where each wave's
-//       share starts, in flight while the block finishes the exact cutoff
-//       (bits 18..9 from the refinement histogram, bits 8..0 from the
-//       candidates; every block computes the same value);
+//   (1) wave 0: the cutoff's bin, the refinement histogram and the candidate
+//       chart values, from which it computes the exact cutoff (every block
+//       gets the same value); wave 1: the per-256-row sums that place each
+//       wave's share, scanned once into LDS;
+//   (2) per wave, the run lengths and activations of the 256 rows where its
+//       share starts;
 //   (3) the share's first chunks of entries, in flight while each row's fp16
 //       key threshold is derived from the cutoff.
 //
@@ -496,14 +565,10 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
     const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
-  static_assert(MUL_T == 1024, "one refinement-histogram bin per thread");
   __shared__ int32_t tile[EFFORT_MAX_GROUP_WIDTH];
-  __shared__ uint32_t hs[1024];
-  __shared__ uint32_t hs3[512];
-  __shared__ uint32_t ctmp[MUL_T / 64 + 1];
-  __shared__ uint32_t csres[8];
+  __shared__ uint32_t h3w[512];  // wave 0: histogram of the cutoff's last digit
   __shared__ uint32_t pfx[256];  // inclusive prefix sums of the group's per-256-row sums
-  __shared__ uint32_t sT;
+  __shared__ uint32_t sT, sCut;
   __shared__ int32_t sS;
   __shared__ uint32_t mrl[MUL_W][DSP_ROWS];  // per wave: run lengths of its first 256 rows
   __shared__ float mv[MUL_W][DSP_ROWS];      // and their activations
@@ -520,20 +585,22 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
   const uint32_t nbd = (uint32_t)a.nbd;
   const uint32_t* rl = runlen + (size_t)g * a.m;
 
-  // ---- round 1
-  const uint32_t h2v = a.hist2[tid];
-  const uint32_t b1 = result[RES_BIN], above1 = result[RES_ABOVE], nc = result[RES_NCAND];
-  uint32_t cb[4];  // candidates p < min(m * P, 4 * MUL_T); those at p >= nc are ignored
-  {
-    const uint64_t cap = (uint64_t)a.m * (uint64_t)a.P;
-    const uint32_t ncap = (uint32_t)(cap < 4u * MUL_T ? cap : 4u * MUL_T);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)a.cand, (short)0, (int)(ncap * 4u), kBufferDword3);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      cb[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u * MUL_T + tid) * 4, 0, 0);
-  }
+  // ---- round 1: wave 0 the exact cutoff, wave 1 the partition sums
   if (wid == 0) {
+    const uint32_t b1 = result[RES_BIN], above1 = result[RES_ABOVE], nc = result[RES_NCAND];
+    const uint64_t cap = (uint64_t)a.m * (uint64_t)a.P;
+    const uint32_t ncap = (uint32_t)(cap < 1024u ? cap : 1024u);
+    uint32_t kp;
+    const uint32_t cut = wave_exact_cutoff(a.hist2, a.cand, ncap, nc, b1, above1, a.K, h3w, &kp);
+    if (lane == 0) {
+      sCut = cut;
+      if (blockIdx.x == 0) {
+        a.result[RES_CUTOFF] = cut;
+        a.result[RES_KPRIME] = kp;
+        a.result[RES_K] = a.K;
+      }
+    }
+  } else if (wid == 1) {
     uint32_t sb[4];
     float sf[4];
 #pragma unroll
@@ -564,11 +631,10 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     }
   }
   for (int c = tid; c < tw; c += MUL_T) tile[c] = 0;
-  if (tid < 512) hs3[tid] = 0u;
-  hs[tid] = h2v;
   __syncthreads();
   const uint32_t T = sT;
   const int S = sS;
+  const float cutoff = __uint_as_float(sCut);
 
   // this wave's share [start, end) of the group's entries, concatenated over rows
   const uint64_t nslots = (uint64_t)bpg * MUL_W;
@@ -605,40 +671,6 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const uint32_t j = (uint32_t)u * 64u + (uint32_t)lane;
     lr[u] = j < nr ? rl[r0 + j] : 0u;
     lv[u] = j < nr ? vvec[r0 + j] : 0.0f;
-  }
-  // the exact cutoff, meanwhile
-  const uint32_t K1 = a.K - above1;
-  find_from_top<MUL_T>(hs, 1024, K1, ctmp, csres);
-  const uint32_t b2 = csres[0] & 1023u, above2 = csres[1];
-  const uint32_t K2 = K1 - above2;
-  const uint32_t pre = (b1 << 10) | b2;  // bits 30..9 of the cutoff
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint32_t p = (uint32_t)u * MUL_T + (uint32_t)tid;
-    if (p < nc && (cb[u] >> 9) == pre) atomicAdd(&hs3[cb[u] & 511u], 1u);
-  }
-  for (uint32_t p0 = 4u * MUL_T; p0 < nc; p0 += 4u * MUL_T) {  // more than 4 * MUL_T candidates
-    uint32_t bits[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t p = p0 + (uint32_t)u * MUL_T + (uint32_t)tid;
-      bits[u] = p < nc ? a.cand[p] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t p = p0 + (uint32_t)u * MUL_T + (uint32_t)tid;
-      if (p < nc && (bits[u] >> 9) == pre) atomicAdd(&hs3[bits[u] & 511u], 1u);
-    }
-  }
-  __syncthreads();  // hs3 complete; every thread has read csres
-  find_from_top<MUL_T>(hs3, 512, K2, ctmp, csres);
-  const uint32_t b3 = csres[0] & 511u, above3 = csres[1];
-  const uint32_t cut_bits = (pre << 9) | b3;
-  const float cutoff = __uint_as_float(cut_bits);
-  if (blockIdx.x == 0 && tid == 0) {
-    a.result[RES_CUTOFF] = cut_bits;
-    a.result[RES_KPRIME] = above1 + above2 + above3 + hs3[b3];
-    a.result[RES_K] = a.K;
   }
 
   // ---- round 3: the share's first rows, their chunks in flight

@@ -113,6 +113,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   sa.result = result;
   sa.y = y;
   sa.n = g.n;
+  sa.vec_ws = 0;
   if (hip_failed(e = launch_select(sa, s, ev ? &ev[0] : nullptr))) return EFFORT_EHIP;
 
   DispatchArgs da;
@@ -131,6 +132,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   da.G = g.G;
   da.G4 = g.G4;
   da.K = K;
+  da.vec_ws = 0;
   if (hip_failed(e = launch_dispatch(da, s, ev ? &ev[1] : nullptr))) return EFFORT_EHIP;
 
   MulArgs ma;
@@ -151,6 +153,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   ma.nbd = (int32_t)((g.m + kDspRows - 1) / kDspRows);
   ma.P = g.P;
   ma.K = K;
+  ma.nv = 1;
+  ma.vec_ws = 0;
+  ma.vbsum = bsum;
   ma.row_kept = dbg ? dbg->row_kept : nullptr;
   ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
   ma.mask = dbg ? dbg->mask : nullptr;
@@ -162,6 +167,102 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   if (dbg && (dbg->cutoff || dbg->K) &&
       hip_failed(launch_debug_result(result, dbg->cutoff, dbg->K, s)))
     return EFFORT_EHIP;
+  return EFFORT_OK;
+}
+
+// Several vectors in one pass over the union of their read lengths: cutoff
+// and dispatch kernels for all vectors at once, then per pass of up to
+// bucketmul_pass_width vectors the union kernel and the multiply.
+int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_t batch, float effort,
+                float* y, uint8_t* ws, hipStream_t s) {
+  const WsLayout w = ws_layout(g);
+  const uint64_t vec_ws = w.slice / 4;  // u32 words between consecutive vectors' slices
+  const uint16_t* probes = reinterpret_cast<const uint16_t*>(layout + g.off_probes);
+  const uint32_t* counts = reinterpret_cast<const uint32_t*>(layout + g.off_counts);
+  const uint32_t* entries = reinterpret_cast<const uint32_t*>(layout + g.off_entries);
+  const uint16_t* rowmax = reinterpret_cast<const uint16_t*>(layout + g.off_rowmax);
+  auto u32 = [&](int32_t b, uint64_t off) {
+    return reinterpret_cast<uint32_t*>(ws + (uint64_t)b * w.slice + off);
+  };
+  const int64_t N = g.m * (int64_t)g.P;
+  const uint32_t K = k_of(effort, N);
+
+  SelectArgs sa;
+  sa.v = v;
+  sa.probes = probes;
+  sa.m = g.m;
+  sa.P = g.P;
+  sa.N = N;
+  sa.hist = u32(0, w.hist);
+  sa.hist2 = u32(0, w.hist2);
+  sa.result = u32(0, w.result);
+  sa.y = y;
+  sa.n = g.n;
+  sa.vec_ws = vec_ws;
+  if (hip_failed(launch_select(sa, s, nullptr, batch))) return EFFORT_EHIP;
+
+  DispatchArgs da;
+  da.v = v;
+  da.probes = probes;
+  da.counts = counts;
+  da.rowmax = rowmax;
+  da.hist = u32(0, w.hist);
+  da.hist2 = u32(0, w.hist2);
+  da.cand = u32(0, w.cand);
+  da.result = u32(0, w.result);
+  da.runlen = u32(0, w.runlen);
+  da.bsum = u32(0, w.bsum);
+  da.m = g.m;
+  da.P = g.P;
+  da.G = g.G;
+  da.G4 = g.G4;
+  da.K = K;
+  da.vec_ws = vec_ws;
+  if (hip_failed(launch_dispatch(da, s, nullptr, batch))) return EFFORT_EHIP;
+
+  uint32_t* urunlen = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.urunlen);
+  uint32_t* ubsum = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.ubsum);
+  const int bp = bucketmul_pass_width(g.TW, batch);
+  int bpg = (cu_count() + g.G - 1) / g.G;
+  if (bpg < 1) bpg = 1;
+  for (int32_t b0 = 0; b0 < batch; b0 += bp) {
+    const int32_t nv = batch - b0 < bp ? batch - b0 : bp;
+    UnionArgs ua;
+    ua.runlen = u32(b0, w.runlen);
+    ua.vec_ws = vec_ws;
+    ua.nv = nv;
+    ua.G = g.G;
+    ua.m = g.m;
+    ua.urunlen = urunlen;
+    ua.ubsum = ubsum;
+    if (hip_failed(launch_union(ua, s))) return EFFORT_EHIP;
+
+    MulArgs ma;
+    ma.v = v + (int64_t)b0 * g.m;
+    ma.entries = entries;
+    ma.runlen = urunlen;
+    ma.bsum = ubsum;
+    ma.hist = u32(b0, w.hist);
+    ma.hist2 = u32(b0, w.hist2);
+    ma.cand = u32(b0, w.cand);
+    ma.result = u32(b0, w.result);
+    ma.y = y + (int64_t)b0 * g.n;
+    ma.m = g.m;
+    ma.n = g.n;
+    ma.row_stride = g.row_stride;
+    ma.G = g.G;
+    ma.TW = g.TW;
+    ma.nbd = (int32_t)((g.m + kDspRows - 1) / kDspRows);
+    ma.P = g.P;
+    ma.K = K;
+    ma.nv = nv;
+    ma.vec_ws = vec_ws;
+    ma.vbsum = u32(b0, w.bsum);
+    ma.row_kept = nullptr;
+    ma.fingerprint = nullptr;
+    ma.mask = nullptr;
+    if (hip_failed(launch_bucketmul(ma, false, bpg, s))) return EFFORT_EHIP;
+  }
   return EFFORT_OK;
 }
 
@@ -177,7 +278,7 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
   if (!effort_ok(effort)) return EFFORT_EINVAL;
   const WsLayout w = ws_layout(g);
-  if (ws_bytes < w.slice * (uint64_t)batch) return EFFORT_ENOSPACE;
+  if (ws_bytes < w.slice * (uint64_t)batch + (batch > 1 ? w.union_bytes : 0)) return EFFORT_ENOSPACE;
   if (dbg) {
     if (dbg->K && !aligned(dbg->K, 8)) return EFFORT_EINVAL;
     if (dbg->fingerprint && !aligned(dbg->fingerprint, 8)) return EFFORT_EINVAL;
@@ -195,6 +296,8 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* layout = static_cast<const uint8_t*>(layout_dev);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  if (batch > 1 && !dbg && !events && bucketmul_pass_width(g.TW, batch) > 0)
+    return run_batched(g, layout, v_dev, batch, effort, y_dev, ws, s);
   for (int32_t b = 0; b < batch; ++b) {
     rc = run_one(g, layout, v_dev + (int64_t)b * g.m, effort, y_dev + (int64_t)b * g.n,
                  ws + (uint64_t)b * w.slice, s, dbg, events ? ev : nullptr);
@@ -242,7 +345,8 @@ int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* byt
   int rc = check_desc(desc, &g);
   if (rc) return rc;
   if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
-  *bytes = ws_layout(g).slice * (uint64_t)batch;
+  const WsLayout w = ws_layout(g);
+  *bytes = w.slice * (uint64_t)batch + (batch > 1 ? w.union_bytes : 0);
   return EFFORT_OK;
 }
 

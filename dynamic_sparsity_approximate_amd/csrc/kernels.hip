@@ -132,6 +132,14 @@ constexpr int CH_T = 256;  // rows per block of the histogram kernel
 __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
   __shared__ uint32_t hist[HIST_BINS];
   const int tid = threadIdx.x;
+  if (blockIdx.y) {  // vector blockIdx.y of a batch
+    const uint64_t k = blockIdx.y;
+    a.v += k * a.m;
+    a.y += k * a.n;
+    a.hist += k * a.vec_ws;
+    a.hist2 += k * a.vec_ws;
+    a.result += k * a.vec_ws;
+  }
   for (int b = tid; b < HIST_BINS; b += CH_T) hist[b] = 0u;
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * CH_T + tid;
@@ -161,13 +169,13 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
   }
 }
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev) {
+hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
   const int64_t blocks = (a.m + CH_T - 1) / CH_T;
+  const dim3 grid((unsigned)blocks, (unsigned)nvec);
   if (ev && ev->start)
-    hipExtLaunchKernelGGL(k_chart_hist, dim3((unsigned)blocks), dim3(CH_T), 0, s, ev->start, ev->stop,
-                          0, a);
+    hipExtLaunchKernelGGL(k_chart_hist, grid, dim3(CH_T), 0, s, ev->start, ev->stop, 0, a);
   else
-    hipLaunchKernelGGL(k_chart_hist, dim3((unsigned)blocks), dim3(CH_T), 0, s, a);
+    hipLaunchKernelGGL(k_chart_hist, grid, dim3(CH_T), 0, s, a);
   return hipGetLastError();
 }
 
@@ -216,6 +224,16 @@ static_assert(HIST_BINS == 16 * DSP_T, "each dispatch thread holds 16 histogram 
 // (probes are descending, so these are segments 0..q-1), and the read length
 // of (row, group) covers segments 0..min(q, P-1) through the counts table.
 __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
+  if (blockIdx.y) {  // vector blockIdx.y of a batch
+    const uint64_t k = blockIdx.y;
+    a.v += k * a.m;
+    a.hist += k * a.vec_ws;
+    a.hist2 += k * a.vec_ws;
+    a.cand += k * a.vec_ws;
+    a.result += k * a.vec_ws;
+    a.runlen += k * a.vec_ws;
+    a.bsum += k * a.vec_ws;
+  }
   __shared__ uint32_t tmp[DSP_T / 64 + 1];
   __shared__ uint32_t sres[2];
   __shared__ uint32_t red[16 * (DSP_T / 64)];
@@ -351,13 +369,43 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   }
 }
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev) {
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
   const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
+  const dim3 grid((unsigned)blocks, (unsigned)nvec);
   if (ev && ev->start)
-    hipExtLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, ev->start, ev->stop,
-                          0, a);
+    hipExtLaunchKernelGGL(k_dispatch, grid, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
   else
-    hipLaunchKernelGGL(k_dispatch, dim3((unsigned)blocks), dim3(DSP_T), 0, s, a);
+    hipLaunchKernelGGL(k_dispatch, grid, dim3(DSP_T), 0, s, a);
+  return hipGetLastError();
+}
+
+// Union read lengths of nv vectors: one thread per row, one block per 256 rows.
+__global__ __launch_bounds__(DSP_T) void k_union(UnionArgs a) {
+  __shared__ uint32_t red[DSP_T / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t i = (int64_t)blockIdx.x * DSP_T + tid;
+  const bool valid = i < a.m;
+  for (int g = 0; g < a.G; ++g) {
+    uint32_t L = 0u;
+    if (valid)
+      for (int k = 0; k < a.nv; ++k)
+        L = max(L, a.runlen[(size_t)k * a.vec_ws + (size_t)g * a.m + i]);
+    if (valid) a.urunlen[(size_t)g * a.m + i] = L;
+    const uint32_t sw = wave_sum(L);
+    if (lane == 0) red[wid] = sw;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t t = 0;
+      for (int w = 0; w < DSP_T / 64; ++w) t += red[w];
+      a.ubsum[(size_t)blockIdx.x * (a.G + 1) + g] = t;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
+  hipLaunchKernelGGL(k_union, dim3((unsigned)blocks), dim3(DSP_T), 0, s, a);
   return hipGetLastError();
 }
 
@@ -560,18 +608,26 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
 // A kept product is fl32(w * v * 2^S) rounded to an integer (relative error
 // 2^-24 plus half a unit of 2^-S) and added to the column's int32 LDS word;
 // integer adds make the tile independent of order.
-template <bool REC>
+template <bool REC, int BP>
 __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
     const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
-  __shared__ int32_t tile[EFFORT_MAX_GROUP_WIDTH];
-  __shared__ uint32_t h3w[512];  // wave 0: histogram of the cutoff's last digit
-  __shared__ uint32_t pfx[256];  // inclusive prefix sums of the group's per-256-row sums
-  __shared__ uint32_t sT, sCut;
-  __shared__ int32_t sS;
-  __shared__ uint32_t mrl[MUL_W][DSP_ROWS];  // per wave: run lengths of its first 256 rows
-  __shared__ float mv[MUL_W][DSP_ROWS];      // and their activations
+  static_assert(BP == 1 || !REC, "parity recording is single-vector");
+  static_assert(BP >= 1 && BP <= 8, "at most 8 vectors per pass");
+  constexpr int PW = BP == 1 ? 1 : BP;  // the wave that scans the partition sums
+  // tiles: one vector's in a static array, several vectors' in dynamic LDS
+  // (vector p's at p * TW)
+  __shared__ int32_t tile1[BP == 1 ? EFFORT_MAX_GROUP_WIDTH : 1];
+  extern __shared__ int32_t tiled[];
+  int32_t* const tile = BP == 1 ? tile1 : tiled;
+  __shared__ uint32_t h3w[BP][512];  // wave p: histogram of vector p's last cutoff digit
+  __shared__ uint32_t pfx[256];      // inclusive prefix sums of the group's per-256-row sums
+  __shared__ uint32_t sT;
+  __shared__ uint32_t sCut[BP];
+  __shared__ int32_t sS[BP];
+  __shared__ uint32_t mrl[MUL_W][DSP_ROWS];           // per wave: run lengths of its first 256 rows
+  __shared__ float mv[BP == 1 ? MUL_W : 1][DSP_ROWS];  // and (one vector) their activations
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int G = a.G;
@@ -584,30 +640,47 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
   const uint32_t m = (uint32_t)a.m;
   const uint32_t nbd = (uint32_t)a.nbd;
   const uint32_t* rl = runlen + (size_t)g * a.m;
+  const int nv = BP == 1 ? 1 : a.nv;
 
-  // ---- round 1: wave 0 the exact cutoff, wave 1 the partition sums
-  if (wid == 0) {
-    const uint32_t b1 = result[RES_BIN], above1 = result[RES_ABOVE], nc = result[RES_NCAND];
+  // ---- round 1: wave p < nv the exact cutoff of vector p (batched: and its
+  // fixed-point scale), wave PW the partition sums
+  if (wid < nv) {
+    const uint64_t vo = (uint64_t)wid * a.vec_ws;
+    const uint32_t* res = result + vo;
+    const uint32_t b1 = res[RES_BIN], above1 = res[RES_ABOVE], nc = res[RES_NCAND];
     const uint64_t cap = (uint64_t)a.m * (uint64_t)a.P;
     const uint32_t ncap = (uint32_t)(cap < 1024u ? cap : 1024u);
     uint32_t kp;
-    const uint32_t cut = wave_exact_cutoff(a.hist2, a.cand, ncap, nc, b1, above1, a.K, h3w, &kp);
+    const uint32_t cut =
+        wave_exact_cutoff(a.hist2 + vo, a.cand + vo, ncap, nc, b1, above1, a.K, h3w[wid], &kp);
     if (lane == 0) {
-      sCut = cut;
+      sCut[wid] = cut;
       if (blockIdx.x == 0) {
-        a.result[RES_CUTOFF] = cut;
-        a.result[RES_KPRIME] = kp;
-        a.result[RES_K] = a.K;
+        a.result[vo + RES_CUTOFF] = cut;
+        a.result[vo + RES_KPRIME] = kp;
+        a.result[vo + RES_K] = a.K;
       }
     }
-  } else if (wid == 1) {
+    if (BP > 1) {
+      float B = 0.0f;
+      for (uint32_t b0 = 0; b0 < nbd; b0 += 64) {
+        const uint32_t b = b0 + lane;
+        B += wave_sum_f(b < nbd ? __uint_as_float(a.vbsum[vo + (size_t)b * G1 + G]) : 0.0f);
+      }
+      if (lane == 0) {
+        int eB = 0;
+        frexpf(B * 1.001f + 1e-38f, &eB);  // the margin covers float summation
+        sS[wid] = 30 - eB;
+      }
+    }
+  } else if (wid == PW) {
     uint32_t sb[4];
     float sf[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
       sb[u] = b < nbd ? bsum[(size_t)b * G1 + g] : 0u;
-      sf[u] = b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f;
+      sf[u] = BP == 1 && b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f;
     }
     uint32_t acc = 0;
     float B = 0.0f;
@@ -616,25 +689,26 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
       const uint32_t inc = wave_incl_scan(sb[u]);
       pfx[u * 64 + lane] = acc + inc;
       acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-      B += wave_sum_f(sf[u]);
+      if (BP == 1) B += wave_sum_f(sf[u]);
     }
     for (uint32_t b0 = 256; b0 < nbd; b0 += 64) {  // more than 256 blocks of rows
       const uint32_t b = b0 + lane;
       acc += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
-      B += wave_sum_f(b < nbd ? __uint_as_float(bsum[(size_t)b * G1 + G]) : 0.0f);
+      if (BP == 1) B += wave_sum_f(b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f);
     }
     if (lane == 0) {
-      int eB = 0;
-      frexpf(B * 1.001f + 1e-38f, &eB);  // the margin covers float summation
       sT = acc;
-      sS = 30 - eB;
+      if (BP == 1) {
+        int eB = 0;
+        frexpf(B * 1.001f + 1e-38f, &eB);  // the margin covers float summation
+        sS[0] = 30 - eB;
+      }
     }
   }
-  for (int c = tid; c < tw; c += MUL_T) tile[c] = 0;
+  for (int p = 0; p < nv; ++p)
+    for (int c = tid; c < tw; c += MUL_T) tile[p * a.TW + c] = 0;
   __syncthreads();
   const uint32_t T = sT;
-  const int S = sS;
-  const float cutoff = __uint_as_float(sCut);
 
   // this wave's share [start, end) of the group's entries, concatenated over rows
   const uint64_t nslots = (uint64_t)bpg * MUL_W;
@@ -670,7 +744,7 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
   for (int u = 0; u < 4; ++u) {
     const uint32_t j = (uint32_t)u * 64u + (uint32_t)lane;
     lr[u] = j < nr ? rl[r0 + j] : 0u;
-    lv[u] = j < nr ? vvec[r0 + j] : 0.0f;
+    lv[u] = BP == 1 && j < nr ? vvec[r0 + j] : 0.0f;
   }
 
   // ---- round 3: the share's first rows, their chunks in flight
@@ -680,7 +754,7 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       mrl[wid][u * 64 + lane] = lr[u];
-      mv[wid][u * 64 + lane] = lv[u];
+      if (BP == 1) mv[wid][u * 64 + lane] = lv[u];
     }
     uint32_t jrow = 0, before_r = 0;
     if (nr > 0u) wave_locate_regs(lr, nr, start - before_b, &jrow, &before_r);
@@ -690,7 +764,7 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
 
   // batch state: up to 64 rows from rowb, one per lane
   uint32_t Lj = 0u, aj = 0u, takej = 0u, batch_take = 0u;
-  float vj = 0.0f;
+  float vj[BP];  // the row's activation in each vector of the pass
   unsigned long long todo = 0ull;
   // chunk sequence: row sj of the batch, entries [ss, se) not yet issued
   uint32_t sj = 0u, ss = 0u, se = 0u;
@@ -698,15 +772,20 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
   auto batch_meta = [&]() {
     const uint32_t r = rowb + (uint32_t)lane;
     Lj = 0u;
-    vj = 0.0f;
+#pragma unroll
+    for (int p = 0; p < BP; ++p) vj[p] = 0.0f;
     if (r < m) {
       if (r >= r0 && r - r0 < nr) {
         Lj = mrl[wid][r - r0];
-        vj = mv[wid][r - r0];
+        if (BP == 1) vj[0] = mv[wid][r - r0];
       } else {
         Lj = rl[r];
-        vj = vvec[r];
+        if (BP == 1) vj[0] = vvec[r];
       }
+      if (BP > 1)
+#pragma unroll
+        for (int p = 0; p < BP; ++p)
+          if (p < nv) vj[p] = vvec[(size_t)p * a.m + r];
       Lj = min(Lj, (uint32_t)tw);
     }
     aj = lane == 0 ? offb : 0u;
@@ -747,12 +826,16 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
         rs, (int)(((c.s0 & ~3u) + (uint32_t)lane * 4u) * 4u), 0, 0);
     buf = make_uint4(q[0], q[1], q[2], q[3]);
   };
-  uint32_t tj = 0x7C00u;
-  float vfj = 0.0f;
+  uint32_t tj[BP];  // per vector: the row's fp16 key threshold and scaled activation
+  float vfj[BP];
   auto process = [&](const Chunk& c, const uint4& buf) {
     if (!c.valid) return;
-    const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tj, c.j);
-    const float vf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj), c.j));
+    float tf[BP], vf[BP];
+#pragma unroll
+    for (int p = 0; p < BP; ++p) {
+      tf[p] = h2f((uint32_t)__builtin_amdgcn_readlane((int)tj[p], c.j));
+      vf[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[p]), c.j));
+    }
     uint32_t ev[4] = {buf.x, buf.y, buf.z, buf.w};
     if (!REC) {
       // Words past s1 are zero.  Words before s0 can only sit in lane 0's
@@ -765,15 +848,17 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
         ev[1] = skip > 1u ? 0u : ev[1];
         ev[2] = skip > 2u ? 0u : ev[2];
       }
-      const float tf = h2f(t);
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
         const uint32_t w = ev[k2];
         const float x = h2f(w);
-        if (fabsf(x) >= tf)  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
-          atomicAdd(&tile[w >> 16], __float2int_rn(__fmul_rn(x, vf)));
+#pragma unroll
+        for (int p = 0; p < BP; ++p)
+          if (fabsf(x) >= tf[p])  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
+            atomicAdd(&tile[p * a.TW + (w >> 16)], __float2int_rn(__fmul_rn(x, vf[p])));
       }
     } else {
+      const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tj[0], c.j);
       const uint32_t row = rowb + c.j;
       const uint32_t p = (c.s0 & ~3u) + (uint32_t)lane * 4u;
       uint32_t cnt = 0u;
@@ -783,7 +868,7 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
         const uint32_t w = ev[k2];
         const uint32_t pos = p + (uint32_t)k2;
         if (pos >= c.s0 && pos < c.s1 && (w & 0x7FFFu) >= t) {
-          atomicAdd(&tile[w >> 16], __float2int_rn(__fmul_rn(h2f(w), vf)));
+          atomicAdd(&tile[w >> 16], __float2int_rn(__fmul_rn(h2f(w), vf[0])));
           const uint64_t flat = (uint64_t)row * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
           if (a.mask) a.mask[flat] = 1u;
           fp += pair_hash(flat);
@@ -806,10 +891,13 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     }
   };
   auto thresholds = [&]() {
-    tj = Lj ? key_threshold_fast(fabsf(vj), cutoff) : 0x7C00u;
-    // clamped: only a row whose weights are all zero can exceed it, and its
-    // products stay 0
-    vfj = fminf(fmaxf(ldexpf(vj, S), -0x1p100f), 0x1p100f);
+#pragma unroll
+    for (int p = 0; p < BP; ++p) {
+      tj[p] = p < nv && Lj ? key_threshold_fast(fabsf(vj[p]), __uint_as_float(sCut[p])) : 0x7C00u;
+      // clamped: only a row whose weights are all zero can exceed it, and its
+      // products stay 0
+      vfj[p] = p < nv ? fminf(fmaxf(ldexpf(vj[p], sS[p]), -0x1p100f), 0x1p100f) : 0.0f;
+    }
   };
   // A ring of 8 chunks in flight: a slot is processed, then refilled with the
   // next chunk, so 7 loads stay outstanding while one is used.
@@ -855,27 +943,70 @@ __global__ __launch_bounds__(MUL_T) void k_bucketmul(
     thresholds();
   }
   __syncthreads();
-  const double unscale = ldexp(1.0, -S);
-  for (int c = tid; c < tw; c += MUL_T) {
-    const int32_t acc = tile[c];
-    if (acc != 0) atomicAdd(&y[col0 + c], (float)((double)acc * unscale));
+  for (int p = 0; p < nv; ++p) {
+    const double unscale = ldexp(1.0, -sS[p]);
+    for (int c = tid; c < tw; c += MUL_T) {
+      const int32_t acc = tile[p * a.TW + c];
+      if (acc != 0) atomicAdd(&y[(size_t)p * a.n + col0 + c], (float)((double)acc * unscale));
+    }
   }
   if (blockIdx.x == 0)  // only the dispatch reads it: ready for the next call
-    for (int b = tid; b < HIST_BINS; b += MUL_T) a.hist[b] = 0u;
+    for (int p = 0; p < nv; ++p)
+      for (int b = tid; b < HIST_BINS; b += MUL_T) a.hist[(size_t)p * a.vec_ws + b] = 0u;
+}
+
+// LDS of a workgroup on gfx950; the batched kernel's static LDS (cutoff
+// histograms, prefix sums, row staging) stays under kMulStaticLds for 8 vectors.
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr size_t kMulStaticLds = 24 * 1024;
+
+// Largest dynamic LDS (the vectors' tiles) a pass of bp vectors may request.
+static size_t pass_tile_budget(int bp) {
+  const size_t per = (kLdsBytes - kMulStaticLds) / (size_t)bp;  // tile + cutoff histogram
+  return (size_t)bp * (per - 2048);
+}
+
+int bucketmul_pass_width(int32_t TW, int32_t batch) {
+  if (batch < 2) return 0;
+  for (int bp = 8; bp >= 2; bp >>= 1)
+    if ((size_t)bp * ((size_t)TW * 4) <= pass_tile_budget(bp)) return bp;
+  return 0;
+}
+
+template <int BP>
+static hipError_t launch_mul_bp(const MulArgs& a, unsigned grid, hipStream_t s) {
+  const size_t lds = (size_t)BP * a.TW * sizeof(int32_t);
+  if (lds > pass_tile_budget(BP)) return hipErrorInvalidValue;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bucketmul<false, BP>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)pass_tile_budget(BP));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_bucketmul<false, BP>), dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
+                     a.runlen, a.bsum, a.result, a.y, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
                             const EventPair* ev) {
   const unsigned grid = (unsigned)(a.G * blocks_per_group);
-  const size_t lds = 0;
+  if (a.nv > 1) {
+    if (record || a.nv > 8) return hipErrorInvalidValue;
+    if (a.nv > 4) return launch_mul_bp<8>(a, grid, s);
+    if (a.nv > 2) return launch_mul_bp<4>(a, grid, s);
+    return launch_mul_bp<2>(a, grid, s);
+  }
   if (ev && ev->start && !record)
-    hipExtLaunchKernelGGL(k_bucketmul<false>, dim3(grid), dim3(MUL_T), (uint32_t)lds, s, ev->start,
+    hipExtLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(MUL_T), 0, s, ev->start,
                           ev->stop, 0, a.v, a.entries, a.runlen, a.bsum, a.result, a.y, a);
   else if (record)
-    hipLaunchKernelGGL(k_bucketmul<true>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
+    hipLaunchKernelGGL((k_bucketmul<true, 1>), dim3(grid), dim3(MUL_T), 0, s, a.v, a.entries,
                        a.runlen, a.bsum, a.result, a.y, a);
   else
-    hipLaunchKernelGGL(k_bucketmul<false>, dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
+    hipLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(MUL_T), 0, s, a.v, a.entries,
                        a.runlen, a.bsum, a.result, a.y, a);
   return hipGetLastError();
 }

@@ -21,6 +21,9 @@ struct SelectArgs {
   uint32_t* result;  // [3] candidate count, cleared here
   float* y;          // zeroed here (the multiply accumulates into it)
   int64_t n;
+  // several vectors in one launch (grid y): vector k reads v + k m, writes
+  // y + k n and uses the workspace words hist/hist2/result + k vec_ws
+  uint64_t vec_ws;
 };
 
 // result words of the workspace
@@ -47,6 +50,18 @@ struct DispatchArgs {
   int64_t m;
   int32_t P, G, G4;
   uint32_t K;
+  uint64_t vec_ws;  // grid y = vector: its v + k m and workspace words + k vec_ws
+};
+
+// Union of several vectors' read lengths (batched multiply): per (group, row)
+// the largest read length over the vectors, and its per-256-row sums.
+struct UnionArgs {
+  const uint32_t* runlen;  // vector 0's [G][m]; vector k at + k vec_ws
+  uint64_t vec_ws;
+  int32_t nv, G;
+  int64_t m;
+  uint32_t* urunlen;  // [G][m]
+  uint32_t* ubsum;    // [ceil(m / DSP_ROWS)][G + 1] (the last column unused)
 };
 
 // bucketMul: every block first finishes the exact cutoff (histograms + the
@@ -54,8 +69,12 @@ struct DispatchArgs {
 // whose magnitude reaches the row threshold, scatters v_i * w into an LDS tile
 // of the group's output columns and adds the tile to y.  The entries of a
 // group, concatenated over rows, are split evenly over the group's waves.  The
-// tile holds 64-bit fixed-point sums (integer LDS atomics); the scale comes from
+// tile holds 32-bit fixed-point sums (integer LDS atomics); the scale comes from
 // the bound sum_i |v_i| * rowmax_i >= |any partial sum|.
+//
+// Batched (nv > 1 vectors of one pass): runlen/bsum are the union read lengths;
+// vector k's v, y, cutoff inputs, bound column and histogram to clear are at
+// v + k m, y + k n and the workspace words + k vec_ws; one tile per vector.
 struct MulArgs {
   const float* v;
   const uint32_t* entries;  // [m][row_stride]
@@ -69,6 +88,10 @@ struct MulArgs {
   int64_t m, n, row_stride;
   int32_t G, TW, nbd, P;
   uint32_t K;
+  int32_t nv;              // vectors of this pass (1: the single-vector path)
+  uint64_t vec_ws;
+  const uint32_t* vbsum;    // vector 0's own per-256-row sums: column G is its bound
+                            // (bsum, the partition's sums, is the union when batched)
   // parity recording (null in the timed path)
   int32_t* row_kept;
   unsigned long long* fingerprint;
@@ -83,8 +106,14 @@ struct EventPair {
   hipEvent_t stop = nullptr;
 };
 
-hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev = nullptr);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev = nullptr);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev = nullptr,
+                         int nvec = 1);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev = nullptr,
+                           int nvec = 1);
+hipError_t launch_union(const UnionArgs& a, hipStream_t s);
+// vectors per pass of the batched multiply that the LDS holds for groups of
+// TW columns (0: none, use single-vector calls)
+int bucketmul_pass_width(int32_t TW, int32_t batch);
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
                             const EventPair* ev = nullptr);
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,

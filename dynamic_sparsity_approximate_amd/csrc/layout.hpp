@@ -78,11 +78,16 @@ inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geomet
 //   runlen   u32[G][m]                per (group, row) entries to read
 //   bsum     u32[ceil(m/256)][G + 1]  per 256 rows: sum of runlen per group, then
 //                                     (as f32) the sum of |v_i| * rowmax_i
-// result, hist and hist2 are zero on entry and left zero.
+// result, hist and hist2 are zero on entry and left zero.  A batched call with b
+// vectors uses b slices and then the union area: urunlen u32[G][m] (per
+// (group, row) the largest read length over the vectors of a pass) and ubsum
+// u32[ceil(m/256)][G + 1] (its per-256-row sums).
 constexpr int64_t kDspRows = 256;
 
 struct WsLayout {
   uint64_t result, hist, hist2, cand, runlen, bsum, slice;
+  // batched calls: after the per-vector slices, the union read lengths
+  uint64_t urunlen, ubsum, union_bytes;
 };
 
 inline WsLayout ws_layout(const Geometry& g) {
@@ -95,6 +100,9 @@ inline WsLayout ws_layout(const Geometry& g) {
   w.runlen = align_up(w.cand + (uint64_t)g.m * g.P * 4, kAlign);
   w.bsum = align_up(w.runlen + (uint64_t)g.G * g.m * 4, kAlign);
   w.slice = align_up(w.bsum + nbd * (g.G + 1) * 4, kAlign);
+  w.urunlen = 0;  // offsets from the end of the slices
+  w.ubsum = align_up((uint64_t)g.G * g.m * 4, kAlign);
+  w.union_bytes = align_up(w.ubsum + nbd * (g.G + 1) * 4, kAlign);
   return w;
 }
 

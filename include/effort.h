@@ -96,9 +96,10 @@ int effort_layout_bytes_ex(int64_t in_dim, int64_t out_dim, int32_t P, int32_t g
                            uint64_t* bytes);
 
 /* Device workspace for one call of effort_matvec* with `batch` vectors
-   (1 <= batch <= EFFORT_MAX_BATCH).  The workspace must be zero-filled before
-   its first use (effort_workspace_init); every call leaves it ready for the
-   next.  One workspace serves one call at a time. */
+   (1 <= batch <= EFFORT_MAX_BATCH): one slice per vector and, for batch > 1,
+   room for the union of the vectors' read lengths.  The workspace must be
+   zero-filled before its first use (effort_workspace_init); every call leaves
+   it ready for the next.  One workspace serves one call at a time. */
 int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* bytes);
 
 /* Zero-fill `ws_bytes` of device memory at ws_dev (stream-ordered). */
@@ -139,7 +140,12 @@ int effort_matvec(const effort_desc* desc, const void* layout_dev, const float* 
                   float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* `batch` independent vectors v_dev[batch][in_dim] -> y_dev[batch][out_dim],
-   each with its own K, cutoff and kept set.  ws >= effort_workspace_bytes(desc, batch). */
+   each with its own K, cutoff and kept set (the same result as `batch` calls
+   of effort_matvec).  The vectors' cutoffs and read lengths come from one
+   launch each; then, per pass of up to 8 vectors (fewer for wide column
+   groups: their LDS tiles must fit), every row's entries are read once up to
+   the longest of the pass's read lengths and each entry is tested against
+   every vector's threshold.  ws >= effort_workspace_bytes(desc, batch). */
 int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                           int32_t batch, float effort, float* y_dev, void* ws_dev,
                           uint64_t ws_bytes, void* stream);

@@ -256,10 +256,14 @@ def test_matvec_rejects_bad_buffers_and_descriptors():
         with pytest.raises(E.EffortError) as ei:
             E.effort_matvec_batched(d, FAKE, FAKE, batch, 0.25, FAKE, FAKE, ws * 17)
         assert ei.value.code == B.EFFORT_EINVAL
+    # b slices, then the union read lengths [G][m] and their per-256-row sums
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    m, G = int(d.in_dim), int(d.groups)
+    wb4 = 4 * ws + up(G * m * 4) + up(-(-m // 256) * (G + 1) * 4)
+    assert E.effort_workspace_bytes(d, 4) == wb4
     with pytest.raises(E.EffortError) as ei:
-        E.effort_matvec_batched(d, FAKE, FAKE, 4, 0.25, FAKE, FAKE, 4 * ws - 1)
+        E.effort_matvec_batched(d, FAKE, FAKE, 4, 0.25, FAKE, FAKE, wb4 - 1)
     assert ei.value.code == B.EFFORT_ENOSPACE
-    assert E.effort_workspace_bytes(d, 4) == 4 * ws
     with pytest.raises(E.EffortError):
         E.effort_workspace_bytes(d, 0)
 

@@ -283,3 +283,34 @@ def test_timed_entry_matches_and_stamps_kernels():
         torch.cuda.synchronize()
         for e in evs:
             E.effort_event_destroy(e)
+
+
+@pytest.mark.parametrize("m,n,G,b,P", [(4096, 14336, 0, 2, 16), (4096, 14336, 0, 9, 16),
+                                       (4096, 14336, 0, 16, 16), (513, 2049, 3, 3, 16),
+                                       (300, 1000, 0, 16, 5), (64, 8192, 1, 4, 8)])
+def test_batched_fused_matches_oracle(m, n, G, b, P):
+    """Fused batched path (passes of up to 8 vectors over the union of their read
+    lengths): every vector's exact cutoff bits, K and K' and y against the oracle."""
+    d = dev()
+    W, _ = case(m, n, seed=m + b, tag="fused")
+    M = E.EffortMatrix(W, P=P, groups=G, device=d, batch=b)
+    V = np.stack([synth.vector("fused", m, seed=s) for s in range(b)])
+    V[1 % b] *= 7.0  # vectors of different scale in one pass
+    effort = 0.25
+    Y = M.matvec_batched(torch.from_numpy(V).to(d), effort)
+    torch.cuda.synchronize()
+    pr = oracle.probes(W, P)
+    sl = E.effort_workspace_bytes(M.desc, 1)
+    ws = M.ws.cpu().numpy()
+    for k in range(b):
+        ref = oracle.run(W, pr, V[k], effort)
+        res = ws[k * sl: k * sl + 16].view(np.uint32)
+        assert res[0] == np.float32(ref["cutoff"]).view(np.uint32), (k, res[0])
+        assert res[2] == ref["K"] and res[1] == ref["Kprime"], k
+        err = rel_l2(Y[k].cpu().numpy(), ref["y"])
+        assert err <= REL_L2_TOL, (k, err)
+    say("fused %dx%d G=%d b=%d ok" % (m, n, M.groups, b))
+    # a second call on the same workspace gives the same result
+    Y2 = M.matvec_batched(torch.from_numpy(V).to(d), effort)
+    torch.cuda.synchronize()
+    assert rel_l2(Y2.cpu().numpy(), Y.cpu().numpy()) < 1e-6

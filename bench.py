@@ -60,6 +60,9 @@ def parse():
                          "vectors against the dense small GEMM; decode: a whole Mistral-7B-"
                          "shaped decode step; moe: a Mixtral-shaped expert block")
     ap.add_argument("--layers", type=int, default=32, help="decode mode: decoder layers")
+    ap.add_argument("--streams", type=int, default=6,
+                    help="decode/moe modes: side streams for matvecs that do not depend on "
+                         "each other (0: one stream)")
     return ap.parse_args()
 
 
@@ -432,12 +435,18 @@ def run_decode(args, torch, np, E, synth, dev):
     hin = to(synth.vector("config2/head_in", MISTRAL["dim"], seed=0))
     step = E.DecodeStep(layers, head, x, a, hin)
     dstep = E.DenseDecodeStep(dlayers, dhead, x, a, hin)
-    us = graph_time_us(torch, lambda: step.enqueue(effort), 20)
-    dus = graph_time_us(torch, lambda: dstep.enqueue(), 20)
+    side = [torch.cuda.Stream() for _ in range(args.streams)] or None
+    us1 = graph_time_us(torch, lambda: step.enqueue(effort), 20)
+    dus1 = graph_time_us(torch, lambda: dstep.enqueue(), 20)
+    us = graph_time_us(torch, lambda: step.enqueue(effort, side_streams=side), 20) if side else us1
+    dus = graph_time_us(torch, lambda: dstep.enqueue(side_streams=side), 20) if side else dus1
     print(json.dumps({"mode": "decode", "workload": "Mistral-7B-shaped decode step, %d layers + head, "
                       "effort %g, batch 1" % (L, effort), "matvecs": step.calls,
-                      "weights": weights, "effort_us_per_token": round(us, 1),
-                      "dense_us_per_token": round(dus, 1), "speedup_vs_dense": round(dus / us, 3),
+                      "weights": weights, "side_streams": args.streams,
+                      "effort_us_per_token": round(us, 1), "dense_us_per_token": round(dus, 1),
+                      "speedup_vs_dense": round(dus / us, 3),
+                      "one_stream": {"effort_us_per_token": round(us1, 1),
+                                     "dense_us_per_token": round(dus1, 1)},
                       "dense_GBps": round(2.0 * weights / dus / 1e3, 1)}))
 
 
@@ -476,11 +485,15 @@ def run_moe(args, torch, np, E, synth, dev):
         E.effort_axpby(o[0], g0, o[1], g1, d, y)
 
     dus = graph_time_us(torch, lambda: [dense_token(t) for t in range(tokens)], 10) / tokens
+    side = [torch.cuda.Stream() for _ in range(max(args.streams, 4))] if args.streams else None
     points = []
     for effort in (0.25, 0.16, 0.12):
-        us = graph_time_us(torch, lambda: [moe.enqueue(xs[t], routes[t], effort)
-                                          for t in range(tokens)], 10) / tokens
+        us1 = graph_time_us(torch, lambda: [moe.enqueue(xs[t], routes[t], effort)
+                                           for t in range(tokens)], 10) / tokens
+        us = graph_time_us(torch, lambda: [moe.enqueue(xs[t], routes[t], effort, side_streams=side)
+                                          for t in range(tokens)], 10) / tokens if side else us1
         points.append({"effort": effort, "effort_us_per_token": round(us, 1),
+                       "one_stream_us_per_token": round(us1, 1),
                        "speedup_vs_dense": round(dus / us, 3)})
         log(json.dumps(points[-1]))
     print(json.dumps({"mode": "moe", "workload": "Mixtral-shaped expert block, 8 experts, top-2, "

@@ -50,14 +50,30 @@ class DecodeStep:
         return {"wq": self.x[l], "wk": self.x[l], "wv": self.x[l], "wo": self.a[l], "w1": self.x[l],
                 "w3": self.x[l], "w2": o["g"]}
 
-    def enqueue(self, effort: float, stream=None):
+    def enqueue(self, effort: float, stream=None, side_streams=None):
+        """Issue every call on `stream` (None: torch's current stream).  With
+        `side_streams` (torch streams), the six matvecs of a layer that do not
+        depend on each other run on separate streams (parallel branches when
+        captured into a graph); w2 and the next layer wait for them."""
+        import torch
+
+        main = stream if stream is not None else torch.cuda.current_stream()
         for l, L in enumerate(self.layers):
             o, ins = self.out[l], self.inputs_of(l)
-            for r in ("wq", "wk", "wv", "wo", "w1", "w3"):
-                L[r].matvec(ins[r], effort, o[r], stream)
-            B.effort_silu_mul(o["w1"], o["w3"], L["w1"].out_dim, o["g"], stream)
-            L["w2"].matvec(o["g"], effort, o["w2"], stream)
-        self.head.matvec(self.head_in, effort, self.logits, stream)
+            roles = ("wq", "wk", "wv", "wo", "w1", "w3")
+            if side_streams:
+                for k, r in enumerate(roles):
+                    ss = side_streams[k % len(side_streams)]
+                    ss.wait_stream(main)
+                    L[r].matvec(ins[r], effort, o[r], ss)
+                for ss in side_streams[:len(roles)]:
+                    main.wait_stream(ss)
+            else:
+                for r in roles:
+                    L[r].matvec(ins[r], effort, o[r], main)
+            B.effort_silu_mul(o["w1"], o["w3"], L["w1"].out_dim, o["g"], main)
+            L["w2"].matvec(o["g"], effort, o["w2"], main)
+        self.head.matvec(self.head_in, effort, self.logits, main)
 
 
 class DenseDecodeStep:
@@ -76,19 +92,29 @@ class DenseDecodeStep:
             self.out.append(o)
         self.logits = torch.empty(head.shape[1], dtype=torch.float32, device=dev)
 
-    def enqueue(self, stream=None):
+    def enqueue(self, stream=None, side_streams=None):
+        import torch
+
+        main = stream if stream is not None else torch.cuda.current_stream()
+        roles = ("wq", "wk", "wv", "wo", "w1", "w3")
         for l, L in enumerate(self.layers):
             o = self.out[l]
             ins = {"wq": self.x[l], "wk": self.x[l], "wv": self.x[l], "wo": self.a[l],
                    "w1": self.x[l], "w3": self.x[l]}
-            for r in ("wq", "wk", "wv", "wo", "w1", "w3"):
+            for k, r in enumerate(roles):
+                ss = side_streams[k % len(side_streams)] if side_streams else main
+                if ss is not main:
+                    ss.wait_stream(main)
                 m, n = L[r].shape
-                B.dense_gemv(L[r], ins[r], m, n, o[r], stream)
-            B.effort_silu_mul(o["w1"], o["w3"], L["w1"].shape[1], o["g"], stream)
+                B.dense_gemv(L[r], ins[r], m, n, o[r], ss)
+            if side_streams:
+                for ss in side_streams[:len(roles)]:
+                    main.wait_stream(ss)
+            B.effort_silu_mul(o["w1"], o["w3"], L["w1"].shape[1], o["g"], main)
             m, n = L["w2"].shape
-            B.dense_gemv(L["w2"], o["g"], m, n, o["w2"], stream)
+            B.dense_gemv(L["w2"], o["g"], m, n, o["w2"], main)
         m, n = self.head.shape
-        B.dense_gemv(self.head, self.head_in, m, n, self.logits, stream)
+        B.dense_gemv(self.head, self.head_in, m, n, self.logits, main)
 
 
 def route_top2(logits):
@@ -123,13 +149,30 @@ class MoEFFN:
         self.o = [mk(d_in), mk(d_in)]
         self.y = mk(d_in)
 
-    def enqueue(self, x, route, effort: float, stream=None):
+    def enqueue(self, x, route, effort: float, stream=None, side_streams=None):
+        """With `side_streams` (at least two torch streams), the two experts run
+        on separate streams, and w1 / w3 of an expert on separate streams when
+        there are four."""
+        import torch
+
+        main = stream if stream is not None else torch.cuda.current_stream()
         e0, e1, g0, g1 = route
+        ns = len(side_streams) if side_streams else 0
         for k, e in enumerate((e0, e1)):
             w1, w3, w2 = self.experts[e]
-            w1.matvec(x, effort, self.h1[k], stream)
-            w3.matvec(x, effort, self.h3[k], stream)
-            B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], stream)
-            w2.matvec(self.g[k], effort, self.o[k], stream)
-        B.effort_axpby(self.o[0], g0, self.o[1], g1, self.d_in, self.y, stream)
+            s1 = side_streams[k % ns] if ns >= 2 else main
+            s3 = side_streams[2 + k] if ns >= 4 else s1
+            for ss in {s1, s3}:
+                if ss is not main:
+                    ss.wait_stream(main)
+            w1.matvec(x, effort, self.h1[k], s1)
+            w3.matvec(x, effort, self.h3[k], s3)
+            if s3 is not s1:
+                s1.wait_stream(s3)
+            B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], s1)
+            w2.matvec(self.g[k], effort, self.o[k], s1)
+        if ns >= 2:
+            for ss in side_streams[:2]:
+                main.wait_stream(ss)
+        B.effort_axpby(self.o[0], g0, self.o[1], g1, self.d_in, self.y, main)
         return self.y

@@ -81,6 +81,15 @@ def test_decode_step_two_layers_and_head():
     err = check_matvec(Wh, hin.cpu().numpy(), logits, effort, "head")
     say("head rel-L2 %.2e" % err)
 
+    # the same step with its independent matvecs on six side streams
+    side = [torch.cuda.Stream() for _ in range(6)]
+    step.enqueue(effort, side_streams=side)
+    torch.cuda.synchronize()
+    assert rel_l2(step.logits.cpu().numpy(), logits) < 1e-6
+    for layer in range(2):
+        for r in E.LAYER_ROLES:
+            assert rel_l2(step.out[layer][r].cpu().numpy(), eager[layer][r]) < 1e-6, (layer, r)
+
     # the chain captured in a graph replays to the eager result
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -135,6 +144,12 @@ def test_moe_block_two_routed_experts(effort):
     y_ref = np.float64(np.float32(g0)) * outs[0] + np.float64(np.float32(g1)) * outs[1]
     err = rel_l2(y.cpu().numpy(), y_ref)
     assert err <= 1e-6, err
+    # experts and their w1 / w3 on side streams give the same block output
+    y1 = y.cpu().numpy().copy()
+    side = [torch.cuda.Stream() for _ in range(4)]
+    y2 = moe.enqueue(x, route, effort, side_streams=side)
+    torch.cuda.synchronize()
+    assert rel_l2(y2.cpu().numpy(), y1) < 1e-6
     say("moe effort %.2f experts %d,%d ok" % (effort, e0, e1))
 
 

@@ -411,7 +411,12 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------- bucketMul
 
-constexpr int MUL_T = 1024;
+// threads per bucketMul block: 8 waves for one vector, 16 for a batched pass
+// (waves 0..7 compute the pass's cutoffs, wave 8 the partition sums)
+template <int BP>
+constexpr int mul_threads() {
+  return BP == 1 ? 512 : 1024;
+}
 constexpr int CH = 256;  // entries per chunk: one 16-byte quad per lane
 
 struct Chunk {
@@ -422,7 +427,6 @@ struct Chunk {
 // Word 3 of a raw buffer descriptor on gfx9-family chips: 32-bit data format
 // (a zero format would make every access out of range).
 constexpr int kBufferDword3 = 0x00020000;
-constexpr int MUL_W = MUL_T / 64;
 
 // Finds, among `count` non-negative values x[0..count) (x(j) loads one), the
 // index j with prefix(j) <= target < prefix(j) + x[j] and x[j] > 0; returns
@@ -609,12 +613,15 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
 // 2^-24 plus half a unit of 2^-S) and added to the column's int32 LDS word;
 // integer adds make the tile independent of order.
 template <bool REC, int BP>
-__global__ __launch_bounds__(MUL_T) void k_bucketmul(
+__global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
     const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
   static_assert(BP == 1 || !REC, "parity recording is single-vector");
   static_assert(BP >= 1 && BP <= 8, "at most 8 vectors per pass");
+  constexpr int MUL_T = mul_threads<BP>();
+  constexpr int MUL_W = MUL_T / 64;
+  static_assert(BP == 1 || MUL_W > BP, "a wave for each cutoff and one for the partition");
   constexpr int PW = BP == 1 ? 1 : BP;  // the wave that scans the partition sums
   // tiles: one vector's in a static array, several vectors' in dynamic LDS
   // (vector p's at p * TW)
@@ -985,7 +992,8 @@ static hipError_t launch_mul_bp(const MulArgs& a, unsigned grid, hipStream_t s) 
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_bucketmul<false, BP>), dim3(grid), dim3(MUL_T), lds, s, a.v, a.entries,
+  hipLaunchKernelGGL((k_bucketmul<false, BP>), dim3(grid), dim3(mul_threads<BP>()), lds, s, a.v,
+                     a.entries,
                      a.runlen, a.bsum, a.result, a.y, a);
   return hipGetLastError();
 }
@@ -1000,13 +1008,15 @@ hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group,
     return launch_mul_bp<2>(a, grid, s);
   }
   if (ev && ev->start && !record)
-    hipExtLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(MUL_T), 0, s, ev->start,
+    hipExtLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, ev->start,
                           ev->stop, 0, a.v, a.entries, a.runlen, a.bsum, a.result, a.y, a);
   else if (record)
-    hipLaunchKernelGGL((k_bucketmul<true, 1>), dim3(grid), dim3(MUL_T), 0, s, a.v, a.entries,
+    hipLaunchKernelGGL((k_bucketmul<true, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
+                       a.entries,
                        a.runlen, a.bsum, a.result, a.y, a);
   else
-    hipLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(MUL_T), 0, s, a.v, a.entries,
+    hipLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
+                       a.entries,
                        a.runlen, a.bsum, a.result, a.y, a);
   return hipGetLastError();
 }

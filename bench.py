@@ -261,6 +261,22 @@ def main():
         dense_us = dms * 1e3 / (dreps * Rd)
         result["dense_us"] = dense_us
         result["dense_gbs"] = 2.0 * m * n / (dense_us * 1e-6) / 1e9
+        # library sanity reference: torch's fp16 matmul (hipBLASLt / rocBLAS) on the
+        # same rotation, v rounded to fp16, fp16 output
+        Whs = [w.view(torch.float16) for w in Wds]
+        vhs = [x.to(torch.float16).reshape(1, m) for x in vds]
+        yhs = [torch.empty((1, n), dtype=torch.float16, device=dev) for _ in range(Rd)]
+
+        def lcycle():
+            for r in range(Rd):
+                torch.matmul(vhs[r], Whs[r], out=yhs[r])
+
+        for _ in range(3):
+            lcycle()
+        gl = capture(torch, lcycle)
+        time_replays(torch, gl, max(1, args.warmup // Rd))
+        lms, _ = time_replays(torch, gl, dreps)
+        result["library_dense_us"] = lms * 1e3 / (dreps * Rd)
         if "us_per_matvec" in result:
             result["speedup_vs_dense"] = dense_us / result["us_per_matvec"]
 
@@ -297,6 +313,7 @@ def main():
                        "groups": result["groups"], "rotation_copies": result["rotation"]},
             "hbm_gbs": result["hbm_gbs"], "kept_fraction": result["kept_fraction"],
             "dense_us": result["dense_us"], "dense_gbs": result["dense_gbs"],
+            "library_dense_us": result["library_dense_us"],
             "speedup_vs_dense": result["speedup_vs_dense"], "stages_us": result["stages_us"],
             "roofline": result["roofline"], "cpu_baseline": cpu,
         }

@@ -518,14 +518,15 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
     h[4 * c + 2] = q.z;
     h[4 * c + 3] = q.w;
   }
-  // the first 16 * 64 candidates, loaded with the histogram (words past the
+  // the first CB * 64 candidates, loaded with the histogram (words past the
   // list's capacity read as zero; those at p >= nc are ignored)
-  uint32_t cv[16];
+  constexpr int CB = 16;
+  uint32_t cv[CB];
   {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)cand, (short)0, (int)(ncap * 4u), kBufferDword3);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) cv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u * 64 + lane) * 4, 0, 0);
+    for (int u = 0; u < CB; ++u) cv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, (u * 64 + lane) * 4, 0, 0);
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) h3[k * 64 + lane] = 0u;
@@ -556,14 +557,21 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
 
   // last digit: histogram of the matching candidates' bits 8..0
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
+  for (int u = 0; u < CB; ++u) {
     const uint32_t p = (uint32_t)(u * 64 + lane);
     if (p < nc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
   }
-  for (uint32_t p0 = 16u * 64u; p0 < nc; p0 += 64u) {  // more than 1024 candidates
-    const uint32_t p = p0 + (uint32_t)lane;
-    const uint32_t c = p < nc ? cand[p] : 0u;
-    if (p < nc && (c >> 9) == pre) atomicAdd(&h3[c & 511u], 1u);
+  for (uint32_t p0 = CB * 64u; p0 < nc; p0 += CB * 64u) {  // more candidates: CB per lane a round
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const uint32_t p = p0 + (uint32_t)(u * 64 + lane);
+      cv[u] = p < nc ? cand[p] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const uint32_t p = p0 + (uint32_t)(u * 64 + lane);
+      if (p < nc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
+    }
   }
   // lane l holds bins [504 - 8 l, 512 - 8 l)
   uint32_t g[8];

@@ -411,11 +411,13 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------- bucketMul
 
-// threads per bucketMul block: 8 waves for one vector, 16 for a batched pass
-// (waves 0..7 compute the pass's cutoffs, wave 8 the partition sums)
+// threads per bucketMul block.  One vector: 9 waves, wave 0 computing the
+// cutoff and 8 streaming (measured faster than 7 or 9 streaming waves);
+// a batched pass: 16 waves (waves 0..7 compute the pass's cutoffs, wave 8 the
+// partition sums, then all stream).
 template <int BP>
 constexpr int mul_threads() {
-  return BP == 1 ? 512 : 1024;
+  return BP == 1 ? 576 : 1024;
 }
 constexpr int CH = 256;  // entries per chunk: one 16-byte quad per lane
 
@@ -606,14 +608,18 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
 // Block (g, s) of the grid: group g's LDS tile, share s of its entries.
 //
 // Prologue, three dependent rounds of global loads:
-//   (1) wave 0: the cutoff's bin, the refinement histogram and the candidate
-//       chart values, from which it computes the exact cutoff (every block
-//       gets the same value); wave 1: the per-256-row sums that place each
-//       wave's share, scanned once into LDS;
+//   (1) the per-256-row sums that place each wave's share (and, for one
+//       vector, give the fixed-point scale); for the cutoff, its bin, the
+//       refinement histogram and the candidate chart values, from which the
+//       exact cutoff is computed (every block gets the same value);
 //   (2) per wave, the run lengths and activations of the 256 rows where its
 //       share starts;
 //   (3) the share's first chunks of entries, in flight while each row's fp16
 //       key threshold is derived from the cutoff.
+// One vector: wave 0 only computes the cutoff, while the other waves run the
+// three rounds; the barrier after round 3 publishes the cutoff.  Batched:
+// waves 0..nv-1 compute the cutoffs and wave PW the partition sums before a
+// barrier, then every wave runs rounds 2 and 3.
 //
 // Accumulation: with B >= |any sum of kept products| and B * 1.001 < 2^eB,
 // the scale 2^S, S = 30 - eB, keeps every tile sum below 2^30 in magnitude.
@@ -644,7 +650,9 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   __shared__ uint32_t mrl[MUL_W][DSP_ROWS];           // per wave: run lengths of its first 256 rows
   __shared__ float mv[BP == 1 ? MUL_W : 1][DSP_ROWS];  // and (one vector) their activations
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  // the wave index made provably uniform: descriptors and per-wave offsets
+  // derived from it stay in scalar registers
+  const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G;
   const int G1 = G + 1;
   const int g = (int)(blockIdx.x % (unsigned)G);
@@ -657,9 +665,9 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   const uint32_t* rl = runlen + (size_t)g * a.m;
   const int nv = BP == 1 ? 1 : a.nv;
 
-  // ---- round 1: wave p < nv the exact cutoff of vector p (batched: and its
-  // fixed-point scale), wave PW the partition sums
-  if (wid < nv) {
+  // ---- round 1
+  // wave p < nv: the exact cutoff of vector p (batched: and its fixed-point scale)
+  auto cutoff_wave = [&]() {
     const uint64_t vo = (uint64_t)wid * a.vec_ws;
     const uint32_t* res = result + vo;
     const uint32_t b1 = res[RES_BIN], above1 = res[RES_ABOVE], nc = res[RES_NCAND];
@@ -688,61 +696,106 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
         sS[wid] = 30 - eB;
       }
     }
-  } else if (wid == PW) {
-    uint32_t sb[4];
-    float sf[4];
+  };
+  // The group's per-256-row sums: index u * 64 + lane in sb[u] (one vector).
+  uint32_t sb[4] = {0u, 0u, 0u, 0u};
+  uint32_t T = 0u;  // the group's entry count
+  int S1 = 0;       // one vector: the fixed-point scale, computed by every share wave
+  if constexpr (BP == 1) {
+    // Wave 0 only computes the cutoff.  Every other wave sums the group's
+    // per-256-row sums itself (the same loads and the same order of addition
+    // in every wave, so the same T and scale) and goes on to stage its rows and
+    // issue its first chunks while the cutoff is being computed; the barrier
+    // before the stream publishes the cutoff.
+    for (int c = tid; c < tw; c += MUL_T) tile[c] = 0;
+    if (wid == 0) {
+      cutoff_wave();
+    } else {
+      float sf[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
-      sb[u] = b < nbd ? bsum[(size_t)b * G1 + g] : 0u;
-      sf[u] = BP == 1 && b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f;
-    }
-    uint32_t acc = 0;
-    float B = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t inc = wave_incl_scan(sb[u]);
-      pfx[u * 64 + lane] = acc + inc;
-      acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-      if (BP == 1) B += wave_sum_f(sf[u]);
-    }
-    for (uint32_t b0 = 256; b0 < nbd; b0 += 64) {  // more than 256 blocks of rows
-      const uint32_t b = b0 + lane;
-      acc += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
-      if (BP == 1) B += wave_sum_f(b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f);
-    }
-    if (lane == 0) {
-      sT = acc;
-      if (BP == 1) {
-        int eB = 0;
-        frexpf(B * 1.001f + 1e-38f, &eB);  // the margin covers float summation
-        sS[0] = 30 - eB;
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
+        sb[u] = b < nbd ? bsum[(size_t)b * G1 + g] : 0u;
+        sf[u] = b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f;
       }
+      float B = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        T += wave_sum(sb[u]);
+        B += wave_sum_f(sf[u]);
+      }
+      for (uint32_t b0 = 256; b0 < nbd; b0 += 64) {  // more than 256 blocks of rows
+        const uint32_t b = b0 + lane;
+        T += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
+        B += wave_sum_f(b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f);
+      }
+      int eB = 0;
+      frexpf(B * 1.001f + 1e-38f, &eB);  // the margin covers float summation
+      S1 = 30 - eB;
+      if (wid == 1 && lane == 0) sS[0] = S1;  // for the flush
     }
+  } else {
+    // Batched: waves 0..nv-1 the cutoffs, wave PW the partition sums, then a
+    // barrier.
+    if (wid < nv) {
+      cutoff_wave();
+    } else if (wid == PW) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
+        sb[u] = b < nbd ? bsum[(size_t)b * G1 + g] : 0u;
+      }
+      uint32_t acc = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t inc = wave_incl_scan(sb[u]);
+        pfx[u * 64 + lane] = acc + inc;
+        acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      }
+      for (uint32_t b0 = 256; b0 < nbd; b0 += 64) {  // more than 256 blocks of rows
+        const uint32_t b = b0 + lane;
+        acc += wave_sum(b < nbd ? bsum[(size_t)b * G1 + g] : 0u);
+      }
+      if (lane == 0) sT = acc;
+    }
+    for (int p = 0; p < nv; ++p)
+      for (int c = tid; c < tw; c += MUL_T) tile[p * a.TW + c] = 0;
+    __syncthreads();
+    T = sT;
   }
-  for (int p = 0; p < nv; ++p)
-    for (int c = tid; c < tw; c += MUL_T) tile[p * a.TW + c] = 0;
-  __syncthreads();
-  const uint32_t T = sT;
 
   // this wave's share [start, end) of the group's entries, concatenated over rows
-  const uint64_t nslots = (uint64_t)bpg * MUL_W;
-  const uint64_t slot = (uint64_t)bslot * MUL_W + wid;
-  const uint32_t start = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T * slot / nslots));
-  const uint32_t end = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)T * (slot + 1) / nslots));
+  constexpr int NCW = BP == 1 ? 1 : 0;  // waves without a share
+  constexpr int SW = MUL_W - NCW;
+  const uint64_t nslots = (uint64_t)bpg * SW;
+  const uint64_t slot = (uint64_t)bslot * SW + (uint64_t)(wid - NCW);
+  // floor(T * slot / nslots) in double: the product (< 2^53) is exact and the
+  // quotient correctly rounded, so the boundaries are non-decreasing in the
+  // slot, the last one is T, and every wave of every block computes the same
+  // values (no 64-bit integer division)
+  uint32_t start = 0u, end = 0u;
+  if (wid >= NCW) {
+    const double Td = (double)T, ns = (double)nslots;
+    start = __builtin_amdgcn_readfirstlane((uint32_t)(Td * (double)slot / ns));
+    end = __builtin_amdgcn_readfirstlane((uint32_t)(Td * (double)(slot + 1) / ns));
+  }
   const bool active = start < end;
 
   // the 256-row block where the share starts: first prefix above start
   uint32_t bstar = nbd, before_b = 0;
   if (active) {
     if (nbd <= 256u) {
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
-        const unsigned long long hit = __ballot(b < nbd && pfx[b] > start);
-        if (hit) {
-          bstar = (uint32_t)u * 64u + (uint32_t)(__ffsll((long long)hit) - 1);
-          before_b = bstar > 0u ? pfx[bstar - 1u] : 0u;
-          break;
+      if constexpr (BP == 1) {
+        wave_locate_regs(sb, nbd, start, &bstar, &before_b);
+      } else {
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
+          const unsigned long long hit = __ballot(b < nbd && pfx[b] > start);
+          if (hit) {
+            bstar = (uint32_t)u * 64u + (uint32_t)(__ffsll((long long)hit) - 1);
+            before_b = bstar > 0u ? pfx[bstar - 1u] : 0u;
+            break;
+          }
         }
       }
     } else {
@@ -834,9 +887,12 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   // range is checked per 4-byte word), so every lane issues the load and the
   // wait counters stay exact.  An empty chunk (s1 = 0) accesses no memory.
   auto issue = [&](const Chunk& c, uint4& buf) {
-    const uint32_t* base = entries + (size_t)(rowb + c.j) * (size_t)a.row_stride + col0;
+    // row and range are wave-uniform; readfirstlane keeps the descriptor scalar
+    const uint32_t row = __builtin_amdgcn_readfirstlane(rowb + c.j);
+    const uint32_t s1 = __builtin_amdgcn_readfirstlane(c.s1);
+    const uint32_t* base = entries + (size_t)row * (size_t)a.row_stride + col0;
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(c.s1 * 4u), kBufferDword3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(s1 * 4u), kBufferDword3);
     const auto q = __builtin_amdgcn_raw_buffer_load_b128(
         rs, (int)(((c.s0 & ~3u) + (uint32_t)lane * 4u) * 4u), 0, 0);
     buf = make_uint4(q[0], q[1], q[2], q[3]);
@@ -911,7 +967,7 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
       tj[p] = p < nv && Lj ? key_threshold_fast(fabsf(vj[p]), __uint_as_float(sCut[p])) : 0x7C00u;
       // clamped: only a row whose weights are all zero can exceed it, and its
       // products stay 0
-      vfj[p] = p < nv ? fminf(fmaxf(ldexpf(vj[p], sS[p]), -0x1p100f), 0x1p100f) : 0.0f;
+      vfj[p] = p < nv ? fminf(fmaxf(ldexpf(vj[p], BP == 1 ? S1 : sS[p]), -0x1p100f), 0x1p100f) : 0.0f;
     }
   };
   // A ring of 4 chunks in flight: a slot is processed, then refilled with the
@@ -929,6 +985,7 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   // share (rowb = m, remaining = 0) gets empty chunks that access no memory
   batch_meta();
   fill();
+  if (BP == 1) __syncthreads();  // the cutoff published, every tile word cleared
   thresholds();
 
   // ---- stream

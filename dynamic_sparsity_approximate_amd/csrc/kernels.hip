@@ -236,7 +236,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   }
   __shared__ uint32_t tmp[DSP_T / 64 + 1];
   __shared__ uint32_t sres[2];
-  __shared__ uint32_t red[16 * (DSP_T / 64)];
+  __shared__ uint32_t red[4 * (DSP_T / 64)];
   __shared__ float redf[DSP_T / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -309,36 +309,39 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
       }
     }
   }
+  // The chart values in bin b1, for the exact cutoff: their slots are
+  // reserved here, so that the reservation's round trip overlaps the work on
+  // the read lengths; the values are stored at the end.
+  uint32_t cnt = 0u, cpos = 0u, cret = 0u;
+  if (a.P <= PMAXR) {
+    cnt = (uint32_t)__popc(hits);
+    const uint32_t incl = wave_incl_scan(cnt);
+    cpos = incl - cnt;
+    if (lane == 63 && incl) cret = atomicAdd(&a.result[RES_NCAND], incl);
+  }
   const int32_t qc = q < a.P ? q : a.P - 1;
   const uint32_t* cr = a.counts + ((size_t)(valid ? i : 0) * a.P + qc) * a.G4;
-  constexpr int GCH = 16;  // groups per pass: their counts are loaded before any store
   constexpr int NW = DSP_T / 64;
   // bound on |any sum of products| of the row
   const float bs = wave_sum_f(valid ? av * h2f(rmax) : 0.0f);
   if (lane == 0) redf[wid] = bs;
-  for (int g0 = 0; g0 < a.G; g0 += GCH) {
-    uint32_t L[GCH];
+  for (int g0 = 0; g0 < a.G; g0 += 4) {  // 4 groups (one 16-byte slice) a pass
+    uint4 c4 = make_uint4(0u, 0u, 0u, 0u);
+    if (!none) c4 = *reinterpret_cast<const uint4*>(cr + g0);
+    const uint32_t L[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-    for (int u4 = 0; u4 < GCH / 4; ++u4) {
-      uint4 c4 = make_uint4(0u, 0u, 0u, 0u);
-      if (!none && g0 + u4 * 4 < a.G) c4 = *reinterpret_cast<const uint4*>(cr + g0 + u4 * 4);
-      L[u4 * 4 + 0] = c4.x;
-      L[u4 * 4 + 1] = c4.y;
-      L[u4 * 4 + 2] = c4.z;
-      L[u4 * 4 + 3] = c4.w;
-    }
-#pragma unroll
-    for (int u = 0; u < GCH; ++u) {
-      if (g0 + u >= a.G) L[u] = 0u;
-      const uint32_t s = wave_sum(L[u]);
-      if (lane == 0) red[u * NW + wid] = s;
+    for (int u = 0; u < 4; ++u) {
+      if (g0 + u < a.G) {
+        const uint32_t s = wave_sum(L[u]);
+        if (lane == 0) red[u * NW + wid] = s;
+      }
     }
     __syncthreads();
     if (valid)
 #pragma unroll
-      for (int u = 0; u < GCH; ++u)
+      for (int u = 0; u < 4; ++u)
         if (g0 + u < a.G) a.runlen[(size_t)(g0 + u) * a.m + i] = L[u];
-    if (tid < GCH && g0 + tid < a.G) {
+    if (tid < 4 && g0 + tid < a.G) {
       uint32_t t = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) t += red[tid * NW + w];
@@ -350,19 +353,14 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
       for (int w = 0; w < NW; ++w) t += redf[w];
       a.bsum[(size_t)blockIdx.x * G1 + a.G] = __float_as_uint(t);
     }
-    if (g0 + GCH < a.G) __syncthreads();  // red[] is reused (more than GCH groups)
+    if (g0 + 4 < a.G) __syncthreads();  // red[] is reused (more than 4 groups)
   }
   if (blockIdx.x == 0 && tid == 0) {
     a.result[RES_BIN] = b1;
     a.result[RES_ABOVE] = above1;
   }
-  // the chart values in bin b1, for the exact cutoff
   if (a.P <= PMAXR) {
-    const uint32_t c = (uint32_t)__popc(hits);
-    const uint32_t incl = wave_incl_scan(c);
-    uint32_t base = 0u;
-    if (lane == 63 && incl) base = atomicAdd(&a.result[RES_NCAND], incl);
-    base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63) + incl - c;
+    uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cret, 63) + cpos;
 #pragma unroll
     for (int k = 0; k < PMAXR; ++k)
       if ((hits >> k) & 1u) a.cand[base++] = __float_as_uint(__fmul_rn(av, h2f(pk[k])));

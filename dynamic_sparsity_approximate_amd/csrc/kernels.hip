@@ -603,6 +603,23 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
   return (pre << 9) | b3;
 }
 
+// Where share wave j's part of a block's entries starts, in 128ths of them.
+// One vector: 8 share waves, waves 1..9 of the block; a workgroup's waves are
+// spread over the CU's 4 SIMDs in turn, so share waves 0..3 are the first
+// share wave on their SIMD and 4..7 the second, which the SIMD's oldest-first
+// issue serves later: the first get 16 + kOlderExtra 128ths and the second
+// 16 - kOlderExtra (measured).  A batched pass: 16 equal shares.
+constexpr uint32_t kOlderExtra = 1;
+template <int BP>
+__device__ __forceinline__ uint32_t share_cum(int j) {
+  if constexpr (BP == 1) {
+    return j <= 4 ? (uint32_t)j * (16u + kOlderExtra)
+                  : 4u * (16u + kOlderExtra) + (uint32_t)(j - 4) * (16u - kOlderExtra);
+  } else {
+    return (uint32_t)j * 8u;
+  }
+}
+
 // Block (g, s) of the grid: group g's LDS tile, share s of its entries.
 //
 // Prologue, three dependent rounds of global loads:
@@ -634,6 +651,7 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   constexpr int MUL_T = mul_threads<BP>();
   constexpr int MUL_W = MUL_T / 64;
   static_assert(BP == 1 || MUL_W > BP, "a wave for each cutoff and one for the partition");
+  static_assert(BP == 1 ? MUL_W == 9 : MUL_W == 16, "share_cum splits a block over 8 or 16 share waves");
   constexpr int PW = BP == 1 ? 1 : BP;  // the wave that scans the partition sums
   // tiles: one vector's in a static array, several vectors' in dynamic LDS
   // (vector p's at p * TW)
@@ -764,18 +782,19 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
 
   // this wave's share [start, end) of the group's entries, concatenated over rows
   constexpr int NCW = BP == 1 ? 1 : 0;  // waves without a share
-  constexpr int SW = MUL_W - NCW;
-  const uint64_t nslots = (uint64_t)bpg * SW;
-  const uint64_t slot = (uint64_t)bslot * SW + (uint64_t)(wid - NCW);
-  // floor(T * slot / nslots) in double: the product (< 2^53) is exact and the
-  // quotient correctly rounded, so the boundaries are non-decreasing in the
-  // slot, the last one is T, and every wave of every block computes the same
-  // values (no 64-bit integer division)
+  // Block boundaries floor(T * b / bpg) in double: the product (< 2^53) is
+  // exact and the quotient correctly rounded, so they are non-decreasing, the
+  // last one is T and every block computes the same values (no 64-bit integer
+  // division).  Within the block, share wave j gets the fraction
+  // (share_cum(j + 1) - share_cum(j)) / 128 of the block's entries.
   uint32_t start = 0u, end = 0u;
   if (wid >= NCW) {
-    const double Td = (double)T, ns = (double)nslots;
-    start = __builtin_amdgcn_readfirstlane((uint32_t)(Td * (double)slot / ns));
-    end = __builtin_amdgcn_readfirstlane((uint32_t)(Td * (double)(slot + 1) / ns));
+    const double Td = (double)T, nb = (double)bpg;
+    const uint32_t bs = (uint32_t)(Td * (double)bslot / nb);
+    const uint32_t be = (uint32_t)(Td * (double)(bslot + 1u) / nb);
+    const int j = wid - NCW;
+    start = __builtin_amdgcn_readfirstlane(bs + (uint32_t)(((uint64_t)(be - bs) * share_cum<BP>(j)) >> 7));
+    end = __builtin_amdgcn_readfirstlane(bs + (uint32_t)(((uint64_t)(be - bs) * share_cum<BP>(j + 1)) >> 7));
   }
   const bool active = start < end;
 

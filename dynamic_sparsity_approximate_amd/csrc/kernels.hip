@@ -604,21 +604,27 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
 }
 
 // Where share wave j's part of a block's entries starts, in 128ths of them.
-// One vector: 8 share waves, waves 1..9 of the block; a workgroup's waves are
-// spread over the CU's 4 SIMDs in turn, so share waves 0..3 are the first
-// share wave on their SIMD and 4..7 the second, which the SIMD's oldest-first
-// issue serves later: the first get 16 + kOlderExtra 128ths and the second
-// 16 - kOlderExtra (measured).  A batched pass: 16 equal shares.
-constexpr uint32_t kOlderExtra = 1;
+// One vector: 8 share waves, waves 1..9 of the block.  A workgroup's waves are
+// spread over the CU's 4 SIMDs in turn and a SIMD issues its older wave first,
+// so share waves 0..3 (the first share wave on their SIMD) stream faster than
+// 4..7; share waves 3 and 7 also share their SIMD with the cutoff wave and
+// start streaming last.  The weights make the waves finish together (fitted to
+// per-wave timestamps, then measured).  A batched pass: 16 equal shares.
+__constant__ constexpr uint32_t kShareW1[8] = {18, 18, 17, 17, 15, 15, 15, 13};
 template <int BP>
 __device__ __forceinline__ uint32_t share_cum(int j) {
   if constexpr (BP == 1) {
-    return j <= 4 ? (uint32_t)j * (16u + kOlderExtra)
-                  : 4u * (16u + kOlderExtra) + (uint32_t)(j - 4) * (16u - kOlderExtra);
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c += k < j ? kShareW1[k] : 0u;
+    return c;
   } else {
     return (uint32_t)j * 8u;
   }
 }
+static_assert(kShareW1[0] + kShareW1[1] + kShareW1[2] + kShareW1[3] + kShareW1[4] + kShareW1[5] +
+                  kShareW1[6] + kShareW1[7] == 128,
+              "one vector's share weights cover the block");
 
 // Block (g, s) of the grid: group g's LDS tile, share s of its entries.
 //
@@ -632,7 +638,7 @@ __device__ __forceinline__ uint32_t share_cum(int j) {
 //   (3) the share's first chunks of entries, in flight while each row's fp16
 //       key threshold is derived from the cutoff.
 // One vector: wave 0 only computes the cutoff, while the other waves run the
-// three rounds; the barrier after round 3 publishes the cutoff.  Batched:
+// three rounds; each waits for the cutoff (an LDS flag) only after round 3.  Batched:
 // waves 0..nv-1 compute the cutoffs and wave PW the partition sums before a
 // barrier, then every wave runs rounds 2 and 3.
 //
@@ -661,6 +667,7 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   __shared__ uint32_t h3w[BP][512];  // wave p: histogram of vector p's last cutoff digit
   __shared__ uint32_t pfx[256];      // inclusive prefix sums of the group's per-256-row sums
   __shared__ uint32_t sT;
+  __shared__ uint32_t sReady;  // one vector: set once the cutoff is in sCut[0]
   __shared__ uint32_t sCut[BP];
   __shared__ int32_t sS[BP];
   __shared__ uint32_t mrl[MUL_W][DSP_ROWS];           // per wave: run lengths of its first 256 rows
@@ -718,14 +725,18 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   uint32_t T = 0u;  // the group's entry count
   int S1 = 0;       // one vector: the fixed-point scale, computed by every share wave
   if constexpr (BP == 1) {
-    // Wave 0 only computes the cutoff.  Every other wave sums the group's
-    // per-256-row sums itself (the same loads and the same order of addition
-    // in every wave, so the same T and scale) and goes on to stage its rows and
-    // issue its first chunks while the cutoff is being computed; the barrier
-    // before the stream publishes the cutoff.
+    // Wave 0 only computes the cutoff and then publishes it through sReady.
+    // Every other wave sums the group's per-256-row sums itself (the same
+    // loads and the same order of addition in every wave, so the same T and
+    // scale), stages its rows, issues its first chunks and waits for the
+    // cutoff only then, each at its own pace.  The one barrier here clears the
+    // tile and the flag before anyone uses them.
     for (int c = tid; c < tw; c += MUL_T) tile[c] = 0;
+    if (tid == 0) sReady = 0u;
+    __syncthreads();
     if (wid == 0) {
       cutoff_wave();
+      if (lane == 0) __hip_atomic_store(&sReady, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else {
       float sf[4];
 #pragma unroll
@@ -1002,7 +1013,12 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   // share (rowb = m, remaining = 0) gets empty chunks that access no memory
   batch_meta();
   fill();
-  if (BP == 1) __syncthreads();  // the cutoff published, every tile word cleared
+  if (BP == 1) {
+    // the cutoff: wave 0 sets the flag unconditionally once sCut[0] is
+    // written, so this wait ends
+    while (__hip_atomic_load(&sReady, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+      __builtin_amdgcn_s_sleep(1);
+  }
   thresholds();
 
   // ---- stream

@@ -103,28 +103,36 @@ __device__ uint32_t block_excl_scan(uint32_t x, uint32_t* tmp, uint32_t* total) 
 // ---------------------------------------------------------------- cutoff
 
 constexpr int SEL_T = 1024;
-// The P <= PM probe keys of row i in registers (16-byte loads when P % 8 == 0).
+// The P <= PM probe keys of row i in registers, two per word: key 2t in the
+// low half of kw[t] (16-byte loads when P % 8 == 0).  Callers unpack a key
+// where they use it (key_at), so every load of the row is in flight before
+// the first wait; unpacking right after each load had serialized them.
 constexpr int PMAXR = 32;
 template <int PM>
 __device__ __forceinline__ void load_row_keys(const uint16_t* probes, int32_t P, int64_t i,
-                                              uint32_t* key) {
+                                              uint32_t* kw) {
   const uint16_t* pr = probes + i * P;
   if ((P & 7) == 0) {
 #pragma unroll
     for (int c = 0; c < PM / 8; ++c) {
       uint4 q = make_uint4(0u, 0u, 0u, 0u);
       if (c * 8 < P) q = *reinterpret_cast<const uint4*>(pr + c * 8);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        key[c * 8 + 2 * j] = w[j] & 0xFFFFu;
-        key[c * 8 + 2 * j + 1] = w[j] >> 16;
-      }
+      kw[4 * c] = q.x;
+      kw[4 * c + 1] = q.y;
+      kw[4 * c + 2] = q.z;
+      kw[4 * c + 3] = q.w;
     }
   } else {
+    uint32_t h[PM];
 #pragma unroll
-    for (int k = 0; k < PM; ++k) key[k] = k < P ? (uint32_t)pr[k] : 0u;
+    for (int k = 0; k < PM; ++k) h[k] = k < P ? (uint32_t)pr[k] : 0u;
+#pragma unroll
+    for (int t = 0; t < PM / 2; ++t) kw[t] = h[2 * t] | (h[2 * t + 1] << 16);
   }
+}
+
+__device__ __forceinline__ uint32_t key_at(const uint32_t* kw, int k) {
+  return (kw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
 }
 
 constexpr int CH_T = 256;  // rows per block of the histogram kernel
@@ -146,11 +154,11 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
   if (i < a.m) {
     const float av = fabsf(a.v[i]);
     if (a.P <= PMAXR) {
-      uint32_t key[PMAXR];
-      load_row_keys<PMAXR>(a.probes, a.P, i, key);
+      uint32_t kw[PMAXR / 2];
+      load_row_keys<PMAXR>(a.probes, a.P, i, kw);
 #pragma unroll
       for (int k = 0; k < PMAXR; ++k)
-        if (k < a.P) atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(key[k]))) >> HIST_SHIFT], 1u);
+        if (k < a.P) atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(key_at(kw, k)))) >> HIST_SHIFT], 1u);
     } else {
       const uint16_t* pr = a.probes + i * a.P;
       for (int k = 0; k < a.P; ++k)
@@ -243,15 +251,9 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   const int64_t i = (int64_t)blockIdx.x * DSP_T + tid;
   const bool valid = i < a.m;
   const int G1 = a.G + 1;
-  // row data and this thread's 16 histogram bins, all loads issued together
-  float av = 0.0f;
-  uint32_t rmax = 0u;
-  uint32_t pk[PMAXR];
-  if (valid) {
-    av = fabsf(a.v[i]);
-    rmax = a.rowmax[i];
-    if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, pk);
-  }
+  // this thread's 16 histogram bins and the row's data, all loads issued
+  // together (|v| is taken after the histogram loads are issued, so that its
+  // wait does not hold them back)
   const int hb = HIST_BINS - 16 * (tid + 1);  // bins hb .. hb + 15, thread 0 holds the top
   uint32_t h[16];
 #pragma unroll
@@ -261,6 +263,14 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
     h[4 * c + 1] = q4.y;
     h[4 * c + 2] = q4.z;
     h[4 * c + 3] = q4.w;
+  }
+  float vi = 0.0f;
+  uint32_t rmax = 0u;
+  uint32_t pk[PMAXR / 2];  // the row's probe keys, two per word
+  if (valid) {
+    vi = a.v[i];
+    rmax = a.rowmax[i];
+    if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, pk);
   }
   uint32_t hs = 0;
 #pragma unroll
@@ -278,6 +288,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
     }
   }
   __syncthreads();
+  const float av = fabsf(vi);
   const uint32_t b1 = sres[0] & (HIST_BINS - 1);
   const uint32_t above1 = sres[1];
   const uint32_t lo_bits = b1 << HIST_SHIFT;
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
 #pragma unroll
       for (int k = 0; k < PMAXR; ++k) {
         if (k < a.P) {
-          const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pk[k])));
+          const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key_at(pk, k))));
           q += bits >= lo_bits ? 1 : 0;
           if ((bits >> HIST_SHIFT) == b1) {
             hits |= 1u << k;
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
     uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cret, 63) + cpos;
 #pragma unroll
     for (int k = 0; k < PMAXR; ++k)
-      if ((hits >> k) & 1u) a.cand[base++] = __float_as_uint(__fmul_rn(av, h2f(pk[k])));
+      if ((hits >> k) & 1u) a.cand[base++] = __float_as_uint(__fmul_rn(av, h2f(key_at(pk, k))));
   }
 }
 
@@ -748,8 +759,10 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
       float B = 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        T += wave_sum(sb[u]);
-        B += wave_sum_f(sf[u]);
+        if ((uint32_t)u * 64u < nbd) {  // rounds past the last block hold zeros
+          T += wave_sum(sb[u]);
+          B += wave_sum_f(sf[u]);
+        }
       }
       for (uint32_t b0 = 256; b0 < nbd; b0 += 64) {  // more than 256 blocks of rows
         const uint32_t b = b0 + lane;

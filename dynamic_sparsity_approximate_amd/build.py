@@ -24,8 +24,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # float atomics compile to hardware ds_add_f32 / global_atomic_add_f32;
 # packed fp32 instructions disabled.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC, "-ffp-contract=off"]
-# The atomic optimizer is off so that a wave's returning atomic (the next-row
-# ticket of the multiply) is waited for where its value is used, not at once.
+# The atomic optimizer is off so that a returning atomic is waited for where
+# its value is used, not at once: the optimizer makes it one atomic per wave
+# followed at once by per-lane offsets, and the dispatch issues its
+# candidate-slot reservation early precisely to use the result last.
 DEVICE = ["--offload-arch=" + ARCH, "-munsafe-fp-atomics", "-fno-gpu-flush-denormals-to-zero",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]

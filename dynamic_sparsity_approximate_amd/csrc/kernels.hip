@@ -102,7 +102,6 @@ __device__ uint32_t block_excl_scan(uint32_t x, uint32_t* tmp, uint32_t* total) 
 
 // ---------------------------------------------------------------- cutoff
 
-constexpr int SEL_T = 1024;
 // The P <= PM probe keys of row i in registers, two per word: key 2t in the
 // low half of kw[t] (16-byte loads when P % 8 == 0).  Callers unpack a key
 // where they use it (key_at), so every load of the row is in flight before
@@ -470,18 +469,6 @@ __device__ __forceinline__ void wave_locate(uint32_t count, uint32_t target, X x
   }
   *idx = count;
   *before = acc;
-}
-
-// Fixed-point accumulation: with B >= |any sum of kept products| and B < 2^eB,
-// scale S = 50 - eB puts every scaled sum below 2^50 in magnitude.  A product
-// w * v * 2^S is exact in double (11 + 24 significant bits); adding 1.5 * 2^52
-// rounds it to an integer held in the low mantissa bits, which are then read
-// as an int64.
-constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
-
-__device__ __forceinline__ int64_t fixed_product(uint32_t w, double vs) {
-  const double d = __builtin_fma((double)h2f(w), vs, kMagic);
-  return (int64_t)(__double_as_longlong(d) - __double_as_longlong(kMagic));
 }
 
 // wave_locate over 256 values already in registers: x[u] holds index u * 64 + lane

@@ -147,14 +147,20 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
     a.hist2 += k * a.vec_ws;
     a.result += k * a.vec_ws;
   }
+  // the row's loads are issued before the histogram is cleared
+  const int64_t i = (int64_t)blockIdx.x * CH_T + tid;
+  const bool valid = i < a.m;
+  float vi = 0.0f;
+  uint32_t kw[PMAXR / 2];
+  if (valid) {
+    vi = a.v[i];
+    if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, kw);
+  }
   for (int b = tid; b < HIST_BINS; b += CH_T) hist[b] = 0u;
   __syncthreads();
-  const int64_t i = (int64_t)blockIdx.x * CH_T + tid;
-  if (i < a.m) {
-    const float av = fabsf(a.v[i]);
+  if (valid) {
+    const float av = fabsf(vi);
     if (a.P <= PMAXR) {
-      uint32_t kw[PMAXR / 2];
-      load_row_keys<PMAXR>(a.probes, a.P, i, kw);
 #pragma unroll
       for (int k = 0; k < PMAXR; ++k)
         if (k < a.P) atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(key_at(kw, k)))) >> HIST_SHIFT], 1u);
@@ -165,8 +171,15 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
     }
   }
   __syncthreads();
-  for (int b = tid; b < HIST_BINS; b += CH_T)
-    if (hist[b]) atomicAdd(&a.hist[b], hist[b]);
+  // merge into the global histogram: every bin read first (one LDS wait, not
+  // one per bin), then one atomic per non-empty bin
+  constexpr int BPT = HIST_BINS / CH_T;
+  uint32_t hv[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) hv[j] = hist[tid + j * CH_T];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j)
+    if (hv[j]) atomicAdd(&a.hist[tid + j * CH_T], hv[j]);
   // y is accumulated by the multiply; global stores come last (no barrier waits on them)
   for (int64_t j = (int64_t)blockIdx.x * CH_T + tid; j < a.n; j += (int64_t)gridDim.x * CH_T)
     a.y[j] = 0.0f;
@@ -250,6 +263,9 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   const int64_t i = (int64_t)blockIdx.x * DSP_T + tid;
   const bool valid = i < a.m;
   const int G1 = a.G + 1;
+  // capacity of the candidate list: the count cannot exceed it when the select
+  // kernel has reset it, and stores beyond it are dropped if it has not
+  const uint64_t capc = (uint64_t)a.m * (uint64_t)a.P;
   // this thread's 16 histogram bins and the row's data, all loads issued
   // together (|v| is taken after the histogram loads are issued, so that its
   // wait does not hold them back)
@@ -311,7 +327,8 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
         q += bits >= lo_bits ? 1 : 0;
         if ((bits >> HIST_SHIFT) == b1) {
           atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
-          a.cand[atomicAdd(&a.result[RES_NCAND], 1u)] = bits;
+          const uint32_t slot = atomicAdd(&a.result[RES_NCAND], 1u);
+          if ((uint64_t)slot < capc) a.cand[slot] = bits;
         }
       }
     }
@@ -375,7 +392,8 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
     for (int k = 0; k < PMAXR; ++k) {
       if ((hits >> k) & 1u) {
         const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key_at(pk, k))));
-        a.cand[base++] = bits;
+        if ((uint64_t)base < capc) a.cand[base] = bits;
+        ++base;
         atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
       }
     }
@@ -696,8 +714,10 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   auto cutoff_wave = [&]() {
     const uint64_t vo = (uint64_t)wid * a.vec_ws;
     const uint32_t* res = result + vo;
-    const uint32_t b1 = res[RES_BIN], above1 = res[RES_ABOVE], nc = res[RES_NCAND];
+    const uint32_t b1 = res[RES_BIN], above1 = res[RES_ABOVE];
     const uint64_t cap = (uint64_t)a.m * (uint64_t)a.P;
+    // the count never exceeds the list's capacity; clamped so that no read can
+    const uint32_t nc = (uint32_t)min((uint64_t)res[RES_NCAND], cap);
     const uint32_t ncap = (uint32_t)(cap < 1024u ? cap : 1024u);
     uint32_t kp;
     const uint32_t cut =

@@ -285,6 +285,16 @@ def test_timed_entry_matches_and_stamps_kernels():
             E.effort_event_destroy(e)
 
 
+@pytest.mark.parametrize("m,n", [(20000, 300), (70000, 64)])
+def test_many_rows_few_columns(m, n):
+    """Tall matrices with a narrow output (one column group): 79 and 274 blocks
+    of 256 rows; above 256 the multiply sums the per-block read lengths in more
+    than one round and locates a share's first block in global memory."""
+    W, v = case(m, n, seed=22, tag="tall")
+    say("tall m=%d n=%d" % (m, n))
+    run_pair(W, v, 16, 0.25, with_mask=False, where="tall")
+
+
 @pytest.mark.parametrize("m,n,G,b,P", [(4096, 14336, 0, 2, 16), (4096, 14336, 0, 9, 16),
                                        (4096, 14336, 0, 16, 16), (513, 2049, 3, 3, 16),
                                        (300, 1000, 0, 16, 5), (64, 8192, 1, 4, 8)])

@@ -79,7 +79,7 @@ _PROTOS = {
     "effort_layout_check": ([_D, _p], ctypes.c_int),
     "effort_matvec": ([_D, _p, _p, _f32, _p, _p, _u64, _p], ctypes.c_int),
     "effort_matvec_batched": ([_D, _p, _p, _i32, _f32, _p, _p, _u64, _p], ctypes.c_int),
-    "effort_matvec_debug": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p, _p, _p, _p, _p], ctypes.c_int),
+    "effort_matvec_debug": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "effort_matvec_timed": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p], ctypes.c_int),
     "dense_gemv": ([_p, _p, _i64, _i64, _p, _p], ctypes.c_int),
     "dense_gemm_small": ([_p, _p, _i32, _i64, _i64, _p, _p], ctypes.c_int),
@@ -217,10 +217,11 @@ def effort_matvec_batched(desc, layout, v, batch: int, effort: float, y, ws, ws_
 
 
 def effort_matvec_debug(desc, layout, v, effort: float, y, ws, ws_bytes: int, cutoff=None, K=None,
-                        row_kept=None, fingerprint=None, kept_mask=None, stream=None):
+                        row_kept=None, fingerprint=None, kept_mask=None, status=None, stream=None):
     _check(_lib.effort_matvec_debug(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
                                     _ptr(ws), ws_bytes, _ptr(cutoff), _ptr(K), _ptr(row_kept),
-                                    _ptr(fingerprint), _ptr(kept_mask), _stream(stream)),
+                                    _ptr(fingerprint), _ptr(kept_mask), _ptr(status),
+                                    _stream(stream)),
            "effort_matvec_debug")
 
 

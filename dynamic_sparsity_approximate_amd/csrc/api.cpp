@@ -73,6 +73,7 @@ struct DebugOut {
   int32_t* row_kept;
   uint64_t* fingerprint;
   uint8_t* mask;
+  uint32_t* status;
 };
 
 // One vector: select, dispatch, bucketMul on `s`.
@@ -99,6 +100,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
     if (dbg->fingerprint && hip_failed(e = launch_zero_bytes(dbg->fingerprint, 8, s)))
       return EFFORT_EHIP;
     if (dbg->mask && hip_failed(e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)))
+      return EFFORT_EHIP;
+    if (dbg->status && (hip_failed(e = launch_zero_bytes(dbg->status, 4, s)) ||
+                        hip_failed(e = launch_check_finite(v, g.m, dbg->status, s))))
       return EFFORT_EHIP;
   }
 
@@ -284,6 +288,7 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
     if (dbg->fingerprint && !aligned(dbg->fingerprint, 8)) return EFFORT_EINVAL;
     if (dbg->row_kept && !aligned(dbg->row_kept, 4)) return EFFORT_EINVAL;
     if (dbg->cutoff && !aligned(dbg->cutoff, 4)) return EFFORT_EINVAL;
+    if (dbg->status && !aligned(dbg->status, 4)) return EFFORT_EINVAL;
   }
   EventPair ev[3];
   if (events) {
@@ -412,8 +417,9 @@ int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const
 int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                         float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
                         float* cutoff_dev, int64_t* K_dev, int32_t* row_kept_dev,
-                        uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, void* stream) {
-  DebugOut d{cutoff_dev, K_dev, row_kept_dev, fingerprint_dev, kept_mask_dev};
+                        uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, uint32_t* status_dev,
+                        void* stream) {
+  DebugOut d{cutoff_dev, K_dev, row_kept_dev, fingerprint_dev, kept_mask_dev, status_dev};
   return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws_dev, ws_bytes, stream, &d,
                        nullptr);
 }

@@ -1295,6 +1295,18 @@ __global__ void k_debug_result(const uint32_t* result, float* cutoff, int64_t* K
   }
 }
 
+__global__ void k_check_finite(const float* __restrict__ v, int64_t m, uint32_t* status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool bad = i < m && (__float_as_uint(v[i]) & 0x7F800000u) == 0x7F800000u;
+  if (__ballot(bad) && (threadIdx.x & 63) == 0) atomicOr(status, 1u);
+}
+
+hipError_t launch_check_finite(const float* v, int64_t m, uint32_t* status, hipStream_t s) {
+  const int64_t blocks = (m + 255) / 256;
+  hipLaunchKernelGGL(k_check_finite, dim3((unsigned)blocks), dim3(256), 0, s, v, m, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_debug_result(const uint32_t* result, float* cutoff, int64_t* K, hipStream_t s) {
   hipLaunchKernelGGL(k_debug_result, dim3(1), dim3(64), 0, s, result, cutoff, K);
   return hipGetLastError();

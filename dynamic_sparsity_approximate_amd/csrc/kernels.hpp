@@ -125,5 +125,7 @@ hipError_t launch_axpby(const float* a, float ga, const float* b, float gb, int6
                         hipStream_t s);
 hipError_t launch_zero_bytes(void* p, uint64_t bytes, hipStream_t s);
 hipError_t launch_debug_result(const uint32_t* result, float* cutoff, int64_t* K, hipStream_t s);
+// *status |= 1 when any of v[0..m) is a NaN or an infinity (status cleared by the caller).
+hipError_t launch_check_finite(const float* v, int64_t m, uint32_t* status, hipStream_t s);
 
 }  // namespace effort

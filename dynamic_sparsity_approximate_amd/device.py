@@ -71,8 +71,9 @@ class EffortMatrix:
         fp = torch.empty(1, dtype=torch.int64, device=dev)
         mask = (torch.empty((self.in_dim, self.out_dim), dtype=torch.uint8, device=dev)
                 if with_mask else None)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
         B.effort_matvec_debug(self.desc, self.layout, v, effort, y, self.ws, self.ws_bytes, cutoff, K,
-                              row_kept, fp, mask, stream)
+                              row_kept, fp, mask, status, stream)
         torch.cuda.synchronize(dev)
         out = {
             "y": y.cpu().numpy(),
@@ -82,6 +83,7 @@ class EffortMatrix:
             "row_kept": row_kept.cpu().numpy().astype(np.int64),
             "fingerprint": int(fp.cpu().numpy().view(np.uint64)[0]),
             "mask": mask.cpu().numpy() if mask is not None else None,
+            "v_nonfinite": bool(int(status.item()) & 1),
         }
         out["total_kept"] = int(out["row_kept"].sum())
         return out

@@ -135,7 +135,8 @@ int effort_layout_check(const effort_desc* desc, const void* layout_host);
    layout_dev: device copy of the prepared blob.  v_dev: device fp32.  y_dev:
    device fp32, overwritten (zeroed by the call).  ws_dev: device workspace of
    >= effort_workspace_bytes(desc, 1) bytes.  effort in (0, 1], else EINVAL.
-   v must be finite (precondition, not checked). */
+   v must be finite (precondition, not checked here; effort_matvec_debug
+   reports a violation). */
 int effort_matvec(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                   float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
 
@@ -155,12 +156,15 @@ int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const
    K_dev[2]             K and K' = #{chart >= cutoff};
    row_kept_dev[in_dim] kept products per row;
    fingerprint_dev[1]   sum over kept (i,j) of splitmix64-output(i*out_dim+j), mod 2^64;
-   kept_mask_dev        uint8 [in_dim][out_dim], 1 where kept.
+   kept_mask_dev        uint8 [in_dim][out_dim], 1 where kept;
+   status_dev[1]        bit 0 set when v holds a NaN or an infinity (outside
+                        the contract: the other outputs are then unspecified).
    Same kernels as effort_matvec with the recording switched on; untimed. */
 int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                         float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
                         float* cutoff_dev, int64_t* K_dev, int32_t* row_kept_dev,
-                        uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, void* stream);
+                        uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, uint32_t* status_dev,
+                        void* stream);
 
 /* effort_matvec with kernel timing, for measurement.  events[0..5] are hipEvent_t
    pairs (start, stop) for the cutoff kernel, the dispatch kernel and the

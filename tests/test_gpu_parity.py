@@ -136,6 +136,21 @@ def test_degenerate_inputs():
     del d
 
 
+def test_debug_flags_nonfinite_activations():
+    """A NaN or an infinity in v is outside the contract; the debug entry point
+    reports it (bit 0 of its status word) and reports nothing for finite v."""
+    W, v = case(300, 700, seed=5, tag="finite")
+    M = E.EffortMatrix(W, P=16, device=dev())
+    assert not M.matvec_debug(torch.from_numpy(v).to(dev()), 0.25, with_mask=False)["v_nonfinite"]
+    for bad in (np.float32("nan"), np.float32("inf"), np.float32("-inf")):
+        vb = v.copy()
+        vb[123] = bad
+        got = M.matvec_debug(torch.from_numpy(vb).to(dev()), 0.25, with_mask=False)
+        assert got["v_nonfinite"], bad
+    # the flag does not stick: the next finite call clears it
+    assert not M.matvec_debug(torch.from_numpy(v).to(dev()), 0.25, with_mask=False)["v_nonfinite"]
+
+
 def test_repeat_calls_and_workspace_reuse():
     W, v = case(512, 3000, seed=3, tag="repeat")
     M = E.EffortMatrix(W, P=16, device=dev())

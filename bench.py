@@ -53,12 +53,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["full", "effort", "dense", "copy", "sweep", "batched",
-                                       "decode", "moe"], default="full",
+                                       "decode", "moe", "mallcheck"], default="full",
                     help="effort/dense: time only that path (for profiler runs); copy: plain "
                          "1 GiB device copies for counter calibration; sweep: the four "
                          "Mistral-7B shapes at efforts 1/.5/.25/.125; batched: b = 1..16 "
                          "vectors against the dense small GEMM; decode: a whole Mistral-7B-"
-                         "shaped decode step; moe: a Mixtral-shaped expert block")
+                         "shaped decode step; moe: a Mixtral-shaped expert block; mallcheck: "
+                         "kernel times with layout rotation, after a cache-evicting write, and warm")
     ap.add_argument("--layers", type=int, default=32, help="decode mode: decoder layers")
     ap.add_argument("--streams", type=int, default=6,
                     help="decode/moe modes: side streams for matvecs that do not depend on "
@@ -517,7 +518,55 @@ def run_moe(args, torch, np, E, synth, dev):
                       "%d tokens" % tokens, "dense_us_per_token": round(dus, 1), "points": points}))
 
 
-EXTRA_MODES = {"sweep": run_sweep, "batched": run_batched, "decode": run_decode, "moe": run_moe}
+def run_mallcheck(args, torch, np, E, synth, dev):
+    """Cross-check of the rotation rule against the 256 MB Infinity Cache: the
+    three kernels' own durations (event pairs stamped by each kernel) for calls
+    cycling over R layout copies (the headline's method), for calls on one
+    layout each after a 1 GiB scratch read or write that evicts the cache (outside
+    the timed kernels), and for repeated calls on one layout (warm cache, for
+    contrast)."""
+    m, n, effort = args.m, args.n, args.effort
+    W = synth.matrix("config1", m, n, seed=0)
+    M = E.EffortMatrix(W, P=args.P, device=dev)
+    v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
+    kept = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
+    R = rotation_copies(4.0 * kept, args.rotate_gib)
+    layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    ev = [E.effort_event_create() for _ in range(6)]
+    reps = 60
+
+    def timed(layout, before=None):
+        ks = []
+        for it in range(reps):
+            if before is not None:
+                before(it)
+            E.effort_matvec_timed(M.desc, layout(it), v0, effort, y, M.ws, M.ws_bytes, ev)
+            torch.cuda.synchronize()
+            ks.append([E.effort_event_elapsed_ms(ev[2 * k], ev[2 * k + 1]) * 1e3 for k in range(3)])
+        ks = np.array(ks)[5:]  # the first calls warm up
+        return {"bucketmul_us": round(float(np.median(ks[:, 2])), 2),
+                "kernels_us": round(float(np.median(ks.sum(axis=1))), 2)}
+
+    scratch.fill_(1.0)
+    torch.cuda.synchronize()
+    rows = {
+        "rotation": timed(lambda it: layouts[it % R]),
+        # a 1 GiB read evicts the cache without leaving dirty lines behind
+        "evicted_by_read": timed(lambda it: M.layout, lambda it: scratch.sum()),
+        # a 1 GiB write also leaves 1 GiB to be written back while the call runs
+        "evicted_by_write": timed(lambda it: M.layout, lambda it: scratch.fill_(float(it))),
+        "warm": timed(lambda it: M.layout),
+    }
+    for e in ev:
+        E.effort_event_destroy(e)
+    print(json.dumps({"mode": "mallcheck", "workload": "%dx%d fp16, effort %g" % (m, n, effort),
+                      "rotation": R, "points": rows}))
+
+
+EXTRA_MODES = {"sweep": run_sweep, "batched": run_batched, "decode": run_decode, "moe": run_moe,
+               "mallcheck": run_mallcheck}
 
 
 if __name__ == "__main__":

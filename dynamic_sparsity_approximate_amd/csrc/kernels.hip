@@ -659,9 +659,9 @@ static_assert(kShareW1[0] + kShareW1[1] + kShareW1[2] + kShareW1[3] + kShareW1[4
 //   (3) the share's first chunks of entries, in flight while each row's fp16
 //       key threshold is derived from the cutoff.
 // One vector: wave 0 only computes the cutoff, while the other waves run the
-// three rounds; each waits for the cutoff (an LDS flag) only after round 3.  Batched:
-// waves 0..nv-1 compute the cutoffs and wave PW the partition sums before a
-// barrier, then every wave runs rounds 2 and 3.
+// three rounds; each waits for the cutoff (an LDS flag) only after round 3.
+// Batched: waves 0..nv-1 compute the cutoffs and wave PW the partition sums
+// before a barrier, then every wave runs rounds 2 and 3.
 //
 // Accumulation: with B >= |any sum of kept products| and B * 1.001 < 2^eB,
 // the scale 2^S, S = 30 - eB, keeps every tile sum below 2^30 in magnitude.

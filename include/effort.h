@@ -105,7 +105,7 @@ int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* byt
 /* Zero-fill `ws_bytes` of device memory at ws_dev (stream-ordered). */
 int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream);
 
-/* ---------------------------------------------------------------- offline converter ("precompute" of [HN]) */
+/* -------------------------------------------------- offline converter ("precompute" of [HN]) */
 
 /* Host fp16 bits W[in_dim][out_dim] (y = v . W) -> host layout blob.
    Per row: entries sorted by |w| descending (ties: column ascending), grouped by

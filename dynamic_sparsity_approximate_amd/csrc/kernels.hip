@@ -40,8 +40,9 @@ __device__ __forceinline__ uint64_t pair_hash(uint64_t x) {
   return z ^ (z >> 31);
 }
 
-// Wave-level scans and sums with DPP row shifts (rows of 16 lanes) and
-// readlane for the four row totals; no LDS traffic.
+// Wave-level scans and sums with DPP: row shifts within rows of 16 lanes,
+// then the row broadcasts of lanes 15 and 31 across rows; no LDS traffic and
+// no branches.
 __device__ __forceinline__ uint32_t row_incl_scan(uint32_t x) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
@@ -52,20 +53,16 @@ __device__ __forceinline__ uint32_t row_incl_scan(uint32_t x) {
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   x = row_incl_scan(x);
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
-  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  const uint32_t add = row == 0 ? 0u : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2;
-  return x + add;
+  // rows 1 and 3 add the last lane of rows 0 and 2 (row_bcast:15), then rows
+  // 2 and 3 add lane 31, the total of rows 0 and 1 (row_bcast:31); rows
+  // outside the row mask add the old value 0
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+  return x;
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  x = row_incl_scan(x);
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 15) +
-         (uint32_t)__builtin_amdgcn_readlane((int)x, 31) +
-         (uint32_t)__builtin_amdgcn_readlane((int)x, 47) +
-         (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), 63);
 }
 
 __device__ __forceinline__ float wave_sum_f(float x) {
@@ -631,21 +628,30 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
 // 4..7; share waves 3 and 7 also share their SIMD with the cutoff wave and
 // start streaming last.  The weights make the waves finish together (fitted to
 // per-wave timestamps, then measured).  A batched pass: 16 equal shares.
-__constant__ constexpr uint32_t kShareW1[8] = {18, 18, 17, 17, 15, 15, 15, 13};
-template <int BP>
-__device__ __forceinline__ uint32_t share_cum(int j) {
-  if constexpr (BP == 1) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c += k < j ? kShareW1[k] : 0u;
-    return c;
-  } else {
-    return (uint32_t)j * 8u;
-  }
-}
+constexpr uint32_t kShareW1[8] = {18, 18, 17, 17, 15, 15, 15, 13};
 static_assert(kShareW1[0] + kShareW1[1] + kShareW1[2] + kShareW1[3] + kShareW1[4] + kShareW1[5] +
                   kShareW1[6] + kShareW1[7] == 128,
               "one vector's share weights cover the block");
+// byte j: the sum of the weights before share wave j (j < 8)
+constexpr uint64_t share_cum_bytes() {
+  uint64_t r = 0;
+  uint32_t c = 0;
+  for (int k = 0; k < 8; ++k) {
+    r |= (uint64_t)c << (8 * k);
+    c += kShareW1[k];
+  }
+  return r;
+}
+constexpr uint64_t kShareCum1 = share_cum_bytes();
+// share_cum(j) for j below the number of share waves (8 or 16); a few scalar
+// instructions
+template <int BP>
+__device__ __forceinline__ uint32_t share_cum(uint32_t j) {
+  if constexpr (BP == 1)
+    return (uint32_t)(kShareCum1 >> (8u * j)) & 0xFFu;
+  else
+    return j * 8u;
+}
 
 // Block (g, s) of the grid: group g's LDS tile, share s of its entries.
 //
@@ -818,19 +824,25 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
 
   // this wave's share [start, end) of the group's entries, concatenated over rows
   constexpr int NCW = BP == 1 ? 1 : 0;  // waves without a share
-  // Block boundaries floor(T * b / bpg) in double: the product (< 2^53) is
-  // exact and the quotient correctly rounded, so they are non-decreasing, the
-  // last one is T and every block computes the same values (no 64-bit integer
-  // division).  Within the block, share wave j gets the fraction
-  // (share_cum(j + 1) - share_cum(j)) / 128 of the block's entries.
+  // Block boundaries bound(b) = floor(T * b R / 2^32) with R = floor(2^32 /
+  // bpg) for b < bpg, and bound(bpg) = T: 32 x 32-bit products (the high word
+  // of each), non-decreasing, the same in every block; block sizes differ by
+  // at most 1 + T bpg / 2^32 entries.  Within the block, share wave j gets
+  // the fraction (share_cum(j + 1) - share_cum(j)) / 128 of the block's
+  // entries (share_cum(j) < 128 below the last share, so share_cum(j) << 25
+  // fits 32 bits).
+  constexpr uint32_t NSH = BP == 1 ? 8u : 16u;  // share waves
   uint32_t start = 0u, end = 0u;
   if (wid >= NCW) {
-    const double Td = (double)T, nb = (double)bpg;
-    const uint32_t bs = (uint32_t)(Td * (double)bslot / nb);
-    const uint32_t be = (uint32_t)(Td * (double)(bslot + 1u) / nb);
-    const int j = wid - NCW;
-    start = __builtin_amdgcn_readfirstlane(bs + (uint32_t)(((uint64_t)(be - bs) * share_cum<BP>(j)) >> 7));
-    end = __builtin_amdgcn_readfirstlane(bs + (uint32_t)(((uint64_t)(be - bs) * share_cum<BP>(j + 1)) >> 7));
+    const uint32_t Tu = __builtin_amdgcn_readfirstlane(T);
+    const uint32_t bs = __umulhi(Tu, bslot * a.bpg_recip);
+    const uint32_t be = bslot + 1u >= bpg ? Tu : __umulhi(Tu, (bslot + 1u) * a.bpg_recip);
+    const uint32_t d = be - bs;
+    const uint32_t j = (uint32_t)(wid - NCW);
+    start = j == 0u ? bs : bs + __umulhi(d, share_cum<BP>(j) << 25);
+    end = j + 1u >= NSH ? be : bs + __umulhi(d, share_cum<BP>(j + 1u) << 25);
+    start = __builtin_amdgcn_readfirstlane(start);
+    end = __builtin_amdgcn_readfirstlane(end);
   }
   const bool active = start < end;
 
@@ -1112,9 +1124,12 @@ static hipError_t launch_mul_bp(const MulArgs& a, unsigned grid, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
+hipError_t launch_bucketmul(const MulArgs& args, bool record, int blocks_per_group, hipStream_t s,
                             const EventPair* ev) {
-  const unsigned grid = (unsigned)(a.G * blocks_per_group);
+  if (blocks_per_group < 1) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(args.G * blocks_per_group);
+  MulArgs a = args;
+  a.bpg_recip = blocks_per_group >= 2 ? (uint32_t)((1ull << 32) / (uint64_t)blocks_per_group) : 0u;
   if (a.nv > 1) {
     if (record || a.nv > 8) return hipErrorInvalidValue;
     if (a.nv > 4) return launch_mul_bp<8>(a, grid, s);

@@ -89,6 +89,7 @@ struct MulArgs {
   int32_t G, TW, nbd, P;
   uint32_t K;
   int32_t nv;              // vectors of this pass (1: the single-vector path)
+  uint32_t bpg_recip;       // floor(2^32 / blocks per group), set by launch_bucketmul
   uint64_t vec_ws;
   const uint32_t* vbsum;    // vector 0's own per-256-row sums: column G is its bound
                             // (bsum, the partition's sums, is the union when batched)

@@ -491,28 +491,6 @@ __device__ __forceinline__ void wave_locate(uint32_t count, uint32_t target, X x
   *before = acc;
 }
 
-// wave_locate over 256 values already in registers: x[u] holds index u * 64 + lane
-// (zero at and beyond `count`).
-__device__ __forceinline__ void wave_locate_regs(const uint32_t* x, uint32_t count, uint32_t target,
-                                                 uint32_t* idx, uint32_t* before) {
-  uint32_t acc = 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint32_t inc = wave_incl_scan(x[u]);
-    const uint32_t lo = acc + inc - x[u];
-    const unsigned long long hit = __ballot(x[u] > 0u && lo <= target && target < lo + x[u]);
-    if (hit) {
-      const int l = __ffsll((long long)hit) - 1;
-      *idx = (uint32_t)u * 64u + (uint32_t)l;
-      *before = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
-      return;
-    }
-    acc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-  }
-  *idx = count;
-  *before = acc;
-}
-
 // The exact cutoff, computed by one wave.  The dispatch found the bin b1 of the
 // K-th largest chart value (bits 30..19) and the count above1 of larger
 // values; the refinement histogram hist2 of the bin's values (bits 18..9)
@@ -751,8 +729,16 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   };
   // The group's per-256-row sums: index u * 64 + lane in sb[u] (one vector).
   uint32_t sb[4] = {0u, 0u, 0u, 0u};
+  uint32_t sp[4] = {0u, 0u, 0u, 0u};
   uint32_t T = 0u;  // the group's entry count
   int S1 = 0;       // one vector: the fixed-point scale, computed by every share wave
+  // One vector: round 1 also loads the run lengths and activations of two
+  // 256-row blocks from w0, around the row where the wave's share would start
+  // if the group's entries were spread evenly over its rows; round 2 loads
+  // only when the share starts outside them.
+  uint32_t w0 = nbd;
+  uint32_t slr[8];
+  float slv[8];
   if constexpr (BP == 1) {
     // Wave 0 only computes the cutoff and then publishes it through sReady.
     // Every other wave sums the group's per-256-row sums itself (the same
@@ -774,11 +760,45 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
         sb[u] = b < nbd ? bsum[(size_t)b * G1 + g] : 0u;
         sf[u] = b < nbd ? __uint_as_float(a.vbsum[(size_t)b * G1 + G]) : 0.0f;
       }
+      // 16-byte loads: byte offsets within 32 bits, both arrays 16-byte aligned
+      if (m <= (1u << 28) && ((reinterpret_cast<uintptr_t>(rl) | reinterpret_cast<uintptr_t>(vvec)) & 15u) == 0u) {
+        // the guessed start row: m times the share's start as a fraction of
+        // the group, (bslot + share_cum / 128) / bpg, in 32-bit fixed point;
+        // the window holds its block and the nearer neighbour
+        const uint32_t F = bslot * a.bpg_recip +
+                           __umulhi(a.bpg_recip, share_cum<1>((uint32_t)(wid - 1)) << 25);
+        const uint32_t gr = __umulhi(m, F);
+        const uint32_t bg = gr / DSP_ROWS;
+        uint32_t lo = gr % DSP_ROWS < DSP_ROWS / 2 && bg > 0u ? bg - 1u : bg;
+        if (lo + 2u > nbd) lo = nbd >= 2u ? nbd - 2u : 0u;
+        w0 = __builtin_amdgcn_readfirstlane(lo);
+        // lane l: rows 4l .. 4l + 3 of each block; words past m read as zero
+        const __amdgpu_buffer_rsrc_t rr =
+            __builtin_amdgcn_make_buffer_rsrc((void*)rl, (short)0, (int)(m * 4u), kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)vvec, (short)0, (int)(m * 4u), kBufferDword3);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int off = (int)((w0 * DSP_ROWS + (uint32_t)h * DSP_ROWS + 4u * (uint32_t)lane) * 4u);
+          const auto qr = __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0);
+          const auto qv = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            slr[4 * h + k] = qr[k];
+            slv[4 * h + k] = __uint_as_float(qv[k]);
+          }
+        }
+      }
+      // inclusive prefix sums of the first 256 block sums (sp), kept for the
+      // search of the share's block
       float B = 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        sp[u] = T;
         if ((uint32_t)u * 64u < nbd) {  // rounds past the last block hold zeros
-          T += wave_sum(sb[u]);
+          const uint32_t inc = wave_incl_scan(sb[u]);
+          sp[u] = T + inc;
+          T += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
           B += wave_sum_f(sf[u]);
         }
       }
@@ -851,7 +871,17 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   if (active) {
     if (nbd <= 256u) {
       if constexpr (BP == 1) {
-        wave_locate_regs(sb, nbd, start, &bstar, &before_b);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t lo = sp[u] - sb[u];
+          const unsigned long long hit = __ballot(sb[u] > 0u && lo <= start && start < sp[u]);
+          if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            bstar = (uint32_t)u * 64u + (uint32_t)l;
+            before_b = (uint32_t)__builtin_amdgcn_readlane((int)lo, l);
+            break;
+          }
+        }
       } else {
         for (int u = 0; u < 4; ++u) {
           const uint32_t b = (uint32_t)u * 64u + (uint32_t)lane;
@@ -870,14 +900,26 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   const uint32_t r0 = bstar < nbd ? bstar * DSP_ROWS : m;
   const uint32_t nr = r0 < m ? (m - r0 < (uint32_t)DSP_ROWS ? m - r0 : (uint32_t)DSP_ROWS) : 0u;
 
-  // ---- round 2
+  // ---- round 2 (one vector: unless the window of round 1 holds the block);
+  // lane l holds rows r0 + 4l .. r0 + 4l + 3
   uint32_t lr[4];
   float lv[4];
+  bool spec = false;
+  if constexpr (BP == 1) spec = bstar == w0 || bstar == w0 + 1u;
+  if (spec) {
+    const bool second = bstar != w0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint32_t j = (uint32_t)u * 64u + (uint32_t)lane;
-    lr[u] = j < nr ? rl[r0 + j] : 0u;
-    lv[u] = BP == 1 && j < nr ? vvec[r0 + j] : 0.0f;
+    for (int u = 0; u < 4; ++u) {
+      lr[u] = second ? slr[u + 4] : slr[u];
+      lv[u] = second ? slv[u + 4] : slv[u];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t j = 4u * (uint32_t)lane + (uint32_t)u;
+      lr[u] = j < nr ? rl[r0 + j] : 0u;
+      lv[u] = BP == 1 && j < nr ? vvec[r0 + j] : 0.0f;
+    }
   }
 
   // ---- round 3: the share's first rows, their chunks in flight
@@ -886,13 +928,34 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   if (active) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      mrl[wid][u * 64 + lane] = lr[u];
-      if (BP == 1) mv[wid][u * 64 + lane] = lv[u];
+      mrl[wid][4 * lane + u] = lr[u];
+      if (BP == 1) mv[wid][4 * lane + u] = lv[u];
     }
-    uint32_t jrow = 0, before_r = 0;
-    if (nr > 0u) wave_locate_regs(lr, nr, start - before_b, &jrow, &before_r);
+    // the row: one scan over the lanes' sums of four, then lane L's four rows
+    // (the first with prefix <= t < prefix + length; zero lengths are passed)
+    const uint32_t t = start - before_b;
+    const uint32_t s4 = lr[0] + lr[1] + lr[2] + lr[3];
+    const uint32_t inc = wave_incl_scan(s4);
+    const uint32_t lo4 = inc - s4;
+    const unsigned long long hit = __ballot(s4 > 0u && lo4 <= t && t < inc);
+    uint32_t jrow = nr, before_r = 0u;
+    if (hit) {
+      const int L = __ffsll((long long)hit) - 1;
+      uint32_t acc = (uint32_t)__builtin_amdgcn_readlane((int)lo4, L);
+      uint32_t k = 3u;
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)lr[u], L);
+        if (k == 3u) {
+          if (t < acc + x) k = (uint32_t)u;
+          else acc += x;
+        }
+      }
+      jrow = 4u * (uint32_t)L + k;
+      before_r = acc;
+    }
     rowb = __builtin_amdgcn_readfirstlane(jrow < nr ? r0 + jrow : m);
-    offb = __builtin_amdgcn_readfirstlane(start - before_b - before_r);
+    offb = __builtin_amdgcn_readfirstlane(t - before_r);
   }
 
   // batch state: up to 64 rows from rowb, one per lane

@@ -240,6 +240,9 @@ static_assert(HIST_BINS == 16 * DSP_T, "each dispatch thread holds 16 histogram 
 // the cutoff), a row keeps whole the probe segments whose chart value is >= lo
 // (probes are descending, so these are segments 0..q-1), and the read length
 // of (row, group) covers segments 0..min(q, P-1) through the counts table.
+// PM: probes per row held in registers (16 or 32); rows with more take a
+// slower loop over memory.
+template <int PM>
 __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   if (blockIdx.y) {  // vector blockIdx.y of a batch
     const uint64_t k = blockIdx.y;
@@ -278,11 +281,13 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   }
   float vi = 0.0f;
   uint32_t rmax = 0u;
-  uint32_t pk[PMAXR / 2];  // the row's probe keys, two per word
+  uint32_t pk[PM / 2];  // the row's probe keys, two per word (zero past P)
+#pragma unroll
+  for (int t = 0; t < PM / 2; ++t) pk[t] = 0u;
   if (valid) {
     vi = a.v[i];
     rmax = a.rowmax[i];
-    if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, pk);
+    if (a.P <= PM) load_row_keys<PM>(a.probes, a.P, i, pk);
   }
   uint32_t hs = 0;
 #pragma unroll
@@ -290,14 +295,19 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   uint32_t tot;
   uint32_t above = block_excl_scan<DSP_T>(hs, tmp, &tot);
   if (above < a.K && a.K <= above + hs) {
+    // from the top bin down, the bins whose running total stays below K lie
+    // wholly above the K-th value: count them (no branches)
+    uint32_t acc = above, nb = 0u, before = above;
 #pragma unroll
     for (int k = 15; k >= 0; --k) {
-      if (above < a.K && a.K <= above + h[k]) {
-        sres[0] = (uint32_t)(hb + k);
-        sres[1] = above;
-      }
-      above += h[k];
+      const uint32_t nxt = acc + h[k];
+      const bool below = nxt < a.K;
+      nb += below ? 1u : 0u;
+      before = below ? nxt : before;
+      acc = nxt;
     }
+    sres[0] = (uint32_t)(hb + 15) - nb;
+    sres[1] = before;
   }
   __syncthreads();
   const float av = fabsf(vi);
@@ -305,18 +315,28 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   const uint32_t above1 = sres[1];
   const uint32_t lo_bits = b1 << HIST_SHIFT;
   const bool none = !valid || __float_as_uint(__fmul_rn(av, h2f(rmax))) < lo_bits;
+  // bin b1 holds the chart bits [lo_bits, hi_bits); no chart reaches 2^31
+  const uint32_t hi_bits = (b1 + 1u) << HIST_SHIFT;
   int32_t q = 0;
-  uint32_t hits = 0u;  // chart entries of this row in bin b1 (P <= PMAXR)
+  uint32_t hits = 0u;  // chart entries of this row in bin b1 (P <= PM)
   if (valid) {
-    if (a.P <= PMAXR) {
+    if (a.P <= PM) {
+      // A row's probes do not increase with k, so neither do its chart
+      // values: the ones at or above a bound form a prefix, and the ones in
+      // bin b1 the range [chi, clo).  The keys past P are 0 and only count
+      // toward clo when lo_bits is 0; the counts are clamped to P.
+      uint32_t clo = 0u, chi = 0u;
 #pragma unroll
-      for (int k = 0; k < PMAXR; ++k) {
-        if (k < a.P) {
-          const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key_at(pk, k))));
-          q += bits >= lo_bits ? 1 : 0;
-          hits |= (bits >> HIST_SHIFT) == b1 ? 1u << k : 0u;
-        }
+      for (int k = 0; k < PM; ++k) {
+        const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key_at(pk, k))));
+        clo += bits >= lo_bits ? 1u : 0u;
+        chi += bits >= hi_bits ? 1u : 0u;
       }
+      clo = min(clo, (uint32_t)a.P);
+      chi = min(chi, (uint32_t)a.P);
+      q = (int32_t)clo;
+      // bits chi .. clo - 1 (clo <= 32; shifts of 32 go through 64 bits)
+      hits = (uint32_t)((1ull << clo) - (1ull << chi));
     } else {
       const uint16_t* pr = a.probes + i * a.P;
       for (int k = 0; k < a.P; ++k) {
@@ -334,7 +354,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   // reserved here, so that the reservation's round trip overlaps the work on
   // the read lengths; the values are stored at the end.
   uint32_t cnt = 0u, cpos = 0u, cret = 0u;
-  if (a.P <= PMAXR) {
+  if (a.P <= PM) {
     cnt = (uint32_t)__popc(hits);
     const uint32_t incl = wave_incl_scan(cnt);
     cpos = incl - cnt;
@@ -383,10 +403,10 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
   // Last, the chart values in bin b1: into the candidate list and the
   // refinement histogram of their bits 18..9 (memory instructions inside the
   // keep loop above, even rarely taken ones, made it 0.4 us slower).
-  if (a.P <= PMAXR) {
+  if (a.P <= PM) {
     uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cret, 63) + cpos;
 #pragma unroll
-    for (int k = 0; k < PMAXR; ++k) {
+    for (int k = 0; k < PM; ++k) {
       if ((hits >> k) & 1u) {
         const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key_at(pk, k))));
         if ((uint64_t)base < capc) a.cand[base] = bits;
@@ -400,10 +420,12 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
   const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
   const dim3 grid((unsigned)blocks, (unsigned)nvec);
+  // probes in registers: 16 when they fit (the common P), else 32
+  auto kern = a.P <= 16 ? k_dispatch<16> : k_dispatch<PMAXR>;
   if (ev && ev->start)
-    hipExtLaunchKernelGGL(k_dispatch, grid, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
   else
-    hipLaunchKernelGGL(k_dispatch, grid, dim3(DSP_T), 0, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(DSP_T), 0, s, a);
   return hipGetLastError();
 }
 

@@ -133,8 +133,11 @@ __device__ __forceinline__ uint32_t key_at(const uint32_t* kw, int k) {
 
 constexpr int CH_T = 256;  // rows per block of the histogram kernel
 
+// PM: probes per row held in registers (16 or 32); rows with more take a
+// slower loop over memory.
+template <int PM>
 __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
-  __shared__ uint32_t hist[HIST_BINS];
+  __shared__ uint32_t hist[HIST_BINS + 1];  // + a slot for the keys past P
   const int tid = threadIdx.x;
   if (blockIdx.y) {  // vector blockIdx.y of a batch
     const uint64_t k = blockIdx.y;
@@ -148,19 +151,22 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
   const int64_t i = (int64_t)blockIdx.x * CH_T + tid;
   const bool valid = i < a.m;
   float vi = 0.0f;
-  uint32_t kw[PMAXR / 2];
+  uint32_t kw[PM / 2];
   if (valid) {
     vi = a.v[i];
-    if (a.P <= PMAXR) load_row_keys<PMAXR>(a.probes, a.P, i, kw);
+    if (a.P <= PM) load_row_keys<PM>(a.probes, a.P, i, kw);
   }
   for (int b = tid; b < HIST_BINS; b += CH_T) hist[b] = 0u;
   __syncthreads();
   if (valid) {
     const float av = fabsf(vi);
-    if (a.P <= PMAXR) {
+    if (a.P <= PM) {
+      // straight-line: the keys past P go to the spare slot, never merged
 #pragma unroll
-      for (int k = 0; k < PMAXR; ++k)
-        if (k < a.P) atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(key_at(kw, k)))) >> HIST_SHIFT], 1u);
+      for (int k = 0; k < PM; ++k) {
+        const uint32_t bin = __float_as_uint(__fmul_rn(av, h2f(key_at(kw, k)))) >> HIST_SHIFT;
+        atomicAdd(&hist[k < a.P ? bin : (uint32_t)HIST_BINS], 1u);
+      }
     } else {
       const uint16_t* pr = a.probes + i * a.P;
       for (int k = 0; k < a.P; ++k)
@@ -189,10 +195,11 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
   const int64_t blocks = (a.m + CH_T - 1) / CH_T;
   const dim3 grid((unsigned)blocks, (unsigned)nvec);
+  auto kern = a.P <= 16 ? k_chart_hist<16> : k_chart_hist<PMAXR>;
   if (ev && ev->start)
-    hipExtLaunchKernelGGL(k_chart_hist, grid, dim3(CH_T), 0, s, ev->start, ev->stop, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, dim3(CH_T), 0, s, ev->start, ev->stop, 0, a);
   else
-    hipLaunchKernelGGL(k_chart_hist, grid, dim3(CH_T), 0, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(CH_T), 0, s, a);
   return hipGetLastError();
 }
 

@@ -555,8 +555,23 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) h3[k * 64 + lane] = 0u;
+  // the next RB * 64 candidates, issued as soon as the count is known so that
+  // their round trip overlaps the second digit's work (words at or past nc
+  // read as zero)
+  constexpr int RB = 48;
+  const bool more = nc > CB * 64u;
+  uint32_t rv[RB];
+  if (more) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)cand, (short)0, (int)(nc * 4u), kBufferDword3);
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      rv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, ((CB + u) * 64 + lane) * 4, 0, 0);
+  }
 
-  // second digit: the bin holding rank K1 within b1, counted from the top
+  // second digit: the bin holding rank K1 within b1, counted from the top.
+  // Every lane counts, from its top bin down, the bins whose running total
+  // stays below K1 (selects, no branches); lane L's answer is kept.
   const uint32_t K1 = K - above1;
   uint32_t sum = 0;
 #pragma unroll
@@ -565,15 +580,18 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
   const unsigned long long hit = __ballot(above < K1 && K1 <= above + sum);
   const int L = __ffsll((long long)hit) - 1;
   uint32_t b2 = 0u, above2 = 0u;
-  if (lane == L) {
+  {
+    uint32_t acc = above, nb = 0u, before = above;
 #pragma unroll
     for (int k = 15; k >= 0; --k) {
-      if (above < K1 && K1 <= above + h[k]) {
-        b2 = (uint32_t)(1008 - 16 * lane + k);
-        above2 = above;
-      }
-      above += h[k];
+      const uint32_t nxt = acc + h[k];
+      const bool below = nxt < K1;
+      nb += below ? 1u : 0u;
+      before = below ? nxt : before;
+      acc = nxt;
     }
+    b2 = (uint32_t)(1008 - 16 * lane + 15) - nb;
+    above2 = before;
   }
   b2 = (uint32_t)__builtin_amdgcn_readlane((int)b2, L);
   above2 = (uint32_t)__builtin_amdgcn_readlane((int)above2, L);
@@ -586,16 +604,24 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
     const uint32_t p = (uint32_t)(u * 64 + lane);
     if (p < nc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
   }
-  for (uint32_t p0 = CB * 64u; p0 < nc; p0 += CB * 64u) {  // more candidates: CB per lane a round
+  if (more) {
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const uint32_t p = p0 + (uint32_t)(u * 64 + lane);
-      cv[u] = p < nc ? cand[p] : 0u;
+    for (int u = 0; u < RB; ++u) {
+      const uint32_t p = (uint32_t)((CB + u) * 64 + lane);
+      if (p < nc && (rv[u] >> 9) == pre) atomicAdd(&h3[rv[u] & 511u], 1u);
     }
+    // still more: CB per lane a round
+    for (uint32_t p0 = (CB + RB) * 64u; p0 < nc; p0 += CB * 64u) {
 #pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const uint32_t p = p0 + (uint32_t)(u * 64 + lane);
-      if (p < nc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
+      for (int u = 0; u < CB; ++u) {
+        const uint32_t p = p0 + (uint32_t)(u * 64 + lane);
+        cv[u] = p < nc ? cand[p] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const uint32_t p = p0 + (uint32_t)(u * 64 + lane);
+        if (p < nc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
+      }
     }
   }
   // lane l holds bins [504 - 8 l, 512 - 8 l)
@@ -610,16 +636,23 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
   const unsigned long long hit3 = __ballot(above < K2 && K2 <= above + sum);
   const int L3 = __ffsll((long long)hit3) - 1;
   uint32_t b3 = 0u, above3 = 0u, c3 = 0u;
-  if (lane == L3) {
+  {
+    // as for the second digit; c3 is the count of the first bin whose running
+    // total reaches K2
+    uint32_t acc = above, nb = 0u, before = above;
+    bool found = false;
 #pragma unroll
     for (int k = 7; k >= 0; --k) {
-      if (above < K2 && K2 <= above + g[k]) {
-        b3 = (uint32_t)(504 - 8 * lane + k);
-        above3 = above;
-        c3 = g[k];
-      }
-      above += g[k];
+      const uint32_t nxt = acc + g[k];
+      const bool below = nxt < K2;
+      nb += below ? 1u : 0u;
+      before = below ? nxt : before;
+      c3 = !below && !found ? g[k] : c3;
+      found = found || !below;
+      acc = nxt;
     }
+    b3 = (uint32_t)(504 - 8 * lane + 7) - nb;
+    above3 = before;
   }
   b3 = (uint32_t)__builtin_amdgcn_readlane((int)b3, L3);
   above3 = (uint32_t)__builtin_amdgcn_readlane((int)above3, L3);

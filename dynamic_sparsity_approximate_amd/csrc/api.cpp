@@ -164,7 +164,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
   ma.mask = dbg ? dbg->mask : nullptr;
   const bool record = dbg && (dbg->row_kept || dbg->fingerprint || dbg->mask);
-  int bpg = (cu_count() + g.G - 1) / g.G;
+  int bpg = cu_count() / g.G;  // at most one block per CU: a larger grid runs a second round
   if (bpg < 1) bpg = 1;
   if (hip_failed(e = launch_bucketmul(ma, record, bpg, s, ev ? &ev[2] : nullptr))) return EFFORT_EHIP;
 
@@ -227,7 +227,7 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
   uint32_t* urunlen = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.urunlen);
   uint32_t* ubsum = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.ubsum);
   const int bp = bucketmul_pass_width(g.TW, batch);
-  int bpg = (cu_count() + g.G - 1) / g.G;
+  int bpg = cu_count() / g.G;  // at most one block per CU: a larger grid runs a second round
   if (bpg < 1) bpg = 1;
   for (int32_t b0 = 0; b0 < batch; b0 += bp) {
     const int32_t nv = batch - b0 < bp ? batch - b0 : bp;

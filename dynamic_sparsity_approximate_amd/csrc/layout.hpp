@@ -36,10 +36,17 @@ struct Geometry {
   uint64_t off_probes = 0, off_counts = 0, off_entries = 0, off_rowmax = 0, total = 0;
 };
 
+// The smallest power of two, at least 2, whose groups hold at most
+// kTargetGroupWidth columns.  A power of two divides the CU count, so the
+// multiply's grid (CUs / G blocks per group) stays one block per CU; at least
+// two groups halve the blocks adding into each output column (one group per
+// 4096 columns measured 10-25 % slower on the Mistral shapes with 4096 or
+// 1024 columns).
 inline int32_t default_groups(int64_t n) {
   if (n < 1) return 1;
-  int64_t g = (n + kTargetGroupWidth - 1) / kTargetGroupWidth;
-  return (int32_t)(g < 1 ? 1 : g);
+  int64_t g = 2;
+  while ((n + g - 1) / g > kTargetGroupWidth) g *= 2;
+  return (int32_t)g;
 }
 
 // Fills g from (m, n, P, groups).  groups = 0 picks the default.  The group

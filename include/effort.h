@@ -84,7 +84,8 @@ const char* effort_last_hip_error(void);
 
 /* ---------------------------------------------------------------- sizing (host only, no HIP calls) */
 
-/* Default number of output-column groups for out_dim columns. */
+/* Default number of output-column groups for out_dim columns: the smallest
+   power of two, at least 2, whose groups hold at most 4096 columns. */
 int32_t effort_default_groups(int64_t out_dim);
 
 /* Bytes of the layout of an in_dim x out_dim matrix with P probes per row and

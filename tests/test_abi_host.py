@@ -63,8 +63,9 @@ def test_strerror_names_codes():
 
 def test_layout_bytes_and_groups():
     assert E.effort_default_groups(14336) == 4
-    assert E.effort_default_groups(4096) == 1
-    assert E.effort_default_groups(1024) == 1
+    assert E.effort_default_groups(4096) == 2
+    assert E.effort_default_groups(1024) == 2
+    assert E.effort_default_groups(12288) == 4  # powers of two only
     assert E.effort_default_groups(32000) == 8
     m, n, P = 4096, 14336, 16
     nb = E.effort_layout_bytes(m, n, P)

@@ -1201,11 +1201,24 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
     thresholds();
   }
   __syncthreads();
+  // Flush: FU tile words per thread are read before any is used (one LDS
+  // wait per round instead of one per word: a group of 3584 columns is one
+  // round), then the non-zero ones are added to y.
+  constexpr int FU = 8;
   for (int p = 0; p < nv; ++p) {
     const double unscale = ldexp(1.0, -sS[p]);
-    for (int c = tid; c < tw; c += MUL_T) {
-      const int32_t acc = tile[p * a.TW + c];
-      if (acc != 0) atomicAdd(&y[(size_t)p * a.n + col0 + c], (float)((double)acc * unscale));
+    for (int c0 = tid; c0 < tw; c0 += MUL_T * FU) {
+      int32_t acc[FU];
+#pragma unroll
+      for (int u = 0; u < FU; ++u) {
+        const int c = c0 + u * MUL_T;
+        acc[u] = c < tw ? tile[p * a.TW + c] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < FU; ++u) {
+        const int c = c0 + u * MUL_T;
+        if (acc[u] != 0) atomicAdd(&y[(size_t)p * a.n + col0 + c], (float)((double)acc[u] * unscale));
+      }
     }
   }
   if (blockIdx.x == 0)  // only the dispatch reads it: ready for the next call

@@ -452,12 +452,15 @@ def run_decode(args, torch, np, E, synth, dev):
     a = [to(synth.vector("config2/attn", MISTRAL["dim"], seed=0, layer=l)) for l in range(L)]
     hin = to(synth.vector("config2/head_in", MISTRAL["dim"], seed=0))
     step = E.DecodeStep(layers, head, x, a, hin)
+    gstep = E.DecodeStep(layers, head, x, a, hin, grouped=True)
     dstep = E.DenseDecodeStep(dlayers, dhead, x, a, hin)
     side = [torch.cuda.Stream() for _ in range(args.streams)] or None
     us1 = graph_time_us(torch, lambda: step.enqueue(effort), 20)
     dus1 = graph_time_us(torch, lambda: dstep.enqueue(), 20)
     us = graph_time_us(torch, lambda: step.enqueue(effort, side_streams=side), 20) if side else us1
     dus = graph_time_us(torch, lambda: dstep.enqueue(side_streams=side), 20) if side else dus1
+    gus1 = graph_time_us(torch, lambda: gstep.enqueue(effort), 20)
+    gus = graph_time_us(torch, lambda: gstep.enqueue(effort, side_streams=side), 20) if side else gus1
     print(json.dumps({"mode": "decode", "workload": "Mistral-7B-shaped decode step, %d layers + head, "
                       "effort %g, batch 1" % (L, effort), "matvecs": step.calls,
                       "weights": weights, "side_streams": args.streams,
@@ -465,6 +468,10 @@ def run_decode(args, torch, np, E, synth, dev):
                       "speedup_vs_dense": round(dus / us, 3),
                       "one_stream": {"effort_us_per_token": round(us1, 1),
                                      "dense_us_per_token": round(dus1, 1)},
+                      "grouped": {"note": "qkv and w1/w3 as multi-matrix calls",
+                                  "one_stream_us_per_token": round(gus1, 1),
+                                  "side_streams_us_per_token": round(gus, 1),
+                                  "speedup_vs_best_dense": round(min(dus, dus1) / min(gus, gus1), 3)},
                       "dense_GBps": round(2.0 * weights / dus / 1e3, 1)}))
 
 
@@ -482,6 +489,7 @@ def run_moe(args, torch, np, E, synth, dev):
         dexperts.append(tuple(torch.from_numpy(W.view(np.int16)).to(dev) for W in Ws))
         log("expert %d prepared" % e)
     moe = E.MoEFFN(experts, dev)
+    gmoe = E.MoEFFN(experts, dev, grouped=True)
     tokens = 16
     xs = [torch.from_numpy(synth.vector("config3/x", d, seed=t)).to(dev) for t in range(tokens)]
     routes = [E.route_top2(synth.normals(8, seed=t, stream=synth.stream_id("config3/router")))
@@ -510,9 +518,16 @@ def run_moe(args, torch, np, E, synth, dev):
                                            for t in range(tokens)], 10) / tokens
         us = graph_time_us(torch, lambda: [moe.enqueue(xs[t], routes[t], effort, side_streams=side)
                                           for t in range(tokens)], 10) / tokens if side else us1
+        gus1 = graph_time_us(torch, lambda: [gmoe.enqueue(xs[t], routes[t], effort)
+                                            for t in range(tokens)], 10) / tokens
+        gus = graph_time_us(torch, lambda: [gmoe.enqueue(xs[t], routes[t], effort, side_streams=side)
+                                           for t in range(tokens)], 10) / tokens if side else gus1
         points.append({"effort": effort, "effort_us_per_token": round(us, 1),
                        "one_stream_us_per_token": round(us1, 1),
-                       "speedup_vs_dense": round(dus / us, 3)})
+                       "speedup_vs_dense": round(dus / us, 3),
+                       "grouped_us_per_token": round(gus1, 1),
+                       "grouped_side_streams_us_per_token": round(gus, 1),
+                       "grouped_speedup_vs_dense": round(dus / min(gus, gus1), 3)})
         log(json.dumps(points[-1]))
     print(json.dumps({"mode": "moe", "workload": "Mixtral-shaped expert block, 8 experts, top-2, "
                       "%d tokens" % tokens, "dense_us_per_token": round(dus, 1), "points": points}))

@@ -9,8 +9,8 @@ device memory and streams.
 from .binding import *  # noqa: F401,F403
 from .binding import EffortError, effort_desc, LIB_PATH  # noqa: F401
 from .chain import LAYER_ROLES, DecodeStep, DenseDecodeStep, MoEFFN, route_top2  # noqa: F401
-from .device import EffortMatrix  # noqa: F401
+from .device import EffortGroup, EffortMatrix  # noqa: F401
 
 __all__ = [n for n in dir() if n.startswith(("effort_", "dense_")) or n in
-           ("EffortError", "EffortMatrix", "LIB_PATH", "LAYER_ROLES", "DecodeStep",
+           ("EffortError", "EffortGroup", "EffortMatrix", "LIB_PATH", "LAYER_ROLES", "DecodeStep",
             "DenseDecodeStep", "MoEFFN", "route_top2")]

@@ -79,6 +79,9 @@ _PROTOS = {
     "effort_layout_check": ([_D, _p], ctypes.c_int),
     "effort_matvec": ([_D, _p, _p, _f32, _p, _p, _u64, _p], ctypes.c_int),
     "effort_matvec_batched": ([_D, _p, _p, _i32, _f32, _p, _p, _u64, _p], ctypes.c_int),
+    "effort_workspace_bytes_multi": ([_D, _i32, ctypes.POINTER(_u64)], ctypes.c_int),
+    "effort_matvec_multi": ([_D, ctypes.POINTER(_p), _i32, _p, ctypes.POINTER(_f32),
+                             ctypes.POINTER(_p), _p, _u64, _p], ctypes.c_int),
     "effort_matvec_debug": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "effort_matvec_timed": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p], ctypes.c_int),
     "dense_gemv": ([_p, _p, _i64, _i64, _p, _p], ctypes.c_int),
@@ -214,6 +217,32 @@ def effort_matvec_batched(desc, layout, v, batch: int, effort: float, y, ws, ws_
     _check(_lib.effort_matvec_batched(ctypes.byref(desc), _ptr(layout), _ptr(v), batch, effort,
                                       _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "effort_matvec_batched")
+
+
+def _desc_array(descs):
+    arr = (effort_desc * len(descs))()
+    for j, d in enumerate(descs):
+        arr[j] = d
+    return arr
+
+
+def effort_workspace_bytes_multi(descs) -> int:
+    b = _u64()
+    _check(_lib.effort_workspace_bytes_multi(_desc_array(descs), len(descs), ctypes.byref(b)),
+           "effort_workspace_bytes_multi")
+    return int(b.value)
+
+
+def effort_matvec_multi(descs, layouts, v, efforts, ys, ws, ws_bytes: int, stream=None):
+    """ys[j] = approximate v . W_j at efforts[j] (a float applies to all)."""
+    n = len(descs)
+    if isinstance(efforts, (int, float)):
+        efforts = [float(efforts)] * n
+    if not (len(layouts) == len(ys) == len(efforts) == n):
+        raise ValueError("descs, layouts, efforts and ys must have one entry per matrix")
+    _check(_lib.effort_matvec_multi(_desc_array(descs), (_p * n)(*[_ptr(x) for x in layouts]), n,
+                                    _ptr(v), (_f32 * n)(*efforts), (_p * n)(*[_ptr(y) for y in ys]),
+                                    _ptr(ws), ws_bytes, _stream(stream)), "effort_matvec_multi")
 
 
 def effort_matvec_debug(desc, layout, v, effort: float, y, ws, ws_bytes: int, cutoff=None, K=None,

@@ -26,10 +26,14 @@ class DecodeStep:
     produces wo's input, is outside this path); w2 multiplies silu(h1) * h3,
     formed from the approximate outputs h1 = x W1 and h3 = x W3.  The head
     multiplies `head_in`.  Inputs are device fp32 vectors supplied by the caller.
+    With `grouped`, the matrices of a layer that share x go through one
+    multi-matrix call each: (wq, wk, wv) and (w1, w3).
     """
 
-    def __init__(self, layers, head, x, a, head_in):
+    def __init__(self, layers, head, x, a, head_in, grouped: bool = False):
         import torch
+
+        from .device import EffortGroup
 
         if len(layers) != len(x) or len(layers) != len(a):
             raise ValueError("one x and one a vector per layer")
@@ -43,6 +47,8 @@ class DecodeStep:
             self.out.append(o)
         self.logits = torch.empty(head.out_dim, dtype=torch.float32, device=dev)
         self.calls = 7 * len(layers) + 1
+        self.groups = ([(EffortGroup([L["wq"], L["wk"], L["wv"]]), EffortGroup([L["w1"], L["w3"]]))
+                        for L in layers] if grouped else None)
 
     def inputs_of(self, l: int) -> dict:
         """role -> the device vector that role's matvec multiplies in layer l."""
@@ -61,7 +67,19 @@ class DecodeStep:
         for l, L in enumerate(self.layers):
             o, ins = self.out[l], self.inputs_of(l)
             roles = ("wq", "wk", "wv", "wo", "w1", "w3")
-            if side_streams:
+            if self.groups:
+                qkv, gu = self.groups[l]
+                side = list(side_streams[:2]) if side_streams else []
+                s_qkv = side[0] if side else main
+                s_o = side[-1] if side else main
+                for ss in side:
+                    ss.wait_stream(main)
+                qkv.matvec(self.x[l], effort, [o["wq"], o["wk"], o["wv"]], s_qkv)
+                L["wo"].matvec(ins["wo"], effort, o["wo"], s_o)
+                gu.matvec(self.x[l], effort, [o["w1"], o["w3"]], main)
+                for ss in side:
+                    main.wait_stream(ss)
+            elif side_streams:
                 for k, r in enumerate(roles):
                     ss = side_streams[k % len(side_streams)]
                     ss.wait_stream(main)
@@ -133,9 +151,11 @@ def route_top2(logits):
 class MoEFFN:
     """A mixture-of-experts feed-forward block: expert e is (w1, w3, w2) as
     EffortMatrix, y = g0 * FFN_e0(x) + g1 * FFN_e1(x) with FFN(x) =
-    (silu(x W1) * x W3) W2.  Only the two routed experts' layouts are read."""
+    (silu(x W1) * x W3) W2.  Only the two routed experts' layouts are read.
+    With `grouped`, the four matrices that multiply x (w1 and w3 of both
+    routed experts) go through one multi-matrix call."""
 
-    def __init__(self, experts, device):
+    def __init__(self, experts, device, grouped: bool = False):
         import torch
 
         self.experts = experts  # entries that are never routed to may be None
@@ -148,6 +168,11 @@ class MoEFFN:
         self.g = [mk(d_hid), mk(d_hid)]
         self.o = [mk(d_in), mk(d_in)]
         self.y = mk(d_in)
+        self.grouped = grouped
+        if grouped:  # one workspace serves every pair of experts (they share shapes)
+            d4 = [first[0].desc, first[1].desc] * 2
+            self.ws_bytes = B.effort_workspace_bytes_multi(d4)
+            self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)
 
     def enqueue(self, x, route, effort: float, stream=None, side_streams=None):
         """With `side_streams` (at least two torch streams), the two experts run
@@ -158,6 +183,22 @@ class MoEFFN:
         main = stream if stream is not None else torch.cuda.current_stream()
         e0, e1, g0, g1 = route
         ns = len(side_streams) if side_streams else 0
+        if self.grouped:
+            mats = [self.experts[e0][0], self.experts[e0][1], self.experts[e1][0], self.experts[e1][1]]
+            B.effort_matvec_multi([M.desc for M in mats], [M.layout for M in mats], x, effort,
+                                  [self.h1[0], self.h3[0], self.h1[1], self.h3[1]], self.ws,
+                                  self.ws_bytes, main)
+            for k, e in enumerate((e0, e1)):
+                ss = side_streams[k % ns] if ns >= 2 else main
+                if ss is not main:
+                    ss.wait_stream(main)
+                B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], ss)
+                self.experts[e][2].matvec(self.g[k], effort, self.o[k], ss)
+            if ns >= 2:
+                for ss in side_streams[:2]:
+                    main.wait_stream(ss)
+            B.effort_axpby(self.o[0], g0, self.o[1], g1, self.d_in, self.y, main)
+            return self.y
         for k, e in enumerate((e0, e1)):
             w1, w3, w2 = self.experts[e]
             s1 = side_streams[k % ns] if ns >= 2 else main

@@ -76,9 +76,16 @@ struct DebugOut {
   uint32_t* status;
 };
 
-// One vector: select, dispatch, bucketMul on `s`.
-int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
-            uint8_t* ws, hipStream_t s, const DebugOut* dbg, const EventPair* ev) {
+// The three kernels' arguments for one vector and one matrix, its workspace
+// slice at `ws`.
+struct CallArgs {
+  SelectArgs sa;
+  DispatchArgs da;
+  MulArgs ma;
+};
+
+void build_args(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
+                uint8_t* ws, CallArgs* c) {
   const WsLayout w = ws_layout(g);
   uint32_t* result = reinterpret_cast<uint32_t*>(ws + w.result);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist);
@@ -92,21 +99,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   const uint16_t* rowmax = reinterpret_cast<const uint16_t*>(layout + g.off_rowmax);
   const int64_t N = g.m * (int64_t)g.P;
   const uint32_t K = k_of(effort, N);
-  hipError_t e;
 
-  if (dbg) {
-    if (dbg->row_kept && hip_failed(e = launch_zero_bytes(dbg->row_kept, (uint64_t)g.m * 4, s)))
-      return EFFORT_EHIP;
-    if (dbg->fingerprint && hip_failed(e = launch_zero_bytes(dbg->fingerprint, 8, s)))
-      return EFFORT_EHIP;
-    if (dbg->mask && hip_failed(e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)))
-      return EFFORT_EHIP;
-    if (dbg->status && (hip_failed(e = launch_zero_bytes(dbg->status, 4, s)) ||
-                        hip_failed(e = launch_check_finite(v, g.m, dbg->status, s))))
-      return EFFORT_EHIP;
-  }
-
-  SelectArgs sa;
+  SelectArgs& sa = c->sa;
+  sa = SelectArgs();
   sa.v = v;
   sa.probes = probes;
   sa.m = g.m;
@@ -118,9 +113,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   sa.y = y;
   sa.n = g.n;
   sa.vec_ws = 0;
-  if (hip_failed(e = launch_select(sa, s, ev ? &ev[0] : nullptr))) return EFFORT_EHIP;
 
-  DispatchArgs da;
+  DispatchArgs& da = c->da;
+  da = DispatchArgs();
   da.v = v;
   da.probes = probes;
   da.counts = counts;
@@ -137,9 +132,9 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   da.G4 = g.G4;
   da.K = K;
   da.vec_ws = 0;
-  if (hip_failed(e = launch_dispatch(da, s, ev ? &ev[1] : nullptr))) return EFFORT_EHIP;
 
-  MulArgs ma;
+  MulArgs& ma = c->ma;
+  ma = MulArgs();
   ma.v = v;
   ma.entries = entries;
   ma.runlen = runlen;
@@ -160,6 +155,34 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   ma.nv = 1;
   ma.vec_ws = 0;
   ma.vbsum = bsum;
+  ma.row_kept = nullptr;
+  ma.fingerprint = nullptr;
+  ma.mask = nullptr;
+}
+
+// One vector: select, dispatch, bucketMul on `s`.
+int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
+            uint8_t* ws, hipStream_t s, const DebugOut* dbg, const EventPair* ev) {
+  CallArgs c;
+  build_args(g, layout, v, effort, y, ws, &c);
+  hipError_t e;
+
+  if (dbg) {
+    if (dbg->row_kept && hip_failed(e = launch_zero_bytes(dbg->row_kept, (uint64_t)g.m * 4, s)))
+      return EFFORT_EHIP;
+    if (dbg->fingerprint && hip_failed(e = launch_zero_bytes(dbg->fingerprint, 8, s)))
+      return EFFORT_EHIP;
+    if (dbg->mask && hip_failed(e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)))
+      return EFFORT_EHIP;
+    if (dbg->status && (hip_failed(e = launch_zero_bytes(dbg->status, 4, s)) ||
+                        hip_failed(e = launch_check_finite(v, g.m, dbg->status, s))))
+      return EFFORT_EHIP;
+  }
+
+  if (hip_failed(e = launch_select(c.sa, s, ev ? &ev[0] : nullptr))) return EFFORT_EHIP;
+  if (hip_failed(e = launch_dispatch(c.da, s, ev ? &ev[1] : nullptr))) return EFFORT_EHIP;
+
+  MulArgs& ma = c.ma;
   ma.row_kept = dbg ? dbg->row_kept : nullptr;
   ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
   ma.mask = dbg ? dbg->mask : nullptr;
@@ -169,7 +192,7 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
   if (hip_failed(e = launch_bucketmul(ma, record, bpg, s, ev ? &ev[2] : nullptr))) return EFFORT_EHIP;
 
   if (dbg && (dbg->cutoff || dbg->K) &&
-      hip_failed(launch_debug_result(result, dbg->cutoff, dbg->K, s)))
+      hip_failed(launch_debug_result(ma.result, dbg->cutoff, dbg->K, s)))
     return EFFORT_EHIP;
   return EFFORT_OK;
 }
@@ -311,6 +334,56 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   return EFFORT_OK;
 }
 
+// Workspace bytes of a multi-matrix call: matrix j's one-vector slice at a
+// 256-byte aligned offset.
+uint64_t multi_ws_offsets(const Geometry* g, int32_t count, uint64_t* off) {
+  uint64_t total = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    off[j] = total;
+    total = align_up(total + ws_layout(g[j]).slice, kAlign);
+  }
+  return total;
+}
+
+int check_multi(const effort_desc* descs, int32_t count, Geometry* g) {
+  if (!descs || count < 1 || count > EFFORT_MAX_MULTI) return EFFORT_EINVAL;
+  for (int32_t j = 0; j < count; ++j) {
+    const int rc = check_desc(&descs[j], &g[j]);
+    if (rc) return rc;
+    if (g[j].m != g[0].m) return EFFORT_EINVAL;  // one input vector for all
+  }
+  return EFFORT_OK;
+}
+
+// Several matrices sharing v: each kernel launched once for all of them.
+// The multiply's CUs are shared out by output width (the kept bytes of each
+// matrix are about proportional to it at one effort), whole blocks per group.
+int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts, const float* v,
+              const float* efforts, float* const* ys, uint8_t* ws, const uint64_t* off,
+              hipStream_t s) {
+  SelectMulti sm;
+  DispatchMulti dm;
+  MulMulti mm;
+  int bpg[EFFORT_MAX_MULTI];
+  int64_t ntot = 0;
+  for (int32_t j = 0; j < count; ++j) ntot += g[j].n;
+  const int cus = cu_count();
+  for (int32_t j = 0; j < count; ++j) {
+    CallArgs c;
+    build_args(g[j], layouts[j], v, efforts[j], ys[j], ws + off[j], &c);
+    sm.a[j] = c.sa;
+    dm.a[j] = c.da;
+    mm.a[j] = c.ma;
+    const int64_t share = (int64_t)cus * g[j].n / ntot;
+    bpg[j] = (int)(share / g[j].G);
+    if (bpg[j] < 1) bpg[j] = 1;
+  }
+  if (hip_failed(launch_select_multi(sm, count, s))) return EFFORT_EHIP;
+  if (hip_failed(launch_dispatch_multi(dm, count, s))) return EFFORT_EHIP;
+  if (hip_failed(launch_bucketmul_multi(mm, count, bpg, s))) return EFFORT_EHIP;
+  return EFFORT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,6 +426,39 @@ int effort_workspace_bytes(const effort_desc* desc, int32_t batch, uint64_t* byt
   const WsLayout w = ws_layout(g);
   *bytes = w.slice * (uint64_t)batch + (batch > 1 ? w.union_bytes : 0);
   return EFFORT_OK;
+}
+
+int effort_workspace_bytes_multi(const effort_desc* descs, int32_t count, uint64_t* bytes) {
+  if (!bytes) return EFFORT_EINVAL;
+  Geometry g[EFFORT_MAX_MULTI];
+  const int rc = check_multi(descs, count, g);
+  if (rc) return rc;
+  uint64_t off[EFFORT_MAX_MULTI];
+  *bytes = multi_ws_offsets(g, count, off);
+  return EFFORT_OK;
+}
+
+int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev, int32_t count,
+                        const float* v_dev, const float* efforts, float* const* ys_dev,
+                        void* ws_dev, uint64_t ws_bytes, void* stream) {
+  Geometry g[EFFORT_MAX_MULTI];
+  int rc = check_multi(descs, count, g);
+  if (rc) return rc;
+  if (!layouts_dev || !ys_dev || !efforts || !v_dev || !ws_dev) return EFFORT_EINVAL;
+  if (!aligned(ws_dev, 256) || !aligned(v_dev, 4)) return EFFORT_EINVAL;
+  const uint8_t* layouts[EFFORT_MAX_MULTI];
+  float* ys[EFFORT_MAX_MULTI];
+  for (int32_t j = 0; j < count; ++j) {
+    if (!effort_ok(efforts[j])) return EFFORT_EINVAL;
+    if (!layouts_dev[j] || !ys_dev[j]) return EFFORT_EINVAL;
+    if (!aligned(layouts_dev[j], 256) || !aligned(ys_dev[j], 4)) return EFFORT_EINVAL;
+    layouts[j] = static_cast<const uint8_t*>(layouts_dev[j]);
+    ys[j] = ys_dev[j];
+  }
+  uint64_t off[EFFORT_MAX_MULTI];
+  if (ws_bytes < multi_ws_offsets(g, count, off)) return EFFORT_ENOSPACE;
+  return run_multi(g, count, layouts, v_dev, efforts, ys, static_cast<uint8_t*>(ws_dev), off,
+                   static_cast<hipStream_t>(stream));
 }
 
 int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream) {

@@ -136,17 +136,9 @@ constexpr int CH_T = 256;  // rows per block of the histogram kernel
 // PM: probes per row held in registers (16 or 32); rows with more take a
 // slower loop over memory.
 template <int PM>
-__global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
+__device__ __forceinline__ void chart_hist_body(const SelectArgs& a) {
   __shared__ uint32_t hist[HIST_BINS + 1];  // + a slot for the keys past P
   const int tid = threadIdx.x;
-  if (blockIdx.y) {  // vector blockIdx.y of a batch
-    const uint64_t k = blockIdx.y;
-    a.v += k * a.m;
-    a.y += k * a.n;
-    a.hist += k * a.vec_ws;
-    a.hist2 += k * a.vec_ws;
-    a.result += k * a.vec_ws;
-  }
   // the row's loads are issued before the histogram is cleared
   const int64_t i = (int64_t)blockIdx.x * CH_T + tid;
   const bool valid = i < a.m;
@@ -190,6 +182,25 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
     for (int b = tid; b < 1024; b += CH_T) a.hist2[b] = 0u;
     if (tid == 0) a.result[RES_NCAND] = 0u;
   }
+}
+
+template <int PM>
+__global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
+  if (blockIdx.y) {  // vector blockIdx.y of a batch
+    const uint64_t k = blockIdx.y;
+    a.v += k * a.m;
+    a.y += k * a.n;
+    a.hist += k * a.vec_ws;
+    a.hist2 += k * a.vec_ws;
+    a.result += k * a.vec_ws;
+  }
+  chart_hist_body<PM>(a);
+}
+
+// Several matrices sharing v: blockIdx.y picks the matrix.
+template <int PM>
+__global__ __launch_bounds__(CH_T) void k_chart_hist_multi(SelectMulti mm) {
+  chart_hist_body<PM>(mm.a[blockIdx.y]);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
@@ -250,17 +261,7 @@ static_assert(HIST_BINS == 16 * DSP_T, "each dispatch thread holds 16 histogram 
 // PM: probes per row held in registers (16 or 32); rows with more take a
 // slower loop over memory.
 template <int PM>
-__global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
-  if (blockIdx.y) {  // vector blockIdx.y of a batch
-    const uint64_t k = blockIdx.y;
-    a.v += k * a.m;
-    a.hist += k * a.vec_ws;
-    a.hist2 += k * a.vec_ws;
-    a.cand += k * a.vec_ws;
-    a.result += k * a.vec_ws;
-    a.runlen += k * a.vec_ws;
-    a.bsum += k * a.vec_ws;
-  }
+__device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
   __shared__ uint32_t tmp[DSP_T / 64 + 1];
   __shared__ uint32_t sres[2];
   __shared__ uint32_t red[4 * (DSP_T / 64)];
@@ -422,6 +423,51 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
       }
     }
   }
+}
+
+template <int PM>
+__global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
+  if (blockIdx.y) {  // vector blockIdx.y of a batch
+    const uint64_t k = blockIdx.y;
+    a.v += k * a.m;
+    a.hist += k * a.vec_ws;
+    a.hist2 += k * a.vec_ws;
+    a.cand += k * a.vec_ws;
+    a.result += k * a.vec_ws;
+    a.runlen += k * a.vec_ws;
+    a.bsum += k * a.vec_ws;
+  }
+  dispatch_body<PM>(a);
+}
+
+// Several matrices sharing v: blockIdx.y picks the matrix.
+template <int PM>
+__global__ __launch_bounds__(DSP_T) void k_dispatch_multi(DispatchMulti mm) {
+  dispatch_body<PM>(mm.a[blockIdx.y]);
+}
+
+hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) {
+  if (count < 1 || count > EFFORT_MAX_MULTI) return hipErrorInvalidValue;
+  int P = 0;
+  for (int j = 0; j < count; ++j) P = mm.a[j].P > P ? mm.a[j].P : P;
+  const dim3 grid((unsigned)((mm.a[0].m + CH_T - 1) / CH_T), (unsigned)count);
+  if (P <= 16)
+    hipLaunchKernelGGL(k_chart_hist_multi<16>, grid, dim3(CH_T), 0, s, mm);
+  else
+    hipLaunchKernelGGL(k_chart_hist_multi<PMAXR>, grid, dim3(CH_T), 0, s, mm);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t s) {
+  if (count < 1 || count > EFFORT_MAX_MULTI) return hipErrorInvalidValue;
+  int P = 0;
+  for (int j = 0; j < count; ++j) P = mm.a[j].P > P ? mm.a[j].P : P;
+  const dim3 grid((unsigned)((mm.a[0].m + DSP_T - 1) / DSP_T), (unsigned)count);
+  if (P <= 16)
+    hipLaunchKernelGGL(k_dispatch_multi<16>, grid, dim3(DSP_T), 0, s, mm);
+  else
+    hipLaunchKernelGGL(k_dispatch_multi<PMAXR>, grid, dim3(DSP_T), 0, s, mm);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
@@ -714,11 +760,14 @@ __device__ __forceinline__ uint32_t share_cum(uint32_t j) {
 // A kept product is fl32(w * v * 2^S) rounded to an integer (relative error
 // 2^-24 plus half a unit of 2^-S) and added to the column's int32 LDS word;
 // integer adds make the tile independent of order.
+// The kernel's body for block `bid` of `nblk` (the grid, or one matrix's
+// part of a multi-matrix grid).
 template <bool REC, int BP>
-__global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
-    const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
-    const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
-    const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
+__device__ __forceinline__ void bucketmul_body(
+    const uint32_t bid, const uint32_t nblk, const float* __restrict__ vvec,
+    const uint32_t* __restrict__ entries, const uint32_t* __restrict__ runlen,
+    const uint32_t* __restrict__ bsum, const uint32_t* __restrict__ result,
+    float* __restrict__ y, const MulArgs& a) {
   static_assert(BP == 1 || !REC, "parity recording is single-vector");
   static_assert(BP >= 1 && BP <= 8, "at most 8 vectors per pass");
   constexpr int MUL_T = mul_threads<BP>();
@@ -745,15 +794,21 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
   const int lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.G;
   const int G1 = G + 1;
-  const int g = (int)(blockIdx.x % (unsigned)G);
-  const uint32_t bslot = blockIdx.x / (unsigned)G;
-  const uint32_t bpg = gridDim.x / (unsigned)G;
+  const int g = (int)(bid % (unsigned)G);
+  const uint32_t bslot = bid / (unsigned)G;
+  const uint32_t bpg = nblk / (unsigned)G;
   const int64_t col0 = (int64_t)g * a.TW;
   const int tw = (int)((int64_t)a.TW < a.n - col0 ? (int64_t)a.TW : a.n - col0);
   const uint32_t m = (uint32_t)a.m;
   const uint32_t nbd = (uint32_t)a.nbd;
   const uint32_t* rl = runlen + (size_t)g * a.m;
   const int nv = BP == 1 ? 1 : a.nv;
+
+  // The chart histogram is read only by the dispatch, which has finished:
+  // cleared here, spread over the grid, ready for the next call.
+  for (int p = 0; p < nv; ++p)
+    for (int b = (int)bid * MUL_T + tid; b < HIST_BINS; b += (int)nblk * MUL_T)
+      a.hist[(size_t)p * a.vec_ws + b] = 0u;
 
   // ---- round 1
   // wave p < nv: the exact cutoff of vector p (batched: and its fixed-point scale)
@@ -770,7 +825,7 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
         wave_exact_cutoff(a.hist2 + vo, a.cand + vo, ncap, nc, b1, above1, a.K, h3w[wid], &kp);
     if (lane == 0) {
       sCut[wid] = cut;
-      if (blockIdx.x == 0) {
+      if (bid == 0) {
         a.result[vo + RES_CUTOFF] = cut;
         a.result[vo + RES_KPRIME] = kp;
         a.result[vo + RES_K] = a.K;
@@ -1221,9 +1276,25 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
       }
     }
   }
-  if (blockIdx.x == 0)  // only the dispatch reads it: ready for the next call
-    for (int p = 0; p < nv; ++p)
-      for (int b = tid; b < HIST_BINS; b += MUL_T) a.hist[(size_t)p * a.vec_ws + b] = 0u;
+}
+
+template <bool REC, int BP>
+__global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
+    const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
+    const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
+    const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
+  bucketmul_body<REC, BP>(blockIdx.x, gridDim.x, vvec, entries, runlen, bsum, result, y, a);
+}
+
+// Several matrices sharing v, one vector each: matrix j owns blocks
+// [first[j], first[j + 1]) of the grid.
+__global__ __launch_bounds__(mul_threads<1>()) void k_bucketmul_multi(MulMulti mm) {
+  int j = 0;
+  for (int k = 1; k < mm.count; ++k)
+    if (blockIdx.x >= mm.first[k]) j = k;
+  const MulArgs& a = mm.a[j];
+  bucketmul_body<false, 1>(blockIdx.x - mm.first[j], mm.first[j + 1] - mm.first[j], a.v, a.entries,
+                           a.runlen, a.bsum, a.result, a.y, a);
 }
 
 // LDS of a workgroup on gfx950; the batched kernel's static LDS (cutoff
@@ -1285,6 +1356,24 @@ hipError_t launch_bucketmul(const MulArgs& args, bool record, int blocks_per_gro
     hipLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
                        a.entries,
                        a.runlen, a.bsum, a.result, a.y, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucketmul_multi(const MulMulti& mm_in, int count, const int* blocks_per_group,
+                                  hipStream_t s) {
+  if (count < 1 || count > EFFORT_MAX_MULTI || !blocks_per_group) return hipErrorInvalidValue;
+  MulMulti mm = mm_in;
+  uint32_t total = 0;
+  for (int j = 0; j < count; ++j) {
+    const int bpg = blocks_per_group[j];
+    if (bpg < 1 || mm.a[j].nv != 1) return hipErrorInvalidValue;
+    mm.a[j].bpg_recip = bpg >= 2 ? (uint32_t)((1ull << 32) / (uint64_t)bpg) : 0u;
+    mm.first[j] = total;
+    total += (uint32_t)(mm.a[j].G * bpg);
+  }
+  for (int j = count; j <= EFFORT_MAX_MULTI; ++j) mm.first[j] = total;
+  mm.count = count;
+  hipLaunchKernelGGL(k_bucketmul_multi, dim3(total), dim3(mul_threads<1>()), 0, s, mm);
   return hipGetLastError();
 }
 

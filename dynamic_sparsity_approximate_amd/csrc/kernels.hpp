@@ -115,6 +115,24 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s);
 // vectors per pass of the batched multiply that the LDS holds for groups of
 // TW columns (0: none, use single-vector calls)
 int bucketmul_pass_width(int32_t TW, int32_t batch);
+// Several matrices that share the input vector (one vector each): argument
+// tables indexed by grid y (chart, dispatch) or by block range (multiply).
+struct SelectMulti {
+  SelectArgs a[EFFORT_MAX_MULTI];
+};
+struct DispatchMulti {
+  DispatchArgs a[EFFORT_MAX_MULTI];
+};
+struct MulMulti {
+  MulArgs a[EFFORT_MAX_MULTI];
+  uint32_t first[EFFORT_MAX_MULTI + 1];  // matrix j owns blocks [first[j], first[j + 1])
+  int32_t count;
+};
+hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s);
+hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t s);
+// blocks_per_group[j]: matrix j's blocks per column group (its grid is G_j times that)
+hipError_t launch_bucketmul_multi(const MulMulti& mm, int count, const int* blocks_per_group,
+                                  hipStream_t s);
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
                             const EventPair* ev = nullptr);
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,

@@ -284,3 +284,38 @@ def test_dense_and_glue_validation():
         with pytest.raises(E.EffortError) as ei:
             E.effort_axpby(*args)
         assert ei.value.code == B.EFFORT_EINVAL
+
+
+def test_multi_sizes_and_rejects():
+    descs = [E.effort_prepare_host(rand_case(16, n, seed=10 + n)[0], 4)[0] for n in (64, 128, 96)]
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    single = [E.effort_workspace_bytes(d, 1) for d in descs]
+    assert E.effort_workspace_bytes_multi(descs) == sum(up(b) for b in single)
+    assert E.effort_workspace_bytes_multi(descs[:1]) == up(single[0])
+    ws = E.effort_workspace_bytes_multi(descs)
+    good = dict(descs=descs, layouts=[FAKE] * 3, efforts=[0.25] * 3, ys=[FAKE] * 3, ws=FAKE,
+                ws_bytes=ws)
+    other_m = E.effort_prepare_host(rand_case(32, 64, seed=3)[0], 4)[0]
+    cases = [
+        (dict(descs=descs + descs[:2], layouts=[FAKE] * 5, efforts=[0.25] * 5, ys=[FAKE] * 5),
+         B.EFFORT_EINVAL),  # more than EFFORT_MAX_MULTI
+        (dict(descs=[descs[0], other_m], layouts=[FAKE] * 2, efforts=[0.25] * 2, ys=[FAKE] * 2),
+         B.EFFORT_EINVAL),  # in_dim differs
+        (dict(efforts=[0.25, 0.0, 0.25]), B.EFFORT_EINVAL),
+        (dict(efforts=[0.25, 0.25, float("nan")]), B.EFFORT_EINVAL),
+        (dict(layouts=[FAKE, None, FAKE]), B.EFFORT_EINVAL),
+        (dict(layouts=[FAKE, FAKE + 16, FAKE]), B.EFFORT_EINVAL),
+        (dict(ys=[FAKE, FAKE, FAKE + 2]), B.EFFORT_EINVAL),
+        (dict(ws=FAKE + 8), B.EFFORT_EINVAL),
+        (dict(ws_bytes=ws - 1), B.EFFORT_ENOSPACE),
+    ]
+    for over, code in cases:
+        a = dict(good)
+        a.update(over)
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_matvec_multi(a["descs"], a["layouts"], FAKE, a["efforts"], a["ys"], a["ws"],
+                                  a["ws_bytes"])
+        assert ei.value.code == code, over
+    with pytest.raises(E.EffortError) as ei:
+        E.effort_workspace_bytes_multi([])
+    assert ei.value.code == B.EFFORT_EINVAL

@@ -10,13 +10,17 @@
 //   k_chart_hist chart |v_i| * probe_i[k] and a histogram of its top 12 bits;
 //                zeroes y.
 //   k_dispatch   per (group, row) how many rank-ordered entries to read, from the
-//                low edge of the bin holding the K-th largest chart value; one
-//                extra block finishes the exact radix selection of the cutoff.
-//   k_bucketmul  per output-column group an LDS tile of y; each wave streams an
-//                equal share of the group's run prefixes with 16-byte loads,
-//                keeps entries whose key reaches the row threshold (from the
-//                exact cutoff), adds v_i * w as 64-bit fixed point into the tile,
-//                and finally adds the tile to y.
+//                low edge of the bin holding the K-th largest chart value; the
+//                chart values in that bin go to a candidate list and a
+//                histogram of their next 10 bits.
+//   k_bucketmul  one wave finishes the exact radix selection of the cutoff;
+//                per output-column group an LDS tile of y; the other waves
+//                stream their shares of the group's run prefixes with 16-byte
+//                loads, keep entries whose key reaches the row threshold (from
+//                the exact cutoff), add v_i * w as 32-bit fixed point into the
+//                tile, and finally add the tile to y.
+// The *_multi kernels run the same bodies for up to four matrices that share
+// the input vector.
 // No MFMA: the multiply is a bandwidth-bound gather-scatter, not a contraction.
 #include <hip/hip_fp16.h>
 #include <hip/hip_ext.h>

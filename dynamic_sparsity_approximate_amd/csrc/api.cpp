@@ -293,6 +293,64 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
   return EFFORT_OK;
 }
 
+// Workspace bytes of a multi-matrix call: matrix j's one-vector slice at a
+// 256-byte aligned offset.
+uint64_t multi_ws_offsets(const Geometry* g, int32_t count, uint64_t* off) {
+  uint64_t total = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    off[j] = total;
+    total = align_up(total + ws_layout(g[j]).slice, kAlign);
+  }
+  return total;
+}
+
+int check_multi(const effort_desc* descs, int32_t count, Geometry* g) {
+  if (!descs || count < 1 || count > EFFORT_MAX_MULTI) return EFFORT_EINVAL;
+  for (int32_t j = 0; j < count; ++j) {
+    const int rc = check_desc(&descs[j], &g[j]);
+    if (rc) return rc;
+    if (g[j].m != g[0].m) return EFFORT_EINVAL;  // one input vector for all
+  }
+  return EFFORT_OK;
+}
+
+// Several (matrix, vector) pairs -- matrices sharing v, or one matrix with
+// several vectors: each kernel launched once for all of them.
+// The multiply's CUs are shared out by output width (the kept bytes of each
+// matrix are about proportional to it at one effort), whole blocks per group.
+int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
+              const float* const* vs, const float* efforts, float* const* ys, uint8_t* ws,
+              const uint64_t* off, hipStream_t s) {
+  SelectMulti sm;
+  DispatchMulti dm;
+  MulMulti mm;
+  int bpg[EFFORT_MAX_MULTI];
+  int64_t ntot = 0;
+  for (int32_t j = 0; j < count; ++j) ntot += g[j].n;
+  const int cus = cu_count();
+  for (int32_t j = 0; j < count; ++j) {
+    CallArgs c;
+    build_args(g[j], layouts[j], vs[j], efforts[j], ys[j], ws + off[j], &c);
+    sm.a[j] = c.sa;
+    dm.a[j] = c.da;
+    mm.a[j] = c.ma;
+    const int64_t share = (int64_t)cus * g[j].n / ntot;
+    bpg[j] = (int)(share / g[j].G);
+    if (bpg[j] < 1) bpg[j] = 1;
+  }
+  if (hip_failed(launch_select_multi(sm, count, s))) return EFFORT_EHIP;
+  if (hip_failed(launch_dispatch_multi(dm, count, s))) return EFFORT_EHIP;
+  if (hip_failed(launch_bucketmul_multi(mm, count, bpg, s))) return EFFORT_EHIP;
+  return EFFORT_OK;
+}
+
+// Batches from this size read the union of the vectors' read lengths once
+// (run_batched); smaller ones run each vector's own multiply, up to four in
+// one launch of each kernel (4096x14336, effort 0.25: 40.6 / 62.3 us at
+// b = 2 / 4 against 46.7 / 70.9 us for the union pass; 123 against 122 us at
+// b = 8 in two launches).
+constexpr int32_t kUnionMinBatch = 5;
+
 int matvec_common(const effort_desc* desc, const void* layout_dev, const float* v_dev, int32_t batch,
                   float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream,
                   const DebugOut* dbg, void* const* events) {
@@ -324,63 +382,38 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* layout = static_cast<const uint8_t*>(layout_dev);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  if (batch > 1 && !dbg && !events && bucketmul_pass_width(g.TW, batch) > 0)
+  if (batch > 1 && !dbg && !events && batch >= kUnionMinBatch &&
+      bucketmul_pass_width(g.TW, batch) > 0)
     return run_batched(g, layout, v_dev, batch, effort, y_dev, ws, s);
+  if (batch > 1 && !dbg && !events) {
+    // up to EFFORT_MAX_MULTI vectors per launch, each its own single-vector
+    // multiply over its own read lengths (the slices are the batch's)
+    for (int32_t b0 = 0; b0 < batch; b0 += EFFORT_MAX_MULTI) {
+      const int32_t cnt = batch - b0 < EFFORT_MAX_MULTI ? batch - b0 : EFFORT_MAX_MULTI;
+      Geometry gs[EFFORT_MAX_MULTI];
+      const uint8_t* ls[EFFORT_MAX_MULTI];
+      const float* vs[EFFORT_MAX_MULTI];
+      float* ys[EFFORT_MAX_MULTI];
+      float es[EFFORT_MAX_MULTI];
+      uint64_t off[EFFORT_MAX_MULTI];
+      for (int32_t j = 0; j < cnt; ++j) {
+        gs[j] = g;
+        ls[j] = layout;
+        vs[j] = v_dev + (int64_t)(b0 + j) * g.m;
+        ys[j] = y_dev + (int64_t)(b0 + j) * g.n;
+        es[j] = effort;
+        off[j] = (uint64_t)(b0 + j) * w.slice;
+      }
+      rc = run_multi(gs, cnt, ls, vs, es, ys, ws, off, s);
+      if (rc) return rc;
+    }
+    return EFFORT_OK;
+  }
   for (int32_t b = 0; b < batch; ++b) {
     rc = run_one(g, layout, v_dev + (int64_t)b * g.m, effort, y_dev + (int64_t)b * g.n,
                  ws + (uint64_t)b * w.slice, s, dbg, events ? ev : nullptr);
     if (rc) return rc;
   }
-  return EFFORT_OK;
-}
-
-// Workspace bytes of a multi-matrix call: matrix j's one-vector slice at a
-// 256-byte aligned offset.
-uint64_t multi_ws_offsets(const Geometry* g, int32_t count, uint64_t* off) {
-  uint64_t total = 0;
-  for (int32_t j = 0; j < count; ++j) {
-    off[j] = total;
-    total = align_up(total + ws_layout(g[j]).slice, kAlign);
-  }
-  return total;
-}
-
-int check_multi(const effort_desc* descs, int32_t count, Geometry* g) {
-  if (!descs || count < 1 || count > EFFORT_MAX_MULTI) return EFFORT_EINVAL;
-  for (int32_t j = 0; j < count; ++j) {
-    const int rc = check_desc(&descs[j], &g[j]);
-    if (rc) return rc;
-    if (g[j].m != g[0].m) return EFFORT_EINVAL;  // one input vector for all
-  }
-  return EFFORT_OK;
-}
-
-// Several matrices sharing v: each kernel launched once for all of them.
-// The multiply's CUs are shared out by output width (the kept bytes of each
-// matrix are about proportional to it at one effort), whole blocks per group.
-int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts, const float* v,
-              const float* efforts, float* const* ys, uint8_t* ws, const uint64_t* off,
-              hipStream_t s) {
-  SelectMulti sm;
-  DispatchMulti dm;
-  MulMulti mm;
-  int bpg[EFFORT_MAX_MULTI];
-  int64_t ntot = 0;
-  for (int32_t j = 0; j < count; ++j) ntot += g[j].n;
-  const int cus = cu_count();
-  for (int32_t j = 0; j < count; ++j) {
-    CallArgs c;
-    build_args(g[j], layouts[j], v, efforts[j], ys[j], ws + off[j], &c);
-    sm.a[j] = c.sa;
-    dm.a[j] = c.da;
-    mm.a[j] = c.ma;
-    const int64_t share = (int64_t)cus * g[j].n / ntot;
-    bpg[j] = (int)(share / g[j].G);
-    if (bpg[j] < 1) bpg[j] = 1;
-  }
-  if (hip_failed(launch_select_multi(sm, count, s))) return EFFORT_EHIP;
-  if (hip_failed(launch_dispatch_multi(dm, count, s))) return EFFORT_EHIP;
-  if (hip_failed(launch_bucketmul_multi(mm, count, bpg, s))) return EFFORT_EHIP;
   return EFFORT_OK;
 }
 
@@ -457,7 +490,9 @@ int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev
   }
   uint64_t off[EFFORT_MAX_MULTI];
   if (ws_bytes < multi_ws_offsets(g, count, off)) return EFFORT_ENOSPACE;
-  return run_multi(g, count, layouts, v_dev, efforts, ys, static_cast<uint8_t*>(ws_dev), off,
+  const float* vs[EFFORT_MAX_MULTI];
+  for (int32_t j = 0; j < count; ++j) vs[j] = v_dev;
+  return run_multi(g, count, layouts, vs, efforts, ys, static_cast<uint8_t*>(ws_dev), off,
                    static_cast<hipStream_t>(stream));
 }
 

@@ -314,8 +314,9 @@ def test_many_rows_few_columns(m, n):
                                        (4096, 14336, 0, 16, 16), (513, 2049, 3, 3, 16),
                                        (300, 1000, 0, 16, 5), (64, 8192, 1, 4, 8)])
 def test_batched_fused_matches_oracle(m, n, G, b, P):
-    """Fused batched path (passes of up to 8 vectors over the union of their read
-    lengths): every vector's exact cutoff bits, K and K' and y against the oracle."""
+    """Batched calls (up to 4 vectors: one multi-vector launch of each kernel;
+    from 5: passes of up to 8 vectors over the union of their read lengths):
+    every vector's exact cutoff bits, K and K' and y against the oracle."""
     d = dev()
     W, _ = case(m, n, seed=m + b, tag="fused")
     M = E.EffortMatrix(W, P=P, groups=G, device=d, batch=b)

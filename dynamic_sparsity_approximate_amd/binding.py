@@ -80,8 +80,8 @@ _PROTOS = {
     "effort_matvec": ([_D, _p, _p, _f32, _p, _p, _u64, _p], ctypes.c_int),
     "effort_matvec_batched": ([_D, _p, _p, _i32, _f32, _p, _p, _u64, _p], ctypes.c_int),
     "effort_workspace_bytes_multi": ([_D, _i32, ctypes.POINTER(_u64)], ctypes.c_int),
-    "effort_matvec_multi": ([_D, ctypes.POINTER(_p), _i32, _p, ctypes.POINTER(_f32),
-                             ctypes.POINTER(_p), _p, _u64, _p], ctypes.c_int),
+    "effort_matvec_multi": ([_D, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p),
+                             ctypes.POINTER(_f32), ctypes.POINTER(_p), _p, _u64, _p], ctypes.c_int),
     "effort_matvec_debug": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p, _p, _p, _p, _p, _p], ctypes.c_int),
     "effort_matvec_timed": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p], ctypes.c_int),
     "dense_gemv": ([_p, _p, _i64, _i64, _p, _p], ctypes.c_int),
@@ -233,16 +233,20 @@ def effort_workspace_bytes_multi(descs) -> int:
     return int(b.value)
 
 
-def effort_matvec_multi(descs, layouts, v, efforts, ys, ws, ws_bytes: int, stream=None):
-    """ys[j] = approximate v . W_j at efforts[j] (a float applies to all)."""
+def effort_matvec_multi(descs, layouts, vs, efforts, ys, ws, ws_bytes: int, stream=None):
+    """ys[j] = approximate vs[j] . W_j at efforts[j].  `vs` may be one vector
+    (shared by all matrices) and `efforts` one float (for all)."""
     n = len(descs)
+    if not isinstance(vs, (list, tuple)):
+        vs = [vs] * n
     if isinstance(efforts, (int, float)):
         efforts = [float(efforts)] * n
-    if not (len(layouts) == len(ys) == len(efforts) == n):
-        raise ValueError("descs, layouts, efforts and ys must have one entry per matrix")
+    if not (len(layouts) == len(vs) == len(ys) == len(efforts) == n):
+        raise ValueError("descs, layouts, vs, efforts and ys must have one entry per matrix")
     _check(_lib.effort_matvec_multi(_desc_array(descs), (_p * n)(*[_ptr(x) for x in layouts]), n,
-                                    _ptr(v), (_f32 * n)(*efforts), (_p * n)(*[_ptr(y) for y in ys]),
-                                    _ptr(ws), ws_bytes, _stream(stream)), "effort_matvec_multi")
+                                    (_p * n)(*[_ptr(v) for v in vs]), (_f32 * n)(*efforts),
+                                    (_p * n)(*[_ptr(y) for y in ys]), _ptr(ws), ws_bytes,
+                                    _stream(stream)), "effort_matvec_multi")
 
 
 def effort_matvec_debug(desc, layout, v, effort: float, y, ws, ws_bytes: int, cutoff=None, K=None,

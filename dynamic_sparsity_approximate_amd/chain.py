@@ -153,7 +153,8 @@ class MoEFFN:
     EffortMatrix, y = g0 * FFN_e0(x) + g1 * FFN_e1(x) with FFN(x) =
     (silu(x W1) * x W3) W2.  Only the two routed experts' layouts are read.
     With `grouped`, the four matrices that multiply x (w1 and w3 of both
-    routed experts) go through one multi-matrix call."""
+    routed experts) go through one multi-matrix call and the two w2 through
+    another (side streams are then not used)."""
 
     def __init__(self, experts, device, grouped: bool = False):
         import torch
@@ -173,6 +174,9 @@ class MoEFFN:
             d4 = [first[0].desc, first[1].desc] * 2
             self.ws_bytes = B.effort_workspace_bytes_multi(d4)
             self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)
+            d2 = [first[2].desc] * 2
+            self.ws2_bytes = B.effort_workspace_bytes_multi(d2)
+            self.ws2 = torch.zeros(self.ws2_bytes, dtype=torch.uint8, device=device)
 
     def enqueue(self, x, route, effort: float, stream=None, side_streams=None):
         """With `side_streams` (at least two torch streams), the two experts run
@@ -188,15 +192,11 @@ class MoEFFN:
             B.effort_matvec_multi([M.desc for M in mats], [M.layout for M in mats], x, effort,
                                   [self.h1[0], self.h3[0], self.h1[1], self.h3[1]], self.ws,
                                   self.ws_bytes, main)
-            for k, e in enumerate((e0, e1)):
-                ss = side_streams[k % ns] if ns >= 2 else main
-                if ss is not main:
-                    ss.wait_stream(main)
-                B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], ss)
-                self.experts[e][2].matvec(self.g[k], effort, self.o[k], ss)
-            if ns >= 2:
-                for ss in side_streams[:2]:
-                    main.wait_stream(ss)
+            for k in range(2):
+                B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], main)
+            w2s = [self.experts[e0][2], self.experts[e1][2]]
+            B.effort_matvec_multi([M.desc for M in w2s], [M.layout for M in w2s], self.g, effort,
+                                  self.o, self.ws2, self.ws2_bytes, main)
             B.effort_axpby(self.o[0], g0, self.o[1], g1, self.d_in, self.y, main)
             return self.y
         for k, e in enumerate((e0, e1)):

@@ -309,13 +309,12 @@ int check_multi(const effort_desc* descs, int32_t count, Geometry* g) {
   for (int32_t j = 0; j < count; ++j) {
     const int rc = check_desc(&descs[j], &g[j]);
     if (rc) return rc;
-    if (g[j].m != g[0].m) return EFFORT_EINVAL;  // one input vector for all
   }
   return EFFORT_OK;
 }
 
-// Several (matrix, vector) pairs -- matrices sharing v, or one matrix with
-// several vectors: each kernel launched once for all of them.
+// Several (matrix, vector) pairs -- matrices sharing v, one matrix with
+// several vectors, or any mix: each kernel launched once for all of them.
 // The multiply's CUs are shared out by output width (the kept bytes of each
 // matrix are about proportional to it at one effort), whole blocks per group.
 int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
@@ -472,26 +471,27 @@ int effort_workspace_bytes_multi(const effort_desc* descs, int32_t count, uint64
 }
 
 int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev, int32_t count,
-                        const float* v_dev, const float* efforts, float* const* ys_dev,
+                        const float* const* vs_dev, const float* efforts, float* const* ys_dev,
                         void* ws_dev, uint64_t ws_bytes, void* stream) {
   Geometry g[EFFORT_MAX_MULTI];
   int rc = check_multi(descs, count, g);
   if (rc) return rc;
-  if (!layouts_dev || !ys_dev || !efforts || !v_dev || !ws_dev) return EFFORT_EINVAL;
-  if (!aligned(ws_dev, 256) || !aligned(v_dev, 4)) return EFFORT_EINVAL;
+  if (!layouts_dev || !vs_dev || !ys_dev || !efforts || !ws_dev) return EFFORT_EINVAL;
+  if (!aligned(ws_dev, 256)) return EFFORT_EINVAL;
   const uint8_t* layouts[EFFORT_MAX_MULTI];
+  const float* vs[EFFORT_MAX_MULTI];
   float* ys[EFFORT_MAX_MULTI];
   for (int32_t j = 0; j < count; ++j) {
     if (!effort_ok(efforts[j])) return EFFORT_EINVAL;
-    if (!layouts_dev[j] || !ys_dev[j]) return EFFORT_EINVAL;
-    if (!aligned(layouts_dev[j], 256) || !aligned(ys_dev[j], 4)) return EFFORT_EINVAL;
+    if (!layouts_dev[j] || !vs_dev[j] || !ys_dev[j]) return EFFORT_EINVAL;
+    if (!aligned(layouts_dev[j], 256) || !aligned(vs_dev[j], 4) || !aligned(ys_dev[j], 4))
+      return EFFORT_EINVAL;
     layouts[j] = static_cast<const uint8_t*>(layouts_dev[j]);
+    vs[j] = vs_dev[j];
     ys[j] = ys_dev[j];
   }
   uint64_t off[EFFORT_MAX_MULTI];
   if (ws_bytes < multi_ws_offsets(g, count, off)) return EFFORT_ENOSPACE;
-  const float* vs[EFFORT_MAX_MULTI];
-  for (int32_t j = 0; j < count; ++j) vs[j] = v_dev;
   return run_multi(g, count, layouts, vs, efforts, ys, static_cast<uint8_t*>(ws_dev), off,
                    static_cast<hipStream_t>(stream));
 }

@@ -447,14 +447,23 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch(DispatchArgs a) {
 // Several matrices sharing v: blockIdx.y picks the matrix.
 template <int PM>
 __global__ __launch_bounds__(DSP_T) void k_dispatch_multi(DispatchMulti mm) {
-  dispatch_body<PM>(mm.a[blockIdx.y]);
+  const DispatchArgs& a = mm.a[blockIdx.y];
+  // past this matrix's rows (a taller one sized the grid): no rows, and no
+  // per-256-row sums to write (the matrix's sum array ends before this block)
+  if ((int64_t)blockIdx.x * DSP_T >= a.m) return;
+  dispatch_body<PM>(a);
 }
 
 hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) {
   if (count < 1 || count > EFFORT_MAX_MULTI) return hipErrorInvalidValue;
   int P = 0;
-  for (int j = 0; j < count; ++j) P = mm.a[j].P > P ? mm.a[j].P : P;
-  const dim3 grid((unsigned)((mm.a[0].m + CH_T - 1) / CH_T), (unsigned)count);
+  int64_t m = 0;
+  for (int j = 0; j < count; ++j) {
+    P = mm.a[j].P > P ? mm.a[j].P : P;
+    m = mm.a[j].m > m ? mm.a[j].m : m;
+  }
+  // sized for the tallest matrix; a shorter one's extra blocks hold no rows
+  const dim3 grid((unsigned)((m + CH_T - 1) / CH_T), (unsigned)count);
   if (P <= 16)
     hipLaunchKernelGGL(k_chart_hist_multi<16>, grid, dim3(CH_T), 0, s, mm);
   else
@@ -465,8 +474,13 @@ hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) 
 hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t s) {
   if (count < 1 || count > EFFORT_MAX_MULTI) return hipErrorInvalidValue;
   int P = 0;
-  for (int j = 0; j < count; ++j) P = mm.a[j].P > P ? mm.a[j].P : P;
-  const dim3 grid((unsigned)((mm.a[0].m + DSP_T - 1) / DSP_T), (unsigned)count);
+  int64_t m = 0;
+  for (int j = 0; j < count; ++j) {
+    P = mm.a[j].P > P ? mm.a[j].P : P;
+    m = mm.a[j].m > m ? mm.a[j].m : m;
+  }
+  // sized for the tallest matrix; a shorter one's extra blocks return at once
+  const dim3 grid((unsigned)((m + DSP_T - 1) / DSP_T), (unsigned)count);
   if (P <= 16)
     hipLaunchKernelGGL(k_dispatch_multi<16>, grid, dim3(DSP_T), 0, s, mm);
   else

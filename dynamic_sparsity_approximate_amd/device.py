@@ -90,28 +90,30 @@ class EffortMatrix:
 
 
 class EffortGroup:
-    """Matrices that share one input vector (all in_dim equal), multiplied by
-    one call: one launch of each kernel for all of them.  Holds its own
-    workspace; the matrices' layouts are shared, not copied."""
+    """Independent (matrix, vector) pairs multiplied by one call: one launch of
+    each kernel for all of them.  Holds its own workspace; the matrices'
+    layouts are shared, not copied."""
 
     def __init__(self, mats):
         import torch
 
         mats = list(mats)
-        if not mats or len({m.in_dim for m in mats}) != 1:
-            raise ValueError("an EffortGroup needs matrices with one in_dim")
+        if not mats:
+            raise ValueError("an EffortGroup needs at least one matrix")
         self.mats = mats
-        self.in_dim = mats[0].in_dim
         self.descs = [m.desc for m in mats]
         self.layouts = [m.layout for m in mats]
         self.ws_bytes = B.effort_workspace_bytes_multi(self.descs)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=mats[0].layout.device)
 
-    def matvec(self, v, efforts, ys=None, stream=None):
-        """ys[j] = approximate v . W_j at efforts[j] (a float applies to all)."""
+    def matvec(self, vs, efforts, ys=None, stream=None):
+        """ys[j] = approximate vs[j] . W_j at efforts[j]; `vs` may be one vector
+        shared by all matrices, `efforts` one float."""
         import torch
 
         if ys is None:
-            ys = [torch.empty(m.out_dim, dtype=torch.float32, device=v.device) for m in self.mats]
-        B.effort_matvec_multi(self.descs, self.layouts, v, efforts, ys, self.ws, self.ws_bytes, stream)
+            dev = (vs[0] if isinstance(vs, (list, tuple)) else vs).device
+            ys = [torch.empty(m.out_dim, dtype=torch.float32, device=dev) for m in self.mats]
+        B.effort_matvec_multi(self.descs, self.layouts, vs, efforts, ys, self.ws, self.ws_bytes,
+                              stream)
         return ys

@@ -155,20 +155,22 @@ int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const
                           int32_t batch, float effort, float* y_dev, void* ws_dev,
                           uint64_t ws_bytes, void* stream);
 
-/* Several matrices that share one input vector (a decode step multiplies a
-   layer's query, key and value matrices, and its gate and up projections, by
-   the same activation), each at its own effort ([HN], the author's reply to
-   refulgentis: effort can be set layer by layer and matrix by matrix):
-   ys_dev[j] = approximate v_dev . W_j at efforts[j] for j < count, each with
-   its own K, cutoff and kept set -- the result of count calls of
-   effort_matvec -- from one launch of each of the three kernels.
-   descs[count], layouts_dev[count], efforts[count], ys_dev[count]: host
-   arrays (the pointers in them are device pointers); all in_dim equal, else
-   EINVAL; 1 <= count <= EFFORT_MAX_MULTI; every effort in (0, 1].
-   ws >= effort_workspace_bytes_multi(descs, count). */
+/* Several independent (matrix, vector) pairs in one launch of each of the
+   three kernels: ys_dev[j] = approximate vs_dev[j] . W_j at efforts[j] for
+   j < count, each with its own K, cutoff and kept set -- the result of count
+   calls of effort_matvec.  For matrices that share an input (a decode step
+   multiplies a layer's query, key and value matrices, and its gate and up
+   projections, by one activation), pass the same vector for each; efforts may
+   differ per matrix ([HN], the author's reply to refulgentis: effort can be
+   set layer by layer and matrix by matrix).  The pairs must not depend on
+   each other's outputs.
+   descs, layouts_dev, vs_dev, efforts, ys_dev: host arrays of count entries
+   (the pointers in them are device pointers; vs_dev[j] holds
+   descs[j].in_dim floats); 1 <= count <= EFFORT_MAX_MULTI; every effort in
+   (0, 1].  ws >= effort_workspace_bytes_multi(descs, count). */
 int effort_workspace_bytes_multi(const effort_desc* descs, int32_t count, uint64_t* bytes);
 int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev, int32_t count,
-                        const float* v_dev, const float* efforts, float* const* ys_dev,
+                        const float* const* vs_dev, const float* efforts, float* const* ys_dev,
                         void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* effort_matvec plus parity outputs (all device pointers; each may be NULL):

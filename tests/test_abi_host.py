@@ -293,14 +293,13 @@ def test_multi_sizes_and_rejects():
     assert E.effort_workspace_bytes_multi(descs) == sum(up(b) for b in single)
     assert E.effort_workspace_bytes_multi(descs[:1]) == up(single[0])
     ws = E.effort_workspace_bytes_multi(descs)
-    good = dict(descs=descs, layouts=[FAKE] * 3, efforts=[0.25] * 3, ys=[FAKE] * 3, ws=FAKE,
-                ws_bytes=ws)
-    other_m = E.effort_prepare_host(rand_case(32, 64, seed=3)[0], 4)[0]
+    good = dict(descs=descs, layouts=[FAKE] * 3, vs=[FAKE] * 3, efforts=[0.25] * 3, ys=[FAKE] * 3,
+                ws=FAKE, ws_bytes=ws)
     cases = [
-        (dict(descs=descs + descs[:2], layouts=[FAKE] * 5, efforts=[0.25] * 5, ys=[FAKE] * 5),
-         B.EFFORT_EINVAL),  # more than EFFORT_MAX_MULTI
-        (dict(descs=[descs[0], other_m], layouts=[FAKE] * 2, efforts=[0.25] * 2, ys=[FAKE] * 2),
-         B.EFFORT_EINVAL),  # in_dim differs
+        (dict(descs=descs + descs[:2], layouts=[FAKE] * 5, vs=[FAKE] * 5, efforts=[0.25] * 5,
+              ys=[FAKE] * 5), B.EFFORT_EINVAL),  # more than EFFORT_MAX_MULTI
+        (dict(vs=[FAKE, None, FAKE]), B.EFFORT_EINVAL),
+        (dict(vs=[FAKE, FAKE + 2, FAKE]), B.EFFORT_EINVAL),
         (dict(efforts=[0.25, 0.0, 0.25]), B.EFFORT_EINVAL),
         (dict(efforts=[0.25, 0.25, float("nan")]), B.EFFORT_EINVAL),
         (dict(layouts=[FAKE, None, FAKE]), B.EFFORT_EINVAL),
@@ -313,7 +312,7 @@ def test_multi_sizes_and_rejects():
         a = dict(good)
         a.update(over)
         with pytest.raises(E.EffortError) as ei:
-            E.effort_matvec_multi(a["descs"], a["layouts"], FAKE, a["efforts"], a["ys"], a["ws"],
+            E.effort_matvec_multi(a["descs"], a["layouts"], a["vs"], a["efforts"], a["ys"], a["ws"],
                                   a["ws_bytes"])
         assert ei.value.code == code, over
     with pytest.raises(E.EffortError) as ei:

@@ -1,5 +1,6 @@
-"""GPU parity of the multi-matrix call (effort_matvec_multi): matrices that
-share one input vector, each at its own effort, in one launch per kernel.
+"""GPU parity of the multi-matrix call (effort_matvec_multi): independent
+(matrix, vector) pairs -- matrices sharing one input, or each with its own,
+of different heights -- each at its own effort, in one launch per kernel.
 
 Each output must equal the single-matrix call on the same matrix and vector
 (the same cutoff and kept set; only the order of the fp32 atomics of the
@@ -89,3 +90,29 @@ def test_multi_repeat_and_reuse():
         for j, (W, e) in enumerate(zip(Ws, efforts)):
             ref = oracle.run(W, oracle.probes(W, 16), v, e)
             assert rel_l2(ys[j].cpu().numpy(), ref["y"]) <= ORACLE_TOL, (k, j)
+
+
+def test_multi_own_inputs_and_heights():
+    """Pairs with their own vectors and different in_dim (the grid of the chart
+    and dispatch kernels is sized by the tallest; the others' extra blocks
+    must leave the rest of the workspace alone)."""
+    d = dev()
+    shapes = [(300, 1000), (2000, 256), (77, 4100), (1024, 64)]
+    efforts = [0.25, 0.5, 0.125, 1.0]
+    Ws = [synth.weights(m, n, seed=40 + j, stream=synth.stream_id("multi2", "W", m, n))
+          for j, (m, n) in enumerate(shapes)]
+    vs = [synth.activations(m, seed=50 + j, stream=synth.stream_id("multi2", "v", m))
+          for j, (m, n) in enumerate(shapes)]
+    mats = [E.EffortMatrix(W, P=16, device=d) for W in Ws]
+    group = E.EffortGroup(mats)
+    vts = [torch.from_numpy(v).to(d) for v in vs]
+    for rep in range(2):
+        ys = group.matvec(vts, efforts)
+        torch.cuda.synchronize()
+        for j, (W, v, e) in enumerate(zip(Ws, vs, efforts)):
+            y = ys[j].cpu().numpy()
+            y1 = mats[j].matvec(vts[j], e).cpu().numpy()
+            assert rel_l2(y, y1) <= SAME_TOL, (rep, j)
+            ref = oracle.run(W, oracle.probes(W, 16), v, e)
+            assert rel_l2(y, ref["y"]) <= ORACLE_TOL, (rep, j)
+        print("multi own inputs rep %d ok" % rep, flush=True)

@@ -112,6 +112,8 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   sa.result = result;
   sa.y = y;
   sa.n = g.n;
+  sa.bsum = bsum;
+  sa.bsum_words = (g.m + kDspRows - 1) / kDspRows * (g.G + 1);
   sa.vec_ws = 0;
 
   DispatchArgs& da = c->da;
@@ -225,6 +227,8 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
   sa.result = u32(0, w.result);
   sa.y = y;
   sa.n = g.n;
+  sa.bsum = u32(0, w.bsum);
+  sa.bsum_words = (g.m + kDspRows - 1) / kDspRows * (g.G + 1);
   sa.vec_ws = vec_ws;
   if (hip_failed(launch_select(sa, s, nullptr, batch))) return EFFORT_EHIP;
 

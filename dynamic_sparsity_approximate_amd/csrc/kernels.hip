@@ -186,6 +186,8 @@ __device__ __forceinline__ void chart_hist_body(const SelectArgs& a) {
     for (int b = tid; b < 1024; b += CH_T) a.hist2[b] = 0u;
     if (tid == 0) a.result[RES_NCAND] = 0u;
   }
+  for (int64_t j = (int64_t)blockIdx.x * CH_T + tid; j < a.bsum_words; j += (int64_t)gridDim.x * CH_T)
+    a.bsum[j] = 0u;
 }
 
 template <int PM>
@@ -197,6 +199,7 @@ __global__ __launch_bounds__(CH_T) void k_chart_hist(SelectArgs a) {
     a.hist += k * a.vec_ws;
     a.hist2 += k * a.vec_ws;
     a.result += k * a.vec_ws;
+    a.bsum += k * a.vec_ws;
   }
   chart_hist_body<PM>(a);
 }
@@ -454,6 +457,183 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_multi(DispatchMulti mm) {
   dispatch_body<PM>(a);
 }
 
+
+// The dispatch for P = 16 with the read lengths of every segment loaded up
+// front: a block holds QR = 64 rows of four lanes, lane s of a row holding
+// probes 4s .. 4s + 3 and the counts slices of those four segments, loaded
+// with the histogram, so no load waits for the bin b1 (the slice used, at
+// segment min(q, P - 1), is already in its lane's registers).  m / 64 blocks;
+// the per-256-row sums are accumulated with atomics into words the chart
+// kernel zeroed, and the candidate slots are reserved once per block.
+constexpr int QR = DSP_T / 4;  // rows per block
+static_assert(DSP_ROWS % QR == 0, "a block's rows lie in one 256-row block");
+constexpr int QG4 = 4;  // one 16-byte counts slice per segment (G4 = 4: up to 4 groups)
+
+__device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
+  constexpr int NW = DSP_T / 64;
+  __shared__ uint32_t tmp[NW + 1];
+  __shared__ uint32_t sres[2];
+  __shared__ uint32_t red[NW][QG4];
+  __shared__ float redf[NW];
+  __shared__ uint32_t sbase;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int sub = tid & 3;                                   // segments 4 sub .. 4 sub + 3
+  const int64_t i = (int64_t)blockIdx.x * QR + (tid >> 2);  // row
+  const bool valid = i < a.m;
+  const int G1 = a.G + 1;
+  const uint64_t capc = (uint64_t)a.m * (uint64_t)a.P;
+  // every load first: 16 histogram bins, the row's v and max key, this lane's
+  // four probe keys and four counts slices
+  const int hb = HIST_BINS - 16 * (tid + 1);  // bins hb .. hb + 15, thread 0 holds the top
+  uint32_t h[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 q4 = *reinterpret_cast<const uint4*>(a.hist + hb + 4 * c);
+    h[4 * c] = q4.x;
+    h[4 * c + 1] = q4.y;
+    h[4 * c + 2] = q4.z;
+    h[4 * c + 3] = q4.w;
+  }
+  float vi = 0.0f;
+  uint32_t rmax = 0u;
+  uint2 kq = make_uint2(0u, 0u);  // keys 4 sub .. 4 sub + 3, two per word
+  // the counts slices of the four segments (G4 = 4: one 16-byte word each)
+  uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0, c2 = c0, c3 = c0;
+  if (valid) {
+    vi = a.v[i];
+    rmax = a.rowmax[i];
+    kq = *reinterpret_cast<const uint2*>(a.probes + i * 16 + 4 * sub);
+    const uint4* cr = reinterpret_cast<const uint4*>(a.counts + ((size_t)i * 16 + 4 * sub) * 4);
+    c0 = cr[0];
+    c1 = cr[1];
+    c2 = cr[2];
+    c3 = cr[3];
+  }
+  uint32_t hs = 0;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) hs += h[t];
+  uint32_t tot;
+  uint32_t above = block_excl_scan<DSP_T>(hs, tmp, &tot);
+  if (above < a.K && a.K <= above + hs) {
+    // from the top bin down, the bins whose running total stays below K lie
+    // wholly above the K-th value: count them (no branches)
+    uint32_t acc = above, nb = 0u, before = above;
+#pragma unroll
+    for (int t = 15; t >= 0; --t) {
+      const uint32_t nxt = acc + h[t];
+      const bool below = nxt < a.K;
+      nb += below ? 1u : 0u;
+      before = below ? nxt : before;
+      acc = nxt;
+    }
+    sres[0] = (uint32_t)(hb + 15) - nb;
+    sres[1] = before;
+  }
+  __syncthreads();
+  const float av = fabsf(vi);
+  const uint32_t b1 = sres[0] & (HIST_BINS - 1);
+  const uint32_t above1 = sres[1];
+  const uint32_t lo_bits = b1 << HIST_SHIFT;
+  const uint32_t hi_bits = (b1 + 1u) << HIST_SHIFT;  // no chart reaches 2^31
+  // this lane's four chart values (probes do not increase with k: the kept
+  // segments of a row are 0 .. q - 1, the ones in bin b1 a range of them)
+  uint32_t bits[4];
+  bits[0] = __float_as_uint(__fmul_rn(av, h2f(kq.x)));
+  bits[1] = __float_as_uint(__fmul_rn(av, h2f(kq.x >> 16)));
+  bits[2] = __float_as_uint(__fmul_rn(av, h2f(kq.y)));
+  bits[3] = __float_as_uint(__fmul_rn(av, h2f(kq.y >> 16)));
+  uint32_t nk = 0u, nh = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    nk += valid && bits[k] >= lo_bits ? 1u : 0u;
+    nh += valid && bits[k] >= lo_bits && bits[k] < hi_bits ? 1u : 0u;
+  }
+  // the candidates' slots: one reservation per block, issued now so that its
+  // round trip overlaps the sums below; the values are stored last
+  const uint32_t cpos = block_excl_scan<DSP_T>(nh, tmp, &tot);
+  uint32_t ret = 0u;  // thread 0: the block's first slot, used (waited for) only at the end
+  if (tid == 0 && tot) ret = atomicAdd(&a.result[RES_NCAND], tot);
+  // q: the row's kept segments, summed over its four lanes
+  uint32_t q = nk;
+  q += (uint32_t)__shfl_xor((int)q, 1, 64);
+  q += (uint32_t)__shfl_xor((int)q, 2, 64);
+  const uint32_t qc = q < 16u ? q : 15u;
+  const bool none = !valid || __float_as_uint(__fmul_rn(av, h2f(rmax))) < lo_bits;
+  const bool owner = valid && (qc >> 2) == (uint32_t)sub;
+  const uint32_t kk = qc & 3u;
+  const uint4 x = kk == 0u ? c0 : kk == 1u ? c1 : kk == 2u ? c2 : c3;
+  const bool use = owner && !none;
+  const uint32_t L[4] = {use ? x.x : 0u, use ? x.y : 0u, use ? x.z : 0u, use ? x.w : 0u};
+  if (owner)
+#pragma unroll
+    for (int g = 0; g < QG4; ++g)
+      if (g < a.G) a.runlen[(size_t)g * a.m + i] = L[g];
+  // per-256-row sums: per wave, per block, then one atomic per column
+#pragma unroll
+  for (int g = 0; g < QG4; ++g)
+    if (g < a.G) {
+      const uint32_t sg = wave_sum(L[g]);
+      if (lane == 0) red[wid][g] = sg;
+    }
+  const float bnd = wave_sum_f(valid && sub == 0 ? av * h2f(rmax) : 0.0f);
+  if (lane == 0) redf[wid] = bnd;
+  __syncthreads();
+  const size_t brow = (size_t)((uint64_t)blockIdx.x * QR / DSP_ROWS) * G1;
+  if (tid < a.G) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += red[w][tid];
+    if (t) atomicAdd(&a.bsum[brow + tid], t);
+  } else if (tid == a.G) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += redf[w];
+    if (t != 0.0f) atomicAdd(reinterpret_cast<float*>(&a.bsum[brow + a.G]), t);
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    a.result[RES_BIN] = b1;
+    a.result[RES_ABOVE] = above1;
+  }
+  // last, the chart values in bin b1: into the candidate list and the
+  // refinement histogram of their bits 18..9
+  if (tid == 0) sbase = ret;
+  __syncthreads();
+  uint32_t base = sbase + cpos;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (valid && bits[k] >= lo_bits && bits[k] < hi_bits) {
+      if ((uint64_t)base < capc) a.cand[base] = bits[k];
+      ++base;
+      atomicAdd(&a.hist2[(bits[k] >> 9) & 1023u], 1u);
+    }
+  }
+}
+
+__global__ __launch_bounds__(DSP_T) void k_dispatch_quad(DispatchArgs a) {
+  if (blockIdx.y) {  // vector blockIdx.y of a batch
+    const uint64_t k = blockIdx.y;
+    a.v += k * a.m;
+    a.hist += k * a.vec_ws;
+    a.hist2 += k * a.vec_ws;
+    a.cand += k * a.vec_ws;
+    a.result += k * a.vec_ws;
+    a.runlen += k * a.vec_ws;
+    a.bsum += k * a.vec_ws;
+  }
+  dispatch_quad_body(a);
+}
+
+// whether the quad-lane dispatch serves these arguments
+static bool quad_dispatch(const DispatchArgs& a) { return a.P == 16 && a.G4 == QG4; }
+
+__global__ __launch_bounds__(DSP_T) void k_dispatch_quad_multi(DispatchMulti mm) {
+  const DispatchArgs& a = mm.a[blockIdx.y];
+  // past this matrix's rows (a taller one sized the grid): nothing to do
+  if ((int64_t)blockIdx.x * QR >= a.m) return;
+  dispatch_quad_body(a);
+}
+
 hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) {
   if (count < 1 || count > EFFORT_MAX_MULTI) return hipErrorInvalidValue;
   int P = 0;
@@ -479,6 +659,13 @@ hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t
     P = mm.a[j].P > P ? mm.a[j].P : P;
     m = mm.a[j].m > m ? mm.a[j].m : m;
   }
+  bool quad = true;
+  for (int j = 0; j < count; ++j) quad = quad && quad_dispatch(mm.a[j]);
+  if (quad) {
+    const dim3 gq((unsigned)((m + QR - 1) / QR), (unsigned)count);
+    hipLaunchKernelGGL(k_dispatch_quad_multi, gq, dim3(DSP_T), 0, s, mm);
+    return hipGetLastError();
+  }
   // sized for the tallest matrix; a shorter one's extra blocks return at once
   const dim3 grid((unsigned)((m + DSP_T - 1) / DSP_T), (unsigned)count);
   if (P <= 16)
@@ -489,6 +676,14 @@ hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
+  if (quad_dispatch(a)) {
+    const dim3 gq((unsigned)((a.m + QR - 1) / QR), (unsigned)nvec);
+    if (ev && ev->start)
+      hipExtLaunchKernelGGL(k_dispatch_quad, gq, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
+    else
+      hipLaunchKernelGGL(k_dispatch_quad, gq, dim3(DSP_T), 0, s, a);
+    return hipGetLastError();
+  }
   const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;
   const dim3 grid((unsigned)blocks, (unsigned)nvec);
   // probes in registers: 16 when they fit (the common P), else 32

@@ -21,6 +21,8 @@ struct SelectArgs {
   uint32_t* result;  // [3] candidate count, cleared here
   float* y;          // zeroed here (the multiply accumulates into it)
   int64_t n;
+  uint32_t* bsum;        // [bsum_words] zeroed here (the dispatch may accumulate into it)
+  int64_t bsum_words;
   // several vectors in one launch (grid y): vector k reads v + k m, writes
   // y + k n and uses the workspace words hist/hist2/result + k vec_ws
   uint64_t vec_ws;

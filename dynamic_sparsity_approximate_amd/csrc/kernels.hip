@@ -280,7 +280,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
   const int G1 = a.G + 1;
   // capacity of the candidate list: the count cannot exceed it when the select
   // kernel has reset it, and stores beyond it are dropped if it has not
-  const uint64_t capc = (uint64_t)a.m * (uint64_t)a.P;
+  const uint64_t capc = cand_capacity(a.m, a.P);
   // this thread's 16 histogram bins and the row's data, all loads issued
   // together (|v| is taken after the histogram loads are issued, so that its
   // wait does not hold them back)
@@ -465,7 +465,8 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_multi(DispatchMulti mm) {
 // segment min(q, P - 1), is already in its lane's registers).  m / 64 blocks;
 // the per-256-row sums are accumulated with atomics into words the chart
 // kernel zeroed, and the candidate slots are reserved once per block.
-constexpr int QR = DSP_T / 4;  // rows per block
+constexpr int QR = QUAD_ROWS;  // rows per block
+static_assert(QR == DSP_T / 4, "four lanes per row");
 static_assert(DSP_ROWS % QR == 0, "a block's rows lie in one 256-row block");
 constexpr int QG4 = 4;  // one 16-byte counts slice per segment (G4 = 4: up to 4 groups)
 
@@ -482,7 +483,8 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   const int64_t i = (int64_t)blockIdx.x * QR + (tid >> 2);  // row
   const bool valid = i < a.m;
   const int G1 = a.G + 1;
-  const uint64_t capc = (uint64_t)a.m * (uint64_t)a.P;
+  const uint64_t capc = cand_capacity(a.m, a.P);
+  const bool regions = cand_regions(a.P, a.G, a.m);
   // every load first: 16 histogram bins, the row's v and max key, this lane's
   // four probe keys and four counts slices
   const int hb = HIST_BINS - 16 * (tid + 1);  // bins hb .. hb + 15, thread 0 holds the top
@@ -553,7 +555,11 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   // round trip overlaps the sums below; the values are stored last
   const uint32_t cpos = block_excl_scan<DSP_T>(nh, tmp, &tot);
   uint32_t ret = 0u;  // thread 0: the block's first slot, used (waited for) only at the end
-  if (tid == 0 && tot) ret = atomicAdd(&a.result[RES_NCAND], tot);
+  if (regions) {
+    if (tid == 0) a.result[RES_RCOUNT + blockIdx.x] = tot;
+  } else if (tid == 0 && tot) {
+    ret = atomicAdd(&a.result[RES_NCAND], tot);
+  }
   // q: the row's kept segments, summed over its four lanes
   uint32_t q = nk;
   q += (uint32_t)__shfl_xor((int)q, 1, 64);
@@ -597,9 +603,14 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   }
   // last, the chart values in bin b1: into the candidate list and the
   // refinement histogram of their bits 18..9
-  if (tid == 0) sbase = ret;
-  __syncthreads();
-  uint32_t base = sbase + cpos;
+  uint32_t base;
+  if (regions) {
+    base = blockIdx.x * (uint32_t)RCAP + cpos;
+  } else {
+    if (tid == 0) sbase = ret;
+    __syncthreads();
+    base = sbase + cpos;
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (valid && bits[k] >= lo_bits && bits[k] < hi_bits) {
@@ -625,7 +636,7 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_quad(DispatchArgs a) {
 }
 
 // whether the quad-lane dispatch serves these arguments
-static bool quad_dispatch(const DispatchArgs& a) { return a.P == 16 && a.G4 == QG4; }
+static bool quad_dispatch(const DispatchArgs& a) { return quad_dispatch_ok(a.P, a.G); }
 
 __global__ __launch_bounds__(DSP_T) void k_dispatch_quad_multi(DispatchMulti mm) {
   const DispatchArgs& a = mm.a[blockIdx.y];
@@ -779,20 +790,89 @@ __device__ __forceinline__ void wave_locate(uint32_t count, uint32_t target, X x
   *before = acc;
 }
 
-// The exact cutoff, computed by one wave.  The dispatch found the bin b1 of the
-// K-th largest chart value (bits 30..19) and the count above1 of larger
-// values; the refinement histogram hist2 of the bin's values (bits 18..9)
-// gives the second digit, and the candidate values that share bits 30..9 give
-// the last nine bits through a 512-bin histogram in the wave's own LDS words
-// h3[512].  Radix selection: every step keeps the bin holding the remaining
-// rank, so the result is the K-th largest value itself.  Returns its bit
-// pattern; *kprime = the number of chart values >= it.  Wave-uniform.
+// Radix selection of the exact cutoff by one wave.  The dispatch found the
+// bin b1 of the K-th largest chart value (bits 30..19) and the count above1 of
+// larger values; the refinement histogram hist2 of the bin's values (bits
+// 18..9) gives the second digit, and the candidate values that share bits
+// 30..9 give the last nine bits through a 512-bin histogram in the wave's own
+// LDS words h3[512].  Every step keeps the bin holding the remaining rank, so
+// the result is the K-th largest value itself.
+
+// The second digit from the refinement histogram (lane l holds bins
+// [1008 - 16 l, 1024 - 16 l), lane 0 the top): every lane counts, from its top
+// bin down, the bins whose running total stays below K1 (selects, no
+// branches), and lane L's answer is kept.  Returns bits 30..9 of the cutoff;
+// *above2 counts the values above its bin within b1.  Wave-uniform.
+__device__ __forceinline__ uint32_t second_digit(const uint32_t* h, uint32_t b1, uint32_t K1,
+                                                 uint32_t* above2) {
+  const int lane = threadIdx.x & 63;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sum += h[k];
+  const uint32_t above = wave_incl_scan(sum) - sum;
+  const unsigned long long hit = __ballot(above < K1 && K1 <= above + sum);
+  const int L = __ffsll((long long)hit) - 1;
+  uint32_t acc = above, nb = 0u, before = above;
+#pragma unroll
+  for (int k = 15; k >= 0; --k) {
+    const uint32_t nxt = acc + h[k];
+    const bool below = nxt < K1;
+    nb += below ? 1u : 0u;
+    before = below ? nxt : before;
+    acc = nxt;
+  }
+  const uint32_t b2 = (uint32_t)__builtin_amdgcn_readlane((int)((uint32_t)(1008 - 16 * lane + 15) - nb), L);
+  *above2 = (uint32_t)__builtin_amdgcn_readlane((int)before, L);
+  return (b1 << 10) | b2;
+}
+
+// The last digit from h3 (filled by the caller with the matching candidates'
+// bits 8..0): returns the cutoff's bit pattern; *kprime = the number of chart
+// values >= it.  Wave-uniform.
+__device__ __forceinline__ uint32_t third_digit(const uint32_t* h3, uint32_t pre, uint32_t K2,
+                                                uint32_t above12, uint32_t* kprime) {
+  const int lane = threadIdx.x & 63;
+  // lane l holds bins [504 - 8 l, 512 - 8 l)
+  uint32_t g[8];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    g[k] = h3[504 - 8 * lane + k];
+    sum += g[k];
+  }
+  const uint32_t above = wave_incl_scan(sum) - sum;
+  const unsigned long long hit3 = __ballot(above < K2 && K2 <= above + sum);
+  const int L3 = __ffsll((long long)hit3) - 1;
+  // as for the second digit; c3 is the count of the first bin whose running
+  // total reaches K2
+  uint32_t acc = above, nb = 0u, before = above, c3 = 0u;
+  bool found = false;
+#pragma unroll
+  for (int k = 7; k >= 0; --k) {
+    const uint32_t nxt = acc + g[k];
+    const bool below = nxt < K2;
+    nb += below ? 1u : 0u;
+    before = below ? nxt : before;
+    c3 = !below && !found ? g[k] : c3;
+    found = found || !below;
+    acc = nxt;
+  }
+  const uint32_t b3 = (uint32_t)__builtin_amdgcn_readlane((int)((uint32_t)(504 - 8 * lane + 7) - nb), L3);
+  const uint32_t above3 = (uint32_t)__builtin_amdgcn_readlane((int)before, L3);
+  c3 = (uint32_t)__builtin_amdgcn_readlane((int)c3, L3);
+  *kprime = above12 + above3 + c3;
+  return (pre << 9) | b3;
+}
+
+// The candidates as one list of nc values (ncap: capacity of the first
+// loads, words past it read as zero).  The first CB * 64 are loaded with the
+// histogram, the next RB * 64 as soon as the count is known, so that their
+// round trip overlaps the second digit's work; more come in rounds.
 __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
                                       const uint32_t* __restrict__ cand, uint32_t ncap, uint32_t nc,
                                       uint32_t b1, uint32_t above1, uint32_t K, uint32_t* h3,
                                       uint32_t* kprime) {
   const int lane = threadIdx.x & 63;
-  // lane l holds refinement bins [1008 - 16 l, 1024 - 16 l): lane 0 the top
   uint32_t h[16];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -802,8 +882,6 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
     h[4 * c + 2] = q.z;
     h[4 * c + 3] = q.w;
   }
-  // the first CB * 64 candidates, loaded with the histogram (words past the
-  // list's capacity read as zero; those at p >= nc are ignored)
   constexpr int CB = 16;
   uint32_t cv[CB];
   {
@@ -814,9 +892,6 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) h3[k * 64 + lane] = 0u;
-  // the next RB * 64 candidates, issued as soon as the count is known so that
-  // their round trip overlaps the second digit's work (words at or past nc
-  // read as zero)
   constexpr int RB = 48;
   const bool more = nc > CB * 64u;
   uint32_t rv[RB];
@@ -827,36 +902,10 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
     for (int u = 0; u < RB; ++u)
       rv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, ((CB + u) * 64 + lane) * 4, 0, 0);
   }
-
-  // second digit: the bin holding rank K1 within b1, counted from the top.
-  // Every lane counts, from its top bin down, the bins whose running total
-  // stays below K1 (selects, no branches); lane L's answer is kept.
   const uint32_t K1 = K - above1;
-  uint32_t sum = 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) sum += h[k];
-  uint32_t above = wave_incl_scan(sum) - sum;
-  const unsigned long long hit = __ballot(above < K1 && K1 <= above + sum);
-  const int L = __ffsll((long long)hit) - 1;
-  uint32_t b2 = 0u, above2 = 0u;
-  {
-    uint32_t acc = above, nb = 0u, before = above;
-#pragma unroll
-    for (int k = 15; k >= 0; --k) {
-      const uint32_t nxt = acc + h[k];
-      const bool below = nxt < K1;
-      nb += below ? 1u : 0u;
-      before = below ? nxt : before;
-      acc = nxt;
-    }
-    b2 = (uint32_t)(1008 - 16 * lane + 15) - nb;
-    above2 = before;
-  }
-  b2 = (uint32_t)__builtin_amdgcn_readlane((int)b2, L);
-  above2 = (uint32_t)__builtin_amdgcn_readlane((int)above2, L);
+  uint32_t above2;
+  const uint32_t pre = second_digit(h, b1, K1, &above2);  // bits 30..9 of the cutoff
   const uint32_t K2 = K1 - above2;
-  const uint32_t pre = (b1 << 10) | b2;  // bits 30..9 of the cutoff
-
   // last digit: histogram of the matching candidates' bits 8..0
 #pragma unroll
   for (int u = 0; u < CB; ++u) {
@@ -883,41 +932,67 @@ __device__ uint32_t wave_exact_cutoff(const uint32_t* __restrict__ hist2,
       }
     }
   }
-  // lane l holds bins [504 - 8 l, 512 - 8 l)
-  uint32_t g[8];
-  sum = 0;
+  return third_digit(h3, pre, K2, above1 + above2, kprime);
+}
+
+// The candidates in nreg <= 64 regions of RCAP slots (region r: the chart
+// values in the cutoff's bin of dispatch block r, counts[r] of them).  Lane r
+// loads its region's count and first RSPEC slots with the histogram (one
+// round trip); a region with more takes further rounds.
+constexpr int RSPEC = 32;
+__device__ uint32_t wave_exact_cutoff_regions(const uint32_t* __restrict__ hist2,
+                                              const uint32_t* __restrict__ cand, uint32_t capw,
+                                              const uint32_t* __restrict__ counts, uint32_t nreg,
+                                              uint32_t b1, uint32_t above1, uint32_t K,
+                                              uint32_t* h3, uint32_t* kprime) {
+  const int lane = threadIdx.x & 63;
+  uint32_t h[16];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    g[k] = h3[504 - 8 * lane + k];
-    sum += g[k];
+  for (int c = 0; c < 4; ++c) {
+    const uint4 q = *reinterpret_cast<const uint4*>(hist2 + 1008 - 16 * lane + 4 * c);
+    h[4 * c] = q.x;
+    h[4 * c + 1] = q.y;
+    h[4 * c + 2] = q.z;
+    h[4 * c + 3] = q.w;
   }
-  above = wave_incl_scan(sum) - sum;
-  const unsigned long long hit3 = __ballot(above < K2 && K2 <= above + sum);
-  const int L3 = __ffsll((long long)hit3) - 1;
-  uint32_t b3 = 0u, above3 = 0u, c3 = 0u;
-  {
-    // as for the second digit; c3 is the count of the first bin whose running
-    // total reaches K2
-    uint32_t acc = above, nb = 0u, before = above;
-    bool found = false;
+  // counts past nreg read as zero, and so do slots past the list's capacity
+  const uint32_t rc = (uint32_t)lane < nreg ? counts[lane] : 0u;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cand, (short)0, (int)(capw * 4u), kBufferDword3);
+  const int rbase = lane * RCAP * 4;  // bytes
+  uint32_t cv[RSPEC];
 #pragma unroll
-    for (int k = 7; k >= 0; --k) {
-      const uint32_t nxt = acc + g[k];
-      const bool below = nxt < K2;
-      nb += below ? 1u : 0u;
-      before = below ? nxt : before;
-      c3 = !below && !found ? g[k] : c3;
-      found = found || !below;
-      acc = nxt;
+  for (int c = 0; c < RSPEC / 4; ++c) {
+    const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, rbase + c * 16, 0, 0);
+    cv[4 * c] = q[0];
+    cv[4 * c + 1] = q[1];
+    cv[4 * c + 2] = q[2];
+    cv[4 * c + 3] = q[3];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h3[k * 64 + lane] = 0u;
+  const uint32_t K1 = K - above1;
+  uint32_t above2;
+  const uint32_t pre = second_digit(h, b1, K1, &above2);  // bits 30..9 of the cutoff
+  const uint32_t K2 = K1 - above2;
+#pragma unroll
+  for (int u = 0; u < RSPEC; ++u)
+    if ((uint32_t)u < rc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
+  // regions with more than RSPEC candidates: RSPEC more per round
+  for (uint32_t s0 = RSPEC; __ballot(rc > s0); s0 += RSPEC) {
+#pragma unroll
+    for (int c = 0; c < RSPEC / 4; ++c) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, rbase + (int)(s0 * 4u) + c * 16, 0, 0);
+      cv[4 * c] = q[0];
+      cv[4 * c + 1] = q[1];
+      cv[4 * c + 2] = q[2];
+      cv[4 * c + 3] = q[3];
     }
-    b3 = (uint32_t)(504 - 8 * lane + 7) - nb;
-    above3 = before;
+#pragma unroll
+    for (int u = 0; u < RSPEC; ++u)
+      if (s0 + (uint32_t)u < rc && (cv[u] >> 9) == pre) atomicAdd(&h3[cv[u] & 511u], 1u);
   }
-  b3 = (uint32_t)__builtin_amdgcn_readlane((int)b3, L3);
-  above3 = (uint32_t)__builtin_amdgcn_readlane((int)above3, L3);
-  c3 = (uint32_t)__builtin_amdgcn_readlane((int)c3, L3);
-  *kprime = above1 + above2 + above3 + c3;
-  return (pre << 9) | b3;
+  return third_digit(h3, pre, K2, above1 + above2, kprime);
 }
 
 // Where share wave j's part of a block's entries starts, in 128ths of them.
@@ -1029,13 +1104,18 @@ __device__ __forceinline__ void bucketmul_body(
     const uint64_t vo = (uint64_t)wid * a.vec_ws;
     const uint32_t* res = result + vo;
     const uint32_t b1 = res[RES_BIN], above1 = res[RES_ABOVE];
-    const uint64_t cap = (uint64_t)a.m * (uint64_t)a.P;
-    // the count never exceeds the list's capacity; clamped so that no read can
-    const uint32_t nc = (uint32_t)min((uint64_t)res[RES_NCAND], cap);
-    const uint32_t ncap = (uint32_t)(cap < 1024u ? cap : 1024u);
-    uint32_t kp;
-    const uint32_t cut =
-        wave_exact_cutoff(a.hist2 + vo, a.cand + vo, ncap, nc, b1, above1, a.K, h3w[wid], &kp);
+    const uint64_t cap = cand_capacity(a.m, a.P);
+    uint32_t kp, cut;
+    if (cand_regions(a.P, a.G, a.m)) {  // the same test the dispatch made
+      const uint32_t nreg = (uint32_t)((a.m + QUAD_ROWS - 1) / QUAD_ROWS);
+      cut = wave_exact_cutoff_regions(a.hist2 + vo, a.cand + vo, (uint32_t)cap, res + RES_RCOUNT,
+                                      nreg, b1, above1, a.K, h3w[wid], &kp);
+    } else {
+      // the count never exceeds the list's capacity; clamped so that no read can
+      const uint32_t nc = (uint32_t)min((uint64_t)res[RES_NCAND], cap);
+      const uint32_t ncap = (uint32_t)(cap < 1024u ? cap : 1024u);
+      cut = wave_exact_cutoff(a.hist2 + vo, a.cand + vo, ncap, nc, b1, above1, a.K, h3w[wid], &kp);
+    }
     if (lane == 0) {
       sCut[wid] = cut;
       if (bid == 0) {

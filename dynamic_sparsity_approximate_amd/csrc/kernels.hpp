@@ -31,6 +31,26 @@ struct SelectArgs {
 // result words of the workspace
 constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN = 4, RES_ABOVE = 5;
 
+// The quad-lane dispatch (P = 16, at most 4 column groups) takes QUAD_ROWS
+// rows per block.  When its blocks number at most 64 (in_dim <= 4096), block r
+// keeps the chart values in the cutoff's bin in a region of RCAP candidate
+// slots of its own, from slot r * RCAP, and their count in result word
+// RES_RCOUNT + r: no slot reservation.  Otherwise the candidates form one list
+// of result[RES_NCAND] values.
+constexpr int QUAD_ROWS = 64;
+constexpr int RCAP = QUAD_ROWS * 16;
+constexpr int RES_RCOUNT = 64;  // 64 region counts after the 64 result words
+__host__ __device__ inline bool quad_dispatch_ok(int32_t P, int32_t G) {
+  return P == 16 && G >= 1 && G <= 4;
+}
+__host__ __device__ inline bool cand_regions(int32_t P, int32_t G, int64_t m) {
+  return quad_dispatch_ok(P, G) && m <= 64 * QUAD_ROWS;
+}
+// words of the candidate list: in_dim rounded up to QUAD_ROWS, times P
+__host__ __device__ inline uint64_t cand_capacity(int64_t m, int32_t P) {
+  return (uint64_t)((m + QUAD_ROWS - 1) / QUAD_ROWS * QUAD_ROWS) * (uint64_t)P;
+}
+
 // Dispatch: per (group, row) read length from a lower bound of the cutoff (the
 // low edge of the histogram bin b1 that holds the K-th largest chart value),
 // per block of DSP_ROWS rows the sum of the read lengths of each group and the

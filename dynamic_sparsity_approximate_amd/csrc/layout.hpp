@@ -78,10 +78,11 @@ inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geomet
 }
 
 // Workspace of one vector (offsets in bytes from the vector's slice start).
-//   result   u32[64]                  [0] cutoff bits, [1] K', [2] K, [3] candidates
+//   result   u32[128]                 [0] cutoff bits, [1] K', [2] K, [3] candidates,
+//                                     [64 + r] candidates of dispatch block r (regions)
 //   hist     u32[4096]                histogram of the chart's top 12 bits
 //   hist2    u32[1024]                bits 18..9 of the chart values in the cutoff's bin
-//   cand     u32[m*P]                 those chart values (bit patterns)
+//   cand     u32[ceil(m/64)*64*P]     those chart values (bit patterns)
 //   runlen   u32[G][m]                per (group, row) entries to read
 //   bsum     u32[ceil(m/256)][G + 1]  per 256 rows: sum of runlen per group, then
 //                                     (as f32) the sum of |v_i| * rowmax_i
@@ -101,10 +102,11 @@ inline WsLayout ws_layout(const Geometry& g) {
   const uint64_t nbd = ((uint64_t)g.m + kDspRows - 1) / kDspRows;
   WsLayout w;
   w.result = 0;
-  w.hist = 256;
+  w.hist = 512;
   w.hist2 = w.hist + 4096 * 4;
   w.cand = align_up(w.hist2 + 1024 * 4, kAlign);
-  w.runlen = align_up(w.cand + (uint64_t)g.m * g.P * 4, kAlign);
+  // the candidate capacity: m rounded up to 64 rows (a dispatch block), times P
+  w.runlen = align_up(w.cand + (uint64_t)((g.m + 63) / 64 * 64) * g.P * 4, kAlign);
   w.bsum = align_up(w.runlen + (uint64_t)g.G * g.m * 4, kAlign);
   w.slice = align_up(w.bsum + nbd * (g.G + 1) * 4, kAlign);
   w.urunlen = 0;  // offsets from the end of the slices

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "effort.h"
 #include "kernels.hpp"
 #include "layout.hpp"
@@ -28,16 +30,21 @@ bool hip_failed(hipError_t e) {
   t_last_hip_error = e;
   return true;
 }
-int g_cu_count[kMaxDevices];  // device property cache (immutable per device)
+// Device property cache (immutable per device; threads may fill it concurrently
+// with the same value).
+std::atomic<int> g_cu_count[kMaxDevices];
 
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  if (dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  if (dev < kMaxDevices) g_cu_count[dev] = cus;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

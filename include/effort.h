@@ -24,13 +24,17 @@
  * Conventions for every function:
  *  - returns int: EFFORT_OK (0) or an error code; effort_strerror() names it.
  *  - pointers are plain host or device pointers as stated per argument; the
- *    caller owns all memory.  The library never allocates device memory and
- *    keeps no global mutable state.
+ *    caller owns all memory.  The library never allocates device memory; its
+ *    only global state is a cache of each device's CU count and, per host
+ *    thread, the last failed HIP status (effort_last_hip_error).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device
  *    work is stream-ordered and asynchronous unless stated otherwise.
  *  - every argument is validated on the host before anything is enqueued, so
  *    EINVAL / ENOSPACE / ECORRUPT leave the stream untouched.
- *  - device pointers must be 16-byte aligned; the layout 256-byte aligned.
+ *  - alignment: layouts and workspaces 256 bytes; float and int32 arrays 4
+ *    bytes, 64-bit outputs 8 bytes, fp16 weights 2 bytes (16-byte aligned
+ *    vectors let the multiply load them 16 bytes at a time).  A misaligned
+ *    pointer is EFFORT_EINVAL.
  */
 #ifndef EFFORT_H
 #define EFFORT_H

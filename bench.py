@@ -53,12 +53,14 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["full", "effort", "dense", "copy", "sweep", "batched",
-                                       "decode", "moe", "mallcheck"], default="full",
+                                       "decode", "moe", "moetraffic", "mallcheck"], default="full",
                     help="effort/dense: time only that path (for profiler runs); copy: plain "
                          "1 GiB device copies for counter calibration; sweep: the four "
                          "Mistral-7B shapes at efforts 1/.5/.25/.125; batched: b = 1..16 "
                          "vectors against the dense small GEMM; decode: a whole Mistral-7B-"
-                         "shaped decode step; moe: a Mixtral-shaped expert block; mallcheck: "
+                         "shaped decode step; moe: a Mixtral-shaped expert block; moetraffic: "
+                         "a few tokens of the grouped expert block and the kept bytes of their "
+                         "six matvecs (for a FETCH_SIZE counter run); mallcheck: "
                          "kernel times with layout rotation, after a cache-evicting write, and warm")
     ap.add_argument("--layers", type=int, default=32, help="decode mode: decoder layers")
     ap.add_argument("--streams", type=int, default=6,
@@ -533,6 +535,53 @@ def run_moe(args, torch, np, E, synth, dev):
                       "%d tokens" % tokens, "dense_us_per_token": round(dus, 1), "points": points}))
 
 
+def run_moetraffic(args, torch, np, E, synth, dev):
+    """What the expert block reads against what the two routed experts keep:
+    `tokens` grouped expert-block calls (the only launches of the *_multi
+    kernels, so a FETCH_SIZE counter run can sum exactly their reads), then,
+    through the recording entry point on the inputs those calls used, the kept
+    products of each of the six matvecs.  Per token it prints the kept bytes
+    (4 per kept entry) and the method's algorithmic bytes (kept bytes + 2mP
+    probes + 4m v + 4n y per matvec); the layouts of all 8 experts hold four
+    times the two routed experts' entries."""
+    d, h = MISTRAL["dim"], MISTRAL["hidden"]
+    effort, tokens = 0.25, 4
+    experts = []
+    for e in range(8):
+        Ws = [synth.matrix("config3", d, h, seed=0, expert=e, w="w1"),
+              synth.matrix("config3", d, h, seed=0, expert=e, w="w3"),
+              synth.matrix("config3", h, d, seed=0, expert=e, w="w2")]
+        experts.append(tuple(E.EffortMatrix(W, P=args.P, device=dev) for W in Ws))
+        log("expert %d prepared" % e)
+    gmoe = E.MoEFFN(experts, dev, grouped=True)
+    xs = [torch.from_numpy(synth.vector("config3/x", d, seed=t)).to(dev) for t in range(tokens)]
+    routes = [E.route_top2(synth.normals(8, seed=t, stream=synth.stream_id("config3/router")))
+              for t in range(tokens)]
+    torch.cuda.synchronize()
+    w2_inputs = []
+    for t in range(tokens):  # the counted calls
+        gmoe.enqueue(xs[t], routes[t], effort)
+        torch.cuda.synchronize()
+        w2_inputs.append([g.clone() for g in gmoe.g])
+    rows = []
+    for t in range(tokens):
+        e0, e1 = routes[t][0], routes[t][1]
+        kept = alg = 0
+        for k, e in enumerate((e0, e1)):
+            w1, w3, w2 = experts[e]
+            for M, v in ((w1, xs[t]), (w3, xs[t]), (w2, w2_inputs[t][k])):
+                kk = M.matvec_debug(v, effort, with_mask=False)["total_kept"]
+                kept += kk
+                alg += 4 * kk + 2 * M.in_dim * args.P + 4 * M.in_dim + 4 * M.out_dim
+        rows.append({"token": t, "experts": [int(e0), int(e1)], "kept_bytes": 4 * kept,
+                     "alg_bytes": alg})
+        log(json.dumps(rows[-1]))
+    print(json.dumps({"mode": "moetraffic", "workload": "Mixtral-shaped expert block, 8 experts, "
+                      "top-2, grouped calls, effort %g, %d tokens" % (effort, tokens),
+                      "kernels": "k_chart_hist_multi, k_dispatch*_multi, k_bucketmul_multi, "
+                      "k_silu_mul, k_axpby", "points": rows}))
+
+
 def run_mallcheck(args, torch, np, E, synth, dev):
     """Cross-check of the rotation rule against the 256 MB Infinity Cache: the
     three kernels' own durations (event pairs stamped by each kernel) for calls
@@ -581,7 +630,7 @@ def run_mallcheck(args, torch, np, E, synth, dev):
 
 
 EXTRA_MODES = {"sweep": run_sweep, "batched": run_batched, "decode": run_decode, "moe": run_moe,
-               "mallcheck": run_mallcheck}
+               "moetraffic": run_moetraffic, "mallcheck": run_mallcheck}
 
 
 if __name__ == "__main__":

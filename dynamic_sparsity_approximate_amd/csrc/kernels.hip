@@ -465,12 +465,16 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_multi(DispatchMulti mm) {
 // segment min(q, P - 1), is already in its lane's registers).  m / 64 blocks;
 // the per-256-row sums are accumulated with atomics into words the chart
 // kernel zeroed, and the candidate slots are reserved once per block.
+// QG4: words of a counts slice (G4), 4 for up to 4 column groups, 8 for up
+// to 8; a segment's slice is QG4 / 4 16-byte words.
 constexpr int QR = QUAD_ROWS;  // rows per block
 static_assert(QR == DSP_T / 4, "four lanes per row");
 static_assert(DSP_ROWS % QR == 0, "a block's rows lie in one 256-row block");
-constexpr int QG4 = 4;  // one 16-byte counts slice per segment (G4 = 4: up to 4 groups)
 
+template <int QG4>
 __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
+  static_assert(QG4 == 4 || QG4 == 8, "counts slices of 4 or 8 words");
+  constexpr int QH = QG4 / 4;  // 16-byte words per segment slice
   constexpr int NW = DSP_T / 64;
   __shared__ uint32_t tmp[NW + 1];
   __shared__ uint32_t sres[2];
@@ -500,17 +504,26 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   float vi = 0.0f;
   uint32_t rmax = 0u;
   uint2 kq = make_uint2(0u, 0u);  // keys 4 sub .. 4 sub + 3, two per word
-  // the counts slices of the four segments (G4 = 4: one 16-byte word each)
+  // the counts slices of the four segments: words 0..3 of segment j in cj,
+  // words 4..7 (8 groups) in cjh -- named values, not arrays, so that the
+  // selection below stays in registers
   uint4 c0 = make_uint4(0u, 0u, 0u, 0u), c1 = c0, c2 = c0, c3 = c0;
+  uint4 c0h = c0, c1h = c0, c2h = c0, c3h = c0;
   if (valid) {
     vi = a.v[i];
     rmax = a.rowmax[i];
     kq = *reinterpret_cast<const uint2*>(a.probes + i * 16 + 4 * sub);
-    const uint4* cr = reinterpret_cast<const uint4*>(a.counts + ((size_t)i * 16 + 4 * sub) * 4);
+    const uint4* cr = reinterpret_cast<const uint4*>(a.counts + ((size_t)i * 16 + 4 * sub) * QG4);
     c0 = cr[0];
-    c1 = cr[1];
-    c2 = cr[2];
-    c3 = cr[3];
+    c1 = cr[QH];
+    c2 = cr[2 * QH];
+    c3 = cr[3 * QH];
+    if constexpr (QH == 2) {
+      c0h = cr[1];
+      c1h = cr[QH + 1];
+      c2h = cr[2 * QH + 1];
+      c3h = cr[3 * QH + 1];
+    }
   }
   uint32_t hs = 0;
 #pragma unroll
@@ -568,9 +581,20 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   const bool none = !valid || __float_as_uint(__fmul_rn(av, h2f(rmax))) < lo_bits;
   const bool owner = valid && (qc >> 2) == (uint32_t)sub;
   const uint32_t kk = qc & 3u;
-  const uint4 x = kk == 0u ? c0 : kk == 1u ? c1 : kk == 2u ? c2 : c3;
   const bool use = owner && !none;
-  const uint32_t L[4] = {use ? x.x : 0u, use ? x.y : 0u, use ? x.z : 0u, use ? x.w : 0u};
+  uint32_t L[QG4];
+  const uint4 x = kk == 0u ? c0 : kk == 1u ? c1 : kk == 2u ? c2 : c3;
+  L[0] = use ? x.x : 0u;
+  L[1] = use ? x.y : 0u;
+  L[2] = use ? x.z : 0u;
+  L[3] = use ? x.w : 0u;
+  if constexpr (QH == 2) {
+    const uint4 xh = kk == 0u ? c0h : kk == 1u ? c1h : kk == 2u ? c2h : c3h;
+    L[4] = use ? xh.x : 0u;
+    L[5] = use ? xh.y : 0u;
+    L[6] = use ? xh.z : 0u;
+    L[7] = use ? xh.w : 0u;
+  }
   if (owner)
 #pragma unroll
     for (int g = 0; g < QG4; ++g)
@@ -621,6 +645,7 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   }
 }
 
+template <int QG4>
 __global__ __launch_bounds__(DSP_T) void k_dispatch_quad(DispatchArgs a) {
   if (blockIdx.y) {  // vector blockIdx.y of a batch
     const uint64_t k = blockIdx.y;
@@ -632,17 +657,20 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_quad(DispatchArgs a) {
     a.runlen += k * a.vec_ws;
     a.bsum += k * a.vec_ws;
   }
-  dispatch_quad_body(a);
+  dispatch_quad_body<QG4>(a);
 }
 
-// whether the quad-lane dispatch serves these arguments
+// whether the quad-lane dispatch serves these arguments (G4 is 4 or 8 then)
 static bool quad_dispatch(const DispatchArgs& a) { return quad_dispatch_ok(a.P, a.G); }
 
 __global__ __launch_bounds__(DSP_T) void k_dispatch_quad_multi(DispatchMulti mm) {
   const DispatchArgs& a = mm.a[blockIdx.y];
   // past this matrix's rows (a taller one sized the grid): nothing to do
   if ((int64_t)blockIdx.x * QR >= a.m) return;
-  dispatch_quad_body(a);
+  if (a.G4 == 4)
+    dispatch_quad_body<4>(a);
+  else
+    dispatch_quad_body<8>(a);
 }
 
 hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) {
@@ -689,10 +717,11 @@ hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
   if (quad_dispatch(a)) {
     const dim3 gq((unsigned)((a.m + QR - 1) / QR), (unsigned)nvec);
+    auto kern = a.G4 == 4 ? k_dispatch_quad<4> : k_dispatch_quad<8>;
     if (ev && ev->start)
-      hipExtLaunchKernelGGL(k_dispatch_quad, gq, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
+      hipExtLaunchKernelGGL(kern, gq, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
     else
-      hipLaunchKernelGGL(k_dispatch_quad, gq, dim3(DSP_T), 0, s, a);
+      hipLaunchKernelGGL(kern, gq, dim3(DSP_T), 0, s, a);
     return hipGetLastError();
   }
   const int64_t blocks = (a.m + DSP_T - 1) / DSP_T;

@@ -31,7 +31,7 @@ struct SelectArgs {
 // result words of the workspace
 constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN = 4, RES_ABOVE = 5;
 
-// The quad-lane dispatch (P = 16, at most 4 column groups) takes QUAD_ROWS
+// The quad-lane dispatch (P = 16, at most 8 column groups) takes QUAD_ROWS
 // rows per block.  When its blocks number at most 64 (in_dim <= 4096), block r
 // keeps the chart values in the cutoff's bin in a region of RCAP candidate
 // slots of its own, from slot r * RCAP, and their count in result word
@@ -41,7 +41,7 @@ constexpr int QUAD_ROWS = 64;
 constexpr int RCAP = QUAD_ROWS * 16;
 constexpr int RES_RCOUNT = 64;  // 64 region counts after the 64 result words
 __host__ __device__ inline bool quad_dispatch_ok(int32_t P, int32_t G) {
-  return P == 16 && G >= 1 && G <= 4;
+  return P == 16 && G >= 1 && G <= 8;
 }
 __host__ __device__ inline bool cand_regions(int32_t P, int32_t G, int64_t m) {
   return quad_dispatch_ok(P, G) && m <= 64 * QUAD_ROWS;

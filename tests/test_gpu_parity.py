@@ -103,7 +103,8 @@ def test_config0(P, effort):
 
 @pytest.mark.parametrize("m,n,P,G", [(300, 1000, 16, 0), (1, 1, 1, 0), (7, 65, 3, 2),
                                      (513, 2049, 16, 3), (64, 8192, 8, 1), (100, 100, 100, 0),
-                                     (2, 5000, 5, 0), (1000, 3, 2, 0), (257, 300, 16, 5)])
+                                     (2, 5000, 5, 0), (1000, 3, 2, 0), (257, 300, 16, 5),
+                                     (600, 4000, 16, 8), (1000, 9000, 16, 6)])
 @pytest.mark.parametrize("effort", [0.05, 0.3, 1.0])
 def test_ragged_shapes(m, n, P, G, effort):
     W, v = case(m, n, seed=m + n, tag="ragged")

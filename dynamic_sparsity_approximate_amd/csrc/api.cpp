@@ -354,12 +354,16 @@ int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
   return EFFORT_OK;
 }
 
-// Batches from this size read the union of the vectors' read lengths once
-// (run_batched); smaller ones run each vector's own multiply, up to four in
-// one launch of each kernel (4096x14336, effort 0.25: 40.6 / 62.3 us at
-// b = 2 / 4 against 46.7 / 70.9 us for the union pass; 123 against 122 us at
-// b = 8 in two launches).
+// Batches from kUnionMinBatch vectors at an effort of at least
+// kUnionMinEffort read the union of the vectors' read lengths once
+// (run_batched); other batches run each vector's own multiply, up to four in
+// one launch of each kernel.  At 4096x14336: b = 2 / 4 at effort 0.25 take
+// 40.6 / 62.3 us against 46.7 / 70.9 us for the union pass; b = 8 in two
+// launches of four against one union pass takes 301 / 121 / 86 us against
+// 168 / 123 / 106 us at effort 1 / 0.25 / 0.125 (the union of low-effort
+// prefixes is long compared with each one).
 constexpr int32_t kUnionMinBatch = 5;
+constexpr float kUnionMinEffort = 0.25f;
 
 int matvec_common(const effort_desc* desc, const void* layout_dev, const float* v_dev, int32_t batch,
                   float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream,
@@ -392,7 +396,7 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* layout = static_cast<const uint8_t*>(layout_dev);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  if (batch > 1 && !dbg && !events && batch >= kUnionMinBatch &&
+  if (batch > 1 && !dbg && !events && batch >= kUnionMinBatch && effort >= kUnionMinEffort &&
       bucketmul_pass_width(g.TW, batch) > 0)
     return run_batched(g, layout, v_dev, batch, effort, y_dev, ws, s);
   if (batch > 1 && !dbg && !events) {

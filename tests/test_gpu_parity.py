@@ -311,19 +311,21 @@ def test_many_rows_few_columns(m, n):
     run_pair(W, v, 16, 0.25, with_mask=False, where="tall")
 
 
-@pytest.mark.parametrize("m,n,G,b,P", [(4096, 14336, 0, 2, 16), (4096, 14336, 0, 9, 16),
-                                       (4096, 14336, 0, 16, 16), (513, 2049, 3, 3, 16),
-                                       (300, 1000, 0, 16, 5), (64, 8192, 1, 4, 8)])
-def test_batched_fused_matches_oracle(m, n, G, b, P):
-    """Batched calls (up to 4 vectors: one multi-vector launch of each kernel;
-    from 5: passes of up to 8 vectors over the union of their read lengths):
-    every vector's exact cutoff bits, K and K' and y against the oracle."""
+@pytest.mark.parametrize("m,n,G,b,P,effort", [(4096, 14336, 0, 2, 16, 0.25), (4096, 14336, 0, 9, 16, 0.25),
+                                              (4096, 14336, 0, 16, 16, 0.25), (513, 2049, 3, 3, 16, 0.25),
+                                              (300, 1000, 0, 16, 5, 0.25), (64, 8192, 1, 4, 8, 0.25),
+                                              (513, 2049, 3, 7, 16, 0.1), (300, 1000, 0, 16, 5, 0.5)])
+def test_batched_fused_matches_oracle(m, n, G, b, P, effort):
+    """Batched calls (up to 4 vectors, or any number below effort 0.25: launches
+    of up to 4 vectors, each with its own multiply; from 5 vectors at effort
+    0.25 and above: passes of up to 8 vectors over the union of their read
+    lengths): every vector's exact cutoff bits, K and K' and y against the
+    oracle."""
     d = dev()
     W, _ = case(m, n, seed=m + b, tag="fused")
     M = E.EffortMatrix(W, P=P, groups=G, device=d, batch=b)
     V = np.stack([synth.vector("fused", m, seed=s) for s in range(b)])
     V[1 % b] *= 7.0  # vectors of different scale in one pass
-    effort = 0.25
     Y = M.matvec_batched(torch.from_numpy(V).to(d), effort)
     torch.cuda.synchronize()
     pr = oracle.probes(W, P)
@@ -336,7 +338,7 @@ def test_batched_fused_matches_oracle(m, n, G, b, P):
         assert res[2] == ref["K"] and res[1] == ref["Kprime"], k
         err = rel_l2(Y[k].cpu().numpy(), ref["y"])
         assert err <= REL_L2_TOL, (k, err)
-    say("fused %dx%d G=%d b=%d ok" % (m, n, M.groups, b))
+    say("fused %dx%d G=%d b=%d effort=%g ok" % (m, n, M.groups, b, effort))
     # a second call on the same workspace gives the same result
     Y2 = M.matvec_batched(torch.from_numpy(V).to(d), effort)
     torch.cuda.synchronize()

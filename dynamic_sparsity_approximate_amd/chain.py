@@ -153,8 +153,9 @@ class MoEFFN:
     EffortMatrix, y = g0 * FFN_e0(x) + g1 * FFN_e1(x) with FFN(x) =
     (silu(x W1) * x W3) W2.  Only the two routed experts' layouts are read.
     With `grouped`, the four matrices that multiply x (w1 and w3 of both
-    routed experts) go through one multi-matrix call and the two w2 through
-    another (side streams are then not used)."""
+    routed experts) go through one multi-matrix call, one gate call covers
+    both experts and the two w2 go through another multi-matrix call (side
+    streams are then not used)."""
 
     def __init__(self, experts, device, grouped: bool = False):
         import torch
@@ -164,9 +165,12 @@ class MoEFFN:
         d_in, d_hid = first[0].in_dim, first[0].out_dim
         self.d_in, self.d_hid = d_in, d_hid
         mk = lambda n: torch.empty(n, dtype=torch.float32, device=device)  # noqa: E731
-        self.h1 = [mk(d_hid), mk(d_hid)]
-        self.h3 = [mk(d_hid), mk(d_hid)]
-        self.g = [mk(d_hid), mk(d_hid)]
+        # both experts' hidden vectors side by side, so that one gate call
+        # covers the pair
+        self.h1_all, self.h3_all, self.g_all = mk(2 * d_hid), mk(2 * d_hid), mk(2 * d_hid)
+        self.h1 = [self.h1_all[:d_hid], self.h1_all[d_hid:]]
+        self.h3 = [self.h3_all[:d_hid], self.h3_all[d_hid:]]
+        self.g = [self.g_all[:d_hid], self.g_all[d_hid:]]
         self.o = [mk(d_in), mk(d_in)]
         self.y = mk(d_in)
         self.grouped = grouped
@@ -192,8 +196,7 @@ class MoEFFN:
             B.effort_matvec_multi([M.desc for M in mats], [M.layout for M in mats], x, effort,
                                   [self.h1[0], self.h3[0], self.h1[1], self.h3[1]], self.ws,
                                   self.ws_bytes, main)
-            for k in range(2):
-                B.effort_silu_mul(self.h1[k], self.h3[k], self.d_hid, self.g[k], main)
+            B.effort_silu_mul(self.h1_all, self.h3_all, 2 * self.d_hid, self.g_all, main)
             w2s = [self.experts[e0][2], self.experts[e1][2]]
             B.effort_matvec_multi([M.desc for M in w2s], [M.layout for M in w2s], self.g, effort,
                                   self.o, self.ws2, self.ws2_bytes, main)

@@ -32,16 +32,25 @@ class EffortError(RuntimeError):
         super().__init__(msg)
 
 
+EFFORT_ENTRY_U32, EFFORT_ENTRY_R12 = 0, 1
+
+
+class effort_prepare_opts(ctypes.Structure):
+    _fields_ = [("groups", ctypes.c_int32), ("entry_format", ctypes.c_int32),
+                ("crop_segments", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class effort_desc(ctypes.Structure):
     _fields_ = [
         ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
         ("in_dim", ctypes.c_int64), ("out_dim", ctypes.c_int64),
         ("probes_per_row", ctypes.c_int32), ("groups", ctypes.c_int32),
         ("group_width", ctypes.c_int32), ("index_bytes", ctypes.c_int32),
-        ("row_stride", ctypes.c_int64),
+        ("row_stride", ctypes.c_int64), ("group_stride", ctypes.c_int64),
+        ("entry_format", ctypes.c_int32), ("crop_segments", ctypes.c_int32),
         ("off_probes", ctypes.c_uint64), ("off_counts", ctypes.c_uint64),
         ("off_entries", ctypes.c_uint64), ("off_rowmax", ctypes.c_uint64),
-        ("total_bytes", ctypes.c_uint64),
+        ("off_floor", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
         ("checksum", ctypes.c_uint64), ("desc_check", ctypes.c_uint64),
     ]
 
@@ -76,6 +85,8 @@ _PROTOS = {
     "effort_prepare_host": ([_p, _i64, _i64, _i32, _p, _u64, _D], ctypes.c_int),
     "effort_prepare_host_ex": ([_p, _i64, _i64, _i32, _i32, _p, _u64, _D], ctypes.c_int),
     "effort_prepare": ([_p, _i64, _i64, _i32, _p, _u64, _D, _p], ctypes.c_int),
+    "effort_layout_bytes_opts": ([_p, _i64, _i64, _i32, _p, ctypes.POINTER(_u64)], ctypes.c_int),
+    "effort_prepare_host_opts": ([_p, _i64, _i64, _i32, _p, _p, _u64, _D], ctypes.c_int),
     "effort_layout_check": ([_D, _p], ctypes.c_int),
     "effort_matvec": ([_D, _p, _p, _f32, _p, _p, _u64, _p], ctypes.c_int),
     "effort_matvec_batched": ([_D, _p, _p, _i32, _f32, _p, _p, _u64, _p], ctypes.c_int),
@@ -83,6 +94,11 @@ _PROTOS = {
     "effort_matvec_multi": ([_D, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p),
                              ctypes.POINTER(_f32), ctypes.POINTER(_p), _p, _u64, _p], ctypes.c_int),
     "effort_matvec_debug": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p, _p, _p, _p, _p, _p], ctypes.c_int),
+    "effort_matvec_batched_debug": ([_D, _p, _p, _i32, _f32, _p, _p, _u64, _p, _p, _p, _p, _p, _p],
+                                    ctypes.c_int),
+    "effort_matvec_multi_debug": ([_D, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p),
+                                   ctypes.POINTER(_f32), ctypes.POINTER(_p), _p, _u64, _p, _p,
+                                   ctypes.POINTER(_p), _p, _p], ctypes.c_int),
     "effort_matvec_timed": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p], ctypes.c_int),
     "dense_gemv": ([_p, _p, _i64, _i64, _p, _p], ctypes.c_int),
     "dense_gemm_small": ([_p, _p, _i32, _i64, _i64, _p, _p], ctypes.c_int),
@@ -140,6 +156,15 @@ def _check(rc: int, where: str):
         raise EffortError(rc, where)
 
 
+def _check_ws(rc: int, where: str, ws, ws_bytes: int, stream):
+    """As _check; after EFFORT_EHIP the workspace is zero-filled again (a call
+    that failed part-way may leave set the words every call expects to find
+    zero) before the error is raised."""
+    if rc == EFFORT_EHIP and ws is not None:
+        _lib.effort_workspace_init(_ptr(ws), ws_bytes, _stream(stream))
+    _check(rc, where)
+
+
 def effort_strerror(status: int) -> str:
     return _lib.effort_strerror(status).decode()
 
@@ -176,19 +201,45 @@ def effort_workspace_init(ws, ws_bytes: int, stream=None):
     _check(_lib.effort_workspace_init(_ptr(ws), ws_bytes, _stream(stream)), "effort_workspace_init")
 
 
-def effort_prepare_host(w_fp16, P: int, groups: int = 0):
-    """Host fp16 bits [in][out] -> (desc, layout blob as a uint8 numpy array)."""
+def _host_w(w_fp16):
     w = np.ascontiguousarray(w_fp16)
     if w.dtype == np.float16:
         w = w.view(np.uint16)
     if w.dtype != np.uint16 or w.ndim != 2:
         raise TypeError("w_fp16 must be a 2-D uint16/float16 array")
+    return w
+
+
+def effort_layout_bytes_opts(w_fp16, P: int, groups: int = 0, entry_format: int = EFFORT_ENTRY_U32,
+                             crop: int = 0) -> int:
+    w = _host_w(w_fp16)
     m, n = w.shape
-    nbytes = effort_layout_bytes_ex(m, n, P, groups)
-    blob = np.empty(nbytes // 8, dtype=np.uint64).view(np.uint8)  # 8-byte aligned
+    o = effort_prepare_opts(groups, entry_format, crop, 0)
+    b = _u64()
+    _check(_lib.effort_layout_bytes_opts(w.ctypes.data, m, n, P, ctypes.byref(o), ctypes.byref(b)),
+           "effort_layout_bytes_opts")
+    return int(b.value)
+
+
+def effort_prepare_host(w_fp16, P: int, groups: int = 0, entry_format: int = EFFORT_ENTRY_U32,
+                        crop: int = 0):
+    """Host fp16 bits [in][out] -> (desc, layout blob as a uint8 numpy array).
+    `entry_format` and `crop` (stored segments, 0 = all) select the layout
+    options of effort_prepare_host_opts."""
+    w = _host_w(w_fp16)
+    m, n = w.shape
     desc = effort_desc()
-    _check(_lib.effort_prepare_host_ex(w.ctypes.data, m, n, P, groups, blob.ctypes.data, nbytes,
-                                       ctypes.byref(desc)), "effort_prepare_host")
+    if entry_format == EFFORT_ENTRY_U32 and crop in (0, P):
+        nbytes = effort_layout_bytes_ex(m, n, P, groups)
+        blob = np.empty(nbytes // 8, dtype=np.uint64).view(np.uint8)  # 8-byte aligned
+        _check(_lib.effort_prepare_host_ex(w.ctypes.data, m, n, P, groups, blob.ctypes.data, nbytes,
+                                           ctypes.byref(desc)), "effort_prepare_host")
+        return desc, blob
+    o = effort_prepare_opts(groups, entry_format, crop, 0)
+    nbytes = effort_layout_bytes_opts(w, P, groups, entry_format, crop)
+    blob = np.empty(nbytes // 8, dtype=np.uint64).view(np.uint8)
+    _check(_lib.effort_prepare_host_opts(w.ctypes.data, m, n, P, ctypes.byref(o), blob.ctypes.data,
+                                         nbytes, ctypes.byref(desc)), "effort_prepare_host_opts")
     return desc, blob
 
 
@@ -208,15 +259,26 @@ def effort_layout_check(desc: effort_desc, blob) -> None:
 
 
 def effort_matvec(desc, layout, v, effort: float, y, ws, ws_bytes: int, stream=None):
-    _check(_lib.effort_matvec(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y), _ptr(ws),
-                              ws_bytes, _stream(stream)), "effort_matvec")
+    _check_ws(_lib.effort_matvec(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
+                                 _ptr(ws), ws_bytes, _stream(stream)), "effort_matvec", ws, ws_bytes,
+              stream)
 
 
 def effort_matvec_batched(desc, layout, v, batch: int, effort: float, y, ws, ws_bytes: int,
                           stream=None):
-    _check(_lib.effort_matvec_batched(ctypes.byref(desc), _ptr(layout), _ptr(v), batch, effort,
-                                      _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
-           "effort_matvec_batched")
+    _check_ws(_lib.effort_matvec_batched(ctypes.byref(desc), _ptr(layout), _ptr(v), batch, effort,
+                                         _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+              "effort_matvec_batched", ws, ws_bytes, stream)
+
+
+def effort_matvec_batched_debug(desc, layout, v, batch: int, effort: float, y, ws, ws_bytes: int,
+                                cutoff=None, K=None, row_kept=None, fingerprint=None,
+                                kept_mask=None, stream=None):
+    _check_ws(_lib.effort_matvec_batched_debug(ctypes.byref(desc), _ptr(layout), _ptr(v), batch,
+                                               effort, _ptr(y), _ptr(ws), ws_bytes, _ptr(cutoff),
+                                               _ptr(K), _ptr(row_kept), _ptr(fingerprint),
+                                               _ptr(kept_mask), _stream(stream)),
+              "effort_matvec_batched_debug", ws, ws_bytes, stream)
 
 
 def _desc_array(descs):
@@ -243,27 +305,50 @@ def effort_matvec_multi(descs, layouts, vs, efforts, ys, ws, ws_bytes: int, stre
         efforts = [float(efforts)] * n
     if not (len(layouts) == len(vs) == len(ys) == len(efforts) == n):
         raise ValueError("descs, layouts, vs, efforts and ys must have one entry per matrix")
-    _check(_lib.effort_matvec_multi(_desc_array(descs), (_p * n)(*[_ptr(x) for x in layouts]), n,
-                                    (_p * n)(*[_ptr(v) for v in vs]), (_f32 * n)(*efforts),
-                                    (_p * n)(*[_ptr(y) for y in ys]), _ptr(ws), ws_bytes,
-                                    _stream(stream)), "effort_matvec_multi")
+    _check_ws(_lib.effort_matvec_multi(_desc_array(descs), (_p * n)(*[_ptr(x) for x in layouts]),
+                                       n, (_p * n)(*[_ptr(v) for v in vs]), (_f32 * n)(*efforts),
+                                       (_p * n)(*[_ptr(y) for y in ys]), _ptr(ws), ws_bytes,
+                                       _stream(stream)), "effort_matvec_multi", ws, ws_bytes, stream)
+
+
+def effort_matvec_multi_debug(descs, layouts, vs, efforts, ys, ws, ws_bytes: int, cutoff=None,
+                              K=None, row_kept=None, fingerprint=None, stream=None):
+    """effort_matvec_multi with parity outputs: cutoff [count], K [count][2],
+    fingerprint [count] (device buffers), row_kept a list of count device
+    buffers (or None)."""
+    n = len(descs)
+    if not isinstance(vs, (list, tuple)):
+        vs = [vs] * n
+    if isinstance(efforts, (int, float)):
+        efforts = [float(efforts)] * n
+    if not (len(layouts) == len(vs) == len(ys) == len(efforts) == n):
+        raise ValueError("descs, layouts, vs, efforts and ys must have one entry per matrix")
+    rk = None if row_kept is None else (_p * n)(*[_ptr(r) for r in row_kept])
+    _check_ws(_lib.effort_matvec_multi_debug(_desc_array(descs),
+                                             (_p * n)(*[_ptr(x) for x in layouts]), n,
+                                             (_p * n)(*[_ptr(v) for v in vs]), (_f32 * n)(*efforts),
+                                             (_p * n)(*[_ptr(y) for y in ys]), _ptr(ws), ws_bytes,
+                                             _ptr(cutoff), _ptr(K), rk, _ptr(fingerprint),
+                                             _stream(stream)),
+              "effort_matvec_multi_debug", ws, ws_bytes, stream)
 
 
 def effort_matvec_debug(desc, layout, v, effort: float, y, ws, ws_bytes: int, cutoff=None, K=None,
                         row_kept=None, fingerprint=None, kept_mask=None, status=None, stream=None):
-    _check(_lib.effort_matvec_debug(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
-                                    _ptr(ws), ws_bytes, _ptr(cutoff), _ptr(K), _ptr(row_kept),
-                                    _ptr(fingerprint), _ptr(kept_mask), _ptr(status),
-                                    _stream(stream)),
-           "effort_matvec_debug")
+    _check_ws(_lib.effort_matvec_debug(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
+                                       _ptr(ws), ws_bytes, _ptr(cutoff), _ptr(K), _ptr(row_kept),
+                                       _ptr(fingerprint), _ptr(kept_mask), _ptr(status),
+                                       _stream(stream)),
+              "effort_matvec_debug", ws, ws_bytes, stream)
 
 
 def effort_matvec_timed(desc, layout, v, effort: float, y, ws, ws_bytes: int, events, stream=None):
     if len(events) != 6:
         raise ValueError("events: six handles, (start, stop) for select, dispatch, bucketMul")
     arr = (_p * 6)(*[e if e else None for e in events])
-    _check(_lib.effort_matvec_timed(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
-                                    _ptr(ws), ws_bytes, _stream(stream), arr), "effort_matvec_timed")
+    _check_ws(_lib.effort_matvec_timed(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
+                                       _ptr(ws), ws_bytes, _stream(stream), arr),
+              "effort_matvec_timed", ws, ws_bytes, stream)
 
 
 def dense_gemv(w, v, in_dim: int, out_dim: int, y, stream=None):

@@ -12,8 +12,10 @@
 #include "layout.hpp"
 
 namespace effort {
-int prepare_host(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t groups, void* layout,
-                 uint64_t layout_bytes, effort_desc* desc_out);
+int prepare_host(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t groups, int32_t format,
+                 int32_t crop, void* layout, uint64_t layout_bytes, effort_desc* desc_out);
+int plan_layout(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t groups, int32_t format,
+                int32_t crop, Geometry* g);
 uint64_t blob_checksum(const void* blob, uint64_t total);
 }  // namespace effort
 
@@ -67,6 +69,9 @@ int check_desc(const effort_desc* d, Geometry* g) {
 
 bool effort_ok(float e) { return e > 0.0f && e <= 1.0f; }  // false for NaN
 
+// Entry formats the multiply reads.
+bool format_supported(const Geometry& g) { return g.format == EFFORT_ENTRY_U32; }
+
 uint32_t k_of(float effort, int64_t N) {
   double k = ceil((double)effort * (double)N);
   if (k < 1.0) k = 1.0;
@@ -74,6 +79,19 @@ uint32_t k_of(float effort, int64_t N) {
   return (uint32_t)k;
 }
 
+// Parity outputs of one vector (or one matrix of a multi-matrix call); every
+// pointer may be null.
+struct Rec {
+  float* cutoff;                    // [1]
+  int64_t* K;                       // [2]: K, K'
+  int32_t* row_kept;                // [in_dim]
+  unsigned long long* fingerprint;  // [1]
+  uint8_t* mask;                    // [in_dim][out_dim]
+  bool records() const { return row_kept || fingerprint || mask; }
+};
+
+// Parity outputs of a call with `count` vectors of one matrix: vector k's at
+// cutoff + k, K + 2k, row_kept + k m, fingerprint + k, mask + k m n.
 struct DebugOut {
   float* cutoff;
   int64_t* K;
@@ -81,7 +99,27 @@ struct DebugOut {
   uint64_t* fingerprint;
   uint8_t* mask;
   uint32_t* status;
+  Rec of(const Geometry& g, int32_t k) const {
+    Rec r;
+    r.cutoff = cutoff ? cutoff + k : nullptr;
+    r.K = K ? K + 2 * k : nullptr;
+    r.row_kept = row_kept ? row_kept + (uint64_t)k * g.m : nullptr;
+    r.fingerprint = fingerprint ? reinterpret_cast<unsigned long long*>(fingerprint) + k : nullptr;
+    r.mask = mask ? mask + (uint64_t)k * g.m * g.n : nullptr;
+    return r;
+  }
 };
+
+// Clears a vector's recording outputs (stream-ordered, before the kernels).
+hipError_t clear_rec(const Geometry& g, const Rec& r, int32_t count, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (r.row_kept && (e = launch_zero_bytes(r.row_kept, (uint64_t)count * g.m * 4, s)) != hipSuccess)
+    return e;
+  if (r.fingerprint && (e = launch_zero_bytes(r.fingerprint, (uint64_t)count * 8, s)) != hipSuccess)
+    return e;
+  if (r.mask && (e = launch_zero_bytes(r.mask, (uint64_t)count * g.m * g.n, s)) != hipSuccess) return e;
+  return e;
+}
 
 // The three kernels' arguments for one vector and one matrix, its workspace
 // slice at `ws`.
@@ -104,6 +142,7 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   const uint32_t* counts = reinterpret_cast<const uint32_t*>(layout + g.off_counts);
   const uint32_t* entries = reinterpret_cast<const uint32_t*>(layout + g.off_entries);
   const uint16_t* rowmax = reinterpret_cast<const uint16_t*>(layout + g.off_rowmax);
+  const uint16_t* floor = g.off_floor ? reinterpret_cast<const uint16_t*>(layout + g.off_floor) : nullptr;
   const int64_t N = g.m * (int64_t)g.P;
   const uint32_t K = k_of(effort, N);
 
@@ -146,6 +185,8 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   ma = MulArgs();
   ma.v = v;
   ma.entries = entries;
+  ma.gstride = g.gstride;
+  ma.floor = floor;
   ma.runlen = runlen;
   ma.bsum = bsum;
   ma.hist = hist;
@@ -169,39 +210,48 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   ma.mask = nullptr;
 }
 
+// After a failed launch part-way through a call, the workspace words that
+// every call expects to find zero (histograms, counters) may be left set:
+// they are cleared again (best effort: if launches keep failing, the caller
+// must run effort_workspace_init before the next call).
+void reset_after_failure(uint8_t* ws, uint64_t bytes, hipStream_t s) {
+  (void)launch_zero_bytes(ws, bytes, s);
+}
+
 // One vector: select, dispatch, bucketMul on `s`.
 int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effort, float* y,
-            uint8_t* ws, hipStream_t s, const DebugOut* dbg, const EventPair* ev) {
+            uint8_t* ws, hipStream_t s, const Rec* rec, uint32_t* status, const EventPair* ev) {
   CallArgs c;
   build_args(g, layout, v, effort, y, ws, &c);
-  hipError_t e;
+  const uint64_t slice = ws_layout(g).slice;
 
-  if (dbg) {
-    if (dbg->row_kept && hip_failed(e = launch_zero_bytes(dbg->row_kept, (uint64_t)g.m * 4, s)))
-      return EFFORT_EHIP;
-    if (dbg->fingerprint && hip_failed(e = launch_zero_bytes(dbg->fingerprint, 8, s)))
-      return EFFORT_EHIP;
-    if (dbg->mask && hip_failed(e = launch_zero_bytes(dbg->mask, (uint64_t)g.m * g.n, s)))
-      return EFFORT_EHIP;
-    if (dbg->status && (hip_failed(e = launch_zero_bytes(dbg->status, 4, s)) ||
-                        hip_failed(e = launch_check_finite(v, g.m, dbg->status, s))))
-      return EFFORT_EHIP;
+  if (rec && hip_failed(clear_rec(g, *rec, 1, s))) return EFFORT_EHIP;
+  if (status && (hip_failed(launch_zero_bytes(status, 4, s)) ||
+                 hip_failed(launch_check_finite(v, g.m, status, s))))
+    return EFFORT_EHIP;
+
+  if (hip_failed(launch_select(c.sa, s, ev ? &ev[0] : nullptr))) {
+    reset_after_failure(ws, slice, s);
+    return EFFORT_EHIP;
   }
-
-  if (hip_failed(e = launch_select(c.sa, s, ev ? &ev[0] : nullptr))) return EFFORT_EHIP;
-  if (hip_failed(e = launch_dispatch(c.da, s, ev ? &ev[1] : nullptr))) return EFFORT_EHIP;
-
+  if (hip_failed(launch_dispatch(c.da, s, ev ? &ev[1] : nullptr))) {
+    reset_after_failure(ws, slice, s);
+    return EFFORT_EHIP;
+  }
   MulArgs& ma = c.ma;
-  ma.row_kept = dbg ? dbg->row_kept : nullptr;
-  ma.fingerprint = dbg ? reinterpret_cast<unsigned long long*>(dbg->fingerprint) : nullptr;
-  ma.mask = dbg ? dbg->mask : nullptr;
-  const bool record = dbg && (dbg->row_kept || dbg->fingerprint || dbg->mask);
+  ma.row_kept = rec ? rec->row_kept : nullptr;
+  ma.fingerprint = rec ? rec->fingerprint : nullptr;
+  ma.mask = rec ? rec->mask : nullptr;
+  const bool record = rec && rec->records();
   int bpg = cu_count() / g.G;  // at most one block per CU: a larger grid runs a second round
   if (bpg < 1) bpg = 1;
-  if (hip_failed(e = launch_bucketmul(ma, record, bpg, s, ev ? &ev[2] : nullptr))) return EFFORT_EHIP;
-
-  if (dbg && (dbg->cutoff || dbg->K) &&
-      hip_failed(launch_debug_result(ma.result, dbg->cutoff, dbg->K, s)))
+  if (hip_failed(launch_bucketmul(ma, record, bpg, s, ev ? &ev[2] : nullptr))) {
+    reset_after_failure(ws, slice, s);
+    return EFFORT_EHIP;
+  }
+  if (((rec && (rec->cutoff || rec->K)) || status) &&
+      hip_failed(launch_debug_result(ma.result, 0, 1, rec ? rec->cutoff : nullptr,
+                                     rec ? rec->K : nullptr, status, s)))
     return EFFORT_EHIP;
   return EFFORT_OK;
 }
@@ -210,8 +260,11 @@ int run_one(const Geometry& g, const uint8_t* layout, const float* v, float effo
 // and dispatch kernels for all vectors at once, then per pass of up to
 // bucketmul_pass_width vectors the union kernel and the multiply.
 int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_t batch, float effort,
-                float* y, uint8_t* ws, hipStream_t s) {
+                float* y, uint8_t* ws, hipStream_t s, const DebugOut* dbg) {
   const WsLayout w = ws_layout(g);
+  const uint64_t ws_total = w.slice * (uint64_t)batch + w.union_bytes;
+  const Rec rec0 = dbg ? dbg->of(g, 0) : Rec{};
+  if (dbg && hip_failed(clear_rec(g, rec0, batch, s))) return EFFORT_EHIP;
   const uint64_t vec_ws = w.slice / 4;  // u32 words between consecutive vectors' slices
   const uint16_t* probes = reinterpret_cast<const uint16_t*>(layout + g.off_probes);
   const uint32_t* counts = reinterpret_cast<const uint32_t*>(layout + g.off_counts);
@@ -237,7 +290,10 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
   sa.bsum = u32(0, w.bsum);
   sa.bsum_words = (g.m + kDspRows - 1) / kDspRows * (g.G + 1);
   sa.vec_ws = vec_ws;
-  if (hip_failed(launch_select(sa, s, nullptr, batch))) return EFFORT_EHIP;
+  if (hip_failed(launch_select(sa, s, nullptr, batch))) {
+    reset_after_failure(ws, ws_total, s);
+    return EFFORT_EHIP;
+  }
 
   DispatchArgs da;
   da.v = v;
@@ -256,7 +312,10 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
   da.G4 = g.G4;
   da.K = K;
   da.vec_ws = vec_ws;
-  if (hip_failed(launch_dispatch(da, s, nullptr, batch))) return EFFORT_EHIP;
+  if (hip_failed(launch_dispatch(da, s, nullptr, batch))) {
+    reset_after_failure(ws, ws_total, s);
+    return EFFORT_EHIP;
+  }
 
   uint32_t* urunlen = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.urunlen);
   uint32_t* ubsum = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.ubsum);
@@ -273,11 +332,16 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
     ua.m = g.m;
     ua.urunlen = urunlen;
     ua.ubsum = ubsum;
-    if (hip_failed(launch_union(ua, s))) return EFFORT_EHIP;
+    if (hip_failed(launch_union(ua, s))) {
+      reset_after_failure(ws, ws_total, s);
+      return EFFORT_EHIP;
+    }
 
     MulArgs ma;
     ma.v = v + (int64_t)b0 * g.m;
     ma.entries = entries;
+    ma.gstride = g.gstride;
+    ma.floor = g.off_floor ? reinterpret_cast<const uint16_t*>(layout + g.off_floor) : nullptr;
     ma.runlen = urunlen;
     ma.bsum = ubsum;
     ma.hist = u32(b0, w.hist);
@@ -296,11 +360,18 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
     ma.nv = nv;
     ma.vec_ws = vec_ws;
     ma.vbsum = u32(b0, w.bsum);
-    ma.row_kept = nullptr;
-    ma.fingerprint = nullptr;
-    ma.mask = nullptr;
-    if (hip_failed(launch_bucketmul(ma, false, bpg, s))) return EFFORT_EHIP;
+    const Rec rec = dbg ? dbg->of(g, b0) : Rec{};
+    ma.row_kept = rec.row_kept;
+    ma.fingerprint = rec.fingerprint;
+    ma.mask = rec.mask;
+    if (hip_failed(launch_bucketmul(ma, rec.records(), bpg, s))) {
+      reset_after_failure(ws, ws_total, s);
+      return EFFORT_EHIP;
+    }
   }
+  if (dbg && (dbg->cutoff || dbg->K) &&
+      hip_failed(launch_debug_result(u32(0, w.result), vec_ws, batch, dbg->cutoff, dbg->K, nullptr, s)))
+    return EFFORT_EHIP;
   return EFFORT_OK;
 }
 
@@ -324,13 +395,29 @@ int check_multi(const effort_desc* descs, int32_t count, Geometry* g) {
   return EFFORT_OK;
 }
 
+int check_multi_formats(const Geometry* g, int32_t count) {
+  for (int32_t j = 0; j < count; ++j)
+    if (!format_supported(g[j])) return EFFORT_EUNSUPPORTED;
+  return EFFORT_OK;
+}
+
 // Several (matrix, vector) pairs -- matrices sharing v, one matrix with
 // several vectors, or any mix: each kernel launched once for all of them.
 // The multiply's CUs are shared out by output width (the kept bytes of each
 // matrix are about proportional to it at one effort), whole blocks per group.
 int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
               const float* const* vs, const float* efforts, float* const* ys, uint8_t* ws,
-              const uint64_t* off, hipStream_t s) {
+              const uint64_t* off, hipStream_t s, const Rec* recs) {
+  bool record = false;
+  if (recs)
+    for (int32_t j = 0; j < count; ++j) {
+      if (hip_failed(clear_rec(g[j], recs[j], 1, s))) return EFFORT_EHIP;
+      record = record || recs[j].records();
+    }
+  auto fail = [&]() {
+    for (int32_t j = 0; j < count; ++j) reset_after_failure(ws + off[j], ws_layout(g[j]).slice, s);
+    return EFFORT_EHIP;
+  };
   SelectMulti sm;
   DispatchMulti dm;
   MulMulti mm;
@@ -344,13 +431,23 @@ int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
     sm.a[j] = c.sa;
     dm.a[j] = c.da;
     mm.a[j] = c.ma;
+    if (recs) {
+      mm.a[j].row_kept = recs[j].row_kept;
+      mm.a[j].fingerprint = recs[j].fingerprint;
+      mm.a[j].mask = recs[j].mask;
+    }
     const int64_t share = (int64_t)cus * g[j].n / ntot;
     bpg[j] = (int)(share / g[j].G);
     if (bpg[j] < 1) bpg[j] = 1;
   }
-  if (hip_failed(launch_select_multi(sm, count, s))) return EFFORT_EHIP;
-  if (hip_failed(launch_dispatch_multi(dm, count, s))) return EFFORT_EHIP;
-  if (hip_failed(launch_bucketmul_multi(mm, count, bpg, s))) return EFFORT_EHIP;
+  if (hip_failed(launch_select_multi(sm, count, s))) return fail();
+  if (hip_failed(launch_dispatch_multi(dm, count, s))) return fail();
+  if (hip_failed(launch_bucketmul_multi(mm, count, bpg, record, s))) return fail();
+  if (recs)
+    for (int32_t j = 0; j < count; ++j)
+      if ((recs[j].cutoff || recs[j].K) &&
+          hip_failed(launch_debug_result(mm.a[j].result, 0, 1, recs[j].cutoff, recs[j].K, nullptr, s)))
+        return EFFORT_EHIP;
   return EFFORT_OK;
 }
 
@@ -376,6 +473,7 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
     return EFFORT_EINVAL;
   if (batch < 1 || batch > EFFORT_MAX_BATCH) return EFFORT_EINVAL;
   if (!effort_ok(effort)) return EFFORT_EINVAL;
+  if (!format_supported(g)) return EFFORT_EUNSUPPORTED;
   const WsLayout w = ws_layout(g);
   if (ws_bytes < w.slice * (uint64_t)batch + (batch > 1 ? w.union_bytes : 0)) return EFFORT_ENOSPACE;
   if (dbg) {
@@ -396,10 +494,11 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* layout = static_cast<const uint8_t*>(layout_dev);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  if (batch > 1 && !dbg && !events && batch >= kUnionMinBatch && effort >= kUnionMinEffort &&
+  // a call with parity outputs takes the same route as one without
+  if (batch > 1 && !events && batch >= kUnionMinBatch && effort >= kUnionMinEffort &&
       bucketmul_pass_width(g.TW, batch) > 0)
-    return run_batched(g, layout, v_dev, batch, effort, y_dev, ws, s);
-  if (batch > 1 && !dbg && !events) {
+    return run_batched(g, layout, v_dev, batch, effort, y_dev, ws, s, dbg);
+  if (batch > 1 && !events) {
     // up to EFFORT_MAX_MULTI vectors per launch, each its own single-vector
     // multiply over its own read lengths (the slices are the batch's)
     for (int32_t b0 = 0; b0 < batch; b0 += EFFORT_MAX_MULTI) {
@@ -410,7 +509,9 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
       float* ys[EFFORT_MAX_MULTI];
       float es[EFFORT_MAX_MULTI];
       uint64_t off[EFFORT_MAX_MULTI];
+      Rec recs[EFFORT_MAX_MULTI];
       for (int32_t j = 0; j < cnt; ++j) {
+        if (dbg) recs[j] = dbg->of(g, b0 + j);
         gs[j] = g;
         ls[j] = layout;
         vs[j] = v_dev + (int64_t)(b0 + j) * g.m;
@@ -418,14 +519,16 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
         es[j] = effort;
         off[j] = (uint64_t)(b0 + j) * w.slice;
       }
-      rc = run_multi(gs, cnt, ls, vs, es, ys, ws, off, s);
+      rc = run_multi(gs, cnt, ls, vs, es, ys, ws, off, s, dbg ? recs : nullptr);
       if (rc) return rc;
     }
     return EFFORT_OK;
   }
   for (int32_t b = 0; b < batch; ++b) {
+    const Rec rec = dbg ? dbg->of(g, b) : Rec{};
     rc = run_one(g, layout, v_dev + (int64_t)b * g.m, effort, y_dev + (int64_t)b * g.n,
-                 ws + (uint64_t)b * w.slice, s, dbg, events ? ev : nullptr);
+                 ws + (uint64_t)b * w.slice, s, dbg ? &rec : nullptr, dbg ? dbg->status : nullptr,
+                 events ? ev : nullptr);
     if (rc) return rc;
   }
   return EFFORT_OK;
@@ -491,6 +594,7 @@ int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev
   Geometry g[EFFORT_MAX_MULTI];
   int rc = check_multi(descs, count, g);
   if (rc) return rc;
+  if ((rc = check_multi_formats(g, count)) != EFFORT_OK) return rc;
   if (!layouts_dev || !vs_dev || !ys_dev || !efforts || !ws_dev) return EFFORT_EINVAL;
   if (!aligned(ws_dev, 256)) return EFFORT_EINVAL;
   const uint8_t* layouts[EFFORT_MAX_MULTI];
@@ -508,7 +612,47 @@ int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev
   uint64_t off[EFFORT_MAX_MULTI];
   if (ws_bytes < multi_ws_offsets(g, count, off)) return EFFORT_ENOSPACE;
   return run_multi(g, count, layouts, vs, efforts, ys, static_cast<uint8_t*>(ws_dev), off,
-                   static_cast<hipStream_t>(stream));
+                   static_cast<hipStream_t>(stream), nullptr);
+}
+
+int effort_matvec_multi_debug(const effort_desc* descs, const void* const* layouts_dev, int32_t count,
+                              const float* const* vs_dev, const float* efforts, float* const* ys_dev,
+                              void* ws_dev, uint64_t ws_bytes, float* cutoff_dev, int64_t* K_dev,
+                              int32_t* const* row_kept_dev, uint64_t* fingerprint_dev, void* stream) {
+  Geometry g[EFFORT_MAX_MULTI];
+  int rc = check_multi(descs, count, g);
+  if (rc) return rc;
+  if ((rc = check_multi_formats(g, count)) != EFFORT_OK) return rc;
+  if (!layouts_dev || !vs_dev || !ys_dev || !efforts || !ws_dev) return EFFORT_EINVAL;
+  if (!aligned(ws_dev, 256)) return EFFORT_EINVAL;
+  if ((cutoff_dev && !aligned(cutoff_dev, 4)) || (K_dev && !aligned(K_dev, 8)) ||
+      (fingerprint_dev && !aligned(fingerprint_dev, 8)))
+    return EFFORT_EINVAL;
+  const uint8_t* layouts[EFFORT_MAX_MULTI];
+  const float* vs[EFFORT_MAX_MULTI];
+  float* ys[EFFORT_MAX_MULTI];
+  Rec recs[EFFORT_MAX_MULTI];
+  for (int32_t j = 0; j < count; ++j) {
+    if (!effort_ok(efforts[j])) return EFFORT_EINVAL;
+    if (!layouts_dev[j] || !vs_dev[j] || !ys_dev[j]) return EFFORT_EINVAL;
+    if (!aligned(layouts_dev[j], 256) || !aligned(vs_dev[j], 4) || !aligned(ys_dev[j], 4))
+      return EFFORT_EINVAL;
+    int32_t* rk = row_kept_dev ? row_kept_dev[j] : nullptr;
+    if (rk && !aligned(rk, 4)) return EFFORT_EINVAL;
+    layouts[j] = static_cast<const uint8_t*>(layouts_dev[j]);
+    vs[j] = vs_dev[j];
+    ys[j] = ys_dev[j];
+    recs[j].cutoff = cutoff_dev ? cutoff_dev + j : nullptr;
+    recs[j].K = K_dev ? K_dev + 2 * j : nullptr;
+    recs[j].row_kept = rk;
+    recs[j].fingerprint =
+        fingerprint_dev ? reinterpret_cast<unsigned long long*>(fingerprint_dev) + j : nullptr;
+    recs[j].mask = nullptr;
+  }
+  uint64_t off[EFFORT_MAX_MULTI];
+  if (ws_bytes < multi_ws_offsets(g, count, off)) return EFFORT_ENOSPACE;
+  return run_multi(g, count, layouts, vs, efforts, ys, static_cast<uint8_t*>(ws_dev), off,
+                   static_cast<hipStream_t>(stream), recs);
 }
 
 int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream) {
@@ -519,12 +663,33 @@ int effort_workspace_init(void* ws_dev, uint64_t ws_bytes, void* stream) {
 int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
                            int32_t groups, void* layout_host, uint64_t layout_bytes,
                            effort_desc* desc_out) {
-  return prepare_host(w_fp16, in_dim, out_dim, P, groups, layout_host, layout_bytes, desc_out);
+  return prepare_host(w_fp16, in_dim, out_dim, P, groups, EFFORT_ENTRY_U32, P, layout_host,
+                      layout_bytes, desc_out);
 }
 
 int effort_prepare_host(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
                         void* layout_host, uint64_t layout_bytes, effort_desc* desc_out) {
-  return prepare_host(w_fp16, in_dim, out_dim, P, 0, layout_host, layout_bytes, desc_out);
+  return prepare_host(w_fp16, in_dim, out_dim, P, 0, EFFORT_ENTRY_U32, P, layout_host, layout_bytes,
+                      desc_out);
+}
+
+int effort_layout_bytes_opts(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                             const effort_prepare_opts* opts, uint64_t* bytes) {
+  if (!opts || !bytes) return EFFORT_EINVAL;
+  Geometry g;
+  const int rc = plan_layout(w_fp16, in_dim, out_dim, P, opts->groups, opts->entry_format,
+                             opts->crop_segments, &g);
+  if (rc) return rc;
+  *bytes = g.total;
+  return EFFORT_OK;
+}
+
+int effort_prepare_host_opts(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                             const effort_prepare_opts* opts, void* layout_host,
+                             uint64_t layout_bytes, effort_desc* desc_out) {
+  if (!opts) return EFFORT_EINVAL;
+  return prepare_host(w_fp16, in_dim, out_dim, P, opts->groups, opts->entry_format,
+                      opts->crop_segments, layout_host, layout_bytes, desc_out);
 }
 
 int effort_prepare(const uint16_t* w_fp16_host, int64_t in_dim, int64_t out_dim, int32_t P,
@@ -536,7 +701,7 @@ int effort_prepare(const uint16_t* w_fp16_host, int64_t in_dim, int64_t out_dim,
   if (layout_bytes < g.total) return EFFORT_ENOSPACE;
   void* tmp = aligned_alloc(256, (size_t)g.total);
   if (!tmp) return EFFORT_ENOSPACE;
-  rc = prepare_host(w_fp16_host, in_dim, out_dim, P, 0, tmp, g.total, desc_out);
+  rc = prepare_host(w_fp16_host, in_dim, out_dim, P, 0, EFFORT_ENTRY_U32, P, tmp, g.total, desc_out);
   if (!rc) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hip_failed(hipMemcpyAsync(layout_dev, tmp, (size_t)g.total, hipMemcpyHostToDevice, s)) ||
@@ -577,6 +742,16 @@ int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const f
                         void* stream) {
   DebugOut d{cutoff_dev, K_dev, row_kept_dev, fingerprint_dev, kept_mask_dev, status_dev};
   return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws_dev, ws_bytes, stream, &d,
+                       nullptr);
+}
+
+int effort_matvec_batched_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                                int32_t batch, float effort, float* y_dev, void* ws_dev,
+                                uint64_t ws_bytes, float* cutoff_dev, int64_t* K_dev,
+                                int32_t* row_kept_dev, uint64_t* fingerprint_dev,
+                                uint8_t* kept_mask_dev, void* stream) {
+  DebugOut d{cutoff_dev, K_dev, row_kept_dev, fingerprint_dev, kept_mask_dev, nullptr};
+  return matvec_common(desc, layout_dev, v_dev, batch, effort, y_dev, ws_dev, ws_bytes, stream, &d,
                        nullptr);
 }
 

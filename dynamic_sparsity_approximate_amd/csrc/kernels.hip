@@ -184,7 +184,10 @@ __device__ __forceinline__ void chart_hist_body(const SelectArgs& a) {
     a.y[j] = 0.0f;
   if (blockIdx.x == 0) {  // the dispatch accumulates into these
     for (int b = tid; b < 1024; b += CH_T) a.hist2[b] = 0u;
-    if (tid == 0) a.result[RES_NCAND] = 0u;
+    if (tid == 0) {
+      a.result[RES_NCAND] = 0u;
+      a.result[RES_FLAGS] = 0u;
+    }
   }
   for (int64_t j = (int64_t)blockIdx.x * CH_T + tid; j < a.bsum_words; j += (int64_t)gridDim.x * CH_T)
     a.bsum[j] = 0u;
@@ -1085,7 +1088,6 @@ __device__ __forceinline__ void bucketmul_body(
     const uint32_t* __restrict__ entries, const uint32_t* __restrict__ runlen,
     const uint32_t* __restrict__ bsum, const uint32_t* __restrict__ result,
     float* __restrict__ y, const MulArgs& a) {
-  static_assert(BP == 1 || !REC, "parity recording is single-vector");
   static_assert(BP >= 1 && BP <= 8, "at most 8 vectors per pass");
   constexpr int MUL_T = mul_threads<BP>();
   constexpr int MUL_W = MUL_T / 64;
@@ -1421,7 +1423,7 @@ __device__ __forceinline__ void bucketmul_body(
 #pragma unroll
         for (int p = 0; p < BP; ++p)
           if (p < nv) vj[p] = vvec[(size_t)p * a.m + r];
-      Lj = min(Lj, (uint32_t)tw);
+      Lj = (uint32_t)min((int64_t)Lj, a.gstride);  // a run holds gstride units
     }
     aj = lane == 0 ? offb : 0u;
     const uint32_t lenj = Lj > aj ? Lj - aj : 0u;
@@ -1457,7 +1459,7 @@ __device__ __forceinline__ void bucketmul_body(
     // row and range are wave-uniform; readfirstlane keeps the descriptor scalar
     const uint32_t row = __builtin_amdgcn_readfirstlane(rowb + c.j);
     const uint32_t s1 = __builtin_amdgcn_readfirstlane(c.s1);
-    const uint32_t* base = entries + (size_t)row * (size_t)a.row_stride + col0;
+    const uint32_t* base = entries + (size_t)row * (size_t)a.row_stride + (size_t)g * (size_t)a.gstride;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(s1 * 4u), kBufferDword3);
     const auto q = __builtin_amdgcn_raw_buffer_load_b128(
@@ -1475,56 +1477,65 @@ __device__ __forceinline__ void bucketmul_body(
       vf[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[p]), c.j));
     }
     uint32_t ev[4] = {buf.x, buf.y, buf.z, buf.w};
-    if (!REC) {
-      // Words past s1 are zero.  Words before s0 can only sit in lane 0's
-      // quad of a share's first chunk: they belong to the previous share and
-      // are zeroed here.  A zero word has key 0 and passes only when the
-      // cutoff is 0, where it adds 0.
-      if (c.s0 & 3u) {
-        const uint32_t skip = lane == 0 ? (c.s0 & 3u) : 0u;
-        ev[0] = skip > 0u ? 0u : ev[0];
-        ev[1] = skip > 1u ? 0u : ev[1];
-        ev[2] = skip > 2u ? 0u : ev[2];
-      }
+    // Words past s1 are zero.  Words before s0 can only sit in lane 0's quad
+    // of a share's first chunk: they belong to the previous share and are
+    // zeroed here.  A zero word has key 0 and passes only when the cutoff is
+    // 0, where it adds 0.
+    if (c.s0 & 3u) {
+      const uint32_t skip = lane == 0 ? (c.s0 & 3u) : 0u;
+      ev[0] = skip > 0u ? 0u : ev[0];
+      ev[1] = skip > 1u ? 0u : ev[1];
+      ev[2] = skip > 2u ? 0u : ev[2];
+    }
+    // The keep test and the accumulation are the same with and without
+    // recording; recording only adds the stores of the kept (row, column)
+    // pairs, counted for words that are entries of the chunk (the zero words
+    // above are not).
+    uint32_t cnt[BP];
+    uint64_t fp[BP];
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const uint32_t w = ev[k2];
-        const float x = h2f(w);
+    for (int p = 0; p < BP; ++p) {
+      cnt[p] = 0u;
+      fp[p] = 0u;
+    }
+    const uint32_t pos0 = (c.s0 & ~3u) + (uint32_t)lane * 4u;
 #pragma unroll
-        for (int p = 0; p < BP; ++p)
-          if (fabsf(x) >= tf[p])  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
-            atomicAdd(&tile[p * a.TW + (w >> 16)], __float2int_rn(__fmul_rn(x, vf[p])));
-      }
-    } else {
-      const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tj[0], c.j);
-      const uint32_t row = rowb + c.j;
-      const uint32_t p = (c.s0 & ~3u) + (uint32_t)lane * 4u;
-      uint32_t cnt = 0u;
-      uint64_t fp = 0u;
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const uint32_t w = ev[k2];
+      const float x = h2f(w);
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const uint32_t w = ev[k2];
-        const uint32_t pos = p + (uint32_t)k2;
-        if (pos >= c.s0 && pos < c.s1 && (w & 0x7FFFu) >= t) {
-          atomicAdd(&tile[w >> 16], __float2int_rn(__fmul_rn(h2f(w), vf[0])));
-          const uint64_t flat = (uint64_t)row * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
-          if (a.mask) a.mask[flat] = 1u;
-          fp += pair_hash(flat);
-          ++cnt;
+      for (int p = 0; p < BP; ++p)
+        if (fabsf(x) >= tf[p]) {  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
+          atomicAdd(&tile[p * a.TW + (w >> 16)], __float2int_rn(__fmul_rn(x, vf[p])));
+          if constexpr (REC) {
+            const uint32_t pos = pos0 + (uint32_t)k2;
+            if (pos >= c.s0 && pos < c.s1) {
+              const uint64_t flat = (uint64_t)(rowb + c.j) * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
+              if (a.mask) a.mask[(uint64_t)p * (uint64_t)a.m * (uint64_t)a.n + flat] = 1u;
+              fp[p] += pair_hash(flat);
+              ++cnt[p];
+            }
+          }
         }
-      }
-      uint32_t flo = (uint32_t)fp, fhi = (uint32_t)(fp >> 32);
-      for (int sh = 32; sh > 0; sh >>= 1) {
-        cnt += __shfl_xor(cnt, sh, 64);
-        const uint32_t olo = __shfl_xor(flo, sh, 64);
-        const uint32_t ohi = __shfl_xor(fhi, sh, 64);
-        const uint64_t sum = ((uint64_t)fhi << 32 | flo) + ((uint64_t)ohi << 32 | olo);
-        flo = (uint32_t)sum;
-        fhi = (uint32_t)(sum >> 32);
-      }
-      if (lane == 0) {
-        if (cnt && a.row_kept) atomicAdd(&a.row_kept[row], (int32_t)cnt);
-        if (a.fingerprint) atomicAdd(a.fingerprint, ((unsigned long long)fhi << 32) | flo);
+    }
+    if constexpr (REC) {
+      const uint32_t row = rowb + c.j;
+#pragma unroll
+      for (int p = 0; p < BP; ++p) {
+        uint32_t cn = cnt[p];
+        uint32_t flo = (uint32_t)fp[p], fhi = (uint32_t)(fp[p] >> 32);
+        for (int sh = 32; sh > 0; sh >>= 1) {
+          cn += __shfl_xor(cn, sh, 64);
+          const uint32_t olo = __shfl_xor(flo, sh, 64);
+          const uint32_t ohi = __shfl_xor(fhi, sh, 64);
+          const uint64_t sum = ((uint64_t)fhi << 32 | flo) + ((uint64_t)ohi << 32 | olo);
+          flo = (uint32_t)sum;
+          fhi = (uint32_t)(sum >> 32);
+        }
+        if (lane == 0 && p < nv) {
+          if (cn && a.row_kept) atomicAdd(&a.row_kept[(size_t)p * a.m + row], (int32_t)cn);
+          if (a.fingerprint) atomicAdd(a.fingerprint + p, ((unsigned long long)fhi << 32) | flo);
+        }
       }
     }
   };
@@ -1535,6 +1546,17 @@ __device__ __forceinline__ void bucketmul_body(
       // clamped: only a row whose weights are all zero can exceed it, and its
       // products stay 0
       vfj[p] = p < nv ? fminf(fmaxf(ldexpf(vj[p], BP == 1 ? S1 : sS[p]), -0x1p100f), 0x1p100f) : 0.0f;
+    }
+    // A cropped layout: a row whose largest dropped magnitude reaches its
+    // threshold has kept products that are not stored (every row with kept
+    // products has a nonzero read length in some group, so some wave sees it).
+    if (a.floor) {
+      const uint32_t r = rowb + (uint32_t)lane;
+      const uint32_t fl = Lj && r < m ? (uint32_t)a.floor[r] : 0u;
+#pragma unroll
+      for (int p = 0; p < BP; ++p)
+        if (__ballot(Lj && fl >= tj[p]) && lane == 0)
+          atomicOr(&a.result[(size_t)p * a.vec_ws + RES_FLAGS], FLAG_CROP_REACHED);
     }
   };
   // A ring of 4 chunks in flight: a slot is processed, then refilled with the
@@ -1610,13 +1632,14 @@ __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
 
 // Several matrices sharing v, one vector each: matrix j owns blocks
 // [first[j], first[j + 1]) of the grid.
+template <bool REC>
 __global__ __launch_bounds__(mul_threads<1>()) void k_bucketmul_multi(MulMulti mm) {
   int j = 0;
   for (int k = 1; k < mm.count; ++k)
     if (blockIdx.x >= mm.first[k]) j = k;
   const MulArgs& a = mm.a[j];
-  bucketmul_body<false, 1>(blockIdx.x - mm.first[j], mm.first[j + 1] - mm.first[j], a.v, a.entries,
-                           a.runlen, a.bsum, a.result, a.y, a);
+  bucketmul_body<REC, 1>(blockIdx.x - mm.first[j], mm.first[j + 1] - mm.first[j], a.v, a.entries,
+                         a.runlen, a.bsum, a.result, a.y, a);
 }
 
 // LDS of a workgroup on gfx950; the batched kernel's static LDS (cutoff
@@ -1637,21 +1660,18 @@ int bucketmul_pass_width(int32_t TW, int32_t batch) {
   return 0;
 }
 
-template <int BP>
+template <bool REC, int BP>
 static hipError_t launch_mul_bp(const MulArgs& a, unsigned grid, hipStream_t s) {
   const size_t lds = (size_t)BP * a.TW * sizeof(int32_t);
   if (lds > pass_tile_budget(BP)) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bucketmul<false, BP>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)pass_tile_budget(BP));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL((k_bucketmul<false, BP>), dim3(grid), dim3(mul_threads<BP>()), lds, s, a.v,
-                     a.entries,
-                     a.runlen, a.bsum, a.result, a.y, a);
+  // the attribute is set on every launch: a per-instantiation flag would be
+  // per device state, and the call costs no device work
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bucketmul<REC, BP>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)pass_tile_budget(BP));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bucketmul<REC, BP>), dim3(grid), dim3(mul_threads<BP>()), lds, s, a.v,
+                     a.entries, a.runlen, a.bsum, a.result, a.y, a);
   return hipGetLastError();
 }
 
@@ -1662,10 +1682,15 @@ hipError_t launch_bucketmul(const MulArgs& args, bool record, int blocks_per_gro
   MulArgs a = args;
   a.bpg_recip = blocks_per_group >= 2 ? (uint32_t)((1ull << 32) / (uint64_t)blocks_per_group) : 0u;
   if (a.nv > 1) {
-    if (record || a.nv > 8) return hipErrorInvalidValue;
-    if (a.nv > 4) return launch_mul_bp<8>(a, grid, s);
-    if (a.nv > 2) return launch_mul_bp<4>(a, grid, s);
-    return launch_mul_bp<2>(a, grid, s);
+    if (a.nv > 8) return hipErrorInvalidValue;
+    if (record) {
+      if (a.nv > 4) return launch_mul_bp<true, 8>(a, grid, s);
+      if (a.nv > 2) return launch_mul_bp<true, 4>(a, grid, s);
+      return launch_mul_bp<true, 2>(a, grid, s);
+    }
+    if (a.nv > 4) return launch_mul_bp<false, 8>(a, grid, s);
+    if (a.nv > 2) return launch_mul_bp<false, 4>(a, grid, s);
+    return launch_mul_bp<false, 2>(a, grid, s);
   }
   if (ev && ev->start && !record)
     hipExtLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, ev->start,
@@ -1682,7 +1707,7 @@ hipError_t launch_bucketmul(const MulArgs& args, bool record, int blocks_per_gro
 }
 
 hipError_t launch_bucketmul_multi(const MulMulti& mm_in, int count, const int* blocks_per_group,
-                                  hipStream_t s) {
+                                  bool record, hipStream_t s) {
   if (count < 1 || count > EFFORT_MAX_MULTI || !blocks_per_group) return hipErrorInvalidValue;
   MulMulti mm = mm_in;
   uint32_t total = 0;
@@ -1695,7 +1720,10 @@ hipError_t launch_bucketmul_multi(const MulMulti& mm_in, int count, const int* b
   }
   for (int j = count; j <= EFFORT_MAX_MULTI; ++j) mm.first[j] = total;
   mm.count = count;
-  hipLaunchKernelGGL(k_bucketmul_multi, dim3(total), dim3(mul_threads<1>()), 0, s, mm);
+  if (record)
+    hipLaunchKernelGGL(k_bucketmul_multi<true>, dim3(total), dim3(mul_threads<1>()), 0, s, mm);
+  else
+    hipLaunchKernelGGL(k_bucketmul_multi<false>, dim3(total), dim3(mul_threads<1>()), 0, s, mm);
   return hipGetLastError();
 }
 
@@ -1849,13 +1877,20 @@ hipError_t launch_dense_gemm_small(const uint16_t* W, const float* v, int batch,
 
 // ---------------------------------------------------------------- parity outputs
 
-__global__ void k_debug_result(const uint32_t* result, float* cutoff, int64_t* K) {
-  if (threadIdx.x == 0) {
-    if (cutoff) *cutoff = __uint_as_float(result[0]);
+// Vector k's result words at result + k * stride (u32 words): its cutoff to
+// cutoff[k], K and K' to K[2k], K[2k + 1]; a reached crop to bit 1 of
+// status[k].
+__global__ void k_debug_result(const uint32_t* result, uint64_t stride, int count, float* cutoff,
+                               int64_t* K, uint32_t* status) {
+  const int k = (int)threadIdx.x;
+  if (k < count) {
+    const uint32_t* r = result + (uint64_t)k * stride;
+    if (cutoff) cutoff[k] = __uint_as_float(r[RES_CUTOFF]);
     if (K) {
-      K[0] = (int64_t)result[2];
-      K[1] = (int64_t)result[1];
+      K[2 * k] = (int64_t)r[RES_K];
+      K[2 * k + 1] = (int64_t)r[RES_KPRIME];
     }
+    if (status && (r[RES_FLAGS] & FLAG_CROP_REACHED)) status[k] |= 2u;
   }
 }
 
@@ -1871,8 +1906,11 @@ hipError_t launch_check_finite(const float* v, int64_t m, uint32_t* status, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_debug_result(const uint32_t* result, float* cutoff, int64_t* K, hipStream_t s) {
-  hipLaunchKernelGGL(k_debug_result, dim3(1), dim3(64), 0, s, result, cutoff, K);
+hipError_t launch_debug_result(const uint32_t* result, uint64_t stride, int count, float* cutoff,
+                               int64_t* K, uint32_t* status, hipStream_t s) {
+  if (count < 1 || count > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_debug_result, dim3(1), dim3(64), 0, s, result, stride, count, cutoff, K,
+                     status);
   return hipGetLastError();
 }
 

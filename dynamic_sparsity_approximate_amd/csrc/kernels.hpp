@@ -18,7 +18,7 @@ struct SelectArgs {
   int64_t N;         // m * P
   uint32_t* hist;    // [HIST_BINS], zero on entry (the multiply clears it)
   uint32_t* hist2;   // [1024] cleared here for the dispatch
-  uint32_t* result;  // [3] candidate count, cleared here
+  uint32_t* result;  // candidate count and flags, cleared here
   float* y;          // zeroed here (the multiply accumulates into it)
   int64_t n;
   uint32_t* bsum;        // [bsum_words] zeroed here (the dispatch may accumulate into it)
@@ -29,7 +29,10 @@ struct SelectArgs {
 };
 
 // result words of the workspace
-constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN = 4, RES_ABOVE = 5;
+constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN = 4, RES_ABOVE = 5,
+              RES_FLAGS = 6;
+// RES_FLAGS bit 0: a cropped layout left out an entry the keep rule keeps
+constexpr uint32_t FLAG_CROP_REACHED = 1u;
 
 // The quad-lane dispatch (P = 16, at most 8 column groups) takes QUAD_ROWS
 // rows per block.  When its blocks number at most 64 (in_dim <= 4096), block r
@@ -99,7 +102,9 @@ struct UnionArgs {
 // v + k m, y + k n and the workspace words + k vec_ws; one tile per vector.
 struct MulArgs {
   const float* v;
-  const uint32_t* entries;  // [m][row_stride]
+  const uint32_t* entries;  // units [m][G][gstride] (u32 format: one word per unit)
+  int64_t gstride;          // units per (row, group) run
+  const uint16_t* floor;    // cropped layouts: [m] largest magnitude key not stored (else null)
   const uint32_t* runlen;   // [G][m]
   const uint32_t* bsum;     // [nbd][G + 1]
   uint32_t* hist;           // [HIST_BINS], cleared here for the next call
@@ -115,7 +120,8 @@ struct MulArgs {
   uint64_t vec_ws;
   const uint32_t* vbsum;    // vector 0's own per-256-row sums: column G is its bound
                             // (bsum, the partition's sums, is the union when batched)
-  // parity recording (null in the timed path)
+  // parity recording (null in the timed path); a batched pass records
+  // vector p of the pass at row_kept + p m, fingerprint + p, mask + p m n
   int32_t* row_kept;
   unsigned long long* fingerprint;
   uint8_t* mask;
@@ -154,7 +160,7 @@ hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s);
 hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t s);
 // blocks_per_group[j]: matrix j's blocks per column group (its grid is G_j times that)
 hipError_t launch_bucketmul_multi(const MulMulti& mm, int count, const int* blocks_per_group,
-                                  hipStream_t s);
+                                  bool record, hipStream_t s);
 hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group, hipStream_t s,
                             const EventPair* ev = nullptr);
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
@@ -165,7 +171,10 @@ hipError_t launch_silu_mul(const float* h1, const float* h3, int64_t n, float* o
 hipError_t launch_axpby(const float* a, float ga, const float* b, float gb, int64_t n, float* out,
                         hipStream_t s);
 hipError_t launch_zero_bytes(void* p, uint64_t bytes, hipStream_t s);
-hipError_t launch_debug_result(const uint32_t* result, float* cutoff, int64_t* K, hipStream_t s);
+// count vectors' cutoffs and (K, K') from their result words, vector k's at
+// result + k * stride (u32 words)
+hipError_t launch_debug_result(const uint32_t* result, uint64_t stride, int count, float* cutoff,
+                               int64_t* K, uint32_t* status, hipStream_t s);
 // *status |= 1 when any of v[0..m) is a NaN or an infinity (status cleared by the caller).
 hipError_t launch_check_finite(const float* v, int64_t m, uint32_t* status, hipStream_t s);
 

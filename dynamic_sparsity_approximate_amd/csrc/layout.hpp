@@ -3,19 +3,26 @@
 // Layout blob (all offsets 256-byte aligned):
 //   [0, 256)        copy of the effort_desc
 //   probes          u16 [m][P]      fp16 magnitude bits at ranks ceil((k+1) n / P)
-//   counts          u32 [m][P][G4]  cumulative entries of group g in rank segments 0..k
+//   counts          u32 [m][P][G4]  cumulative units of group g in rank segments 0..k
 //                                   (G4 = G rounded up to 4, so a (row, segment) slice
-//                                   is 16-byte aligned)
-//   entries         u32 [m][G*TW]   per row, per group, the group's entries in rank
-//                                   order: low 16 bits = fp16 value bits, high 16
-//                                   bits = column index inside the group
+//                                   is 16-byte aligned); constant from segment crop - 1 on
+//   entries         units [m][G][gstride]
+//                                   per row, per group, the group's entries of the stored
+//                                   segments, segment by segment.  Format u32: one unit
+//                                   = one 32-bit entry, low 16 bits the fp16 value bits,
+//                                   high 16 bits the column inside the group, rank order
+//                                   inside a segment.  Format r12: one unit = a record of
+//                                   three 32-bit words holding 4 entries of one segment
+//                                   in column order (see the converter).
 //   rowmax          u16 [m]         largest magnitude key of each row
+//   floor           u16 [m]         (cropped layouts) largest magnitude key of the
+//                                   entries not stored
 //
 // Rank order is |w| descending, ties by column ascending.  Segment k of a row is
 // ranks (ceil(k n / P), ceil((k+1) n / P)]; its smallest magnitude is probe k.
-// Because a group's entries are stored in rank order, the entries of one row and
-// group that can pass the keep test form a prefix of its run, and the counts
-// table bounds that prefix by whole segments.
+// Because a group's entries are stored segment by segment in rank order, the
+// entries of one row and group that can pass the keep test lie in a prefix of
+// its run, and the counts table bounds that prefix by whole segments.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -32,9 +39,15 @@ inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 struct Geometry {
   int64_t m = 0, n = 0;
   int32_t P = 0, G = 0, G4 = 0, TW = 0;
-  int64_t row_stride = 0;
-  uint64_t off_probes = 0, off_counts = 0, off_entries = 0, off_rowmax = 0, total = 0;
+  int32_t format = EFFORT_ENTRY_U32;  // EFFORT_ENTRY_U32 or EFFORT_ENTRY_R12
+  int32_t crop = 0;                   // stored segments 0..crop-1 (crop = P: all)
+  int64_t gstride = 0;                // units per (row, group) run
+  int64_t row_stride = 0;             // units per row = G * gstride
+  uint64_t off_probes = 0, off_counts = 0, off_entries = 0, off_rowmax = 0, off_floor = 0, total = 0;
 };
+
+// 32-bit words per unit of the entries region
+inline int32_t unit_words(int32_t format) { return format == EFFORT_ENTRY_R12 ? 3 : 1; }
 
 // The smallest power of two, at least 2, whose groups hold at most
 // kTargetGroupWidth columns.  A power of two divides the CU count, so the
@@ -49,9 +62,25 @@ inline int32_t default_groups(int64_t n) {
   return (int32_t)g;
 }
 
-// Fills g from (m, n, P, groups).  groups = 0 picks the default.  The group
-// width is ceil(n / groups) rounded up to 64 columns, and the effective group
-// count is ceil(n / width), so no group is empty.
+// Offsets of the regions from the shape, the group stride and the options.
+inline void place_regions(Geometry* g) {
+  g->row_stride = (int64_t)g->G * g->gstride;
+  g->off_probes = kAlign;
+  g->off_counts = align_up(g->off_probes + (uint64_t)g->m * g->P * 2, kAlign);
+  g->off_entries = align_up(g->off_counts + (uint64_t)g->m * g->P * g->G4 * 4, kAlign);
+  g->off_rowmax = align_up(g->off_entries + (uint64_t)g->m * g->row_stride * unit_words(g->format) * 4,
+                           kAlign);
+  const bool cropped = g->crop < g->P;
+  g->off_floor = cropped ? align_up(g->off_rowmax + (uint64_t)g->m * 2, kAlign) : 0;
+  g->total = align_up((cropped ? g->off_floor : g->off_rowmax) + (uint64_t)g->m * 2, kAlign);
+}
+
+// Fills g from (m, n, P, groups) for an uncropped u32 layout, whose runs hold
+// every entry of their group (gstride = TW).  groups = 0 picks the default.
+// The group width is ceil(n / groups) rounded up to 64 columns, and the
+// effective group count is ceil(n / width), so no group is empty.  Other
+// formats and cropped layouts take the same shape and a data-dependent
+// gstride (the converter sets it, then calls place_regions).
 inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geometry* g) {
   if (m < 1 || n < 1 || P < 1 || (int64_t)P > n || groups < 0) return EFFORT_EINVAL;
   if (m > (1ll << 31) - 1 || n > (1ll << 31) - 1) return EFFORT_EUNSUPPORTED;
@@ -68,12 +97,10 @@ inline int make_geometry(int64_t m, int64_t n, int32_t P, int32_t groups, Geomet
   g->G = (int32_t)G;
   g->G4 = (int32_t)((G + 3) / 4 * 4);
   g->TW = (int32_t)tw;
-  g->row_stride = G * tw;
-  g->off_probes = kAlign;
-  g->off_counts = align_up(g->off_probes + (uint64_t)m * P * 2, kAlign);
-  g->off_entries = align_up(g->off_counts + (uint64_t)m * P * g->G4 * 4, kAlign);
-  g->off_rowmax = align_up(g->off_entries + (uint64_t)m * g->row_stride * 4, kAlign);
-  g->total = align_up(g->off_rowmax + (uint64_t)m * 2, kAlign);
+  g->format = EFFORT_ENTRY_U32;
+  g->crop = P;
+  g->gstride = tw;
+  place_regions(g);
   return EFFORT_OK;
 }
 
@@ -137,13 +164,28 @@ inline uint64_t desc_check_of(const effort_desc& d) {
   return h;
 }
 
+// Largest units per (row, group) run a layout of this shape may hold.
+inline int64_t max_gstride(const Geometry& g) {
+  // u32: one unit per entry; r12: every record holds at least one entry
+  return g.TW;
+}
+
 inline bool geometry_from_desc(const effort_desc* d, Geometry* g) {
   Geometry x;
   if (make_geometry(d->in_dim, d->out_dim, d->probes_per_row, d->groups, &x) != EFFORT_OK) return false;
+  if (d->entry_format != EFFORT_ENTRY_U32 && d->entry_format != EFFORT_ENTRY_R12) return false;
+  if (d->crop_segments < 1 || d->crop_segments > d->probes_per_row) return false;
+  x.format = d->entry_format;
+  x.crop = d->crop_segments;
+  if (d->group_stride < 1 || d->group_stride > max_gstride(x)) return false;
+  x.gstride = d->group_stride;
+  if (x.format == EFFORT_ENTRY_R12 && x.TW > 4096) return false;  // 12-bit column base
+  place_regions(&x);
   if (x.G != d->groups || x.TW != d->group_width || x.row_stride != d->row_stride ||
       x.off_probes != d->off_probes || x.off_counts != d->off_counts ||
       x.off_entries != d->off_entries || x.off_rowmax != d->off_rowmax ||
-      x.total != d->total_bytes || d->index_bytes != 2)
+      x.off_floor != d->off_floor || x.total != d->total_bytes ||
+      d->index_bytes != (x.format == EFFORT_ENTRY_U32 ? 2 : 0))
     return false;
   *g = x;
   return true;

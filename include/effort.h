@@ -55,7 +55,7 @@ enum {
 };
 
 #define EFFORT_MAGIC 0x4F464645u /* "EFFO" little-endian */
-#define EFFORT_VERSION 2u
+#define EFFORT_VERSION 3u
 #define EFFORT_MAX_GROUP_WIDTH 8192 /* output columns per group (fp32 LDS tile of 32 KiB) */
 #define EFFORT_MAX_BATCH 16
 #define EFFORT_MAX_MULTI 4 /* matrices of one effort_matvec_multi call */
@@ -63,18 +63,27 @@ enum {
 /* Host-side descriptor of a prepared layout; filled by effort_prepare*, passed
    by pointer to the multiply.  Plain old data; a copy is stored at the start of
    the layout blob. */
+/* Entry formats of a layout (effort_desc.entry_format). */
+#define EFFORT_ENTRY_U32 0 /* 4 bytes per entry: fp16 value, 16-bit column in the group */
+#define EFFORT_ENTRY_R12 1 /* 3 bytes per entry: records of 4 entries in 12 bytes (see
+                              effort_prepare_host_opts) */
+
 typedef struct effort_desc {
   uint32_t magic, version;
   int64_t in_dim, out_dim;    /* m, n */
   int32_t probes_per_row;     /* P, 1 <= P <= n */
   int32_t groups;             /* G: output-column groups */
   int32_t group_width;        /* TW: columns per group, multiple of 64; last group may be narrower */
-  int32_t index_bytes;        /* bytes of the in-group column index of an entry (2) */
-  int64_t row_stride;         /* entries per stored row = G * TW */
+  int32_t index_bytes;        /* bytes of the column index of an entry: 2 (u32), 0 (r12) */
+  int64_t row_stride;         /* storage units per stored row = G * group_stride */
+  int64_t group_stride;       /* storage units per (row, group) run (u32: entries, r12: records) */
+  int32_t entry_format;       /* EFFORT_ENTRY_U32 or EFFORT_ENTRY_R12 */
+  int32_t crop_segments;      /* c: rank segments 0..c-1 of every row are stored; c = P: all */
   uint64_t off_probes;        /* byte offsets inside the layout */
   uint64_t off_counts;
   uint64_t off_entries;
   uint64_t off_rowmax;
+  uint64_t off_floor;         /* cropped layouts: largest magnitude key not stored, per row (else 0) */
   uint64_t total_bytes;
   uint64_t checksum;          /* FNV-1a-64 over the blob's 8-byte words after the header */
   uint64_t desc_check;        /* FNV-1a-64 over all fields above */
@@ -124,6 +133,48 @@ int effort_prepare_host(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim,
 int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
                            int32_t groups, void* layout_host, uint64_t layout_bytes,
                            effort_desc* desc_out);
+
+/* Layout options (effort_prepare_host_opts):
+   groups         output-column groups, 0 = effort_default_groups(out_dim).
+   entry_format   EFFORT_ENTRY_U32: per entry the fp16 value and a 16-bit column
+                  inside its group, rank order inside a segment.
+                  EFFORT_ENTRY_R12 (group width <= 4096, else EUNSUPPORTED): inside
+                  each (row, group, segment) the entries in column order, 4 to a
+                  12-byte record -- two words of fp16 values, then the first
+                  column (12 bits) and three column steps (7, 7, 6 bits); a step
+                  that does not fit ends the record early and pads (value
+                  0x8000, step 0) fill it; a -0.0 weight is stored as +0.0.
+                  The position bits an entry spends against what its bucket
+                  already tells is the trade-off of the author's reply to kwikiel
+                  in [HN].
+   crop_segments  0 or P: every segment is stored.  c in [1, P): only the rank
+                  segments 0..c-1 of each row (the largest magnitudes) are stored
+                  ([HN] post text: the format lets one skip a share of the least
+                  important weights; the reply about running Mixtral from its top
+                  ~70 %).  Probes and rowmax still describe the whole row, so the
+                  cutoff is the uncropped one; a call keeps exactly the uncropped
+                  kept set whenever none of its kept products lies in a dropped
+                  segment, and otherwise keeps the stored part of it and reports
+                  that (effort_matvec_debug status bit 1).
+   reserved       0. */
+typedef struct effort_prepare_opts {
+  int32_t groups;
+  int32_t entry_format;
+  int32_t crop_segments;
+  int32_t reserved;
+} effort_prepare_opts;
+
+/* Exact layout bytes of W with these options: a host pass over W (the length
+   of a cropped or r12 run depends on the data).  EINVAL: bad options or
+   non-finite W; EUNSUPPORTED as effort_layout_bytes_ex. */
+int effort_layout_bytes_opts(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                             const effort_prepare_opts* opts, uint64_t* bytes);
+
+/* effort_prepare_host with options; layout_bytes must be at least
+   effort_layout_bytes_opts of the same arguments (ENOSPACE otherwise). */
+int effort_prepare_host_opts(const uint16_t* w_fp16, int64_t in_dim, int64_t out_dim, int32_t P,
+                             const effort_prepare_opts* opts, void* layout_host,
+                             uint64_t layout_bytes, effort_desc* desc_out);
 
 /* Same, then copies the blob into caller-owned device memory layout_dev on
    `stream`.  Uses a temporary host buffer and synchronizes `stream` before
@@ -186,13 +237,41 @@ int effort_matvec_multi(const effort_desc* descs, const void* const* layouts_dev
    fingerprint_dev[1]   sum over kept (i,j) of splitmix64-output(i*out_dim+j), mod 2^64;
    kept_mask_dev        uint8 [in_dim][out_dim], 1 where kept;
    status_dev[1]        bit 0 set when v holds a NaN or an infinity (outside
-                        the contract: the other outputs are then unspecified).
-   Same kernels as effort_matvec with the recording switched on; untimed. */
+                        the contract: the other outputs are then unspecified);
+                        bit 1 set when the layout is cropped and the keep rule
+                        keeps a product of a dropped segment (the outputs then
+                        cover the stored part of the kept set).
+   Same kernels as effort_matvec with the recording switched on: the keep test
+   and the accumulation are the timed path's own; recording only adds the
+   stores of the kept pairs.  Untimed. */
 int effort_matvec_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                         float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
                         float* cutoff_dev, int64_t* K_dev, int32_t* row_kept_dev,
                         uint64_t* fingerprint_dev, uint8_t* kept_mask_dev, uint32_t* status_dev,
                         void* stream);
+
+/* effort_matvec_batched plus the parity outputs of every vector (device
+   pointers, each may be NULL): cutoff_dev[batch], K_dev[batch][2] (K, K'),
+   row_kept_dev[batch][in_dim], fingerprint_dev[batch], kept_mask_dev
+   [batch][in_dim][out_dim], each as in effort_matvec_debug.  The call takes
+   the same route as effort_matvec_batched for the same batch and effort (the
+   union pass over up to 8 vectors, or launches of up to 4 vectors with their
+   own multiplies), with recording switched on in those kernels. */
+int effort_matvec_batched_debug(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                                int32_t batch, float effort, float* y_dev, void* ws_dev,
+                                uint64_t ws_bytes, float* cutoff_dev, int64_t* K_dev,
+                                int32_t* row_kept_dev, uint64_t* fingerprint_dev,
+                                uint8_t* kept_mask_dev, void* stream);
+
+/* effort_matvec_multi plus the parity outputs of every pair (device pointers,
+   each may be NULL): cutoff_dev[count], K_dev[count][2], fingerprint_dev
+   [count]; row_kept_dev is a host array of count device pointers (each may be
+   NULL), pair j's counts [descs[j].in_dim].  Same kernels and launches as
+   effort_matvec_multi with recording switched on. */
+int effort_matvec_multi_debug(const effort_desc* descs, const void* const* layouts_dev, int32_t count,
+                              const float* const* vs_dev, const float* efforts, float* const* ys_dev,
+                              void* ws_dev, uint64_t ws_bytes, float* cutoff_dev, int64_t* K_dev,
+                              int32_t* const* row_kept_dev, uint64_t* fingerprint_dev, void* stream);
 
 /* effort_matvec with kernel timing, for measurement.  events[0..5] are hipEvent_t
    pairs (start, stop) for the cutoff kernel, the dispatch kernel and the

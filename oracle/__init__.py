@@ -16,6 +16,11 @@ Parity status of each function (pins live in tests/test_oracle_pins.py):
                invariants; dropped-mass bound
   run          composition of the above
   dense        pinned: numpy float64 matmul
+  stored_mask  pinned: numpy lexsort of (|w| desc, column asc) per row; crop = P stores all
+  run_cropped  pinned: crop = P equals run(); effort 1 keeps exactly the stored pairs; a
+               call whose kept set lies in the stored part equals run(); numpy sums
+  silu_mul     pinned: silu(x) - silu(-x) = x, silu(0) = 0, silu(ln 3) = (3/4) ln 3,
+               silu(x) -> x for large x, linear in the second operand
 """
 from __future__ import annotations
 
@@ -58,8 +63,10 @@ def _load():
     lib.oracle_keep_sum.argtypes = [p, i64, i64, p, f32, p, p, p, p, p]
     lib.oracle_run.argtypes = [p, i64, i64, p, i32, p, f32, p, p, p, p, p, p, p, p, p]
     lib.oracle_dense.argtypes = [p, i64, i64, p, p]
+    lib.oracle_stored_mask.argtypes = [p, i64, i64, i32, i32, p]
+    lib.oracle_run_cropped.argtypes = [p, i64, i64, p, i32, i32, p, f32, p, p, p, p, p, p, p, p, p]
     for f in (lib.oracle_probes, lib.oracle_chart, lib.oracle_cutoff, lib.oracle_keep_sum,
-              lib.oracle_run, lib.oracle_dense):
+              lib.oracle_run, lib.oracle_dense, lib.oracle_stored_mask, lib.oracle_run_cropped):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -159,6 +166,39 @@ def run(W, pr, v, effort: float, mask: bool = False) -> dict:
     return {"cutoff": np.float32(c.value), "K": int(K.value), "Kprime": int(Kp.value),
             "y": y, "row_kept": rk, "row_chart_kept": rck, "fingerprint": int(fp.value),
             "mask": mk, "total_kept": int(tot.value), "m": m, "n": n, "P": P}
+
+
+def stored_mask(W, P: int, crop: int) -> np.ndarray:
+    """uint8 [m][n]: the pairs a layout cropped to segments 0..crop-1 stores."""
+    W = _w(W)
+    m, n = W.shape
+    out = np.empty((m, n), dtype=np.uint8)
+    if _load().oracle_stored_mask(_ptr(W), m, n, P, crop, _ptr(out)):
+        raise ValueError("oracle_stored_mask: invalid argument")
+    return out
+
+
+def run_cropped(W, pr, v, effort: float, crop: int, mask: bool = False) -> dict:
+    """The rule on a layout cropped to segments 0..crop-1 of P = pr.shape[1]."""
+    W = _w(W)
+    m, n = W.shape
+    pr = np.ascontiguousarray(pr, dtype=np.float32)
+    P = pr.shape[1]
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    y = np.empty(n, dtype=np.float64)
+    rk = np.empty(m, dtype=np.int64)
+    fp, tot, K, Kp = ctypes.c_uint64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    c, reached = ctypes.c_float(), ctypes.c_int32()
+    mk = np.empty((m, n), dtype=np.uint8) if mask else None
+    rc = _load().oracle_run_cropped(_ptr(W), m, n, _ptr(pr), P, crop, _ptr(v), effort,
+                                    ctypes.byref(c), ctypes.byref(K), ctypes.byref(Kp), _ptr(y),
+                                    _ptr(rk), ctypes.byref(fp), _ptr(mk), ctypes.byref(tot),
+                                    ctypes.byref(reached))
+    if rc:
+        raise ValueError("oracle_run_cropped: invalid argument")
+    return {"cutoff": np.float32(c.value), "K": int(K.value), "Kprime": int(Kp.value), "y": y,
+            "row_kept": rk, "fingerprint": int(fp.value), "mask": mk, "total_kept": int(tot.value),
+            "crop_reached": bool(reached.value), "m": m, "n": n, "P": P}
 
 
 def dense(W, v) -> np.ndarray:

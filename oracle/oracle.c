@@ -126,9 +126,9 @@ int oracle_cutoff(const float* chart, int64_t N, float effort, int64_t* K, float
 
 /* bucketMul of the [HN] pseudocode, done without buckets: every product whose
    fp32 magnitude reaches the cutoff is kept (O(effort * inDim * outDim)
-   multiplications in the real method, [HT]); kept products are scattered into
-   the output ("multiply it by 256, and add it into the output vector at the 3rd
-   row", the passage bigcat12345678 quotes).  Here all m*n pairs are swept. */
+   multiplications in the real method, [HT]); each kept product is added into
+   the output element its column names (the scatter step of the write-up that
+   bigcat12345678 quotes in [HN]).  Here all m*n pairs are swept. */
 int oracle_keep_sum(const uint16_t* W, int64_t m, int64_t n, const float* v, float cutoff,
                     double* y_double, int64_t* row_kept, uint64_t* fingerprint, uint8_t* mask,
                     int64_t* total_kept) {
@@ -156,6 +156,100 @@ int oracle_keep_sum(const uint16_t* W, int64_t m, int64_t n, const float* v, flo
   }
   if (fingerprint) *fingerprint = fp;
   if (total_kept) *total_kept = total;
+  return 0;
+}
+
+/* The stored part of a cropped layout (the [HN] post text: the data format
+   lets one load only part of the model, skipping a share of the least
+   important weights; the author runs Mixtral from its top ~70 %).  Reading
+   used here: rows are cut into the same P rank segments as the probes, and
+   segments 0..crop-1 -- the ceil(crop n / P) largest magnitudes of the row,
+   ties going to the lower column -- are stored.  stored[i*n+j] = 1 for those. */
+typedef struct {
+  uint16_t key;
+  int64_t col;
+} key_col;
+
+static int cmp_key_desc_col_asc(const void* a, const void* b) {
+  const key_col* x = (const key_col*)a;
+  const key_col* y = (const key_col*)b;
+  if (x->key != y->key) return (x->key < y->key) - (x->key > y->key);
+  return (x->col > y->col) - (x->col < y->col);
+}
+
+int oracle_stored_mask(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t crop,
+                       uint8_t* stored) {
+  if (!W || !stored || m <= 0 || n <= 0 || P < 1 || P > n || crop < 1 || crop > P) return 1;
+  key_col* kc = (key_col*)malloc((size_t)n * sizeof(key_col));
+  if (!kc) return 1;
+  int64_t keep = ((int64_t)crop * n + P - 1) / P; /* ceil(crop n / P) */
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t j = 0; j < n; ++j) {
+      kc[j].key = (uint16_t)(W[i * n + j] & 0x7FFF);
+      kc[j].col = j;
+      stored[i * n + j] = 0;
+    }
+    qsort(kc, (size_t)n, sizeof(key_col), cmp_key_desc_col_asc);
+    for (int64_t r = 0; r < keep; ++r) stored[i * n + kc[r].col] = 1;
+  }
+  free(kc);
+  return 0;
+}
+
+/* The rule on a cropped layout: probes, chart and cutoff of the whole matrix
+   (the crop drops entries, not the statistics that place the cutoff); kept =
+   the stored pairs whose product reaches the cutoff; *crop_reached = 1 when a
+   pair that is not stored reaches it too (the uncropped rule would keep it). */
+int oracle_run_cropped(const uint16_t* W, int64_t m, int64_t n, const float* probes, int32_t P,
+                       int32_t crop, const float* v, float effort, float* cutoff, int64_t* K,
+                       int64_t* Kprime, double* y_double, int64_t* row_kept, uint64_t* fingerprint,
+                       uint8_t* mask, int64_t* total_kept, int32_t* crop_reached) {
+  if (!W || !probes || !v || !y_double || m <= 0 || n <= 0 || P < 1 || P > n) return 1;
+  int64_t N = m * P;
+  float* chart = (float*)malloc((size_t)N * sizeof(float));
+  uint8_t* stored = (uint8_t*)malloc((size_t)(m * n));
+  if (!chart || !stored) {
+    free(chart);
+    free(stored);
+    return 1;
+  }
+  float c = 0.0f;
+  int rc = oracle_chart(v, probes, m, P, chart);
+  if (!rc) rc = oracle_cutoff(chart, N, effort, K, &c, Kprime);
+  if (!rc) rc = oracle_stored_mask(W, m, n, P, crop, stored);
+  free(chart);
+  if (rc) {
+    free(stored);
+    return rc;
+  }
+  for (int64_t j = 0; j < n; ++j) y_double[j] = 0.0;
+  uint64_t fp = 0;
+  int64_t total = 0;
+  int32_t reached = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    float av = fabsf(v[i]);
+    double vi = (double)v[i];
+    int64_t cnt = 0;
+    for (int64_t j = 0; j < n; ++j) {
+      uint16_t h = W[i * n + j];
+      int keep = (av * magnitude_f32(h) >= c);
+      if (keep && !stored[i * n + j]) reached = 1;
+      keep = keep && stored[i * n + j];
+      if (mask) mask[i * n + j] = (uint8_t)keep;
+      if (keep) {
+        y_double[j] += vi * oracle_f16_to_f64(h);
+        fp += oracle_pair_hash((uint64_t)(i * n + j));
+        ++cnt;
+      }
+    }
+    if (row_kept) row_kept[i] = cnt;
+    total += cnt;
+  }
+  free(stored);
+  if (cutoff) *cutoff = c;
+  if (fingerprint) *fingerprint = fp;
+  if (total_kept) *total_kept = total;
+  if (crop_reached) *crop_reached = reached;
   return 0;
 }
 

@@ -57,6 +57,19 @@ int oracle_run(const uint16_t* W, int64_t m, int64_t n, const float* probes, int
                double* y_double, int64_t* row_kept, int64_t* row_chart_kept,
                uint64_t* fingerprint, uint8_t* mask, int64_t* total_kept);
 
+/* Cropped layouts: stored[m][n] = 1 for the ceil(crop n / P) largest
+   magnitudes of each row (ties: lower column first), 1 <= crop <= P. */
+int oracle_stored_mask(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t crop,
+                       uint8_t* stored);
+
+/* The rule with only the stored pairs of a cropped layout kept: cutoff from
+   the whole matrix's probes; kept = stored pairs reaching it; *crop_reached =
+   1 when an unstored pair reaches it.  Outputs as oracle_run. */
+int oracle_run_cropped(const uint16_t* W, int64_t m, int64_t n, const float* probes, int32_t P,
+                       int32_t crop, const float* v, float effort, float* cutoff, int64_t* K,
+                       int64_t* Kprime, double* y_double, int64_t* row_kept, uint64_t* fingerprint,
+                       uint8_t* mask, int64_t* total_kept, int32_t* crop_reached);
+
 /* plain dense y_j = sum_i v_i W_ij in double, i ascending */
 int oracle_dense(const uint16_t* W, int64_t m, int64_t n, const float* v, double* y_double);
 

@@ -318,3 +318,182 @@ def test_multi_sizes_and_rejects():
     with pytest.raises(E.EffortError) as ei:
         E.effort_workspace_bytes_multi([])
     assert ei.value.code == B.EFFORT_EINVAL
+
+
+# ---------------------------------------------------------------- error handling of the binding
+
+def test_binding_reinitialises_workspace_after_hip_error(monkeypatch):
+    """A call that fails with EFFORT_EHIP part-way may leave set the workspace
+    words every call expects to find zero; the binding zero-fills the
+    workspace again before raising.  The library is replaced by a stand-in
+    that reports the error, so nothing runs on a device."""
+    calls = []
+    real = B._lib
+
+    class StandIn:
+        def __getattr__(self, name):
+            return getattr(real, name)
+
+        def _fail(self, name, code):
+            def f(*args):
+                calls.append((name,))
+                return code
+            return f
+
+        def effort_workspace_init(self, ws, nbytes, stream):
+            calls.append(("init", ws, nbytes))
+            return B.EFFORT_OK
+
+    fake = StandIn()
+    monkeypatch.setattr(B, "_lib", fake)
+    desc, blob = _desc_and_blob()
+    ws = np.zeros(4096, np.uint8)  # host memory standing in for a device workspace
+    v = np.zeros(desc.in_dim, np.float32)
+    y = np.zeros(desc.out_dim, np.float32)
+    entries = [
+        ("effort_matvec", lambda: B.effort_matvec(desc, blob, v, 0.25, y, ws, ws.size)),
+        ("effort_matvec_batched", lambda: B.effort_matvec_batched(desc, blob, v, 1, 0.25, y, ws, ws.size)),
+        ("effort_matvec_debug", lambda: B.effort_matvec_debug(desc, blob, v, 0.25, y, ws, ws.size)),
+        ("effort_matvec_batched_debug",
+         lambda: B.effort_matvec_batched_debug(desc, blob, v, 1, 0.25, y, ws, ws.size)),
+        ("effort_matvec_multi", lambda: B.effort_matvec_multi([desc], [blob], v, 0.25, [y], ws, ws.size)),
+        ("effort_matvec_multi_debug",
+         lambda: B.effort_matvec_multi_debug([desc], [blob], v, 0.25, [y], ws, ws.size)),
+    ]
+    for name, call in entries:
+        for code in (B.EFFORT_EHIP, B.EFFORT_EINVAL):
+            calls.clear()
+            monkeypatch.setattr(StandIn, name, lambda self, *a, _n=name, _c=code: (calls.append((_n,)), _c)[1],
+                                raising=False)
+            with pytest.raises(E.EffortError) as ei:
+                call()
+            assert ei.value.code == code, name
+            if code == B.EFFORT_EHIP:
+                assert calls == [(name,), ("init", ws.ctypes.data, ws.size)], (name, calls)
+            else:
+                assert calls == [(name,)], (name, calls)
+
+
+# ---------------------------------------------------------------- layout options: crop, r12 records
+
+def decode_runs(desc, blob):
+    """Per (row, group): the storage units of the run decoded to a list of
+    (unit index, in-group column, value bits) in storage order; pads of r12
+    records are dropped.  Also the counts table [m][P][G]."""
+    m, P, G = desc.in_dim, desc.probes_per_row, desc.groups
+    G4 = (G + 3) // 4 * 4
+    cnt = blob[desc.off_counts: desc.off_counts + m * P * G4 * 4].view(np.uint32).reshape(m, P, G4)[:, :, :G]
+    uw = 3 if desc.entry_format == B.EFFORT_ENTRY_R12 else 1
+    words = blob[desc.off_entries: desc.off_entries + m * desc.row_stride * uw * 4].view(np.uint32)
+    words = words.reshape(m, G, desc.group_stride * uw)
+    runs = {}
+    for i in range(m):
+        for g in range(G):
+            L = int(cnt[i, P - 1, g])
+            w = words[i, g]
+            out = []
+            if uw == 1:
+                for u in range(L):
+                    out.append((u, int(w[u] >> 16), int(w[u] & 0xFFFF)))
+            else:
+                for u in range(L):
+                    w0, w1, w2 = (int(x) for x in w[3 * u: 3 * u + 3])
+                    vals = [w0 & 0xFFFF, w0 >> 16, w1 & 0xFFFF, w1 >> 16]
+                    c0 = w2 & 0xFFF
+                    c1 = c0 + ((w2 >> 12) & 0x7F)
+                    c2 = c1 + ((w2 >> 19) & 0x7F)
+                    c3 = c2 + (w2 >> 26)
+                    for c, val in zip((c0, c1, c2, c3), vals):
+                        if val != 0x8000:
+                            out.append((u, c, val))
+            runs[(i, g)] = out
+    return cnt, runs
+
+
+@pytest.mark.parametrize("m,n,P,G,fmt,crop", [
+    (9, 300, 16, 3, 0, 12), (6, 1000, 16, 2, 1, 0), (6, 1000, 16, 2, 1, 9), (5, 37, 3, 0, 1, 0),
+    (4, 4096, 16, 1, 1, 16), (3, 130, 7, 3, 0, 1), (8, 5000, 8, 0, 1, 5), (2, 64, 64, 1, 1, 40)])
+def test_layout_options_roundtrip(m, n, P, G, fmt, crop):
+    W, _ = rand_case(m, n, seed=m + n + P + crop, tag="opts")
+    if m > 2:
+        W[1, ::3] = W[1, 0]        # ties
+        W[2, : n // 2] = 0         # zeros
+        W[2, n // 2: n // 2 + 5] = 0x8000  # negative zeros
+    d, blob = E.effort_prepare_host(W, P, G, fmt, crop)
+    E.effort_layout_check(d, blob)
+    assert d.total_bytes == E.effort_layout_bytes_opts(W, P, G, fmt, crop) <= blob.size
+    c = crop or P
+    assert d.entry_format == fmt and d.crop_segments == c
+    assert d.index_bytes == (2 if fmt == 0 else 0)
+    st = oracle.stored_mask(W, P, c)
+    pr, _, _ = decode(d, blob) if fmt == 0 else (None, None, None)
+    probes = blob[d.off_probes: d.off_probes + m * P * 2].view(np.uint16).reshape(m, P)
+    assert np.array_equal(probes.view(np.float16).astype(np.float32), oracle.probes(W, P))
+    assert np.array_equal(decode_rowmax(d, blob), (W & 0x7FFF).max(axis=1))
+    if c < P:
+        floor = blob[d.off_floor: d.off_floor + m * 2].view(np.uint16)
+        for i in range(m):
+            dropped = (W[i] & 0x7FFF)[st[i] == 0]
+            assert floor[i] == (dropped.max() if dropped.size else 0)
+    else:
+        assert d.off_floor == 0
+    cnt, runs = decode_runs(d, blob)
+    TW = d.group_width
+    for i in range(m):
+        keys = (W[i] & 0x7FFF).astype(np.int64)
+        order = np.lexsort((np.arange(n), -keys))
+        rank = np.empty(n, np.int64)
+        rank[order] = np.arange(1, n + 1)
+        seg = np.searchsorted([-(-(k + 1) * n // P) for k in range(P)], rank)  # segment of each column
+        seen = np.zeros(n, bool)
+        for g in range(d.groups):
+            width = min(TW, n - g * TW)
+            ents = runs[(i, g)]
+            assert int(cnt[i, P - 1, g]) <= d.group_stride
+            for k in range(c, P):  # constant past the crop
+                assert cnt[i, k, g] == cnt[i, c - 1, g]
+            cols = np.array([g * TW + e[1] for e in ents], np.int64)
+            vals = np.array([e[2] for e in ents], np.int64)
+            units = np.array([e[0] for e in ents], np.int64)
+            assert np.all(cols - g * TW < width)
+            want_vals = W[i, cols].astype(np.int64)
+            if fmt == 1:
+                want_vals[want_vals == 0x8000] = 0  # -0 stored as +0
+            assert np.array_equal(vals, want_vals)
+            assert not seen[cols].any()
+            seen[cols] = True
+            # every unit lies in the segment the counts table gives it
+            lo = np.concatenate([[0], cnt[i, :, g][:-1]]).astype(np.int64)
+            for k in range(c):
+                inside = (units >= lo[k]) & (units < cnt[i, k, g])
+                assert np.all(seg[cols[inside]] == k), (i, g, k)
+                ck = cols[inside]
+                if fmt == 0:
+                    assert np.all(np.diff(rank[ck]) > 0)  # rank order in the segment
+                else:
+                    assert np.all(np.diff(ck) > 0)        # column order in the segment
+        assert np.array_equal(seen, st[i].astype(bool))  # exactly the stored pairs
+
+
+def test_r12_records_are_three_bytes_per_entry():
+    """At 4096 columns and P = 16 (a step above 63 or 127 columns is rare) the
+    records hold close to 4 entries: the entries region is within a few
+    percent of 3 bytes per weight, against 4 for the u32 format."""
+    W, _ = rand_case(64, 4096, seed=7, tag="r12size")
+    d, blob = E.effort_prepare_host(W, 16, 1, B.EFFORT_ENTRY_R12)
+    ent_bytes = d.off_rowmax - d.off_entries
+    assert ent_bytes <= 3.1 * W.size
+    cnt, runs = decode_runs(d, blob)
+    used = sum(int(cnt[i, 15, 0]) for i in range(64))
+    assert used * 4 <= 1.03 * W.size  # record slots per weight
+
+
+def test_layout_options_reject():
+    W, _ = rand_case(4, 9000, seed=8, tag="rej")
+    with pytest.raises(E.EffortError) as ei:  # r12 columns need groups of at most 4096
+        E.effort_prepare_host(W, 16, 1, B.EFFORT_ENTRY_R12)
+    assert ei.value.code == B.EFFORT_EUNSUPPORTED
+    for bad in ((2, 0), (0, 17), (0, -1)):
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_prepare_host(W, 16, 0, *bad)
+        assert ei.value.code == B.EFFORT_EINVAL

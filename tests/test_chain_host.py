@@ -39,3 +39,26 @@ def test_route_top2_ties_and_shift():
     r1 = E.route_top2([0.1, 2.0, -1.0, 1.5])
     r2 = E.route_top2([100.1, 102.0, 99.0, 101.5])
     assert r1[:2] == r2[:2] and math.isclose(r1[2], r2[2], rel_tol=1e-9)
+
+
+def test_effort_schedule_lookup_order():
+    from dynamic_sparsity_approximate_amd import EffortSchedule
+    s = EffortSchedule(0.25, {(3, "wq"): 0.5, (None, "w2"): 0.125, (7, None): 0.75})
+    assert s(3, "wq") == 0.5          # (unit, role)
+    assert s(3, "w2") == 0.125        # (None, role) before (unit, None)
+    assert s(7, "w2") == 0.125
+    assert s(7, "wk") == 0.75         # (unit, None)
+    assert s(0, "wk") == 0.25         # default
+    a = EffortSchedule.from_array([[0.1] * 7, [0.3] * 7], head=0.9)
+    assert a(1, "w1") == 0.3 and a(None, "head") == 0.9 and abs(a.default - 0.2) < 1e-12
+
+
+def test_effort_schedule_rejects_bad_efforts():
+    from dynamic_sparsity_approximate_amd import EffortSchedule
+    for bad in (0.0, -0.1, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            EffortSchedule(bad)
+        with pytest.raises(ValueError):
+            EffortSchedule(0.5, {(0, "wq"): bad})
+    with pytest.raises(ValueError):
+        EffortSchedule.from_array([[0.5, 0.5]])

@@ -1,0 +1,87 @@
+"""GPU parity of cropped layouts (only rank segments 0..c-1 of every row are
+stored): against the oracle's cropped rule -- the cutoff of the whole matrix,
+the stored part of its kept set -- and, whenever the kept set lies inside the
+stored part (the call reports whether it does), against the uncropped rule
+itself.  Cutoff bits, K, K', per-row kept counts, fingerprint, mask (small
+cases), y within rel-L2 1e-3, and the reported flag equal to the oracle's."""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import dynamic_sparsity_approximate_amd as E  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from _parity import check  # noqa: E402
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("m,n,G,crop", [(513, 2049, 3, 12), (300, 1000, 0, 6), (4096, 14336, 0, 11),
+                                        (1000, 300, 1, 15)])
+def test_cropped_matches_oracle(m, n, G, crop):
+    d = dev()
+    P = 16
+    W = synth.weights(m, n, seed=crop, stream=synth.stream_id("crop", "W", m, n))
+    full_d, _ = E.effort_prepare_host(W, P, G)
+    M = E.EffortMatrix(W, P=P, groups=G, device=d, crop=crop)
+    assert M.desc.crop_segments == crop
+    assert M.layout_bytes < full_d.total_bytes
+    say("crop %d/%d of %dx%d: layout %.1f MB against %.1f MB" % (
+        crop, P, m, n, M.layout_bytes / 1e6, full_d.total_bytes / 1e6))
+    pr = oracle.probes(W, P)
+    small = m * n <= (1 << 22)
+    reached = []
+    for seed in (0, 1):
+        v = synth.activations(m, seed=seed, stream=synth.stream_id("crop", "v", m))
+        vt = torch.from_numpy(v).to(d)
+        for effort in (1.0, 0.5, 0.25, 0.05):
+            got = M.matvec_debug(vt, effort, with_mask=small)
+            ref = oracle.run_cropped(W, pr, v, effort, crop, mask=small)
+            where = (m, n, crop, seed, effort)
+            check(got, ref, small, where)
+            assert got["crop_reached"] == ref["crop_reached"], where
+            if not ref["crop_reached"]:
+                full = oracle.run(W, pr, v, effort)
+                check(got, full, False, where)
+            reached.append(ref["crop_reached"])
+            # the unrecorded call gives the same y
+            y = M.matvec(vt, effort)
+            torch.cuda.synchronize()
+            assert np.linalg.norm(y.cpu().numpy() - got["y"]) <= 1e-6 * max(np.linalg.norm(got["y"]), 1e-30)
+    assert any(reached) and not all(reached)  # both sides of the crop are exercised
+
+
+def test_cropped_batched_and_multi():
+    d = dev()
+    m, n, P, crop = 700, 3000, 16, 10
+    W = synth.weights(m, n, seed=3, stream=synth.stream_id("crop2", "W", m, n))
+    M = E.EffortMatrix(W, P=P, device=d, batch=6, crop=crop)
+    pr = oracle.probes(W, P)
+    V = np.stack([synth.activations(m, seed=s, stream=synth.stream_id("crop2", "v", m)) for s in range(6)])
+    for effort, b in ((0.25, 6), (0.1, 3)):
+        got = M.matvec_batched_debug(torch.from_numpy(V[:b]).to(d), effort)
+        for k in range(b):
+            check(got[k], oracle.run_cropped(W, pr, V[k], effort, crop), where=("batched", effort, k))
+    W2 = synth.weights(m, 1500, seed=4, stream=synth.stream_id("crop2", "W2", m))
+    M2 = E.EffortMatrix(W2, P=P, device=d, crop=crop)
+    group = E.EffortGroup([M, M2])
+    rec = E.Recorder(d)
+    vt = torch.from_numpy(V[0]).to(d)
+    ys = group.matvec(vt, [0.3, 0.2], record=(rec, [0, 1]))
+    res = rec.results()
+    for j, (Wj, e) in enumerate(((W, 0.3), (W2, 0.2))):
+        ref = oracle.run_cropped(Wj, oracle.probes(Wj, P), V[0], e, crop)
+        check(res[j], ref, where=("multi", j), y=ys[j].cpu().numpy())

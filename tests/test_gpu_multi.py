@@ -2,10 +2,12 @@
 (matrix, vector) pairs -- matrices sharing one input, or each with its own,
 of different heights -- each at its own effort, in one launch per kernel.
 
-Each output must equal the single-matrix call on the same matrix and vector
-(the same cutoff and kept set; only the order of the fp32 atomics of the
-flush differs, so rel-L2 <= 1e-5 is asked) and lie within rel-L2 1e-3 of the
-oracle.
+Each pair records its parity outputs (the same kernels and launches with
+recording on) and must match the oracle: cutoff bits, K, K', per-row kept
+counts, kept-set fingerprint, y within rel-L2 1e-3.  The unrecorded call must
+give the single-matrix call's output (the same cutoff and kept set; only the
+order of the fp32 atomics of the flush differs, so rel-L2 <= 1e-5 is asked)
+and the recorded call's.
 """
 import sys
 
@@ -18,6 +20,7 @@ torch = pytest.importorskip("torch")
 import dynamic_sparsity_approximate_amd as E  # noqa: E402
 import oracle  # noqa: E402
 import synth  # noqa: E402
+from _parity import check  # noqa: E402
 
 SAME_TOL = 1e-5
 ORACLE_TOL = 1e-3
@@ -36,7 +39,15 @@ def rel_l2(y, ref):
     return float(d / nr) if nr else float(d)
 
 
-def run_case(m, ns, efforts, seed, with_oracle=True):
+def recorded(group, vs, efforts):
+    """One recorded multi-matrix call: outputs and per-pair parity dicts."""
+    rec = E.Recorder(group.mats[0].layout.device)
+    ys = group.matvec(vs, efforts, record=(rec, list(range(len(group.mats)))))
+    res = rec.results()
+    return [y.cpu().numpy() for y in ys], [res[j] for j in range(len(group.mats))]
+
+
+def run_case(m, ns, efforts, seed):
     d = dev()
     Ws = [synth.weights(m, n, seed=seed + j, stream=synth.stream_id("multi", "W", m, n)) for j, n in
           enumerate(ns)]
@@ -47,14 +58,16 @@ def run_case(m, ns, efforts, seed, with_oracle=True):
     ys = group.matvec(vt, efforts)
     singles = [M.matvec(vt, e) for M, e in zip(mats, efforts)]
     torch.cuda.synchronize()
+    ys = [y.cpu().numpy() for y in ys]
+    yr, got = recorded(group, vt, efforts)
     print("multi m=%d ns=%s efforts=%s" % (m, ns, efforts), flush=True)
     sys.stdout.flush()
     for j, (W, e) in enumerate(zip(Ws, efforts)):
-        y, ys1 = ys[j].cpu().numpy(), singles[j].cpu().numpy()
-        assert rel_l2(y, ys1) <= SAME_TOL, (j, rel_l2(y, ys1))
-        if with_oracle:
-            ref = oracle.run(W, oracle.probes(W, 16), v, e)
-            assert rel_l2(y, ref["y"]) <= ORACLE_TOL, (j, rel_l2(y, ref["y"]))
+        ys1 = singles[j].cpu().numpy()
+        assert rel_l2(ys[j], ys1) <= SAME_TOL, (j, rel_l2(ys[j], ys1))
+        assert rel_l2(ys[j], yr[j]) <= SAME_TOL, j
+        ref = oracle.run(W, oracle.probes(W, 16), v, e)
+        check(got[j], ref, where=("pair", j), y=ys[j])
     return ys
 
 
@@ -69,8 +82,8 @@ def test_multi_small(m, ns, efforts):
 
 
 def test_multi_mistral_qkv_and_gate_up():
-    run_case(4096, (4096, 1024, 1024), (0.25, 0.25, 0.25), seed=11, with_oracle=False)
-    run_case(4096, (14336, 14336), (0.25, 0.16), seed=12, with_oracle=False)
+    run_case(4096, (4096, 1024, 1024), (0.25, 0.25, 0.25), seed=11)
+    run_case(4096, (14336, 14336), (0.25, 0.16), seed=12)
 
 
 def test_multi_repeat_and_reuse():
@@ -85,11 +98,10 @@ def test_multi_repeat_and_reuse():
     for k, efforts in enumerate(((0.25, 0.5), (0.05, 1.0), (0.25, 0.5))):
         v = synth.activations(m, seed=30 + k, stream=synth.stream_id("multi", "v", m))
         vt = torch.from_numpy(v).to(d)
-        ys = group.matvec(vt, efforts)
-        torch.cuda.synchronize()
+        ys, got = recorded(group, vt, efforts)
         for j, (W, e) in enumerate(zip(Ws, efforts)):
             ref = oracle.run(W, oracle.probes(W, 16), v, e)
-            assert rel_l2(ys[j].cpu().numpy(), ref["y"]) <= ORACLE_TOL, (k, j)
+            check(got[j], ref, where=(k, j), y=ys[j])
 
 
 def test_multi_own_inputs_and_heights():
@@ -107,12 +119,12 @@ def test_multi_own_inputs_and_heights():
     group = E.EffortGroup(mats)
     vts = [torch.from_numpy(v).to(d) for v in vs]
     for rep in range(2):
-        ys = group.matvec(vts, efforts)
-        torch.cuda.synchronize()
+        ys = [y.cpu().numpy() for y in group.matvec(vts, efforts)]
+        yr, got = recorded(group, vts, efforts)
         for j, (W, v, e) in enumerate(zip(Ws, vs, efforts)):
-            y = ys[j].cpu().numpy()
             y1 = mats[j].matvec(vts[j], e).cpu().numpy()
-            assert rel_l2(y, y1) <= SAME_TOL, (rep, j)
+            assert rel_l2(ys[j], y1) <= SAME_TOL, (rep, j)
+            assert rel_l2(ys[j], yr[j]) <= SAME_TOL, (rep, j)
             ref = oracle.run(W, oracle.probes(W, 16), v, e)
-            assert rel_l2(y, ref["y"]) <= ORACLE_TOL, (rep, j)
+            check(got[j], ref, where=(rep, j), y=ys[j])
         print("multi own inputs rep %d ok" % rep, flush=True)

@@ -22,6 +22,7 @@ torch = pytest.importorskip("torch")
 import dynamic_sparsity_approximate_amd as E  # noqa: E402
 import oracle  # noqa: E402
 import synth  # noqa: E402
+from _parity import check, rel_l2  # noqa: E402
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -37,26 +38,6 @@ def say(*a):
     sys.stdout.flush()
 
 
-def rel_l2(y, ref):
-    ref = np.asarray(ref, np.float64)
-    y = np.asarray(y, np.float64)
-    nr = np.linalg.norm(ref)
-    if nr == 0.0:
-        return 0.0 if np.max(np.abs(y), initial=0.0) <= 1e-30 else np.inf
-    return float(np.linalg.norm(y - ref) / nr)
-
-
-def check(got, ref, with_mask=True, where=""):
-    assert np.float32(got["cutoff"]).view(np.uint32) == np.float32(ref["cutoff"]).view(np.uint32), \
-        (where, got["cutoff"], ref["cutoff"])
-    assert got["K"] == ref["K"] and got["Kprime"] == ref["Kprime"], where
-    assert np.array_equal(got["row_kept"], ref["row_kept"]), where
-    assert got["fingerprint"] == ref["fingerprint"], where
-    if with_mask:
-        assert np.array_equal(got["mask"], ref["mask"]), where
-    err = rel_l2(got["y"], ref["y"])
-    assert err <= REL_L2_TOL, (where, err)
-    return err
 
 
 def case(m, n, seed, tag):
@@ -174,12 +155,17 @@ def test_batched_matches_single_vectors():
     W = synth.matrix("batched", 1024, 2048, seed=0)
     M = E.EffortMatrix(W, P=16, device=d, batch=5)
     V = np.stack([synth.vector("batched", 1024, seed=s) for s in range(5)])
-    Y = M.matvec_batched(torch.from_numpy(V).to(d), 0.25)
+    Vt = torch.from_numpy(V).to(d)
+    Y = M.matvec_batched(Vt, 0.25)
     torch.cuda.synchronize()
+    got = M.matvec_batched_debug(Vt, 0.25, with_mask=True)
     pr = oracle.probes(W, 16)
     for b in range(5):
-        ref = oracle.run(W, pr, V[b], 0.25)
-        assert rel_l2(Y[b].cpu().numpy(), ref["y"]) <= REL_L2_TOL
+        ref = oracle.run(W, pr, V[b], 0.25, mask=True)
+        check(got[b], ref, with_mask=True, where=("batched", b))
+        assert rel_l2(Y[b].cpu().numpy(), got[b]["y"]) < 1e-6
+        single = M.matvec_debug(Vt[b].contiguous(), 0.25, with_mask=False)
+        assert single["fingerprint"] == got[b]["fingerprint"]
 
 
 # ---------------------------------------------------------------- comparators and glue
@@ -227,24 +213,53 @@ _probe_cache = {}
 @pytest.mark.parametrize("shape", SHAPES)
 def test_mistral_shapes(shape):
     """Full-size matrices in the configuration the benchmark times (P = 16,
-    default groups): every effort of the sweep, full mask on seed 0, counts and
-    fingerprint on seed 1."""
+    default groups): every effort of the sweep on seeds 0-4, the full uint8
+    mask compared on every point."""
+    from concurrent.futures import ThreadPoolExecutor
+
     d = dev()
     m, n = shape
     W = synth.matrix("config1", m, n, seed=0)
     say("shape %dx%d: oracle probes" % (m, n))
     pr = oracle.probes(W, 16)
     M = E.EffortMatrix(W, P=16, device=d)
-    for seed in (0, 1):
+    pts = [(seed, effort) for seed in range(5) for effort in (1.0, 0.5, 0.25, 0.125)]
+    V = {seed: synth.vector("config1", m, seed=seed) for seed in range(5)}
+    with ThreadPoolExecutor(4) as ex:  # the oracle's C calls release the GIL
+        for (seed, effort), ref in zip(pts, ex.map(lambda p: oracle.run(W, pr, V[p[0]], p[1], mask=True),
+                                                    pts)):
+            got = M.matvec_debug(torch.from_numpy(V[seed]).to(d), effort, with_mask=True)
+            err = check(got, ref, True, where="%dx%d/%d/%g" % (m, n, seed, effort))
+            say("shape %dx%d seed %d effort %g ok kept=%.4f relL2=%.2e" % (
+                m, n, seed, effort, ref["total_kept"] / W.size, err))
+
+
+def test_headline_timed_entry_several_seeds():
+    """The benchmarked entry point itself (effort_matvec, no recording) at
+    4096x14336, effort 0.25, seeds 0-4: its cutoff bits, K and K' (the result
+    words it leaves in the workspace) and y against the oracle; the recording
+    entry point on the same input (the same kernels, recording on) gives the
+    same y and the oracle's kept set, fingerprint and full mask."""
+    d = dev()
+    m, n, effort = 4096, 14336, 0.25
+    W = synth.matrix("config1", m, n, seed=0)
+    pr = oracle.probes(W, 16)
+    M = E.EffortMatrix(W, P=16, device=d)
+    for seed in range(5):
         v = synth.vector("config1", m, seed=seed)
         vt = torch.from_numpy(v).to(d)
-        for effort in (1.0, 0.5, 0.25, 0.125):
-            with_mask = seed == 0
-            say("shape %dx%d seed %d effort %g" % (m, n, seed, effort))
-            got = M.matvec_debug(vt, effort, with_mask=with_mask)
-            ref = oracle.run(W, pr, v, effort, mask=with_mask)
-            err = check(got, ref, with_mask, where="%dx%d/%d/%g" % (m, n, seed, effort))
-            say("  ok kept=%.4f relL2=%.2e" % (ref["total_kept"] / W.size, err))
+        ref = oracle.run(W, pr, v, effort, mask=True)
+        y = M.matvec(vt, effort)
+        torch.cuda.synchronize()
+        res = M.ws[:16].cpu().numpy().view(np.uint32)
+        assert res[0] == np.float32(ref["cutoff"]).view(np.uint32), seed
+        assert res[2] == ref["K"] and res[1] == ref["Kprime"], seed
+        y = y.cpu().numpy()
+        assert rel_l2(y, ref["y"]) <= REL_L2_TOL, seed
+        got = M.matvec_debug(vt, effort, with_mask=True)
+        check(got, ref, True, where=("headline", seed))
+        assert rel_l2(got["y"], y) < 1e-6, seed
+        say("headline seed %d: timed entry and recording entry equal the oracle" % seed)
 
 
 def test_graph_replays_match_eager():
@@ -326,19 +341,25 @@ def test_batched_fused_matches_oracle(m, n, G, b, P, effort):
     M = E.EffortMatrix(W, P=P, groups=G, device=d, batch=b)
     V = np.stack([synth.vector("fused", m, seed=s) for s in range(b)])
     V[1 % b] *= 7.0  # vectors of different scale in one pass
-    Y = M.matvec_batched(torch.from_numpy(V).to(d), effort)
+    Vt = torch.from_numpy(V).to(d)
+    Y = M.matvec_batched(Vt, effort)
     torch.cuda.synchronize()
     pr = oracle.probes(W, P)
     sl = E.effort_workspace_bytes(M.desc, 1)
     ws = M.ws.cpu().numpy()
+    got = M.matvec_batched_debug(Vt, effort, with_mask=m * n * b <= (1 << 26))
     for k in range(b):
-        ref = oracle.run(W, pr, V[k], effort)
+        ref = oracle.run(W, pr, V[k], effort, mask=got[k]["mask"] is not None)
+        # the unrecorded call's own result words and output
         res = ws[k * sl: k * sl + 16].view(np.uint32)
         assert res[0] == np.float32(ref["cutoff"]).view(np.uint32), (k, res[0])
         assert res[2] == ref["K"] and res[1] == ref["Kprime"], k
         err = rel_l2(Y[k].cpu().numpy(), ref["y"])
         assert err <= REL_L2_TOL, (k, err)
-    say("fused %dx%d G=%d b=%d effort=%g ok" % (m, n, M.groups, b, effort))
+        # the recorded call (same route and kernels): the kept set
+        check(got[k], ref, got[k]["mask"] is not None, where=("batched", k))
+        assert rel_l2(got[k]["y"], Y[k].cpu().numpy()) < 1e-6, k
+    say("fused %dx%d G=%d b=%d effort=%g ok (kept sets recorded)" % (m, n, M.groups, b, effort))
     # a second call on the same workspace gives the same result
     Y2 = M.matvec_batched(torch.from_numpy(V).to(d), effort)
     torch.cuda.synchronize()

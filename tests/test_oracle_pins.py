@@ -389,3 +389,94 @@ def test_fingerprint_and_counts_follow_the_mask():
     assert r["fingerprint"] == fp
     assert np.array_equal(r["row_kept"], r["mask"].sum(axis=1))
     assert r["total_kept"] == len(ii)
+
+
+# ---------------------------------------------------------------- glue and input generator
+
+def test_silu_mul_identities():
+    """silu(x) = x / (1 + e^-x): its odd part is x/2 (so silu(x) - silu(-x) =
+    x), silu(0) = 0, silu(ln 3) = ln 3 / (1 + 1/3) = (3/4) ln 3 (a sign error in
+    the exponent gives ln 3 / 4), silu(x) -> x for large x, and the gate is
+    linear in its second operand."""
+    x = np.linspace(-30.0, 30.0, 1201)
+    one = np.ones_like(x)
+    d = oracle.silu_mul(x, one) - oracle.silu_mul(-x, one)
+    assert np.allclose(d, x, rtol=1e-14, atol=1e-14)
+    assert oracle.silu_mul(np.array([0.0]), np.array([1.0]))[0] == 0.0
+    l3 = math.log(3.0)
+    assert abs(oracle.silu_mul(np.array([l3]), np.array([1.0]))[0] - 0.75 * l3) <= 1e-15
+    assert abs(oracle.silu_mul(np.array([40.0]), np.array([1.0]))[0] - 40.0) <= 1e-12
+    h1 = synth.activations(257, seed=2, stream=3).astype(np.float64)
+    h3 = synth.activations(257, seed=4, stream=5).astype(np.float64)
+    assert np.array_equal(oracle.silu_mul(h1, 2.0 * h3), 2.0 * oracle.silu_mul(h1, h3))
+
+
+def test_philox4x32_10_known_answers():
+    """Philox4x32-10 against the known-answer vectors published with the
+    Random123 library of Salmon, Moraes, Dror and Shaw (SC'11): counter, key,
+    expected output."""
+    kat = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+           ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+           ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+            (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in kat:
+        assert synth.philox4x32_10(ctr, key) == want, (ctr, key)
+
+
+# ---------------------------------------------------------------- cropped layouts
+
+def _stored_numpy(W, P, crop):
+    m, n = W.shape
+    keep = -(-crop * n // P)
+    st = np.zeros((m, n), np.uint8)
+    keys = (W & 0x7FFF).astype(np.int64)
+    for i in range(m):
+        order = np.lexsort((np.arange(n), -keys[i]))  # key descending, then column ascending
+        st[i, order[:keep]] = 1
+    return st
+
+
+@pytest.mark.parametrize("m,n,P,crop", [(40, 300, 16, 12), (9, 37, 5, 2), (5, 64, 64, 63), (3, 20, 4, 4)])
+def test_stored_mask_is_top_ranks(m, n, P, crop):
+    W, _ = rand_case(m, n, seed=m + crop, tag="crop")
+    W[:, ::5] = W[:, 1::5][:, : W[:, ::5].shape[1]] if n > 5 else W[:, ::5]  # ties across columns
+    got = oracle.stored_mask(W, P, crop)
+    assert np.array_equal(got, _stored_numpy(W, P, crop))
+    assert np.all(got.sum(axis=1) == -(-crop * n // P))
+
+
+def test_run_cropped_reduces_to_run():
+    W, v = rand_case(64, 512, seed=1, tag="crop2")
+    P = 16
+    pr = oracle.probes(W, P)
+    for effort in (1.0, 0.3, 0.05):
+        full = oracle.run(W, pr, v, effort, mask=True)
+        c = oracle.run_cropped(W, pr, v, effort, P, mask=True)  # crop = P stores everything
+        for k in ("cutoff", "K", "Kprime", "fingerprint", "total_kept"):
+            assert c[k] == full[k], k
+        assert np.array_equal(c["mask"], full["mask"]) and np.array_equal(c["y"], full["y"])
+        assert not c["crop_reached"]
+
+
+def test_run_cropped_keeps_stored_part():
+    W, v = rand_case(48, 400, seed=2, tag="crop3")
+    P, crop = 16, 10
+    pr = oracle.probes(W, P)
+    st = _stored_numpy(W, P, crop)
+    vals = W.view(np.float16).astype(np.float64)
+    for effort in (1.0, 0.6, 0.25, 0.02):
+        full = oracle.run(W, pr, v, effort, mask=True)
+        c = oracle.run_cropped(W, pr, v, effort, crop, mask=True)
+        assert c["cutoff"] == full["cutoff"] and c["K"] == full["K"] and c["Kprime"] == full["Kprime"]
+        want = full["mask"] & st
+        assert np.array_equal(c["mask"], want)
+        assert c["crop_reached"] == bool(np.any(full["mask"] & (1 - st)))
+        assert np.allclose(c["y"], (v.astype(np.float64)[:, None] * vals * want).sum(axis=0),
+                           rtol=1e-12, atol=1e-12)
+        if not c["crop_reached"]:  # the kept set lies in the stored part: the uncropped result
+            assert c["fingerprint"] == full["fingerprint"] and np.array_equal(c["y"], full["y"])
+    # effort 1 keeps every stored pair (no zero activations here) and reaches the crop
+    c1 = oracle.run_cropped(W, pr, v, 1.0, crop)
+    assert np.all(c1["row_kept"] == -(-crop * 400 // P)) and c1["crop_reached"]
+    # a small effort keeps only the largest products, inside the stored part
+    assert not oracle.run_cropped(W, pr, v, 0.02, crop)["crop_reached"]

@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--effort", type=float, default=0.25)
     ap.add_argument("--P", type=int, default=16)
     ap.add_argument("--groups", type=int, default=0)
+    ap.add_argument("--format", choices=["u32", "r12"], default="u32",
+                    help="entry format of the layout: u32 (4 bytes per entry) or r12 (3 bytes)")
+    ap.add_argument("--crop", type=int, default=0, help="stored segments per row (0: all)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -67,6 +70,11 @@ def parse():
                     help="decode/moe modes: side streams for matvecs that do not depend on "
                          "each other (0: one stream)")
     return ap.parse_args()
+
+
+def entry_bytes(fmt: str) -> float:
+    """Bytes the method reads per kept entry in this layout format."""
+    return 3.0 if fmt == "r12" else 4.0
 
 
 def log(*a):
@@ -165,13 +173,15 @@ def main():
     log("generating W %dx%d and converting" % (m, n))
     W = synth.matrix("config1", m, n, seed=0)
     t0 = time.perf_counter()
-    M = E.EffortMatrix(W, P=P, groups=args.groups, device=dev)
+    fmt = E.EFFORT_ENTRY_R12 if args.format == "r12" else E.EFFORT_ENTRY_U32
+    ebytes = entry_bytes(args.format)
+    M = E.EffortMatrix(W, P=P, groups=args.groups, device=dev, entry_format=fmt, crop=args.crop)
     log("layout %.1f MB, G=%d, prepare %.1fs" % (M.layout_bytes / 1e6, M.groups, time.perf_counter() - t0))
 
     # kept counts of the vectors (parity-path run, untimed)
     v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
     kept0 = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
-    call_bytes = 4.0 * kept0
+    call_bytes = ebytes * kept0
     R = max(2, int(math.ceil(args.rotate_gib * GiB / call_bytes)))
     Rd = max(2, int(math.ceil(args.rotate_gib * GiB / (2.0 * m * n))))
     log("rotation: %d layouts (%.0f MB read per call), %d dense copies" % (R, call_bytes / 1e6, Rd))
@@ -223,8 +233,8 @@ def main():
                 dsp.append(E.effort_event_elapsed_ms(e[2], e[3]))
                 mul.append(E.effort_event_elapsed_ms(e[4], e[5]))
         mul_us = statistics.mean(mul) * 1e3
-        alg_mul = 4.0 * kept_mean + 4.0 * m + 4.0 * n
-        alg_step = 4.0 * kept_mean + 2.0 * m * P + 4.0 * m + 4.0 * n
+        alg_mul = ebytes * kept_mean + 4.0 * m + 4.0 * n
+        alg_step = ebytes * kept_mean + 2.0 * m * P + 4.0 * m + 4.0 * n
         achieved = alg_mul / (mul_us * 1e-6) / 1e9
         traffic = read_counters()
         result.update({
@@ -313,7 +323,8 @@ def main():
             "vs_baseline": None, "dtype": "f32 (fp16 weights)", "data": "synthetic",
             "config": {"workload": "effort matvec %dx%d fp16, effort %g, batch 1" % (m, n, effort),
                        "in_dim": m, "out_dim": n, "effort": effort, "P": P,
-                       "groups": result["groups"], "rotation_copies": result["rotation"]},
+                       "groups": result["groups"], "rotation_copies": result["rotation"],
+                       "entry_format": args.format, "crop_segments": args.crop or P},
             "hbm_gbs": result["hbm_gbs"], "kept_fraction": result["kept_fraction"],
             "dense_us": result["dense_us"], "dense_gbs": result["dense_gbs"],
             "library_dense_us": result["library_dense_us"],

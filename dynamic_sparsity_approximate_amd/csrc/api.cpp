@@ -70,7 +70,9 @@ int check_desc(const effort_desc* d, Geometry* g) {
 bool effort_ok(float e) { return e > 0.0f && e <= 1.0f; }  // false for NaN
 
 // Entry formats the multiply reads.
-bool format_supported(const Geometry& g) { return g.format == EFFORT_ENTRY_U32; }
+bool format_supported(const Geometry& g) {
+  return g.format == EFFORT_ENTRY_U32 || g.format == EFFORT_ENTRY_R12;
+}
 
 uint32_t k_of(float effort, int64_t N) {
   double k = ceil((double)effort * (double)N);
@@ -186,6 +188,7 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   ma.v = v;
   ma.entries = entries;
   ma.gstride = g.gstride;
+  ma.format = g.format;
   ma.floor = floor;
   ma.runlen = runlen;
   ma.bsum = bsum;
@@ -341,6 +344,7 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
     ma.v = v + (int64_t)b0 * g.m;
     ma.entries = entries;
     ma.gstride = g.gstride;
+    ma.format = g.format;
     ma.floor = g.off_floor ? reinterpret_cast<const uint16_t*>(layout + g.off_floor) : nullptr;
     ma.runlen = urunlen;
     ma.bsum = ubsum;
@@ -395,9 +399,10 @@ int check_multi(const effort_desc* descs, int32_t count, Geometry* g) {
   return EFFORT_OK;
 }
 
+// One launch serves one entry format: the pairs of a multi-matrix call share it.
 int check_multi_formats(const Geometry* g, int32_t count) {
   for (int32_t j = 0; j < count; ++j)
-    if (!format_supported(g[j])) return EFFORT_EUNSUPPORTED;
+    if (!format_supported(g[j]) || g[j].format != g[0].format) return EFFORT_EUNSUPPORTED;
   return EFFORT_OK;
 }
 
@@ -767,8 +772,13 @@ int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_
                float* y_dev, void* stream) {
   if (!w_dev || !v_dev || !y_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
   if (!aligned(w_dev, 2) || !aligned(v_dev, 4) || !aligned(y_dev, 4)) return EFFORT_EINVAL;
-  const int64_t strips = (out_dim + 63) / 64;
   const int cus = cu_count();
+  // full-height strips when they give at least half a block per CU: no zero
+  // fill and no atomics
+  if (dense_strip_serves(out_dim, cus, w_dev) && (out_dim / 8) * 2 >= cus)
+    return status_of(launch_dense_strip(w_dev, v_dev, in_dim, out_dim, y_dev, cus,
+                                        static_cast<hipStream_t>(stream)));
+  const int64_t strips = (out_dim + 63) / 64;
   int rs = 1;
   if (strips < cus) {
     int64_t want = (2 * cus + strips - 1) / strips;

@@ -778,7 +778,13 @@ template <int BP>
 constexpr int mul_threads() {
   return BP == 1 ? 576 : 1024;
 }
-constexpr int CH = 256;  // entries per chunk: one 16-byte quad per lane
+constexpr int CH = 256;  // u32 format: entries per chunk, one 16-byte quad per lane
+// Units per chunk: a quad of 4 entries per lane (u32), one 12-byte record of 4
+// entries per lane (r12).
+template <int FMT>
+constexpr uint32_t chunk_units() {
+  return FMT == EFFORT_ENTRY_R12 ? 64u : (uint32_t)CH;
+}
 
 struct Chunk {
   uint32_t j, s0, s1;  // row of the batch, entries [s0, s1) of its run
@@ -1082,7 +1088,7 @@ __device__ __forceinline__ uint32_t share_cum(uint32_t j) {
 // integer adds make the tile independent of order.
 // The kernel's body for block `bid` of `nblk` (the grid, or one matrix's
 // part of a multi-matrix grid).
-template <bool REC, int BP>
+template <bool REC, int BP, int FMT>
 __device__ __forceinline__ void bucketmul_body(
     const uint32_t bid, const uint32_t nblk, const float* __restrict__ vvec,
     const uint32_t* __restrict__ entries, const uint32_t* __restrict__ runlen,
@@ -1448,7 +1454,10 @@ __device__ __forceinline__ void bucketmul_body(
     c.valid = ss < se;
     c.j = sj;
     c.s0 = ss;
-    c.s1 = c.valid ? min(se, (ss & ~3u) + (uint32_t)CH) : 0u;
+    // u32: chunks start at a quad boundary (a share's first may start inside
+    // one); r12: one record per lane from any record
+    const uint32_t cs = FMT == EFFORT_ENTRY_R12 ? ss : (ss & ~3u);
+    c.s1 = c.valid ? min(se, cs + chunk_units<FMT>()) : 0u;
     ss = c.valid ? c.s1 : ss;
   };
   // Loads the chunk's quad for this lane through a buffer descriptor whose
@@ -1459,12 +1468,20 @@ __device__ __forceinline__ void bucketmul_body(
     // row and range are wave-uniform; readfirstlane keeps the descriptor scalar
     const uint32_t row = __builtin_amdgcn_readfirstlane(rowb + c.j);
     const uint32_t s1 = __builtin_amdgcn_readfirstlane(c.s1);
-    const uint32_t* base = entries + (size_t)row * (size_t)a.row_stride + (size_t)g * (size_t)a.gstride;
+    constexpr uint32_t UW = FMT == EFFORT_ENTRY_R12 ? 3u : 1u;  // words per unit
+    const uint32_t* base =
+        entries + ((size_t)row * (size_t)a.row_stride + (size_t)g * (size_t)a.gstride) * UW;
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(s1 * 4u), kBufferDword3);
-    const auto q = __builtin_amdgcn_raw_buffer_load_b128(
-        rs, (int)(((c.s0 & ~3u) + (uint32_t)lane * 4u) * 4u), 0, 0);
-    buf = make_uint4(q[0], q[1], q[2], q[3]);
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(s1 * UW * 4u), kBufferDword3);
+    if constexpr (FMT == EFFORT_ENTRY_R12) {
+      // a whole record per lane: in range or (past s1) all zero
+      const auto q = __builtin_amdgcn_raw_buffer_load_b96(rs, (int)((c.s0 + (uint32_t)lane) * 12u), 0, 0);
+      buf = make_uint4(q[0], q[1], q[2], 0u);
+    } else {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, (int)(((c.s0 & ~3u) + (uint32_t)lane * 4u) * 4u), 0, 0);
+      buf = make_uint4(q[0], q[1], q[2], q[3]);
+    }
   };
   uint32_t tj[BP];  // per vector: the row's fp16 key threshold and scaled activation
   float vfj[BP];
@@ -1476,16 +1493,47 @@ __device__ __forceinline__ void bucketmul_body(
       tf[p] = h2f((uint32_t)__builtin_amdgcn_readlane((int)tj[p], c.j));
       vf[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[p]), c.j));
     }
-    uint32_t ev[4] = {buf.x, buf.y, buf.z, buf.w};
-    // Words past s1 are zero.  Words before s0 can only sit in lane 0's quad
-    // of a share's first chunk: they belong to the previous share and are
-    // zeroed here.  A zero word has key 0 and passes only when the cutoff is
-    // 0, where it adds 0.
-    if (c.s0 & 3u) {
-      const uint32_t skip = lane == 0 ? (c.s0 & 3u) : 0u;
-      ev[0] = skip > 0u ? 0u : ev[0];
-      ev[1] = skip > 1u ? 0u : ev[1];
-      ev[2] = skip > 2u ? 0u : ev[2];
+    // The chunk's 4 entries of this lane: fp16 value bits (low half) and the
+    // column inside the group.
+    uint32_t ev[4], col[4];
+    bool entry[4];  // an entry of the chunk (not a zero fill, not a pad)
+    if constexpr (FMT == EFFORT_ENTRY_R12) {
+      // One record: two words of values, then the first column (12 bits) and
+      // three steps (7, 7, 6 bits).  A record past s1 reads as zero words:
+      // values 0 (key 0, kept only when the cutoff is 0, adding 0) at column
+      // 0.  Pads (0x8000, step 0) have key 0 as well.
+      ev[0] = buf.x;
+      ev[1] = buf.x >> 16;
+      ev[2] = buf.y;
+      ev[3] = buf.y >> 16;
+      col[0] = buf.z & 0xFFFu;
+      col[1] = col[0] + ((buf.z >> 12) & 0x7Fu);
+      col[2] = col[1] + ((buf.z >> 19) & 0x7Fu);
+      col[3] = col[2] + (buf.z >> 26);
+      const bool in = c.s0 + (uint32_t)lane < c.s1;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) entry[k2] = in && (ev[k2] & 0xFFFFu) != 0x8000u;
+    } else {
+      ev[0] = buf.x;
+      ev[1] = buf.y;
+      ev[2] = buf.z;
+      ev[3] = buf.w;
+      // Words past s1 are zero.  Words before s0 can only sit in lane 0's
+      // quad of a share's first chunk: they belong to the previous share and
+      // are zeroed here.  A zero word has key 0 and passes only when the
+      // cutoff is 0, where it adds 0.
+      if (c.s0 & 3u) {
+        const uint32_t skip = lane == 0 ? (c.s0 & 3u) : 0u;
+        ev[0] = skip > 0u ? 0u : ev[0];
+        ev[1] = skip > 1u ? 0u : ev[1];
+        ev[2] = skip > 2u ? 0u : ev[2];
+      }
+      const uint32_t pos0 = (c.s0 & ~3u) + (uint32_t)lane * 4u;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        col[k2] = ev[k2] >> 16;
+        entry[k2] = pos0 + (uint32_t)k2 >= c.s0 && pos0 + (uint32_t)k2 < c.s1;
+      }
     }
     // The keep test and the accumulation are the same with and without
     // recording; recording only adds the stores of the kept (row, column)
@@ -1498,19 +1546,16 @@ __device__ __forceinline__ void bucketmul_body(
       cnt[p] = 0u;
       fp[p] = 0u;
     }
-    const uint32_t pos0 = (c.s0 & ~3u) + (uint32_t)lane * 4u;
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
-      const uint32_t w = ev[k2];
-      const float x = h2f(w);
+      const float x = h2f(ev[k2]);
 #pragma unroll
       for (int p = 0; p < BP; ++p)
         if (fabsf(x) >= tf[p]) {  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
-          atomicAdd(&tile[p * a.TW + (w >> 16)], __float2int_rn(__fmul_rn(x, vf[p])));
+          atomicAdd(&tile[p * a.TW + col[k2]], __float2int_rn(__fmul_rn(x, vf[p])));
           if constexpr (REC) {
-            const uint32_t pos = pos0 + (uint32_t)k2;
-            if (pos >= c.s0 && pos < c.s1) {
-              const uint64_t flat = (uint64_t)(rowb + c.j) * (uint64_t)a.n + (uint64_t)col0 + (w >> 16);
+            if (entry[k2]) {
+              const uint64_t flat = (uint64_t)(rowb + c.j) * (uint64_t)a.n + (uint64_t)col0 + col[k2];
               if (a.mask) a.mask[(uint64_t)p * (uint64_t)a.m * (uint64_t)a.n + flat] = 1u;
               fp[p] += pair_hash(flat);
               ++cnt[p];
@@ -1622,24 +1667,24 @@ __device__ __forceinline__ void bucketmul_body(
   }
 }
 
-template <bool REC, int BP>
+template <bool REC, int BP, int FMT>
 __global__ __launch_bounds__(mul_threads<BP>()) void k_bucketmul(
     const float* __restrict__ vvec, const uint32_t* __restrict__ entries,
     const uint32_t* __restrict__ runlen, const uint32_t* __restrict__ bsum,
     const uint32_t* __restrict__ result, float* __restrict__ y, MulArgs a) {
-  bucketmul_body<REC, BP>(blockIdx.x, gridDim.x, vvec, entries, runlen, bsum, result, y, a);
+  bucketmul_body<REC, BP, FMT>(blockIdx.x, gridDim.x, vvec, entries, runlen, bsum, result, y, a);
 }
 
 // Several matrices sharing v, one vector each: matrix j owns blocks
 // [first[j], first[j + 1]) of the grid.
-template <bool REC>
+template <bool REC, int FMT>
 __global__ __launch_bounds__(mul_threads<1>()) void k_bucketmul_multi(MulMulti mm) {
   int j = 0;
   for (int k = 1; k < mm.count; ++k)
     if (blockIdx.x >= mm.first[k]) j = k;
   const MulArgs& a = mm.a[j];
-  bucketmul_body<REC, 1>(blockIdx.x - mm.first[j], mm.first[j + 1] - mm.first[j], a.v, a.entries,
-                         a.runlen, a.bsum, a.result, a.y, a);
+  bucketmul_body<REC, 1, FMT>(blockIdx.x - mm.first[j], mm.first[j + 1] - mm.first[j], a.v, a.entries,
+                              a.runlen, a.bsum, a.result, a.y, a);
 }
 
 // LDS of a workgroup on gfx950; the batched kernel's static LDS (cutoff
@@ -1660,18 +1705,44 @@ int bucketmul_pass_width(int32_t TW, int32_t batch) {
   return 0;
 }
 
-template <bool REC, int BP>
+template <bool REC, int BP, int FMT>
 static hipError_t launch_mul_bp(const MulArgs& a, unsigned grid, hipStream_t s) {
   const size_t lds = (size_t)BP * a.TW * sizeof(int32_t);
   if (lds > pass_tile_budget(BP)) return hipErrorInvalidValue;
   // the attribute is set on every launch: a per-instantiation flag would be
   // per device state, and the call costs no device work
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bucketmul<REC, BP>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bucketmul<REC, BP, FMT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)pass_tile_budget(BP));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bucketmul<REC, BP>), dim3(grid), dim3(mul_threads<BP>()), lds, s, a.v,
+  hipLaunchKernelGGL((k_bucketmul<REC, BP, FMT>), dim3(grid), dim3(mul_threads<BP>()), lds, s, a.v,
                      a.entries, a.runlen, a.bsum, a.result, a.y, a);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_mul_fmt(const MulArgs& a, bool record, unsigned grid, hipStream_t s,
+                                 const EventPair* ev) {
+  if (a.nv > 1) {
+    if (a.nv > 8) return hipErrorInvalidValue;
+    if (record) {
+      if (a.nv > 4) return launch_mul_bp<true, 8, FMT>(a, grid, s);
+      if (a.nv > 2) return launch_mul_bp<true, 4, FMT>(a, grid, s);
+      return launch_mul_bp<true, 2, FMT>(a, grid, s);
+    }
+    if (a.nv > 4) return launch_mul_bp<false, 8, FMT>(a, grid, s);
+    if (a.nv > 2) return launch_mul_bp<false, 4, FMT>(a, grid, s);
+    return launch_mul_bp<false, 2, FMT>(a, grid, s);
+  }
+  if (ev && ev->start && !record)
+    hipExtLaunchKernelGGL((k_bucketmul<false, 1, FMT>), dim3(grid), dim3(mul_threads<1>()), 0, s,
+                          ev->start, ev->stop, 0, a.v, a.entries, a.runlen, a.bsum, a.result, a.y, a);
+  else if (record)
+    hipLaunchKernelGGL((k_bucketmul<true, 1, FMT>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
+                       a.entries, a.runlen, a.bsum, a.result, a.y, a);
+  else
+    hipLaunchKernelGGL((k_bucketmul<false, 1, FMT>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
+                       a.entries, a.runlen, a.bsum, a.result, a.y, a);
   return hipGetLastError();
 }
 
@@ -1681,29 +1752,8 @@ hipError_t launch_bucketmul(const MulArgs& args, bool record, int blocks_per_gro
   const unsigned grid = (unsigned)(args.G * blocks_per_group);
   MulArgs a = args;
   a.bpg_recip = blocks_per_group >= 2 ? (uint32_t)((1ull << 32) / (uint64_t)blocks_per_group) : 0u;
-  if (a.nv > 1) {
-    if (a.nv > 8) return hipErrorInvalidValue;
-    if (record) {
-      if (a.nv > 4) return launch_mul_bp<true, 8>(a, grid, s);
-      if (a.nv > 2) return launch_mul_bp<true, 4>(a, grid, s);
-      return launch_mul_bp<true, 2>(a, grid, s);
-    }
-    if (a.nv > 4) return launch_mul_bp<false, 8>(a, grid, s);
-    if (a.nv > 2) return launch_mul_bp<false, 4>(a, grid, s);
-    return launch_mul_bp<false, 2>(a, grid, s);
-  }
-  if (ev && ev->start && !record)
-    hipExtLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, ev->start,
-                          ev->stop, 0, a.v, a.entries, a.runlen, a.bsum, a.result, a.y, a);
-  else if (record)
-    hipLaunchKernelGGL((k_bucketmul<true, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
-                       a.entries,
-                       a.runlen, a.bsum, a.result, a.y, a);
-  else
-    hipLaunchKernelGGL((k_bucketmul<false, 1>), dim3(grid), dim3(mul_threads<1>()), 0, s, a.v,
-                       a.entries,
-                       a.runlen, a.bsum, a.result, a.y, a);
-  return hipGetLastError();
+  if (a.format == EFFORT_ENTRY_R12) return launch_mul_fmt<EFFORT_ENTRY_R12>(a, record, grid, s, ev);
+  return launch_mul_fmt<EFFORT_ENTRY_U32>(a, record, grid, s, ev);
 }
 
 hipError_t launch_bucketmul_multi(const MulMulti& mm_in, int count, const int* blocks_per_group,
@@ -1720,10 +1770,21 @@ hipError_t launch_bucketmul_multi(const MulMulti& mm_in, int count, const int* b
   }
   for (int j = count; j <= EFFORT_MAX_MULTI; ++j) mm.first[j] = total;
   mm.count = count;
-  if (record)
-    hipLaunchKernelGGL(k_bucketmul_multi<true>, dim3(total), dim3(mul_threads<1>()), 0, s, mm);
+  for (int j = 1; j < count; ++j)  // one instantiation per launch: the pairs share a format
+    if (mm.a[j].format != mm.a[0].format) return hipErrorInvalidValue;
+  const bool r12 = mm.a[0].format == EFFORT_ENTRY_R12;
+  if (record && r12)
+    hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_R12>), dim3(total), dim3(mul_threads<1>()),
+                       0, s, mm);
+  else if (record)
+    hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_U32>), dim3(total), dim3(mul_threads<1>()),
+                       0, s, mm);
+  else if (r12)
+    hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_R12>), dim3(total),
+                       dim3(mul_threads<1>()), 0, s, mm);
   else
-    hipLaunchKernelGGL(k_bucketmul_multi<false>, dim3(total), dim3(mul_threads<1>()), 0, s, mm);
+    hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_U32>), dim3(total),
+                       dim3(mul_threads<1>()), 0, s, mm);
   return hipGetLastError();
 }
 
@@ -1819,6 +1880,82 @@ __global__ __launch_bounds__(DN_T) void k_dense(const uint16_t* __restrict__ W,
   }
 }
 
+// Dense GEMV without split rows: block b owns the column strip of `lpr`
+// 8-column octets [b lpr, (b + 1) lpr) over all rows, the strip width chosen so
+// that the grid is about one block per CU; y is written with plain stores (no
+// zero fill, no atomics).  A lane reads 16 bytes (8 fp16) of one row per load
+// and keeps UNR loads in flight; the 16 waves of the block take interleaved
+// rows; v is staged in LDS.  The partial sums are reduced over waves, then
+// over the rows a wave covers, in LDS.
+constexpr int DS_T = 1024;
+constexpr int DS_W = DS_T / 64;
+constexpr int DS_VLDS = 16384;  // v elements staged in LDS (64 KiB)
+template <int UNR>
+__global__ __launch_bounds__(DS_T) void k_dense_strip(const uint16_t* __restrict__ W,
+                                                      const float* __restrict__ v, int64_t m,
+                                                      int64_t n, float* __restrict__ y, int lpr) {
+  __shared__ float vs[DS_VLDS];
+  __shared__ float red[DS_W][64 * 8 + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rpw = 64 / lpr;  // rows per wave load
+  const int rl = lane / lpr, oc = lane - rl * lpr;
+  const int64_t col = ((int64_t)blockIdx.x * lpr + oc) * 8;
+  const bool ok = rl < rpw && col < n;
+  const int64_t mv = m < DS_VLDS ? m : DS_VLDS;
+  for (int64_t i = tid; i < mv; i += DS_T) vs[i] = v[i];
+  __syncthreads();
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+  const int64_t step = (int64_t)DS_W * rpw;
+  for (int64_t r0 = (int64_t)wave * rpw + rl; r0 < m; r0 += step * UNR) {
+    uint4 q[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t r = r0 + u * step;
+      q[u] = ok && r < m ? *reinterpret_cast<const uint4*>(W + r * n + col) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t r = r0 + u * step;
+      const float vr = r < mv ? vs[r] : (r < m ? v[r] : 0.0f);
+      const uint32_t qq[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] = __builtin_fmaf(vr, h2f(qq[k]), acc[2 * k]);
+        acc[2 * k + 1] = __builtin_fmaf(vr, h2f(qq[k] >> 16), acc[2 * k + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[wave][lane * 8 + k] = acc[k];
+  __syncthreads();
+  // over the waves: thread t < 512 sums slot t of every wave
+  if (tid < 64 * 8) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < DS_W; ++w) t += red[w][tid];
+    red[0][tid] = t;
+  }
+  __syncthreads();
+  // over the rows of a wave load: column oc * 8 + k of the strip
+  if (tid < lpr * 8) {
+    const int o = tid >> 3, k = tid & 7;
+    float t = 0.0f;
+    for (int r = 0; r < rpw; ++r) t += red[0][(r * lpr + o) * 8 + k];
+    const int64_t c = ((int64_t)blockIdx.x * lpr + o) * 8 + k;
+    if (c < n) y[c] = t;
+  }
+}
+
+// Octets per strip for the strip kernel (0: it does not serve this shape).
+static int dense_strip_width(int64_t n, int cus, const uint16_t* W) {
+  if ((n & 7) != 0 || (reinterpret_cast<uintptr_t>(W) & 15) != 0 || cus < 1) return 0;
+  const int64_t oct = n / 8;
+  const int64_t lpr = (oct + cus - 1) / cus;
+  return lpr <= 16 ? (int)lpr : 0;
+}
+
 template <int LPR, int B>
 static hipError_t dense_launch(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                                int row_splits, hipStream_t s) {
@@ -1837,6 +1974,17 @@ static hipError_t dense_launch(const uint16_t* W, const float* v, int64_t m, int
                      m, n, y, rps, gy > 1 ? 1 : 0, aligned);
   return hipGetLastError();
 }
+
+hipError_t launch_dense_strip(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
+                              int cus, hipStream_t s) {
+  const int lpr = dense_strip_width(n, cus, W);
+  if (lpr < 1) return hipErrorInvalidValue;
+  const int64_t blocks = (n / 8 + lpr - 1) / lpr;
+  hipLaunchKernelGGL(k_dense_strip<4>, dim3((unsigned)blocks), dim3(DS_T), 0, s, W, v, m, n, y, lpr);
+  return hipGetLastError();
+}
+
+bool dense_strip_serves(int64_t n, int cus, const uint16_t* W) { return dense_strip_width(n, cus, W) > 0; }
 
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                              int lanes_per_row, int row_splits, hipStream_t s) {

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "effort.h"
+
 namespace effort {
 
 // Cutoff, first pass: chart = fl32(|v_i| * probe_i[k]); a histogram of the
@@ -104,6 +106,7 @@ struct MulArgs {
   const float* v;
   const uint32_t* entries;  // units [m][G][gstride] (u32 format: one word per unit)
   int64_t gstride;          // units per (row, group) run
+  int32_t format;           // EFFORT_ENTRY_U32 or EFFORT_ENTRY_R12 (all pairs of a multi launch alike)
   const uint16_t* floor;    // cropped layouts: [m] largest magnitude key not stored (else null)
   const uint32_t* runlen;   // [G][m]
   const uint32_t* bsum;     // [nbd][G + 1]
@@ -165,6 +168,12 @@ hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group,
                             const EventPair* ev = nullptr);
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                              int lanes_per_row, int row_splits, hipStream_t s);
+// Dense GEMV over full-height column strips, about one block per CU, y written
+// with plain stores; serves out_dim a multiple of 8 up to 16 * 8 * cus columns
+// with W 16-byte aligned (dense_strip_serves).
+bool dense_strip_serves(int64_t n, int cus, const uint16_t* W);
+hipError_t launch_dense_strip(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
+                              int cus, hipStream_t s);
 hipError_t launch_dense_gemm_small(const uint16_t* W, const float* v, int batch, int64_t m,
                                    int64_t n, float* y, hipStream_t s);
 hipError_t launch_silu_mul(const float* h1, const float* h3, int64_t n, float* out, hipStream_t s);

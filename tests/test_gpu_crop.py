@@ -47,7 +47,7 @@ def test_cropped_matches_oracle(m, n, G, crop):
     for seed in (0, 1):
         v = synth.activations(m, seed=seed, stream=synth.stream_id("crop", "v", m))
         vt = torch.from_numpy(v).to(d)
-        for effort in (1.0, 0.5, 0.25, 0.05):
+        for effort in (1.0, 0.5, 0.25, 0.05, 0.01, 0.002):
             got = M.matvec_debug(vt, effort, with_mask=small)
             ref = oracle.run_cropped(W, pr, v, effort, crop, mask=small)
             where = (m, n, crop, seed, effort)

@@ -170,7 +170,8 @@ def test_batched_matches_single_vectors():
 
 # ---------------------------------------------------------------- comparators and glue
 
-@pytest.mark.parametrize("m,n", [(256, 256), (4096, 1024), (300, 1001), (1, 8), (77, 4100)])
+@pytest.mark.parametrize("m,n", [(256, 256), (4096, 1024), (300, 1001), (1, 8), (77, 4100),
+                                 (4096, 14336), (14336, 4096), (4096, 32000), (513, 2048), (5, 16384)])
 def test_dense_gemv(m, n):
     d = dev()
     W, v = case(m, n, seed=7, tag="dense")

@@ -90,6 +90,7 @@ _PROTOS = {
     "effort_layout_check": ([_D, _p], ctypes.c_int),
     "effort_matvec": ([_D, _p, _p, _f32, _p, _p, _u64, _p], ctypes.c_int),
     "effort_matvec_batched": ([_D, _p, _p, _i32, _f32, _p, _p, _u64, _p], ctypes.c_int),
+    "effort_matvec_noalloc": ([_D, _p, _p, _f32, _p, _p], ctypes.c_int),
     "effort_workspace_bytes_multi": ([_D, _i32, ctypes.POINTER(_u64)], ctypes.c_int),
     "effort_matvec_multi": ([_D, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p),
                              ctypes.POINTER(_f32), ctypes.POINTER(_p), _p, _u64, _p], ctypes.c_int),
@@ -262,6 +263,14 @@ def effort_matvec(desc, layout, v, effort: float, y, ws, ws_bytes: int, stream=N
     _check_ws(_lib.effort_matvec(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
                                  _ptr(ws), ws_bytes, _stream(stream)), "effort_matvec", ws, ws_bytes,
               stream)
+
+
+EFFORT_NOALLOC_WORKSPACE_BYTES = 8 << 20
+
+
+def effort_matvec_noalloc(desc, layout, v, effort: float, y, stream=None):
+    _check(_lib.effort_matvec_noalloc(ctypes.byref(desc), _ptr(layout), _ptr(v), effort, _ptr(y),
+                                      _stream(stream)), "effort_matvec_noalloc")
 
 
 def effort_matvec_batched(desc, layout, v, batch: int, effort: float, y, ws, ws_bytes: int,

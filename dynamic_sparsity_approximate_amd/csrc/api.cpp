@@ -733,6 +733,23 @@ int effort_matvec(const effort_desc* desc, const void* layout_dev, const float* 
                        nullptr);
 }
 
+int effort_matvec_noalloc(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                          float effort, float* y_dev, void* stream) {
+  Geometry g;
+  int rc = check_desc(desc, &g);
+  if (rc) return rc;
+  if (!layout_dev || !v_dev || !y_dev) return EFFORT_EINVAL;
+  if (!aligned(layout_dev, 256) || !aligned(v_dev, 4) || !aligned(y_dev, 4)) return EFFORT_EINVAL;
+  if (!effort_ok(effort)) return EFFORT_EINVAL;
+  if (!format_supported(g)) return EFFORT_EUNSUPPORTED;
+  const uint64_t need = ws_layout(g).slice;
+  if (need > kNoallocScratchBytes) return EFFORT_ENOSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  if (hip_failed(noalloc_workspace(s, &ws))) return EFFORT_EHIP;
+  return matvec_common(desc, layout_dev, v_dev, 1, effort, y_dev, ws, need, stream, nullptr, nullptr);
+}
+
 int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                           int32_t batch, float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes,
                           void* stream) {

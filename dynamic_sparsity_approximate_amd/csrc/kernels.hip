@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "effort.h"
 #include "kernels.hpp"
 
@@ -2115,6 +2117,41 @@ hipError_t launch_zero_bytes(void* p, uint64_t bytes, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_bytes, dim3((unsigned)blocks), dim3(256), 0, s,
                      static_cast<uint8_t*>(p), bytes, aligned);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- allocation-free workspace
+
+// The workspace of effort_matvec_noalloc: a file-scope device array, one copy
+// per device, held until the process ends.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t noalloc_workspace(hipStream_t s, uint8_t** ws) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the words every call expects to find zero start at zero (a fill kernel,
+    // stream-ordered before this device's first call)
+    e = launch_zero_bytes(p, kNoallocScratchBytes, s);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ws = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+  return hipSuccess;
 }
 
 }  // namespace effort

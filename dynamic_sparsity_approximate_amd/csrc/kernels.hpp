@@ -187,4 +187,10 @@ hipError_t launch_debug_result(const uint32_t* result, uint64_t stride, int coun
 // *status |= 1 when any of v[0..m) is a NaN or an infinity (status cleared by the caller).
 hipError_t launch_check_finite(const float* v, int64_t m, uint32_t* status, hipStream_t s);
 
+// The device workspace of effort_matvec_noalloc on the current device (its
+// address, set up on the first call: the symbol's address and a zero fill on
+// `s`).  kNoallocScratchBytes bytes; calls on one device share it.
+constexpr uint64_t kNoallocScratchBytes = EFFORT_NOALLOC_WORKSPACE_BYTES;
+hipError_t noalloc_workspace(hipStream_t s, uint8_t** ws);
+
 }  // namespace effort

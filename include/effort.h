@@ -59,6 +59,7 @@ enum {
 #define EFFORT_MAX_GROUP_WIDTH 8192 /* output columns per group (fp32 LDS tile of 32 KiB) */
 #define EFFORT_MAX_BATCH 16
 #define EFFORT_MAX_MULTI 4 /* matrices of one effort_matvec_multi call */
+#define EFFORT_NOALLOC_WORKSPACE_BYTES (8ull << 20) /* effort_matvec_noalloc's workspace per device */
 
 /* Host-side descriptor of a prepared layout; filled by effort_prepare*, passed
    by pointer to the multiply.  Plain old data; a copy is stored at the start of
@@ -196,6 +197,20 @@ int effort_layout_check(const effort_desc* desc, const void* layout_host);
    reports a violation). */
 int effort_matvec(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                   float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* effort_matvec for callers that cannot allocate device memory or pass a
+   workspace (code under HIP graph capture, tight serving loops, harnesses that
+   forbid allocation): the same kernels, with the workspace in a static device
+   array of EFFORT_NOALLOC_WORKSPACE_BYTES that the library holds on each device
+   until the process ends.  The first call on a device looks up the array's
+   address and zero-fills it on `stream`; no call allocates or frees memory.
+   ENOSPACE when the matrix needs a larger workspace than the array
+   (effort_workspace_bytes(desc, 1) > EFFORT_NOALLOC_WORKSPACE_BYTES); other
+   errors as effort_matvec.  All calls on one device share the array and leave
+   it ready for the next call: calls that overlap on one device (other
+   streams, other host threads) race and must be ordered by the caller. */
+int effort_matvec_noalloc(const effort_desc* desc, const void* layout_dev, const float* v_dev,
+                          float effort, float* y_dev, void* stream);
 
 /* `batch` independent vectors v_dev[batch][in_dim] -> y_dev[batch][out_dim],
    each with its own K, cutoff and kept set (the same result as `batch` calls

@@ -790,10 +790,8 @@ int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_
   if (!w_dev || !v_dev || !y_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
   if (!aligned(w_dev, 2) || !aligned(v_dev, 4) || !aligned(y_dev, 4)) return EFFORT_EINVAL;
   const int cus = cu_count();
-  // full-height strips when they give at least half a block per CU: no zero
-  // fill and no atomics
-  if (dense_strip_serves(out_dim, cus, w_dev) && (out_dim / 8) * 2 >= cus)
-    return status_of(launch_dense_strip(w_dev, v_dev, in_dim, out_dim, y_dev, cus,
+  if (dense_split_serves(out_dim, w_dev))
+    return status_of(launch_dense_split(w_dev, v_dev, in_dim, out_dim, y_dev,
                                         static_cast<hipStream_t>(stream)));
   const int64_t strips = (out_dim + 63) / 64;
   int rs = 1;

@@ -788,8 +788,28 @@ constexpr uint32_t chunk_units() {
   return FMT == EFFORT_ENTRY_R12 ? 64u : (uint32_t)CH;
 }
 
+// Chunks in flight per wave: a ring of loads, a slot processed and then
+// refilled, so RING - 1 loads stay outstanding while one is used.  4-byte
+// entries: 4 (measured faster than 2, 6 or 8).  12-byte records carry 3/4 of
+// the bytes per chunk, so their ring is deeper for the same bytes in flight.
+#ifndef EFFORT_RING_U32
+#define EFFORT_RING_U32 4
+#endif
+#ifndef EFFORT_RING_R12
+#define EFFORT_RING_R12 5
+#endif
+template <int FMT>
+constexpr int ring_depth() {
+  return FMT == EFFORT_ENTRY_R12 ? EFFORT_RING_R12 : EFFORT_RING_U32;
+}
+
+// A chunk of one row's run: units [s0, s1), at most chunk_units; `run` is the
+// row's run, `tf` / `vf` the row's fp32 magnitude threshold and scaled
+// activation (one vector), all wave-uniform.
 struct Chunk {
-  uint32_t j, s0, s1;  // row of the batch, entries [s0, s1) of its run
+  const uint32_t* run;
+  uint32_t j, s0, s1;  // row of the batch, units [s0, s1) of its run
+  float tf, vf;
   bool valid;
 };
 
@@ -1444,66 +1464,80 @@ __device__ __forceinline__ void bucketmul_body(
     ss = 0u;
     se = 0u;
   };
-  // Next chunk of the batch: <= CH entries of one row, one 16-byte quad per
-  // lane.  Wave-uniform.
+  // Next chunk of the batch: <= chunk_units units of one row.  What depends
+  // only on the row -- its run's address, threshold and activation -- is read
+  // once when the row starts, not per chunk.  Wave-uniform.
+  constexpr uint32_t UW = FMT == EFFORT_ENTRY_R12 ? 3u : 1u;  // words per unit
+  const uint32_t* srun = entries;
+  float stf = 0.0f, svf = 0.0f;
+  uint32_t tfj[BP];  // per lane: the row's threshold as fp32 bits (from thresholds())
+  uint32_t tj[BP];   // per vector: the row's fp16 key threshold and scaled activation
+  float vfj[BP];
   auto take = [&](Chunk& c) {
     if (ss >= se && todo) {
       sj = (uint32_t)(__ffsll((long long)todo) - 1);
       todo &= todo - 1ull;
       ss = (uint32_t)__builtin_amdgcn_readlane((int)aj, sj);
       se = ss + (uint32_t)__builtin_amdgcn_readlane((int)takej, sj);
+      const uint32_t row = rowb + sj;
+      srun = entries + ((size_t)row * (size_t)a.row_stride + (size_t)g * (size_t)a.gstride) * UW;
+      if constexpr (BP == 1) {
+        stf = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)tfj[0], sj));
+        svf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[0]), sj));
+      }
     }
     c.valid = ss < se;
     c.j = sj;
     c.s0 = ss;
-    // u32: chunks start at a quad boundary (a share's first may start inside
-    // one); r12: one record per lane from any record
+    c.run = srun;
+    c.tf = stf;
+    c.vf = svf;
+    // u32: chunk ends on quad boundaries of the run (a share's first chunk
+    // in a row may start inside a quad); r12: one record per lane
     const uint32_t cs = FMT == EFFORT_ENTRY_R12 ? ss : (ss & ~3u);
     c.s1 = c.valid ? min(se, cs + chunk_units<FMT>()) : 0u;
     ss = c.valid ? c.s1 : ss;
   };
-  // Loads the chunk's quad for this lane through a buffer descriptor whose
-  // range ends at s1: words past it read as zero without a memory access (the
-  // range is checked per 4-byte word), so every lane issues the load and the
-  // wait counters stay exact.  An empty chunk (s1 = 0) accesses no memory.
+  // Loads the chunk for this lane through a buffer descriptor that starts at
+  // unit s0 and ends at s1: lane l reads units from s0 + l (r12: one record)
+  // or words from s0 + 4l (u32: four entries).  Words past s1 read as zero
+  // without a memory access (the range is checked per 4-byte word), so every
+  // lane issues the load and the wait counters stay exact; an empty chunk
+  // accesses no memory.
   auto issue = [&](const Chunk& c, uint4& buf) {
-    // row and range are wave-uniform; readfirstlane keeps the descriptor scalar
-    const uint32_t row = __builtin_amdgcn_readfirstlane(rowb + c.j);
-    const uint32_t s1 = __builtin_amdgcn_readfirstlane(c.s1);
-    constexpr uint32_t UW = FMT == EFFORT_ENTRY_R12 ? 3u : 1u;  // words per unit
-    const uint32_t* base =
-        entries + ((size_t)row * (size_t)a.row_stride + (size_t)g * (size_t)a.gstride) * UW;
+    const uint32_t units = c.valid ? c.s1 - c.s0 : 0u;
+    const uint32_t* p0 = c.run + (size_t)c.s0 * UW;
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(s1 * UW * 4u), kBufferDword3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)p0, (short)0, (int)(units * UW * 4u), kBufferDword3);
     if constexpr (FMT == EFFORT_ENTRY_R12) {
-      // a whole record per lane: in range or (past s1) all zero
-      const auto q = __builtin_amdgcn_raw_buffer_load_b96(rs, (int)((c.s0 + (uint32_t)lane) * 12u), 0, 0);
+      const auto q = __builtin_amdgcn_raw_buffer_load_b96(rs, lane * 12, 0, 0);
       buf = make_uint4(q[0], q[1], q[2], 0u);
     } else {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, (int)(((c.s0 & ~3u) + (uint32_t)lane * 4u) * 4u), 0, 0);
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0, 0);
       buf = make_uint4(q[0], q[1], q[2], q[3]);
     }
   };
-  uint32_t tj[BP];  // per vector: the row's fp16 key threshold and scaled activation
-  float vfj[BP];
   auto process = [&](const Chunk& c, const uint4& buf) {
     if (!c.valid) return;
     float tf[BP], vf[BP];
+    if constexpr (BP == 1) {
+      tf[0] = c.tf;
+      vf[0] = c.vf;
+    } else {
 #pragma unroll
-    for (int p = 0; p < BP; ++p) {
-      tf[p] = h2f((uint32_t)__builtin_amdgcn_readlane((int)tj[p], c.j));
-      vf[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[p]), c.j));
+      for (int p = 0; p < BP; ++p) {
+        tf[p] = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)tfj[p], c.j));
+        vf[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[p]), c.j));
+      }
     }
     // The chunk's 4 entries of this lane: fp16 value bits (low half) and the
-    // column inside the group.
+    // column inside the group; `in` whether they are units of the chunk
+    // (words past s1 read as zero).
     uint32_t ev[4], col[4];
-    bool entry[4];  // an entry of the chunk (not a zero fill, not a pad)
+    bool entry[4], unit[4];  // an entry of the chunk; a unit of the chunk (pads included)
     if constexpr (FMT == EFFORT_ENTRY_R12) {
       // One record: two words of values, then the first column (12 bits) and
-      // three steps (7, 7, 6 bits).  A record past s1 reads as zero words:
-      // values 0 (key 0, kept only when the cutoff is 0, adding 0) at column
-      // 0.  Pads (0x8000, step 0) have key 0 as well.
+      // three steps (7, 7, 6 bits).  Pads (0x8000, step 0) have key 0.
       ev[0] = buf.x;
       ev[1] = buf.x >> 16;
       ev[2] = buf.y;
@@ -1512,35 +1546,29 @@ __device__ __forceinline__ void bucketmul_body(
       col[1] = col[0] + ((buf.z >> 12) & 0x7Fu);
       col[2] = col[1] + ((buf.z >> 19) & 0x7Fu);
       col[3] = col[2] + (buf.z >> 26);
-      const bool in = c.s0 + (uint32_t)lane < c.s1;
+      const bool in = (uint32_t)lane < c.s1 - c.s0;
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) entry[k2] = in && (ev[k2] & 0xFFFFu) != 0x8000u;
+      for (int k2 = 0; k2 < 4; ++k2) {
+        unit[k2] = in;
+        entry[k2] = in && (ev[k2] & 0xFFFFu) != 0x8000u;
+      }
     } else {
       ev[0] = buf.x;
       ev[1] = buf.y;
       ev[2] = buf.z;
       ev[3] = buf.w;
-      // Words past s1 are zero.  Words before s0 can only sit in lane 0's
-      // quad of a share's first chunk: they belong to the previous share and
-      // are zeroed here.  A zero word has key 0 and passes only when the
-      // cutoff is 0, where it adds 0.
-      if (c.s0 & 3u) {
-        const uint32_t skip = lane == 0 ? (c.s0 & 3u) : 0u;
-        ev[0] = skip > 0u ? 0u : ev[0];
-        ev[1] = skip > 1u ? 0u : ev[1];
-        ev[2] = skip > 2u ? 0u : ev[2];
-      }
-      const uint32_t pos0 = (c.s0 & ~3u) + (uint32_t)lane * 4u;
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
         col[k2] = ev[k2] >> 16;
-        entry[k2] = pos0 + (uint32_t)k2 >= c.s0 && pos0 + (uint32_t)k2 < c.s1;
+        entry[k2] = 4u * (uint32_t)lane + (uint32_t)k2 < c.s1 - c.s0;
+        unit[k2] = entry[k2];
       }
     }
     // The keep test and the accumulation are the same with and without
     // recording; recording only adds the stores of the kept (row, column)
-    // pairs, counted for words that are entries of the chunk (the zero words
-    // above are not).
+    // pairs.  Every slot adds: a kept product, or 0 -- to its own column,
+    // or (a word past the chunk, column 0 for all such lanes) to a word of
+    // its own lane, so that the zero adds do not all meet at one address.
     uint32_t cnt[BP];
     uint64_t fp[BP];
 #pragma unroll
@@ -1551,19 +1579,21 @@ __device__ __forceinline__ void bucketmul_body(
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
       const float x = h2f(ev[k2]);
+      const uint32_t addr = unit[k2] ? col[k2] : (uint32_t)lane;
 #pragma unroll
-      for (int p = 0; p < BP; ++p)
-        if (fabsf(x) >= tf[p]) {  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
-          atomicAdd(&tile[p * a.TW + col[k2]], __float2int_rn(__fmul_rn(x, vf[p])));
-          if constexpr (REC) {
-            if (entry[k2]) {
-              const uint64_t flat = (uint64_t)(rowb + c.j) * (uint64_t)a.n + (uint64_t)col0 + col[k2];
-              if (a.mask) a.mask[(uint64_t)p * (uint64_t)a.m * (uint64_t)a.n + flat] = 1u;
-              fp[p] += pair_hash(flat);
-              ++cnt[p];
-            }
+      for (int p = 0; p < BP; ++p) {
+        const bool keep = fabsf(x) >= tf[p];  // |w| >= t, exact: the fp16 -> fp32 widening is monotone
+        const int32_t add = __float2int_rn(__fmul_rn(x, vf[p]));
+        atomicAdd(&tile[p * a.TW + addr], keep ? add : 0);
+        if constexpr (REC) {
+          if (keep && entry[k2]) {
+            const uint64_t flat = (uint64_t)(rowb + c.j) * (uint64_t)a.n + (uint64_t)col0 + col[k2];
+            if (a.mask) a.mask[(uint64_t)p * (uint64_t)a.m * (uint64_t)a.n + flat] = 1u;
+            fp[p] += pair_hash(flat);
+            ++cnt[p];
           }
         }
+      }
     }
     if constexpr (REC) {
       const uint32_t row = rowb + c.j;
@@ -1590,6 +1620,7 @@ __device__ __forceinline__ void bucketmul_body(
 #pragma unroll
     for (int p = 0; p < BP; ++p) {
       tj[p] = p < nv && Lj ? key_threshold_fast(fabsf(vj[p]), __uint_as_float(sCut[p])) : 0x7C00u;
+      tfj[p] = __float_as_uint(h2f(tj[p]));
       // clamped: only a row whose weights are all zero can exceed it, and its
       // products stay 0
       vfj[p] = p < nv ? fminf(fmaxf(ldexpf(vj[p], BP == 1 ? S1 : sS[p]), -0x1p100f), 0x1p100f) : 0.0f;
@@ -1606,16 +1637,30 @@ __device__ __forceinline__ void bucketmul_body(
           atomicOr(&a.result[(size_t)p * a.vec_ws + RES_FLAGS], FLAG_CROP_REACHED);
     }
   };
-  // A ring of 4 chunks in flight: a slot is processed, then refilled with the
-  // next chunk, so 3 loads stay outstanding while one is used (4 measured
-  // faster than 2, 6 or 8: fewer outstanding requests stream better here).
-  Chunk d0, d1, d2, d3;
-  uint4 q0, q1, q2, q3;
+  // The ring of chunks in flight (ring_depth).
+  constexpr int RING = ring_depth<FMT>();
+  Chunk d[RING];
+  uint4 q[RING];
   auto fill = [&]() {
-    take(d0); issue(d0, q0);
-    take(d1); issue(d1, q1);
-    take(d2); issue(d2, q2);
-    take(d3); issue(d3, q3);
+#pragma unroll
+    for (int k = 0; k < RING; ++k) {
+      take(d[k]);
+      issue(d[k], q[k]);
+    }
+  };
+  // The ring is filled before the rows' thresholds are known (their loads
+  // overlap the threshold work); the chunks already taken get the row values
+  // afterwards.
+  auto refresh = [&]() {
+    if constexpr (BP == 1) {
+#pragma unroll
+      for (int k = 0; k < RING; ++k) {
+        d[k].tf = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)tfj[0], d[k].j));
+        d[k].vf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[0]), d[k].j));
+      }
+      stf = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)tfj[0], sj));
+      svf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[0]), sj));
+    }
   };
   // unconditional, so that the wait counters stay exact: a wave without a
   // share (rowb = m, remaining = 0) gets empty chunks that access no memory
@@ -1628,15 +1673,20 @@ __device__ __forceinline__ void bucketmul_body(
       __builtin_amdgcn_s_sleep(1);
   }
   thresholds();
+  refresh();
 
   // ---- stream
   while (active && rowb < m) {
     for (;;) {
-      process(d0, q0); take(d0); issue(d0, q0);
-      process(d1, q1); take(d1); issue(d1, q1);
-      process(d2, q2); take(d2); issue(d2, q2);
-      process(d3, q3); take(d3); issue(d3, q3);
-      if (!(d0.valid || d1.valid || d2.valid || d3.valid)) break;
+      bool any = false;
+#pragma unroll
+      for (int k = 0; k < RING; ++k) {
+        process(d[k], q[k]);
+        take(d[k]);
+        issue(d[k], q[k]);
+        any = any || d[k].valid;
+      }
+      if (!any) break;
     }
     remaining -= batch_take;
     rowb += 64u;
@@ -1645,6 +1695,7 @@ __device__ __forceinline__ void bucketmul_body(
     batch_meta();
     fill();
     thresholds();
+    refresh();
   }
   __syncthreads();
   // Flush: FU tile words per thread are read before any is used (one LDS
@@ -1882,50 +1933,50 @@ __global__ __launch_bounds__(DN_T) void k_dense(const uint16_t* __restrict__ W,
   }
 }
 
-// Dense GEMV without split rows: block b owns the column strip of `lpr`
-// 8-column octets [b lpr, (b + 1) lpr) over all rows, the strip width chosen so
-// that the grid is about one block per CU; y is written with plain stores (no
-// zero fill, no atomics).  A lane reads 16 bytes (8 fp16) of one row per load
-// and keeps UNR loads in flight; the 16 waves of the block take interleaved
-// rows; v is staged in LDS.  The partial sums are reduced over waves, then
-// over the rows a wave covers, in LDS.
-constexpr int DS_T = 1024;
+// Dense GEMV over 128-column strips (256 bytes of each row, line aligned)
+// with the rows split so that the grid holds about 448 blocks: lane l of a
+// wave reads 16 bytes (8 fp16) of row l / 16, a wave 4 rows per load, UNR
+// loads in flight per lane; 8 waves per block take interleaved rows; the
+// partial sums are reduced over the waves and the rows of a load in LDS and
+// added to y with one atomic per column and split (y zero-filled first).
+// Measured against full-height strips of n / 8 / CUs octets (one block per
+// CU, no atomics: 43 us at 4096x14336 -- rows of 112 or 32 bytes per block
+// share cache lines between CUs) and 64-column strips (26.6 us).
+constexpr int DS_T = 512;
 constexpr int DS_W = DS_T / 64;
-constexpr int DS_VLDS = 16384;  // v elements staged in LDS (64 KiB)
+constexpr int DS_LPR = 16;  // lanes per row: 16 x 16 bytes = 128 columns
 template <int UNR>
-__global__ __launch_bounds__(DS_T) void k_dense_strip(const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(DS_T) void k_dense_split(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ v, int64_t m,
-                                                      int64_t n, float* __restrict__ y, int lpr) {
-  __shared__ float vs[DS_VLDS];
+                                                      int64_t n, float* __restrict__ y, int64_t rps) {
+  constexpr int RPW = 64 / DS_LPR;  // rows per wave load
   __shared__ float red[DS_W][64 * 8 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rpw = 64 / lpr;  // rows per wave load
-  const int rl = lane / lpr, oc = lane - rl * lpr;
-  const int64_t col = ((int64_t)blockIdx.x * lpr + oc) * 8;
-  const bool ok = rl < rpw && col < n;
-  const int64_t mv = m < DS_VLDS ? m : DS_VLDS;
-  for (int64_t i = tid; i < mv; i += DS_T) vs[i] = v[i];
-  __syncthreads();
+  const int rl = lane / DS_LPR, oc = lane % DS_LPR;
+  const int64_t col = ((int64_t)blockIdx.x * DS_LPR + oc) * 8;
+  const bool ok = col < n;
+  const int64_t r0 = (int64_t)blockIdx.y * rps;
+  const int64_t r1 = r0 + rps < m ? r0 + rps : m;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
-  const int64_t step = (int64_t)DS_W * rpw;
-  for (int64_t r0 = (int64_t)wave * rpw + rl; r0 < m; r0 += step * UNR) {
+  constexpr int64_t STEP = (int64_t)DS_W * RPW;
+  for (int64_t rb = r0 + wave * RPW + rl; rb < r1; rb += STEP * UNR) {
     uint4 q[UNR];
+    float vr[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t r = r0 + u * step;
-      q[u] = ok && r < m ? *reinterpret_cast<const uint4*>(W + r * n + col) : make_uint4(0u, 0u, 0u, 0u);
+      const int64_t r = rb + u * STEP;
+      q[u] = ok && r < r1 ? *reinterpret_cast<const uint4*>(W + r * n + col) : make_uint4(0u, 0u, 0u, 0u);
+      vr[u] = r < r1 ? v[r] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t r = r0 + u * step;
-      const float vr = r < mv ? vs[r] : (r < m ? v[r] : 0.0f);
       const uint32_t qq[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        acc[2 * k] = __builtin_fmaf(vr, h2f(qq[k]), acc[2 * k]);
-        acc[2 * k + 1] = __builtin_fmaf(vr, h2f(qq[k] >> 16), acc[2 * k + 1]);
+        acc[2 * k] = __builtin_fmaf(vr[u], h2f(qq[k]), acc[2 * k]);
+        acc[2 * k + 1] = __builtin_fmaf(vr[u], h2f(qq[k] >> 16), acc[2 * k + 1]);
       }
     }
   }
@@ -1933,29 +1984,42 @@ __global__ __launch_bounds__(DS_T) void k_dense_strip(const uint16_t* __restrict
   for (int k = 0; k < 8; ++k) red[wave][lane * 8 + k] = acc[k];
   __syncthreads();
   // over the waves: thread t < 512 sums slot t of every wave
-  if (tid < 64 * 8) {
+  {
     float t = 0.0f;
 #pragma unroll
     for (int w = 0; w < DS_W; ++w) t += red[w][tid];
     red[0][tid] = t;
   }
   __syncthreads();
-  // over the rows of a wave load: column oc * 8 + k of the strip
-  if (tid < lpr * 8) {
+  // over the rows of a wave load: column o * 8 + k of the strip
+  if (tid < DS_LPR * 8) {
     const int o = tid >> 3, k = tid & 7;
     float t = 0.0f;
-    for (int r = 0; r < rpw; ++r) t += red[0][(r * lpr + o) * 8 + k];
-    const int64_t c = ((int64_t)blockIdx.x * lpr + o) * 8 + k;
-    if (c < n) y[c] = t;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) t += red[0][(r * DS_LPR + o) * 8 + k];
+    const int64_t c = ((int64_t)blockIdx.x * DS_LPR + o) * 8 + k;
+    if (c < n) atomicAdd(&y[c], t);
   }
 }
 
-// Octets per strip for the strip kernel (0: it does not serve this shape).
-static int dense_strip_width(int64_t n, int cus, const uint16_t* W) {
-  if ((n & 7) != 0 || (reinterpret_cast<uintptr_t>(W) & 15) != 0 || cus < 1) return 0;
-  const int64_t oct = n / 8;
-  const int64_t lpr = (oct + cus - 1) / cus;
-  return lpr <= 16 ? (int)lpr : 0;
+bool dense_split_serves(int64_t n, const uint16_t* W) {
+  return (n & 7) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+}
+
+hipError_t launch_dense_split(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
+                              hipStream_t s) {
+  if (!dense_split_serves(n, W)) return hipErrorInvalidValue;
+  const int64_t strips = (n + DS_LPR * 8 - 1) / (DS_LPR * 8);
+  int64_t splits = (448 + strips / 2) / strips;
+  const int64_t max_splits = (m + 63) / 64;  // at least 64 rows per split
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  const int64_t rps = (m + splits - 1) / splits;
+  hipError_t e = launch_zero_bytes(y, (uint64_t)n * sizeof(float), s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dense_split<2>, dim3((unsigned)strips, (unsigned)splits), dim3(DS_T), 0, s, W, v,
+                     m, n, y, rps);
+  return hipGetLastError();
 }
 
 template <int LPR, int B>
@@ -1976,17 +2040,6 @@ static hipError_t dense_launch(const uint16_t* W, const float* v, int64_t m, int
                      m, n, y, rps, gy > 1 ? 1 : 0, aligned);
   return hipGetLastError();
 }
-
-hipError_t launch_dense_strip(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
-                              int cus, hipStream_t s) {
-  const int lpr = dense_strip_width(n, cus, W);
-  if (lpr < 1) return hipErrorInvalidValue;
-  const int64_t blocks = (n / 8 + lpr - 1) / lpr;
-  hipLaunchKernelGGL(k_dense_strip<4>, dim3((unsigned)blocks), dim3(DS_T), 0, s, W, v, m, n, y, lpr);
-  return hipGetLastError();
-}
-
-bool dense_strip_serves(int64_t n, int cus, const uint16_t* W) { return dense_strip_width(n, cus, W) > 0; }
 
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                              int lanes_per_row, int row_splits, hipStream_t s) {

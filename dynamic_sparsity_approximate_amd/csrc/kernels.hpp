@@ -168,12 +168,12 @@ hipError_t launch_bucketmul(const MulArgs& a, bool record, int blocks_per_group,
                             const EventPair* ev = nullptr);
 hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                              int lanes_per_row, int row_splits, hipStream_t s);
-// Dense GEMV over full-height column strips, about one block per CU, y written
-// with plain stores; serves out_dim a multiple of 8 up to 16 * 8 * cus columns
-// with W 16-byte aligned (dense_strip_serves).
-bool dense_strip_serves(int64_t n, int cus, const uint16_t* W);
-hipError_t launch_dense_strip(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
-                              int cus, hipStream_t s);
+// Dense GEMV over 128-column strips with split rows (y zero-filled, then one
+// atomic per column and split); serves out_dim a multiple of 8 with W 16-byte
+// aligned (dense_split_serves).
+bool dense_split_serves(int64_t n, const uint16_t* W);
+hipError_t launch_dense_split(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
+                              hipStream_t s);
 hipError_t launch_dense_gemm_small(const uint16_t* W, const float* v, int batch, int64_t m,
                                    int64_t n, float* y, hipStream_t s);
 hipError_t launch_silu_mul(const float* h1, const float* h3, int64_t n, float* out, hipStream_t s);

@@ -72,6 +72,12 @@ def parse():
     return ap.parse_args()
 
 
+def layout_opts(args, E) -> dict:
+    """EffortMatrix options of the --format / --crop / --groups flags."""
+    return {"entry_format": E.EFFORT_ENTRY_R12 if args.format == "r12" else E.EFFORT_ENTRY_U32,
+            "crop": args.crop, "groups": args.groups}
+
+
 def entry_bytes(fmt: str) -> float:
     """Bytes the method reads per kept entry in this layout format."""
     return 3.0 if fmt == "r12" else 4.0
@@ -361,7 +367,7 @@ def run_sweep(args, torch, np, E, synth, dev):
     rows = []
     for (m, n) in shapes:
         W = synth.matrix("config1", m, n, seed=0)
-        M = E.EffortMatrix(W, P=args.P, device=dev)
+        M = E.EffortMatrix(W, P=args.P, device=dev, **layout_opts(args, E))
         Wd = torch.from_numpy(W.view(np.int16)).to(dev)
         Rd = rotation_copies(2.0 * m * n)
         Wds = [Wd] + [Wd.clone() for _ in range(Rd - 1)]
@@ -372,7 +378,7 @@ def run_sweep(args, torch, np, E, synth, dev):
         for effort in (1.0, 0.5, 0.25, 0.125):
             v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
             kept = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
-            R = rotation_copies(4.0 * kept)
+            R = rotation_copies(entry_bytes(args.format) * kept)
             layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
             vs = [torch.from_numpy(synth.vector("config1", m, seed=r)).to(dev) for r in range(R)]
             ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
@@ -384,7 +390,8 @@ def run_sweep(args, torch, np, E, synth, dev):
             us = graph_time_us(torch, cyc, max(5, 2000 // R)) / R
             rows.append({"in": m, "out": n, "effort": effort, "us": round(us, 2),
                          "kept_fraction": round(kept / (m * n), 4),
-                         "alg_GBps": round((4.0 * kept + 2.0 * m * args.P + 4.0 * (m + n)) / us / 1e3, 1),
+                         "alg_GBps": round((entry_bytes(args.format) * kept + 2.0 * m * args.P
+                                            + 4.0 * (m + n)) / us / 1e3, 1),
                          "dense_us": round(dense_us, 2), "speedup_vs_dense": round(dense_us / us, 3),
                          "rotation": R})
             log(json.dumps(rows[-1]))
@@ -397,13 +404,13 @@ def run_batched(args, torch, np, E, synth, dev):
     the dense small GEMM that reads W once for all b."""
     m, n, effort = args.m, args.n, args.effort
     W = synth.matrix("config1", m, n, seed=0)
-    M = E.EffortMatrix(W, P=args.P, device=dev, batch=16)
+    M = E.EffortMatrix(W, P=args.P, device=dev, batch=16, **layout_opts(args, E))
     Wd = torch.from_numpy(W.view(np.int16)).to(dev)
     Rd = rotation_copies(2.0 * m * n)
     Wds = [Wd] + [Wd.clone() for _ in range(Rd - 1)]
     v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
     kept = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
-    R = rotation_copies(4.0 * kept)
+    R = rotation_copies(entry_bytes(args.format) * kept)
     layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
     rows = []
     for b in (1, 2, 4, 8, 16):
@@ -449,7 +456,7 @@ def run_decode(args, torch, np, E, synth, dev):
         for r in E.LAYER_ROLES:
             m, n = shapes[r]
             W = synth.matrix("config2", m, n, seed=0, layer=l, w=r)
-            EL[r] = E.EffortMatrix(W, P=args.P, device=dev)
+            EL[r] = E.EffortMatrix(W, P=args.P, device=dev, **layout_opts(args, E))
             DL[r] = torch.from_numpy(W.view(np.int16)).to(dev)
             weights += m * n
         layers.append(EL)
@@ -498,7 +505,7 @@ def run_moe(args, torch, np, E, synth, dev):
         Ws = [synth.matrix("config3", d, h, seed=0, expert=e, w="w1"),
               synth.matrix("config3", d, h, seed=0, expert=e, w="w3"),
               synth.matrix("config3", h, d, seed=0, expert=e, w="w2")]
-        experts.append(tuple(E.EffortMatrix(W, P=args.P, device=dev) for W in Ws))
+        experts.append(tuple(E.EffortMatrix(W, P=args.P, device=dev, **layout_opts(args, E)) for W in Ws))
         dexperts.append(tuple(torch.from_numpy(W.view(np.int16)).to(dev) for W in Ws))
         log("expert %d prepared" % e)
     moe = E.MoEFFN(experts, dev)
@@ -562,7 +569,7 @@ def run_moetraffic(args, torch, np, E, synth, dev):
         Ws = [synth.matrix("config3", d, h, seed=0, expert=e, w="w1"),
               synth.matrix("config3", d, h, seed=0, expert=e, w="w3"),
               synth.matrix("config3", h, d, seed=0, expert=e, w="w2")]
-        experts.append(tuple(E.EffortMatrix(W, P=args.P, device=dev) for W in Ws))
+        experts.append(tuple(E.EffortMatrix(W, P=args.P, device=dev, **layout_opts(args, E)) for W in Ws))
         log("expert %d prepared" % e)
     gmoe = E.MoEFFN(experts, dev, grouped=True)
     xs = [torch.from_numpy(synth.vector("config3/x", d, seed=t)).to(dev) for t in range(tokens)]
@@ -583,9 +590,10 @@ def run_moetraffic(args, torch, np, E, synth, dev):
             for M, v in ((w1, xs[t]), (w3, xs[t]), (w2, w2_inputs[t][k])):
                 kk = M.matvec_debug(v, effort, with_mask=False)["total_kept"]
                 kept += kk
-                alg += 4 * kk + 2 * M.in_dim * args.P + 4 * M.in_dim + 4 * M.out_dim
-        rows.append({"token": t, "experts": [int(e0), int(e1)], "kept_bytes": 4 * kept,
-                     "alg_bytes": alg})
+                alg += (entry_bytes(args.format) * kk + 2 * M.in_dim * args.P + 4 * M.in_dim
+                        + 4 * M.out_dim)
+        rows.append({"token": t, "experts": [int(e0), int(e1)],
+                     "kept_bytes": entry_bytes(args.format) * kept, "alg_bytes": alg})
         log(json.dumps(rows[-1]))
     print(json.dumps({"mode": "moetraffic", "workload": "Mixtral-shaped expert block, 8 experts, "
                       "top-2, grouped calls, effort %g, %d tokens" % (effort, tokens),
@@ -602,10 +610,10 @@ def run_mallcheck(args, torch, np, E, synth, dev):
     contrast)."""
     m, n, effort = args.m, args.n, args.effort
     W = synth.matrix("config1", m, n, seed=0)
-    M = E.EffortMatrix(W, P=args.P, device=dev)
+    M = E.EffortMatrix(W, P=args.P, device=dev, **layout_opts(args, E))
     v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
     kept = M.matvec_debug(v0, effort, with_mask=False)["total_kept"]
-    R = rotation_copies(4.0 * kept, args.rotate_gib)
+    R = rotation_copies(entry_bytes(args.format) * kept, args.rotate_gib)
     layouts = [M.layout] + [M.layout.clone() for _ in range(R - 1)]
     y = torch.empty(n, dtype=torch.float32, device=dev)
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB

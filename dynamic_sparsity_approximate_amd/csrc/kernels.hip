@@ -1933,18 +1933,21 @@ __global__ __launch_bounds__(DN_T) void k_dense(const uint16_t* __restrict__ W,
   }
 }
 
-// Dense GEMV over 128-column strips (256 bytes of each row, line aligned)
-// with the rows split so that the grid holds about 448 blocks: lane l of a
-// wave reads 16 bytes (8 fp16) of row l / 16, a wave 4 rows per load, UNR
-// loads in flight per lane; 8 waves per block take interleaved rows; the
+// Dense GEMV over 256-column strips (512 bytes of each row, line aligned)
+// with the rows split so that the grid holds about one block per CU: lane l
+// of a wave reads 16 bytes (8 fp16) of row l / 32, a wave 2 rows per load,
+// UNR loads in flight per lane; 16 waves per block take interleaved rows; the
 // partial sums are reduced over the waves and the rows of a load in LDS and
 // added to y with one atomic per column and split (y zero-filled first).
-// Measured against full-height strips of n / 8 / CUs octets (one block per
-// CU, no atomics: 43 us at 4096x14336 -- rows of 112 or 32 bytes per block
-// share cache lines between CUs) and 64-column strips (26.6 us).
-constexpr int DS_T = 512;
+// Swept on MI355X (strips of 128/256/512 columns, 2-32 splits, 256-1024
+// threads, 1-8 loads in flight): this shape was fastest at 4096x14336,
+// 14336x4096 and 4096x4096 (about 19.5 us at the first two without the fill);
+// full-height strips of n / 8 / CUs octets, one block per CU without atomics,
+// took 24.5 us (128-byte rows) to 43 us (112-byte rows sharing cache lines
+// between CUs).
+constexpr int DS_T = 1024;
 constexpr int DS_W = DS_T / 64;
-constexpr int DS_LPR = 16;  // lanes per row: 16 x 16 bytes = 128 columns
+constexpr int DS_LPR = 32;  // lanes per row: 32 x 16 bytes = 256 columns
 template <int UNR>
 __global__ __launch_bounds__(DS_T) void k_dense_split(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ v, int64_t m,
@@ -1984,7 +1987,7 @@ __global__ __launch_bounds__(DS_T) void k_dense_split(const uint16_t* __restrict
   for (int k = 0; k < 8; ++k) red[wave][lane * 8 + k] = acc[k];
   __syncthreads();
   // over the waves: thread t < 512 sums slot t of every wave
-  {
+  if (tid < 64 * 8) {
     float t = 0.0f;
 #pragma unroll
     for (int w = 0; w < DS_W; ++w) t += red[w][tid];
@@ -2010,7 +2013,7 @@ hipError_t launch_dense_split(const uint16_t* W, const float* v, int64_t m, int6
                               hipStream_t s) {
   if (!dense_split_serves(n, W)) return hipErrorInvalidValue;
   const int64_t strips = (n + DS_LPR * 8 - 1) / (DS_LPR * 8);
-  int64_t splits = (448 + strips / 2) / strips;
+  int64_t splits = 256 / strips;
   const int64_t max_splits = (m + 63) / 64;  // at least 64 rows per split
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;

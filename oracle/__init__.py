@@ -19,6 +19,8 @@ Parity status of each function (pins live in tests/test_oracle_pins.py):
   stored_mask  pinned: numpy lexsort of (|w| desc, column asc) per row; crop = P stores all
   run_cropped  pinned: crop = P equals run(); effort 1 keeps exactly the stored pairs; a
                call whose kept set lies in the stored part equals run(); numpy sums
+  quantize_q8  pinned: levels by brute force from the definition (numpy), nearest level per
+               weight, probes unchanged, lo maps to itself, signs kept, error bound
   silu_mul     pinned: silu(x) - silu(-x) = x, silu(0) = 0, silu(ln 3) = (3/4) ln 3,
                silu(x) -> x for large x, linear in the second operand
 """
@@ -64,6 +66,8 @@ def _load():
     lib.oracle_run.argtypes = [p, i64, i64, p, i32, p, f32, p, p, p, p, p, p, p, p, p]
     lib.oracle_dense.argtypes = [p, i64, i64, p, p]
     lib.oracle_stored_mask.argtypes = [p, i64, i64, i32, i32, p]
+    lib.oracle_quantize_q8.argtypes = [p, i64, i64, i32, p]
+    lib.oracle_quantize_q8.restype = ctypes.c_int
     lib.oracle_run_cropped.argtypes = [p, i64, i64, p, i32, i32, p, f32, p, p, p, p, p, p, p, p, p]
     for f in (lib.oracle_probes, lib.oracle_chart, lib.oracle_cutoff, lib.oracle_keep_sum,
               lib.oracle_run, lib.oracle_dense, lib.oracle_stored_mask, lib.oracle_run_cropped):
@@ -199,6 +203,17 @@ def run_cropped(W, pr, v, effort: float, crop: int, mask: bool = False) -> dict:
     return {"cutoff": np.float32(c.value), "K": int(K.value), "Kprime": int(Kp.value), "y": y,
             "row_kept": rk, "fingerprint": int(fp.value), "mask": mk, "total_kept": int(tot.value),
             "crop_reached": bool(reached.value), "m": m, "n": n, "P": P}
+
+
+def quantize_q8(W, P: int) -> np.ndarray:
+    """fp16 bits of W in the Q8 bucketed form (each magnitude on its rank
+    bucket's 16-level grid, sign kept); the rule runs on the result."""
+    W = _w(W)
+    m, n = W.shape
+    out = np.empty((m, n), dtype=np.uint16)
+    if _load().oracle_quantize_q8(_ptr(W), m, n, P, _ptr(out)):
+        raise ValueError("oracle_quantize_q8: invalid argument")
+    return out
 
 
 def dense(W, v) -> np.ndarray:

@@ -253,6 +253,61 @@ int oracle_run_cropped(const uint16_t* W, int64_t m, int64_t n, const float* pro
   return 0;
 }
 
+/* The Q8 bucketed form (the [HN] post text: Q8 is in the works; the author's
+   reply to kwikiel: in a bucketed Q8 entry 4 bits store the weight, 1 bit the
+   sign and 3 bits the location, and the 4 bits only have to cover the range
+   of the weight's bucket).  Reading used here: the buckets are the P rank
+   segments of each row; bucket k covers magnitude keys from lo = probe k (its
+   smallest) to hi = probe k-1 (for k = 0: the row's largest), and its 16
+   levels are lo + c 2^s (c = 0..15, s the smallest shift with 15 2^s >= hi -
+   lo) capped at hi, in the integer order of binary16 magnitude bits -- a
+   quasi-logarithmic grid.  A weight takes the level nearest to its key (ties
+   to the upper level) and keeps its sign.  wq[m][n] receives the quantized
+   fp16 bits.  The levels include lo and stay within [lo, hi], so the
+   quantized rows have the same probes as the original ones. */
+static int cmp_u16_desc_col(const void* a, const void* b) { return cmp_key_desc_col_asc(a, b); }
+
+int oracle_quantize_q8(const uint16_t* W, int64_t m, int64_t n, int32_t P, uint16_t* wq) {
+  if (!W || !wq || m <= 0 || n <= 0 || P < 1 || P > n) return 1;
+  key_col* kc = (key_col*)malloc((size_t)n * sizeof(key_col));
+  if (!kc) return 1;
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t j = 0; j < n; ++j) {
+      kc[j].key = (uint16_t)(W[i * n + j] & 0x7FFF);
+      kc[j].col = j;
+    }
+    qsort(kc, (size_t)n, sizeof(key_col), cmp_u16_desc_col);
+    int64_t start = 0; /* first rank (0-based) of bucket k */
+    for (int32_t k = 0; k < P; ++k) {
+      int64_t end = ((int64_t)(k + 1) * n + P - 1) / P; /* one past its last rank */
+      uint32_t lo = kc[end - 1].key;
+      uint32_t hi = k == 0 ? kc[0].key : kc[start - 1].key;
+      uint32_t d = hi - lo, sh = 0;
+      while (15u * (1u << sh) < d) ++sh;
+      for (int64_t r = start; r < end; ++r) {
+        /* the two levels around the key (the top one capped at hi), the
+           nearer taken, ties to the upper */
+        uint32_t x = kc[r].key;
+        uint32_t c = (x - lo) >> sh;
+        if (c > 15u) c = 15u;
+        uint32_t below = lo + (c << sh);
+        if (below > hi) below = hi;
+        uint32_t q = below;
+        if (c < 15u) {
+          uint32_t above = lo + ((c + 1u) << sh);
+          if (above > hi) above = hi;
+          if (above - x <= x - below) q = above;
+        }
+        int64_t j = kc[r].col;
+        wq[i * n + j] = (uint16_t)((W[i * n + j] & 0x8000) | q);
+      }
+      start = end;
+    }
+  }
+  free(kc);
+  return 0;
+}
+
 int oracle_run(const uint16_t* W, int64_t m, int64_t n, const float* probes, int32_t P,
                const float* v, float effort, float* cutoff, int64_t* K, int64_t* Kprime,
                double* y_double, int64_t* row_kept, int64_t* row_chart_kept,

@@ -70,6 +70,10 @@ int oracle_run_cropped(const uint16_t* W, int64_t m, int64_t n, const float* pro
                        int64_t* Kprime, double* y_double, int64_t* row_kept, uint64_t* fingerprint,
                        uint8_t* mask, int64_t* total_kept, int32_t* crop_reached);
 
+/* Q8 bucketed form: wq[m][n] = W with each magnitude moved to the nearest of
+   its rank bucket's 16 levels (see oracle.c); the rule then runs on wq. */
+int oracle_quantize_q8(const uint16_t* W, int64_t m, int64_t n, int32_t P, uint16_t* wq);
+
 /* plain dense y_j = sum_i v_i W_ij in double, i ascending */
 int oracle_dense(const uint16_t* W, int64_t m, int64_t n, const float* v, double* y_double);
 

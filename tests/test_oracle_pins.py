@@ -480,3 +480,64 @@ def test_run_cropped_keeps_stored_part():
     assert np.all(c1["row_kept"] == -(-crop * 400 // P)) and c1["crop_reached"]
     # a small effort keeps only the largest products, inside the stored part
     assert not oracle.run_cropped(W, pr, v, 0.02, crop)["crop_reached"]
+
+
+# ---------------------------------------------------------------- Q8 bucketed form
+
+def _q8_brute(W, P):
+    """Per row and rank bucket: the 16 levels enumerated from the definition,
+    each magnitude key moved to the nearest level by search (ties to the
+    upper one)."""
+    m, n = W.shape
+    out = np.empty_like(W)
+    for i in range(m):
+        keys = (W[i] & 0x7FFF).astype(np.int64)
+        order = np.lexsort((np.arange(n), -keys))
+        ends = [-(-(k + 1) * n // P) for k in range(P)]
+        start = 0
+        for k, end in enumerate(ends):
+            lo = keys[order[end - 1]]
+            hi = keys[order[0]] if k == 0 else keys[order[start - 1]]
+            sh = 0
+            while 15 * 2 ** sh < hi - lo:
+                sh += 1
+            levels = np.minimum(lo + np.arange(16) * 2 ** sh, hi)
+            for r in range(start, end):
+                j = order[r]
+                dist = np.abs(levels - keys[j])
+                best = np.flatnonzero(dist == dist.min())[-1]  # ties: the upper level
+                out[i, j] = (int(W[i, j]) & 0x8000) | int(levels[best])
+            start = end
+    return out
+
+
+@pytest.mark.parametrize("m,n,P", [(6, 200, 16), (4, 37, 5), (3, 64, 64), (5, 33, 1), (2, 1000, 8)])
+def test_quantize_q8_against_search(m, n, P):
+    W, _ = rand_case(m, n, seed=n + P, tag="q8")
+    W[0, ::7] = W[0, 1]        # ties
+    W[1 % m, : n // 3] &= 0x83FF  # subnormals
+    q = oracle.quantize_q8(W, P)
+    assert np.array_equal(q, _q8_brute(W, P))
+    assert np.array_equal(q & 0x8000, W & 0x8000)          # signs kept
+    assert np.array_equal(oracle.probes(q, P), oracle.probes(W, P))  # buckets' lower ends kept
+
+
+def test_quantize_q8_properties():
+    W, v = rand_case(32, 4096, seed=3, tag="q8p")
+    P = 16
+    q = oracle.quantize_q8(W, P)
+    keys, qk = (W & 0x7FFF).astype(np.int64), (q & 0x7FFF).astype(np.int64)
+    # every weight stays inside its bucket: between that bucket's probe and the next larger one
+    pr = oracle.probes(W, P).view(np.uint32)  # fp32 bits are monotone in magnitude, like the keys
+    assert np.all(qk <= keys.max(axis=1, keepdims=True))
+    # at most 16 distinct magnitudes per bucket, so each row uses at most 16 P levels
+    for i in range(32):
+        assert len(np.unique(qk[i])) <= 16 * P
+    # error in key units below half the largest level step of the row
+    assert np.all(np.abs(qk - keys) <= keys.max(axis=1, keepdims=True) // 15)
+    # the rule on the quantized matrix is a rule like any other: effort 1 is its dense product
+    full = oracle.run(q, oracle.probes(q, P), v, 1.0)
+    assert np.allclose(full["y"], oracle.dense(q, v), rtol=1e-12, atol=1e-12)
+    # quantizing again keeps the grid: levels are fixed points of their own buckets
+    assert np.array_equal(oracle.probes(oracle.quantize_q8(q, P), P), oracle.probes(q, P))
+    del pr

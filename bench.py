@@ -49,8 +49,9 @@ def parse():
     ap.add_argument("--effort", type=float, default=0.25)
     ap.add_argument("--P", type=int, default=16)
     ap.add_argument("--groups", type=int, default=0)
-    ap.add_argument("--format", choices=["u32", "r12"], default="u32",
-                    help="entry format of the layout: u32 (4 bytes per entry) or r12 (3 bytes)")
+    ap.add_argument("--format", choices=["u32", "r12", "q8"], default="u32",
+                    help="entry format of the layout: u32 (4 bytes per entry), r12 (3 bytes) "
+                         "or q8 (2 bytes, the Q8 bucketed weights: the product of the quantized matrix)")
     ap.add_argument("--crop", type=int, default=0, help="stored segments per row (0: all)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -74,13 +75,16 @@ def parse():
 
 def layout_opts(args, E) -> dict:
     """EffortMatrix options of the --format / --crop / --groups flags."""
-    return {"entry_format": E.EFFORT_ENTRY_R12 if args.format == "r12" else E.EFFORT_ENTRY_U32,
-            "crop": args.crop, "groups": args.groups}
+    return {"entry_format": format_code(args.format, E), "crop": args.crop, "groups": args.groups}
+
+
+def format_code(fmt: str, E) -> int:
+    return {"u32": E.EFFORT_ENTRY_U32, "r12": E.EFFORT_ENTRY_R12, "q8": E.EFFORT_ENTRY_Q8}[fmt]
 
 
 def entry_bytes(fmt: str) -> float:
     """Bytes the method reads per kept entry in this layout format."""
-    return 3.0 if fmt == "r12" else 4.0
+    return {"u32": 4.0, "r12": 3.0, "q8": 2.0}[fmt]
 
 
 def log(*a):
@@ -179,7 +183,7 @@ def main():
     log("generating W %dx%d and converting" % (m, n))
     W = synth.matrix("config1", m, n, seed=0)
     t0 = time.perf_counter()
-    fmt = E.EFFORT_ENTRY_R12 if args.format == "r12" else E.EFFORT_ENTRY_U32
+    fmt = format_code(args.format, E)
     ebytes = entry_bytes(args.format)
     M = E.EffortMatrix(W, P=P, groups=args.groups, device=dev, entry_format=fmt, crop=args.crop)
     log("layout %.1f MB, G=%d, prepare %.1fs" % (M.layout_bytes / 1e6, M.groups, time.perf_counter() - t0))

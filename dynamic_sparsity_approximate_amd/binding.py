@@ -32,7 +32,7 @@ class EffortError(RuntimeError):
         super().__init__(msg)
 
 
-EFFORT_ENTRY_U32, EFFORT_ENTRY_R12 = 0, 1
+EFFORT_ENTRY_U32, EFFORT_ENTRY_R12, EFFORT_ENTRY_Q8 = 0, 1, 2
 
 
 class effort_prepare_opts(ctypes.Structure):

@@ -71,7 +71,7 @@ bool effort_ok(float e) { return e > 0.0f && e <= 1.0f; }  // false for NaN
 
 // Entry formats the multiply reads.
 bool format_supported(const Geometry& g) {
-  return g.format == EFFORT_ENTRY_U32 || g.format == EFFORT_ENTRY_R12;
+  return g.format == EFFORT_ENTRY_U32 || g.format == EFFORT_ENTRY_R12 || g.format == EFFORT_ENTRY_Q8;
 }
 
 uint32_t k_of(float effort, int64_t N) {
@@ -190,6 +190,8 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   ma.gstride = g.gstride;
   ma.format = g.format;
   ma.floor = floor;
+  ma.probes = probes;
+  ma.rowmax = rowmax;
   ma.runlen = runlen;
   ma.bsum = bsum;
   ma.hist = hist;
@@ -322,7 +324,7 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
 
   uint32_t* urunlen = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.urunlen);
   uint32_t* ubsum = reinterpret_cast<uint32_t*>(ws + (uint64_t)batch * w.slice + w.ubsum);
-  const int bp = bucketmul_pass_width(g.TW, batch);
+  const int bp = bucketmul_pass_width(g.TW, batch, g.format);
   int bpg = cu_count() / g.G;  // at most one block per CU: a larger grid runs a second round
   if (bpg < 1) bpg = 1;
   for (int32_t b0 = 0; b0 < batch; b0 += bp) {
@@ -346,6 +348,8 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
     ma.gstride = g.gstride;
     ma.format = g.format;
     ma.floor = g.off_floor ? reinterpret_cast<const uint16_t*>(layout + g.off_floor) : nullptr;
+    ma.probes = probes;
+    ma.rowmax = rowmax;
     ma.runlen = urunlen;
     ma.bsum = ubsum;
     ma.hist = u32(b0, w.hist);
@@ -501,7 +505,7 @@ int matvec_common(const effort_desc* desc, const void* layout_dev, const float* 
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   // a call with parity outputs takes the same route as one without
   if (batch > 1 && !events && batch >= kUnionMinBatch && effort >= kUnionMinEffort &&
-      bucketmul_pass_width(g.TW, batch) > 0)
+      bucketmul_pass_width(g.TW, batch, g.format) > 0)
     return run_batched(g, layout, v_dev, batch, effort, y_dev, ws, s, dbg);
   if (batch > 1 && !events) {
     // up to EFFORT_MAX_MULTI vectors per launch, each its own single-vector

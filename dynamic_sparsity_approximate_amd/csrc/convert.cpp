@@ -26,6 +26,23 @@
 //    A step that does not fit ends the record early; unused slots are pads
 //    (value 0x8000, step 0).  A stored -0.0 weight becomes +0.0 so that a pad
 //    is never a weight (|-0| = |+0|: the kept set and the sums are unchanged).
+//  * format q8 is the bucketed Q8 form of the author's reply to kwikiel: per
+//    entry 4 bits of weight, 1 sign bit and 3 bits of position, the 4 weight
+//    bits spanning only the bucket's range.  The bucket of an entry is its
+//    rank segment k; its range runs from lo = probe k up to hi = probe k - 1
+//    (the row's largest magnitude for k = 0) in 16 levels lo + c 2^s, capped
+//    at hi, s the smallest shift that reaches hi; the entry keeps its sign
+//    and takes the level nearest to its magnitude key (on a tie the upper
+//    one).  Since every level lies in [lo, hi] and lo itself is a level, the
+//    quantized row has the same probes and largest magnitude, and the key at
+//    each rank is a level of that rank's bucket.  The layout is then the one
+//    of the quantized row (its own ranking decides segments, crop and floor),
+//    each value written as its level code in its segment's bucket.
+//    Inside a (row, group, segment) the entries are in column order, 4 to an
+//    8-byte record: a header word (segment, entries - 1, the first entry's
+//    8-column cell and three cell steps of 6, 6 and 5 bits) and one byte per
+//    entry (sign, level, column in the cell).  A cell step that does not fit
+//    ends the record early; the header's count marks the rest as unused.
 #include <stdint.h>
 #include <string.h>
 
@@ -81,16 +98,108 @@ void pack_records(const std::vector<uint32_t>& cols, const uint16_t* vals_row, i
   }
 }
 
-inline int64_t count_records(const std::vector<uint32_t>& cols) {
+// q8: cell steps of the header, per position 1..3 of a record
+constexpr uint32_t kCellStepMax[3] = {63u, 63u, 31u};
+
+// Whether column b may follow column a at position k (1..3) of a record.
+inline bool joins(int32_t format, int k, uint32_t a, uint32_t b) {
+  if (format == EFFORT_ENTRY_Q8) return (b >> 3) - (a >> 3) <= kCellStepMax[k - 1];
+  return b - a <= kStepMax[k - 1];
+}
+
+inline int64_t count_records(const std::vector<uint32_t>& cols, int32_t format) {
   int64_t r = 0;
   size_t e = 0;
   while (e < cols.size()) {
     int k = 1;
-    while (k < 4 && e + k < cols.size() && cols[e + k] - cols[e + k - 1] <= kStepMax[k - 1]) ++k;
+    while (k < 4 && e + k < cols.size() && joins(format, k, cols[e + k - 1], cols[e + k])) ++k;
     e += (size_t)k;
     ++r;
   }
   return r;
+}
+
+// A Q8 bucket: magnitude keys lo..hi, level step 2^sh.
+struct Q8Bucket {
+  uint32_t lo, hi, sh;
+};
+
+Q8Bucket q8_bucket(uint32_t lo, uint32_t hi) {
+  Q8Bucket b{lo, hi, 0u};
+  while ((15u << b.sh) < hi - lo) ++b.sh;
+  return b;
+}
+
+inline uint32_t q8_level(const Q8Bucket& b, uint32_t c) { return std::min(b.lo + (c << b.sh), b.hi); }
+
+// The code of the level nearest to key x (a tie goes to the larger level),
+// found by trying all 16.
+uint32_t q8_code(const Q8Bucket& b, uint32_t x) {
+  uint32_t best = 0, bl = q8_level(b, 0);
+  uint32_t bd = x > bl ? x - bl : bl - x;
+  for (uint32_t c = 1; c < 16; ++c) {
+    const uint32_t l = q8_level(b, c);
+    const uint32_t dd = x > l ? x - l : l - x;
+    if (dd < bd || (dd == bd && l > bl)) {
+      best = c;
+      bl = l;
+      bd = dd;
+    }
+  }
+  return best;
+}
+
+// The bucket of segment k of a row (probes and rowmax already written).
+inline Q8Bucket row_bucket(const uint16_t* probes_row, uint16_t rowmax, int32_t k) {
+  return q8_bucket(probes_row[k], k == 0 ? rowmax : probes_row[k - 1]);
+}
+
+// The row the layout stores: W's row itself, or (q8) its quantized form in q.
+const uint16_t* stored_row(const uint16_t* row, const Geometry& g, std::vector<uint64_t>& tmp,
+                           std::vector<uint32_t>& order, std::vector<uint16_t>& q) {
+  if (g.format != EFFORT_ENTRY_Q8) return row;
+  const int64_t n = g.n;
+  rank_row(row, n, tmp, order);
+  int64_t r = 0;
+  for (int32_t k = 0; k < g.P; ++k) {
+    const int64_t end = seg_end(n, g.P, k);
+    const uint32_t lo = row[order[end - 1]] & 0x7FFFu;
+    const uint32_t hi = row[order[k == 0 ? 0 : seg_end(n, g.P, k - 1) - 1]] & 0x7FFFu;
+    const Q8Bucket bk = q8_bucket(lo, hi);
+    for (; r < end; ++r) {
+      const uint16_t w = row[order[r]];
+      q[order[r]] = (uint16_t)((w & 0x8000u) | q8_level(bk, q8_code(bk, w & 0x7FFFu)));
+    }
+  }
+  return q.data();
+}
+
+// Packs one (row, group, segment k) list of in-group columns, ascending, into
+// q8 records appended to out (2 words each); vals_row is the quantized row,
+// whose keys are levels of the segment's bucket.
+void pack_q8(const std::vector<uint32_t>& cols, const uint16_t* vals_row, int64_t col0, const Q8Bucket& bk,
+             int32_t k, std::vector<uint32_t>* out) {
+  size_t e = 0;
+  while (e < cols.size()) {
+    int cnt = 1;
+    while (cnt < 4 && e + cnt < cols.size() && joins(EFFORT_ENTRY_Q8, cnt, cols[e + cnt - 1], cols[e + cnt]))
+      ++cnt;
+    uint32_t head = (uint32_t)k | ((uint32_t)(cnt - 1) << 4) | ((cols[e] >> 3) << 6);
+    uint32_t bytes = 0;
+    for (int t = 0; t < cnt; ++t) {
+      const uint32_t c = cols[e + t];
+      const uint16_t w = vals_row[col0 + c];
+      const uint32_t code = q8_code(bk, w & 0x7FFFu);
+      bytes |= (((uint32_t)(w >> 15) << 7) | (code << 3) | (c & 7u)) << (8 * t);
+      if (t > 0) {
+        static const int kShift[3] = {15, 21, 27};
+        head |= ((c >> 3) - (cols[e + t - 1] >> 3)) << kShift[t - 1];
+      }
+    }
+    out->push_back(head);
+    out->push_back(bytes);
+    e += (size_t)cnt;
+  }
 }
 
 // Per (group, segment < crop): the in-group columns of the row's entries in
@@ -114,9 +223,9 @@ int64_t run_units(const Geometry& g, std::vector<std::vector<uint32_t>>& lists, 
   int64_t u = 0;
   for (int32_t k = 0; k < g.crop; ++k) {
     auto& l = lists[(size_t)grp * g.P + k];
-    if (g.format == EFFORT_ENTRY_R12) {
+    if (g.format != EFFORT_ENTRY_U32) {
       std::sort(l.begin(), l.end());
-      u += count_records(l);
+      u += count_records(l, g.format);
     } else {
       u += (int64_t)l.size();
     }
@@ -129,9 +238,10 @@ void max_run_rows(const uint16_t* W, const Geometry& g, int64_t r0, int64_t r1, 
   std::vector<uint64_t> tmp((size_t)g.n);
   std::vector<uint32_t> order((size_t)g.n);
   std::vector<std::vector<uint32_t>> lists((size_t)g.G * g.P);
+  std::vector<uint16_t> q((size_t)g.n);
   int64_t mx = 0;
   for (int64_t i = r0; i < r1; ++i) {
-    rank_row(W + i * g.n, g.n, tmp, order);
+    rank_row(stored_row(W + i * g.n, g, tmp, order, q), g.n, tmp, order);
     split_row(order, g, lists);
     for (int32_t grp = 0; grp < g.G; ++grp) mx = std::max(mx, run_units(g, lists, grp));
   }
@@ -152,8 +262,9 @@ void convert_rows(const uint16_t* W, const Geometry& g, uint8_t* blob, int64_t r
   std::vector<uint32_t> order((size_t)n);
   std::vector<std::vector<uint32_t>> lists((size_t)G * P);
   std::vector<uint32_t> recs;
+  std::vector<uint16_t> q((size_t)n);
   for (int64_t i = r0; i < r1; ++i) {
-    const uint16_t* row = W + i * n;
+    const uint16_t* row = stored_row(W + i * n, g, tmp, order, q);
     rank_row(row, n, tmp, order);
     rowmax[i] = (uint16_t)(row[order[0]] & 0x7FFFu);
     for (int32_t k = 0; k < P; ++k) probes[i * P + k] = (uint16_t)(row[order[seg_end(n, P, k) - 1]] & 0x7FFFu);
@@ -176,6 +287,12 @@ void convert_rows(const uint16_t* W, const Geometry& g, uint8_t* blob, int64_t r
             pack_records(l, row, col0, &recs);
             memcpy(run + (size_t)acc * 3, recs.data(), recs.size() * 4);
             acc += (uint32_t)(recs.size() / 3);
+          } else if (g.format == EFFORT_ENTRY_Q8) {
+            std::sort(l.begin(), l.end());
+            recs.clear();
+            pack_q8(l, row, col0, row_bucket(probes + i * P, rowmax[i], k), k, &recs);
+            memcpy(run + (size_t)acc * 2, recs.data(), recs.size() * 4);
+            acc += (uint32_t)(recs.size() / 2);
           } else {  // rank order: the list is already in it
             for (uint32_t c : l) run[acc++] = (uint32_t)row[col0 + c] | (c << 16);
           }
@@ -231,10 +348,13 @@ int plan_layout(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t grou
   if (!W) return EFFORT_EINVAL;
   int rc = make_geometry(m, n, P, groups, g);
   if (rc) return rc;
-  if (format != EFFORT_ENTRY_U32 && format != EFFORT_ENTRY_R12) return EFFORT_EINVAL;
+  if (format != EFFORT_ENTRY_U32 && format != EFFORT_ENTRY_R12 && format != EFFORT_ENTRY_Q8)
+    return EFFORT_EINVAL;
   if (crop == 0) crop = P;
   if (crop < 1 || crop > P) return EFFORT_EINVAL;
-  if (format == EFFORT_ENTRY_R12 && g->TW > 4096) return EFFORT_EUNSUPPORTED;  // 12-bit column base
+  // 12-bit column base (r12), 9-bit cell (q8)
+  if (format != EFFORT_ENTRY_U32 && g->TW > 4096) return EFFORT_EUNSUPPORTED;
+  if (format == EFFORT_ENTRY_Q8 && P > 16) return EFFORT_EUNSUPPORTED;  // 4-bit segment field
   // the method is defined on finite weights
   const int64_t total = m * n;
   for (int64_t e = 0; e < total; ++e)

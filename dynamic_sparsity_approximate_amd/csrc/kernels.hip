@@ -785,7 +785,7 @@ constexpr int CH = 256;  // u32 format: entries per chunk, one 16-byte quad per 
 // entries per lane (r12).
 template <int FMT>
 constexpr uint32_t chunk_units() {
-  return FMT == EFFORT_ENTRY_R12 ? 64u : (uint32_t)CH;
+  return FMT == EFFORT_ENTRY_U32 ? (uint32_t)CH : 64u;
 }
 
 // Chunks in flight per wave: a ring of loads, a slot processed and then
@@ -798,10 +798,48 @@ constexpr uint32_t chunk_units() {
 #ifndef EFFORT_RING_R12
 #define EFFORT_RING_R12 5
 #endif
+#ifndef EFFORT_RING_Q8
+#define EFFORT_RING_Q8 6
+#endif
 template <int FMT>
 constexpr int ring_depth() {
-  return FMT == EFFORT_ENTRY_R12 ? EFFORT_RING_R12 : EFFORT_RING_U32;
+  return FMT == EFFORT_ENTRY_R12 ? EFFORT_RING_R12 : FMT == EFFORT_ENTRY_Q8 ? EFFORT_RING_Q8 : EFFORT_RING_U32;
 }
+
+// The q8 format: per wave, a table of the bucket bounds of its batch's 64
+// rows, 17 slots a row (16 segments, padded so that the rows' slots spread
+// over the LDS banks).  One vector: {lo | hi << 16, shift}; a batched pass,
+// whose LDS holds several tiles: lo | hi << 16 only, the shift recomputed.
+constexpr int Q8_ROW_SLOTS = 17;
+template <int BP>
+struct Q8Slot {
+  using T = uint32_t;
+};
+template <>
+struct Q8Slot<1> {
+  using T = uint2;
+};
+// The level shift of a bucket with key range d = hi - lo: the smallest s with
+// 15 * 2^s >= d, i.e. the bit length of floor((d - 1) / 15) for d >= 1, and 0
+// for d = 0.  floor(x / 15) = (x * 0x8889) >> 19 for x < 2^15.
+__device__ __forceinline__ uint32_t q8_shift(uint32_t d) {
+  const uint32_t q = ((max(d, 1u) - 1u) * 0x8889u) >> 19;
+  return 31u - (uint32_t)__builtin_clz(2u * q + 1u);
+}
+__device__ __forceinline__ void q8_bounds(uint2 t, uint32_t& lo, uint32_t& hi, uint32_t& sh) {
+  lo = t.x & 0xFFFFu;
+  hi = t.x >> 16;
+  sh = t.y;
+}
+__device__ __forceinline__ void q8_bounds(uint32_t t, uint32_t& lo, uint32_t& hi, uint32_t& sh) {
+  lo = t & 0xFFFFu;
+  hi = t >> 16;
+  sh = q8_shift(hi - lo);
+}
+__device__ __forceinline__ void q8_make(uint32_t lo, uint32_t hi, uint2& t) {
+  t = make_uint2(lo | (hi << 16), q8_shift(hi - lo));
+}
+__device__ __forceinline__ void q8_make(uint32_t lo, uint32_t hi, uint32_t& t) { t = lo | (hi << 16); }
 
 // A chunk of one row's run: units [s0, s1), at most chunk_units; `run` is the
 // row's run, `tf` / `vf` the row's fp32 magnitude threshold and scaled
@@ -1135,6 +1173,9 @@ __device__ __forceinline__ void bucketmul_body(
   __shared__ int32_t sS[BP];
   __shared__ uint32_t mrl[MUL_W][DSP_ROWS];           // per wave: run lengths of its first 256 rows
   __shared__ float mv[BP == 1 ? MUL_W : 1][DSP_ROWS];  // and (one vector) their activations
+  constexpr bool Q8 = FMT == EFFORT_ENTRY_Q8;
+  using QT = typename Q8Slot<BP>::T;
+  __shared__ QT qtab[Q8 ? MUL_W : 1][Q8 ? 64 * Q8_ROW_SLOTS : 1];  // q8: the batch's bucket bounds
   const int tid = threadIdx.x;
   // the wave index made provably uniform: descriptors and per-wave offsets
   // derived from it stay in scalar registers
@@ -1430,6 +1471,7 @@ __device__ __forceinline__ void bucketmul_body(
   // batch state: up to 64 rows from rowb, one per lane
   uint32_t Lj = 0u, aj = 0u, takej = 0u, batch_take = 0u;
   float vj[BP];  // the row's activation in each vector of the pass
+  uint32_t pkj[Q8 ? 17 : 1];  // q8: the row's largest key and its probe keys
   unsigned long long todo = 0ull;
   // chunk sequence: row sj of the batch, entries [ss, se) not yet issued
   uint32_t sj = 0u, ss = 0u, se = 0u;
@@ -1453,6 +1495,15 @@ __device__ __forceinline__ void bucketmul_body(
           if (p < nv) vj[p] = vvec[(size_t)p * a.m + r];
       Lj = (uint32_t)min((int64_t)Lj, a.gstride);  // a run holds gstride units
     }
+    if constexpr (Q8) {
+      // loaded here, written to the table after the batch's first chunks are
+      // in flight
+      const bool ok = r < m;
+      pkj[0] = ok ? (uint32_t)a.rowmax[r] : 0u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        pkj[k + 1] = ok && k < a.P ? (uint32_t)a.probes[(size_t)r * (uint32_t)a.P + (uint32_t)k] : 0u;
+    }
     aj = lane == 0 ? offb : 0u;
     const uint32_t lenj = Lj > aj ? Lj - aj : 0u;
     const uint32_t incl = wave_incl_scan(lenj);
@@ -1467,7 +1518,7 @@ __device__ __forceinline__ void bucketmul_body(
   // Next chunk of the batch: <= chunk_units units of one row.  What depends
   // only on the row -- its run's address, threshold and activation -- is read
   // once when the row starts, not per chunk.  Wave-uniform.
-  constexpr uint32_t UW = FMT == EFFORT_ENTRY_R12 ? 3u : 1u;  // words per unit
+  constexpr uint32_t UW = FMT == EFFORT_ENTRY_R12 ? 3u : FMT == EFFORT_ENTRY_Q8 ? 2u : 1u;  // words per unit
   const uint32_t* srun = entries;
   float stf = 0.0f, svf = 0.0f;
   uint32_t tfj[BP];  // per lane: the row's threshold as fp32 bits (from thresholds())
@@ -1493,14 +1544,14 @@ __device__ __forceinline__ void bucketmul_body(
     c.tf = stf;
     c.vf = svf;
     // u32: chunk ends on quad boundaries of the run (a share's first chunk
-    // in a row may start inside a quad); r12: one record per lane
-    const uint32_t cs = FMT == EFFORT_ENTRY_R12 ? ss : (ss & ~3u);
+    // in a row may start inside a quad); r12, q8: one record per lane
+    const uint32_t cs = FMT == EFFORT_ENTRY_U32 ? (ss & ~3u) : ss;
     c.s1 = c.valid ? min(se, cs + chunk_units<FMT>()) : 0u;
     ss = c.valid ? c.s1 : ss;
   };
   // Loads the chunk for this lane through a buffer descriptor that starts at
-  // unit s0 and ends at s1: lane l reads units from s0 + l (r12: one record)
-  // or words from s0 + 4l (u32: four entries).  Words past s1 read as zero
+  // unit s0 and ends at s1: lane l reads units from s0 + l (r12, q8: one
+  // record) or words from s0 + 4l (u32: four entries).  Words past s1 read as zero
   // without a memory access (the range is checked per 4-byte word), so every
   // lane issues the load and the wait counters stay exact; an empty chunk
   // accesses no memory.
@@ -1512,6 +1563,9 @@ __device__ __forceinline__ void bucketmul_body(
     if constexpr (FMT == EFFORT_ENTRY_R12) {
       const auto q = __builtin_amdgcn_raw_buffer_load_b96(rs, lane * 12, 0, 0);
       buf = make_uint4(q[0], q[1], q[2], 0u);
+    } else if constexpr (FMT == EFFORT_ENTRY_Q8) {
+      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0);
+      buf = make_uint4(q[0], q[1], 0u, 0u);
     } else {
       const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0, 0);
       buf = make_uint4(q[0], q[1], q[2], q[3]);
@@ -1551,6 +1605,30 @@ __device__ __forceinline__ void bucketmul_body(
       for (int k2 = 0; k2 < 4; ++k2) {
         unit[k2] = in;
         entry[k2] = in && (ev[k2] & 0xFFFFu) != 0x8000u;
+      }
+    } else if constexpr (FMT == EFFORT_ENTRY_Q8) {
+      // One record: a header (segment, entries - 1, first 8-column cell, cell
+      // steps of 6, 6 and 5 bits) and one byte per entry (sign, level code,
+      // column in the cell).  The level: min(lo + (code << shift), hi) in the
+      // bucket of the record's segment.  Unused slots and words past the
+      // chunk give -0 (adds nothing).
+      const uint32_t H = buf.x, E = buf.y;
+      const bool in = (uint32_t)lane < c.s1 - c.s0;
+      uint32_t lo, hi, sh;
+      q8_bounds(qtab[wid][c.j * (uint32_t)Q8_ROW_SLOTS + (H & 15u)], lo, hi, sh);
+      const uint32_t last = (H >> 4) & 3u;
+      uint32_t cell = (H >> 6) & 511u;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        if (k2 == 1) cell += (H >> 15) & 63u;
+        if (k2 == 2) cell += (H >> 21) & 63u;
+        if (k2 == 3) cell += H >> 27;
+        const uint32_t b = E >> (8 * k2);
+        const uint32_t key = min(lo + (((b >> 3) & 15u) << sh), hi);
+        unit[k2] = in;
+        entry[k2] = in && (uint32_t)k2 <= last;
+        ev[k2] = entry[k2] ? (key | ((b & 0x80u) << 8)) : 0x8000u;
+        col[k2] = (cell << 3) | (b & 7u);
       }
     } else {
       ev[0] = buf.x;
@@ -1617,6 +1695,14 @@ __device__ __forceinline__ void bucketmul_body(
     }
   };
   auto thresholds = [&]() {
+    if constexpr (Q8) {
+      // lane l: row rowb + l's buckets; read back by every lane of this wave
+      // only (a wave's LDS accesses take effect in order)
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < a.P) q8_make(pkj[k + 1], pkj[k], qtab[wid][lane * Q8_ROW_SLOTS + k]);
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int p = 0; p < BP; ++p) {
       tj[p] = p < nv && Lj ? key_threshold_fast(fabsf(vj[p]), __uint_as_float(sCut[p])) : 0x7C00u;
@@ -1745,28 +1831,31 @@ __global__ __launch_bounds__(mul_threads<1>()) void k_bucketmul_multi(MulMulti m
 constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kMulStaticLds = 24 * 1024;
 
+// The q8 bucket table of a batched pass (16 waves).
+constexpr size_t kQ8PassTable = 16 * 64 * Q8_ROW_SLOTS * sizeof(uint32_t);
+
 // Largest dynamic LDS (the vectors' tiles) a pass of bp vectors may request.
-static size_t pass_tile_budget(int bp) {
+static size_t pass_tile_budget(int bp, int format) {
   const size_t per = (kLdsBytes - kMulStaticLds) / (size_t)bp;  // tile + cutoff histogram
-  return (size_t)bp * (per - 2048);
+  return (size_t)bp * (per - 2048) - (format == EFFORT_ENTRY_Q8 ? kQ8PassTable : 0);
 }
 
-int bucketmul_pass_width(int32_t TW, int32_t batch) {
+int bucketmul_pass_width(int32_t TW, int32_t batch, int32_t format) {
   if (batch < 2) return 0;
   for (int bp = 8; bp >= 2; bp >>= 1)
-    if ((size_t)bp * ((size_t)TW * 4) <= pass_tile_budget(bp)) return bp;
+    if ((size_t)bp * ((size_t)TW * 4) <= pass_tile_budget(bp, format)) return bp;
   return 0;
 }
 
 template <bool REC, int BP, int FMT>
 static hipError_t launch_mul_bp(const MulArgs& a, unsigned grid, hipStream_t s) {
   const size_t lds = (size_t)BP * a.TW * sizeof(int32_t);
-  if (lds > pass_tile_budget(BP)) return hipErrorInvalidValue;
+  if (lds > pass_tile_budget(BP, FMT)) return hipErrorInvalidValue;
   // the attribute is set on every launch: a per-instantiation flag would be
   // per device state, and the call costs no device work
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bucketmul<REC, BP, FMT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)pass_tile_budget(BP));
+                                     (int)pass_tile_budget(BP, FMT));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_bucketmul<REC, BP, FMT>), dim3(grid), dim3(mul_threads<BP>()), lds, s, a.v,
                      a.entries, a.runlen, a.bsum, a.result, a.y, a);
@@ -1806,6 +1895,7 @@ hipError_t launch_bucketmul(const MulArgs& args, bool record, int blocks_per_gro
   MulArgs a = args;
   a.bpg_recip = blocks_per_group >= 2 ? (uint32_t)((1ull << 32) / (uint64_t)blocks_per_group) : 0u;
   if (a.format == EFFORT_ENTRY_R12) return launch_mul_fmt<EFFORT_ENTRY_R12>(a, record, grid, s, ev);
+  if (a.format == EFFORT_ENTRY_Q8) return launch_mul_fmt<EFFORT_ENTRY_Q8>(a, record, grid, s, ev);
   return launch_mul_fmt<EFFORT_ENTRY_U32>(a, record, grid, s, ev);
 }
 
@@ -1825,19 +1915,18 @@ hipError_t launch_bucketmul_multi(const MulMulti& mm_in, int count, const int* b
   mm.count = count;
   for (int j = 1; j < count; ++j)  // one instantiation per launch: the pairs share a format
     if (mm.a[j].format != mm.a[0].format) return hipErrorInvalidValue;
-  const bool r12 = mm.a[0].format == EFFORT_ENTRY_R12;
-  if (record && r12)
-    hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_R12>), dim3(total), dim3(mul_threads<1>()),
-                       0, s, mm);
-  else if (record)
-    hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_U32>), dim3(total), dim3(mul_threads<1>()),
-                       0, s, mm);
-  else if (r12)
-    hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_R12>), dim3(total),
-                       dim3(mul_threads<1>()), 0, s, mm);
-  else
-    hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_U32>), dim3(total),
-                       dim3(mul_threads<1>()), 0, s, mm);
+  const int f = mm.a[0].format;
+  const dim3 gr(total), bl(mul_threads<1>());
+  if (f == EFFORT_ENTRY_R12) {
+    if (record) hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_R12>), gr, bl, 0, s, mm);
+    else hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_R12>), gr, bl, 0, s, mm);
+  } else if (f == EFFORT_ENTRY_Q8) {
+    if (record) hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_Q8>), gr, bl, 0, s, mm);
+    else hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_Q8>), gr, bl, 0, s, mm);
+  } else {
+    if (record) hipLaunchKernelGGL((k_bucketmul_multi<true, EFFORT_ENTRY_U32>), gr, bl, 0, s, mm);
+    else hipLaunchKernelGGL((k_bucketmul_multi<false, EFFORT_ENTRY_U32>), gr, bl, 0, s, mm);
+  }
   return hipGetLastError();
 }
 

@@ -106,8 +106,10 @@ struct MulArgs {
   const float* v;
   const uint32_t* entries;  // units [m][G][gstride] (u32 format: one word per unit)
   int64_t gstride;          // units per (row, group) run
-  int32_t format;           // EFFORT_ENTRY_U32 or EFFORT_ENTRY_R12 (all pairs of a multi launch alike)
+  int32_t format;           // EFFORT_ENTRY_* (all pairs of a multi launch alike)
   const uint16_t* floor;    // cropped layouts: [m] largest magnitude key not stored (else null)
+  const uint16_t* probes;   // [m][P] probe keys, rowmax [m]: the q8 format's bucket bounds
+  const uint16_t* rowmax;
   const uint32_t* runlen;   // [G][m]
   const uint32_t* bsum;     // [nbd][G + 1]
   uint32_t* hist;           // [HIST_BINS], cleared here for the next call
@@ -145,7 +147,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair
 hipError_t launch_union(const UnionArgs& a, hipStream_t s);
 // vectors per pass of the batched multiply that the LDS holds for groups of
 // TW columns (0: none, use single-vector calls)
-int bucketmul_pass_width(int32_t TW, int32_t batch);
+int bucketmul_pass_width(int32_t TW, int32_t batch, int32_t format);
 // Several matrices that share the input vector (one vector each): argument
 // tables indexed by grid y (chart, dispatch) or by block range (multiply).
 struct SelectMulti {

@@ -13,6 +13,8 @@
 //                                   high 16 bits the column inside the group, rank order
 //                                   inside a segment.  Format r12: one unit = a record of
 //                                   three 32-bit words holding 4 entries of one segment
+//                                   in column order; format q8: a record of 2 words,
+//                                   a header and 4 one-byte Q8 entries of one segment
 //                                   in column order (see the converter).
 //   rowmax          u16 [m]         largest magnitude key of each row
 //   floor           u16 [m]         (cropped layouts) largest magnitude key of the
@@ -47,7 +49,9 @@ struct Geometry {
 };
 
 // 32-bit words per unit of the entries region
-inline int32_t unit_words(int32_t format) { return format == EFFORT_ENTRY_R12 ? 3 : 1; }
+inline int32_t unit_words(int32_t format) {
+  return format == EFFORT_ENTRY_R12 ? 3 : format == EFFORT_ENTRY_Q8 ? 2 : 1;
+}
 
 // The smallest power of two, at least 2, whose groups hold at most
 // kTargetGroupWidth columns.  A power of two divides the CU count, so the
@@ -173,13 +177,16 @@ inline int64_t max_gstride(const Geometry& g) {
 inline bool geometry_from_desc(const effort_desc* d, Geometry* g) {
   Geometry x;
   if (make_geometry(d->in_dim, d->out_dim, d->probes_per_row, d->groups, &x) != EFFORT_OK) return false;
-  if (d->entry_format != EFFORT_ENTRY_U32 && d->entry_format != EFFORT_ENTRY_R12) return false;
+  if (d->entry_format != EFFORT_ENTRY_U32 && d->entry_format != EFFORT_ENTRY_R12 &&
+      d->entry_format != EFFORT_ENTRY_Q8)
+    return false;
   if (d->crop_segments < 1 || d->crop_segments > d->probes_per_row) return false;
   x.format = d->entry_format;
   x.crop = d->crop_segments;
   if (d->group_stride < 1 || d->group_stride > max_gstride(x)) return false;
   x.gstride = d->group_stride;
-  if (x.format == EFFORT_ENTRY_R12 && x.TW > 4096) return false;  // 12-bit column base
+  if (x.format != EFFORT_ENTRY_U32 && x.TW > 4096) return false;  // 12-bit column / 9-bit cell
+  if (x.format == EFFORT_ENTRY_Q8 && x.P > 16) return false;      // 4-bit segment field
   place_regions(&x);
   if (x.G != d->groups || x.TW != d->group_width || x.row_stride != d->row_stride ||
       x.off_probes != d->off_probes || x.off_counts != d->off_counts ||

@@ -68,6 +68,10 @@ enum {
 #define EFFORT_ENTRY_U32 0 /* 4 bytes per entry: fp16 value, 16-bit column in the group */
 #define EFFORT_ENTRY_R12 1 /* 3 bytes per entry: records of 4 entries in 12 bytes (see
                               effort_prepare_host_opts) */
+#define EFFORT_ENTRY_Q8 2  /* Q8 bucketed entries, 2 bytes per entry: records of 4 one-byte
+                              entries (sign, 4-bit level, 3-bit location) and a 4-byte
+                              header (see effort_prepare_host_opts); lossy: the multiply
+                              runs on the quantized matrix */
 
 typedef struct effort_desc {
   uint32_t magic, version;
@@ -148,6 +152,20 @@ int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_d
                   The position bits an entry spends against what its bucket
                   already tells is the trade-off of the author's reply to kwikiel
                   in [HN].
+                  EFFORT_ENTRY_Q8 (P <= 16, group width <= 4096): the Q8 bucketed
+                  form of the author's reply to kwikiel in [HN] (4 bits of weight,
+                  1 sign bit, 3 location bits, the weight bits covering only its
+                  bucket's range).  Buckets are the rank segments of a row: bucket
+                  k spans magnitude keys from lo = probe k to hi = probe k-1 (the
+                  row's largest for k = 0) in 16 levels lo + c 2^s capped at hi (s
+                  the smallest shift with 15 2^s >= hi - lo); each weight moves to
+                  the nearest level (ties up), sign kept.  The quantized matrix
+                  has the same probes; the call computes the rule on it.  Storage:
+                  per (row, group, segment) the entries in column order, 4 to an
+                  8-byte record: a header word (bits 0-3 segment, 4-5 entries - 1,
+                  6-14 the first entry's 8-column cell, then cell steps of 6, 6 and
+                  5 bits) and a word of 4 entry bytes (bit 7 sign, bits 6-3 level,
+                  bits 2-0 column in the cell).
    crop_segments  0 or P: every segment is stored.  c in [1, P): only the rank
                   segments 0..c-1 of each row (the largest magnitudes) are stored
                   ([HN] post text: the format lets one skip a share of the least

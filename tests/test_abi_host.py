@@ -374,16 +374,27 @@ def test_binding_reinitialises_workspace_after_hip_error(monkeypatch):
                 assert calls == [(name,)], (name, calls)
 
 
-# ---------------------------------------------------------------- layout options: crop, r12 records
+# ---------------------------------------------------------------- layout options: crop, r12 / q8 records
+
+def q8_level(lo, hi, code):
+    """Level `code` of the Q8 bucket [lo, hi]: lo + code 2^s capped at hi, s the
+    smallest shift with 15 2^s >= hi - lo."""
+    s = 0
+    while (15 << s) < hi - lo:
+        s += 1
+    return min(lo + (code << s), hi)
+
 
 def decode_runs(desc, blob):
     """Per (row, group): the storage units of the run decoded to a list of
-    (unit index, in-group column, value bits) in storage order; pads of r12
-    records are dropped.  Also the counts table [m][P][G]."""
+    (unit index, in-group column, value bits[, q8: header segment]) in storage
+    order; unused record slots are dropped.  Also the counts table [m][P][G]."""
     m, P, G = desc.in_dim, desc.probes_per_row, desc.groups
     G4 = (G + 3) // 4 * 4
     cnt = blob[desc.off_counts: desc.off_counts + m * P * G4 * 4].view(np.uint32).reshape(m, P, G4)[:, :, :G]
-    uw = 3 if desc.entry_format == B.EFFORT_ENTRY_R12 else 1
+    uw = {B.EFFORT_ENTRY_U32: 1, B.EFFORT_ENTRY_R12: 3, B.EFFORT_ENTRY_Q8: 2}[desc.entry_format]
+    probes = blob[desc.off_probes: desc.off_probes + m * P * 2].view(np.uint16).reshape(m, P)
+    rowmax = decode_rowmax(desc, blob)
     words = blob[desc.off_entries: desc.off_entries + m * desc.row_stride * uw * 4].view(np.uint32)
     words = words.reshape(m, G, desc.group_stride * uw)
     runs = {}
@@ -395,6 +406,19 @@ def decode_runs(desc, blob):
             if uw == 1:
                 for u in range(L):
                     out.append((u, int(w[u] >> 16), int(w[u] & 0xFFFF)))
+            elif uw == 2:
+                for u in range(L):
+                    h, e = int(w[2 * u]), int(w[2 * u + 1])
+                    seg, last, cell = h & 15, (h >> 4) & 3, (h >> 6) & 511
+                    steps = ((h >> 15) & 63, (h >> 21) & 63, h >> 27)
+                    lo = int(probes[i, seg])
+                    hi = int(rowmax[i]) if seg == 0 else int(probes[i, seg - 1])
+                    for t in range(last + 1):
+                        if t:
+                            cell += steps[t - 1]
+                        b = (e >> (8 * t)) & 255
+                        key = q8_level(lo, hi, (b >> 3) & 15)
+                        out.append((u, cell * 8 + (b & 7), key | ((b >> 7) << 15), seg))
             else:
                 for u in range(L):
                     w0, w1, w2 = (int(x) for x in w[3 * u: 3 * u + 3])
@@ -412,14 +436,23 @@ def decode_runs(desc, blob):
 
 @pytest.mark.parametrize("m,n,P,G,fmt,crop", [
     (9, 300, 16, 3, 0, 12), (6, 1000, 16, 2, 1, 0), (6, 1000, 16, 2, 1, 9), (5, 37, 3, 0, 1, 0),
-    (4, 4096, 16, 1, 1, 16), (3, 130, 7, 3, 0, 1), (8, 5000, 8, 0, 1, 5), (2, 64, 64, 1, 1, 40)])
+    (4, 4096, 16, 1, 1, 16), (3, 130, 7, 3, 0, 1), (8, 5000, 8, 0, 1, 5), (2, 64, 64, 1, 1, 40),
+    (9, 300, 16, 3, 2, 12), (6, 1000, 16, 2, 2, 0), (5, 37, 3, 0, 2, 0), (4, 4096, 16, 1, 2, 16),
+    (8, 5000, 8, 0, 2, 5), (7, 700, 16, 2, 2, 3), (3, 20, 1, 1, 2, 0)])
 def test_layout_options_roundtrip(m, n, P, G, fmt, crop):
+    """Every stored pair exactly once, in its segment, in the format's order;
+    probes, rowmax and floor.  A q8 layout is the layout of the quantized
+    matrix (oracle.quantize_q8): its values, ranks, crop and floor."""
     W, _ = rand_case(m, n, seed=m + n + P + crop, tag="opts")
     if m > 2:
         W[1, ::3] = W[1, 0]        # ties
         W[2, : n // 2] = 0         # zeros
         W[2, n // 2: n // 2 + 5] = 0x8000  # negative zeros
     d, blob = E.effort_prepare_host(W, P, G, fmt, crop)
+    if fmt == B.EFFORT_ENTRY_Q8:
+        Wq = oracle.quantize_q8(W, P)
+        assert np.array_equal(oracle.probes(Wq, P), oracle.probes(W, P))
+        W = Wq
     E.effort_layout_check(d, blob)
     assert d.total_bytes == E.effort_layout_bytes_opts(W, P, G, fmt, crop) <= blob.size
     c = crop or P
@@ -467,6 +500,8 @@ def test_layout_options_roundtrip(m, n, P, G, fmt, crop):
             for k in range(c):
                 inside = (units >= lo[k]) & (units < cnt[i, k, g])
                 assert np.all(seg[cols[inside]] == k), (i, g, k)
+                if fmt == B.EFFORT_ENTRY_Q8:
+                    assert all(e[3] == k for e, x in zip(ents, inside) if x)
                 ck = cols[inside]
                 if fmt == 0:
                     assert np.all(np.diff(rank[ck]) > 0)  # rank order in the segment
@@ -488,12 +523,26 @@ def test_r12_records_are_three_bytes_per_entry():
     assert used * 4 <= 1.03 * W.size  # record slots per weight
 
 
+def test_q8_records_are_two_bytes_per_entry():
+    """Q8 at 4096 columns and P = 16: 8-byte records of close to 4 entries."""
+    W, _ = rand_case(64, 4096, seed=7, tag="q8size")
+    d, blob = E.effort_prepare_host(W, 16, 1, B.EFFORT_ENTRY_Q8)
+    assert d.off_rowmax - d.off_entries <= 2.1 * W.size
+    cnt, runs = decode_runs(d, blob)
+    used = sum(int(cnt[i, 15, 0]) for i in range(64))
+    assert used * 4 <= 1.03 * W.size
+
+
 def test_layout_options_reject():
     W, _ = rand_case(4, 9000, seed=8, tag="rej")
-    with pytest.raises(E.EffortError) as ei:  # r12 columns need groups of at most 4096
-        E.effort_prepare_host(W, 16, 1, B.EFFORT_ENTRY_R12)
+    for fmt in (B.EFFORT_ENTRY_R12, B.EFFORT_ENTRY_Q8):  # 12-bit columns, 9-bit cells
+        with pytest.raises(E.EffortError) as ei:
+            E.effort_prepare_host(W, 16, 1, fmt)
+        assert ei.value.code == B.EFFORT_EUNSUPPORTED
+    with pytest.raises(E.EffortError) as ei:  # a 4-bit segment field
+        E.effort_prepare_host(W[:, :4096], 17, 1, B.EFFORT_ENTRY_Q8)
     assert ei.value.code == B.EFFORT_EUNSUPPORTED
-    for bad in ((2, 0), (0, 17), (0, -1)):
+    for bad in ((3, 0), (0, 17), (0, -1)):
         with pytest.raises(E.EffortError) as ei:
             E.effort_prepare_host(W, 16, 0, *bad)
         assert ei.value.code == B.EFFORT_EINVAL

@@ -49,9 +49,10 @@ def parse():
     ap.add_argument("--effort", type=float, default=0.25)
     ap.add_argument("--P", type=int, default=16)
     ap.add_argument("--groups", type=int, default=0)
-    ap.add_argument("--format", choices=["u32", "r12", "q8"], default="u32",
-                    help="entry format of the layout: u32 (4 bytes per entry), r12 (3 bytes) "
-                         "or q8 (2 bytes, the Q8 bucketed weights: the product of the quantized matrix)")
+    ap.add_argument("--format", choices=["u32", "r12", "q8"], default="r12",
+                    help="entry format of the layout: r12 (3 bytes per entry, the default), u32 "
+                         "(4 bytes) or q8 (2 bytes, the Q8 bucketed weights: the product of the "
+                         "quantized matrix)")
     ap.add_argument("--crop", type=int, default=0, help="stored segments per row (0: all)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -95,9 +96,10 @@ def kernels_sha():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_counters():
+def read_counters(fmt: str):
     """HBM traffic of the bucketMul kernel from the committed rocprofv3 --pmc summary,
-    or None if it is missing or was taken on a different kernels.hip."""
+    or None if it is missing, was taken on a different kernels.hip or on another
+    entry format."""
     if not os.path.exists(COUNTERS):
         return None
     kv = {}
@@ -105,7 +107,7 @@ def read_counters():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernels_sha256") != kernels_sha():
+    if kv.get("kernels_sha256") != kernels_sha() or kv.get("entry_format") != fmt:
         return None
     try:
         return float(kv["hbm_bytes_per_dispatch"])
@@ -246,7 +248,7 @@ def main():
         alg_mul = ebytes * kept_mean + 4.0 * m + 4.0 * n
         alg_step = ebytes * kept_mean + 2.0 * m * P + 4.0 * m + 4.0 * n
         achieved = alg_mul / (mul_us * 1e-6) / 1e9
-        traffic = read_counters()
+        traffic = read_counters(args.format)
         result.update({
             "us_per_matvec": us_per,
             "ms_per_step": ms / steps,

@@ -235,17 +235,19 @@ def test_mistral_shapes(shape):
                 m, n, seed, effort, ref["total_kept"] / W.size, err))
 
 
-def test_headline_timed_entry_several_seeds():
+@pytest.mark.parametrize("fmt", [E.EFFORT_ENTRY_R12, E.EFFORT_ENTRY_U32])
+def test_headline_timed_entry_several_seeds(fmt):
     """The benchmarked entry point itself (effort_matvec, no recording) at
-    4096x14336, effort 0.25, seeds 0-4: its cutoff bits, K and K' (the result
-    words it leaves in the workspace) and y against the oracle; the recording
-    entry point on the same input (the same kernels, recording on) gives the
-    same y and the oracle's kept set, fingerprint and full mask."""
+    4096x14336, effort 0.25, seeds 0-4, on the layout the benchmark times (r12
+    entries) and the 4-byte one: its cutoff bits, K and K' (the result words
+    it leaves in the workspace) and y against the oracle; the recording entry
+    point on the same input (the same kernels, recording on) gives the same y
+    and the oracle's kept set, fingerprint and full mask."""
     d = dev()
     m, n, effort = 4096, 14336, 0.25
     W = synth.matrix("config1", m, n, seed=0)
     pr = oracle.probes(W, 16)
-    M = E.EffortMatrix(W, P=16, device=d)
+    M = E.EffortMatrix(W, P=16, device=d, entry_format=fmt)
     for seed in range(5):
         v = synth.vector("config1", m, seed=seed)
         vt = torch.from_numpy(v).to(d)
@@ -260,7 +262,7 @@ def test_headline_timed_entry_several_seeds():
         got = M.matvec_debug(vt, effort, with_mask=True)
         check(got, ref, True, where=("headline", seed))
         assert rel_l2(got["y"], y) < 1e-6, seed
-        say("headline seed %d: timed entry and recording entry equal the oracle" % seed)
+        say("headline format %d seed %d: timed entry and recording entry equal the oracle" % (fmt, seed))
 
 
 def test_graph_replays_match_eager():

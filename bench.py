@@ -565,9 +565,9 @@ def run_moetraffic(args, torch, np, E, synth, dev):
     kernels, so a FETCH_SIZE counter run can sum exactly their reads), then,
     through the recording entry point on the inputs those calls used, the kept
     products of each of the six matvecs.  Per token it prints the kept bytes
-    (4 per kept entry) and the method's algorithmic bytes (kept bytes + 2mP
-    probes + 4m v + 4n y per matvec); the layouts of all 8 experts hold four
-    times the two routed experts' entries."""
+    (the layout's bytes per entry, 3 for r12, per kept entry) and the method's
+    algorithmic bytes (kept bytes + 2mP probes + 4m v + 4n y per matvec); the
+    layouts of all 8 experts hold four times the two routed experts' entries."""
     d, h = MISTRAL["dim"], MISTRAL["hidden"]
     effort, tokens = 0.25, 4
     experts = []

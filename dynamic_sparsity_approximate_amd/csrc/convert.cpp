@@ -370,7 +370,10 @@ int plan_layout(const uint16_t* W, int64_t m, int64_t n, int32_t P, int32_t grou
     for (auto& th : pool) th.join();
     int64_t gs = 1;
     for (int64_t x : mx) gs = std::max(gs, x);
-    g->gstride = gs;
+    // every run starts on a 128-byte line: 32 units of 4 or 12 bytes, 16 of
+    // 8 (TW is a multiple of 64, so the rounded stride stays within it)
+    const int64_t a = format == EFFORT_ENTRY_Q8 ? 16 : 32;
+    g->gstride = std::min((gs + a - 1) / a * a, (int64_t)g->TW);
   }
   place_regions(g);
   return EFFORT_OK;

@@ -272,12 +272,10 @@ def main():
         Wds = [Wd0] + [Wd0.clone() for _ in range(Rd - 1)]
         vds = [torch.from_numpy(synth.vector("config1", m, seed=r)).to(dev) for r in range(Rd)]
         yds = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(Rd)]
-        dwsb = E.dense_workspace_bytes(m, n)
-        dws = torch.zeros(max(dwsb, 256), dtype=torch.uint8, device=dev)
 
         def dcycle():
             for r in range(Rd):
-                E.dense_gemv_ws(Wds[r], vds[r], m, n, yds[r], dws, dwsb)
+                E.dense_gemv(Wds[r], vds[r], m, n, yds[r])
 
         for _ in range(3):
             dcycle()
@@ -381,10 +379,7 @@ def run_sweep(args, torch, np, E, synth, dev):
         Wds = [Wd] + [Wd.clone() for _ in range(Rd - 1)]
         vd = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
         yd = torch.empty(n, dtype=torch.float32, device=dev)
-        dwsb = E.dense_workspace_bytes(m, n)
-        dws = torch.zeros(max(dwsb, 256), dtype=torch.uint8, device=dev)
-        dense_us = graph_time_us(torch, lambda: [E.dense_gemv_ws(w, vd, m, n, yd, dws, dwsb) for w in Wds],
-                                 50) / Rd
+        dense_us = graph_time_us(torch, lambda: [E.dense_gemv(w, vd, m, n, yd) for w in Wds], 50) / Rd
         del Wds
         for effort in (1.0, 0.5, 0.25, 0.125):
             v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
@@ -531,17 +526,14 @@ def run_moe(args, torch, np, E, synth, dev):
     o = [torch.empty(d, dtype=torch.float32, device=dev) for _ in range(2)]
     y = torch.empty(d, dtype=torch.float32, device=dev)
 
-    dwsb = max(E.dense_workspace_bytes(d, h), E.dense_workspace_bytes(h, d))
-    dws = torch.zeros(max(dwsb, 256), dtype=torch.uint8, device=dev)  # calls in stream order share it
-
     def dense_token(t):
         e0, e1, g0, g1 = routes[t]
         for k, e in enumerate((e0, e1)):
             w1, w3, w2 = dexperts[e]
-            E.dense_gemv_ws(w1, xs[t], d, h, hbuf, dws, dwsb)
-            E.dense_gemv_ws(w3, xs[t], d, h, h3buf, dws, dwsb)
+            E.dense_gemv(w1, xs[t], d, h, hbuf)
+            E.dense_gemv(w3, xs[t], d, h, h3buf)
             E.effort_silu_mul(hbuf, h3buf, h, gbuf)
-            E.dense_gemv_ws(w2, gbuf, h, d, o[k], dws, dwsb)
+            E.dense_gemv(w2, gbuf, h, d, o[k])
         E.effort_axpby(o[0], g0, o[1], g1, d, y)
 
     dus = graph_time_us(torch, lambda: [dense_token(t) for t in range(tokens)], 10) / tokens

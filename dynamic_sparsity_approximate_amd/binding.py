@@ -102,8 +102,6 @@ _PROTOS = {
                                    ctypes.POINTER(_p), _p, _p], ctypes.c_int),
     "effort_matvec_timed": ([_D, _p, _p, _f32, _p, _p, _u64, _p, _p], ctypes.c_int),
     "dense_gemv": ([_p, _p, _i64, _i64, _p, _p], ctypes.c_int),
-    "dense_workspace_bytes": ([_i64, _i64, ctypes.POINTER(_u64)], ctypes.c_int),
-    "dense_gemv_ws": ([_p, _p, _i64, _i64, _p, _p, _u64, _p], ctypes.c_int),
     "dense_gemm_small": ([_p, _p, _i32, _i64, _i64, _p, _p], ctypes.c_int),
     "effort_silu_mul": ([_p, _p, _i64, _p, _p], ctypes.c_int),
     "effort_axpby": ([_p, _f32, _p, _f32, _i64, _p, _p], ctypes.c_int),
@@ -364,19 +362,6 @@ def effort_matvec_timed(desc, layout, v, effort: float, y, ws, ws_bytes: int, ev
 
 def dense_gemv(w, v, in_dim: int, out_dim: int, y, stream=None):
     _check(_lib.dense_gemv(_ptr(w), _ptr(v), in_dim, out_dim, _ptr(y), _stream(stream)), "dense_gemv")
-
-
-def dense_workspace_bytes(in_dim: int, out_dim: int) -> int:
-    b = _u64()
-    _check(_lib.dense_workspace_bytes(in_dim, out_dim, ctypes.byref(b)), "dense_workspace_bytes")
-    return int(b.value)
-
-
-def dense_gemv_ws(w, v, in_dim: int, out_dim: int, y, ws, ws_bytes: int, stream=None):
-    """dense_gemv in one kernel; `ws` (zero-filled once, at least
-    dense_workspace_bytes) is left zero by the call."""
-    _check(_lib.dense_gemv_ws(_ptr(w), _ptr(v), in_dim, out_dim, _ptr(y), _ptr(ws), ws_bytes,
-                              _stream(stream)), "dense_gemv_ws")
 
 
 def dense_gemm_small(w, v, batch: int, in_dim: int, out_dim: int, y, stream=None):

@@ -152,9 +152,7 @@ class DecodeStep:
 
 
 class DenseDecodeStep:
-    """The same chain with the dense fp16 GEMV (weights as device fp16 [in][out]),
-    each call one kernel (dense_gemv_ws); every role has its own workspace, so
-    roles on different side streams never share one."""
+    """The same chain with the dense fp16 GEMV (weights as device fp16 [in][out])."""
 
     def __init__(self, layers, head, x, a, head_in):
         import torch
@@ -168,12 +166,6 @@ class DenseDecodeStep:
             o["g"] = torch.empty(L["w1"].shape[1], dtype=torch.float32, device=dev)
             self.out.append(o)
         self.logits = torch.empty(head.shape[1], dtype=torch.float32, device=dev)
-        shapes = {r: [tuple(L[r].shape) for L in layers] for r in LAYER_ROLES}
-        shapes["head"] = [tuple(head.shape)]
-        self.ws = {}
-        for r, sh in shapes.items():
-            nb = max(B.dense_workspace_bytes(m, n) for m, n in sh)
-            self.ws[r] = (torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev), nb)
 
     def enqueue(self, stream=None, side_streams=None):
         import torch
@@ -189,15 +181,15 @@ class DenseDecodeStep:
                 if ss is not main:
                     ss.wait_stream(main)
                 m, n = L[r].shape
-                B.dense_gemv_ws(L[r], ins[r], m, n, o[r], *self.ws[r], ss)
+                B.dense_gemv(L[r], ins[r], m, n, o[r], ss)
             if side_streams:
                 for ss in side_streams[:len(roles)]:
                     main.wait_stream(ss)
             B.effort_silu_mul(o["w1"], o["w3"], L["w1"].shape[1], o["g"], main)
             m, n = L["w2"].shape
-            B.dense_gemv_ws(L["w2"], o["g"], m, n, o["w2"], *self.ws["w2"], main)
+            B.dense_gemv(L["w2"], o["g"], m, n, o["w2"], main)
         m, n = self.head.shape
-        B.dense_gemv_ws(self.head, self.head_in, m, n, self.logits, *self.ws["head"], main)
+        B.dense_gemv(self.head, self.head_in, m, n, self.logits, main)
 
 
 def route_top2(logits):

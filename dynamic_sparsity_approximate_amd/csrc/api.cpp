@@ -809,23 +809,6 @@ int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_
                            static_cast<hipStream_t>(stream)));
 }
 
-int dense_workspace_bytes(int64_t in_dim, int64_t out_dim, uint64_t* bytes) {
-  if (!bytes || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
-  *bytes = dense_split_ws_bytes(in_dim, out_dim);
-  return EFFORT_OK;
-}
-
-int dense_gemv_ws(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_t out_dim,
-                  float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream) {
-  if (!w_dev || !v_dev || !y_dev || !ws_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;
-  if (!aligned(w_dev, 2) || !aligned(v_dev, 4) || !aligned(y_dev, 4) || !aligned(ws_dev, 256))
-    return EFFORT_EINVAL;
-  if (ws_bytes < dense_split_ws_bytes(in_dim, out_dim)) return EFFORT_ENOSPACE;
-  if (!dense_split_serves(out_dim, w_dev)) return dense_gemv(w_dev, v_dev, in_dim, out_dim, y_dev, stream);
-  return status_of(launch_dense_split_ws(w_dev, v_dev, in_dim, out_dim, y_dev, ws_dev,
-                                         static_cast<hipStream_t>(stream)));
-}
-
 int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, int64_t in_dim,
                      int64_t out_dim, float* y_dev, void* stream) {
   if (!w_dev || !v_dev || !y_dev || in_dim < 1 || out_dim < 1) return EFFORT_EINVAL;

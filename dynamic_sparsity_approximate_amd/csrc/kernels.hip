@@ -2050,24 +2050,13 @@ __global__ __launch_bounds__(DN_T) void k_dense(const uint16_t* __restrict__ W,
 // full-height strips of n / 8 / CUs octets, one block per CU without atomics,
 // took 24.5 us (128-byte rows) to 43 us (112-byte rows sharing cache lines
 // between CUs).
-//
-// RED: no zero fill and no atomics on y.  Split k of strip s stores its
-// partial sums to part[k][...] with device-scope atomic stores, waits until
-// they are performed, and takes a ticket on cnt[s]; the block that takes the
-// last ticket reads every split's partials with device-scope atomic loads,
-// adds them in split order (so y does not depend on which block came last)
-// and stores y, then sets cnt[s] back to 0 for the next call.  Device-scope
-// atomics are coherent across the XCDs' L2s by themselves; a device-scope
-// fence would instead write back and invalidate the L2 in every block (it
-// made this kernel four times slower).
 constexpr int DS_T = 1024;
 constexpr int DS_W = DS_T / 64;
 constexpr int DS_LPR = 32;  // lanes per row: 32 x 16 bytes = 256 columns
-template <int UNR, bool RED>
+template <int UNR>
 __global__ __launch_bounds__(DS_T) void k_dense_split(const uint16_t* __restrict__ W,
                                                       const float* __restrict__ v, int64_t m,
-                                                      int64_t n, float* __restrict__ y, int64_t rps,
-                                                      float* __restrict__ part, uint32_t* __restrict__ cnt) {
+                                                      int64_t n, float* __restrict__ y, int64_t rps) {
   constexpr int RPW = 64 / DS_LPR;  // rows per wave load
   __shared__ float red[DS_W][64 * 8 + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2117,37 +2106,7 @@ __global__ __launch_bounds__(DS_T) void k_dense_split(const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < RPW; ++r) t += red[0][(r * DS_LPR + o) * 8 + k];
     const int64_t c = ((int64_t)blockIdx.x * DS_LPR + o) * 8 + k;
-    if constexpr (!RED) {
-      if (c < n) atomicAdd(&y[c], t);
-    } else if (gridDim.y == 1) {
-      if (c < n) y[c] = t;
-    } else {
-      if (c < n)
-        __hip_atomic_store(&part[(int64_t)blockIdx.y * n + c], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  if constexpr (RED) {
-    if (gridDim.y == 1) return;
-    __shared__ uint32_t sLast;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partials performed before the barrier
-    __syncthreads();
-    if (tid == 0)
-      sLast = __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      gridDim.y - 1u
-                  ? 1u
-                  : 0u;
-    __syncthreads();
-    if (!sLast) return;
-    if (tid < DS_LPR * 8) {
-      const int64_t c = (int64_t)blockIdx.x * DS_LPR * 8 + tid;
-      if (c < n) {
-        float t = 0.0f;
-        for (uint32_t k = 0; k < gridDim.y; ++k)
-          t += __hip_atomic_load(&part[(int64_t)k * n + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        y[c] = t;
-      }
-    }
-    if (tid == 0) __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c < n) atomicAdd(&y[c], t);
   }
 }
 
@@ -2155,47 +2114,19 @@ bool dense_split_serves(int64_t n, const uint16_t* W) {
   return (n & 7) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
 }
 
-// The split shape of the dense GEMV: strips of 256 columns, rows split so
-// that the grid holds about one block per CU.
-static void dense_split_shape(int64_t m, int64_t n, int64_t* strips, int64_t* splits) {
-  *strips = (n + DS_LPR * 8 - 1) / (DS_LPR * 8);
-  int64_t sp = 256 / *strips;
-  const int64_t max_splits = (m + 63) / 64;  // at least 64 rows per split
-  if (sp > max_splits) sp = max_splits;
-  if (sp < 1) sp = 1;
-  *splits = sp;
-}
-
 hipError_t launch_dense_split(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                               hipStream_t s) {
   if (!dense_split_serves(n, W)) return hipErrorInvalidValue;
-  int64_t strips, splits;
-  dense_split_shape(m, n, &strips, &splits);
+  const int64_t strips = (n + DS_LPR * 8 - 1) / (DS_LPR * 8);
+  int64_t splits = 256 / strips;
+  const int64_t max_splits = (m + 63) / 64;  // at least 64 rows per split
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
   const int64_t rps = (m + splits - 1) / splits;
   hipError_t e = launch_zero_bytes(y, (uint64_t)n * sizeof(float), s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_dense_split<2, false>), dim3((unsigned)strips, (unsigned)splits), dim3(DS_T), 0, s,
-                     W, v, m, n, y, rps, nullptr, nullptr);
-  return hipGetLastError();
-}
-
-uint64_t dense_split_ws_bytes(int64_t m, int64_t n) {
-  int64_t strips, splits;
-  dense_split_shape(m, n, &strips, &splits);
-  // counters (a 256-byte line group), then splits x n partial sums
-  return (uint64_t)((strips * 4 + 255) / 256 * 256) + (uint64_t)(splits > 1 ? splits : 0) * (uint64_t)n * 4u;
-}
-
-hipError_t launch_dense_split_ws(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
-                                 void* ws, hipStream_t s) {
-  if (!dense_split_serves(n, W)) return hipErrorInvalidValue;
-  int64_t strips, splits;
-  dense_split_shape(m, n, &strips, &splits);
-  const int64_t rps = (m + splits - 1) / splits;
-  uint32_t* cnt = static_cast<uint32_t*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (strips * 4 + 255) / 256 * 256);
-  hipLaunchKernelGGL((k_dense_split<2, true>), dim3((unsigned)strips, (unsigned)splits), dim3(DS_T), 0, s,
-                     W, v, m, n, y, rps, part, cnt);
+  hipLaunchKernelGGL(k_dense_split<2>, dim3((unsigned)strips, (unsigned)splits), dim3(DS_T), 0, s, W, v,
+                     m, n, y, rps);
   return hipGetLastError();
 }
 

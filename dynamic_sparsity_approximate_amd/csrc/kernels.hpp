@@ -174,11 +174,6 @@ hipError_t launch_dense_gemv(const uint16_t* W, const float* v, int64_t m, int64
 // atomic per column and split); serves out_dim a multiple of 8 with W 16-byte
 // aligned (dense_split_serves).
 bool dense_split_serves(int64_t n, const uint16_t* W);
-// The same GEMV without the zero fill: the row splits' partial sums meet in a
-// workspace of dense_split_ws_bytes (its counters zero on entry, left zero).
-uint64_t dense_split_ws_bytes(int64_t m, int64_t n);
-hipError_t launch_dense_split_ws(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
-                                 void* ws, hipStream_t s);
 hipError_t launch_dense_split(const uint16_t* W, const float* v, int64_t m, int64_t n, float* y,
                               hipStream_t s);
 hipError_t launch_dense_gemm_small(const uint16_t* W, const float* v, int batch, int64_t m,

@@ -324,20 +324,6 @@ int effort_matvec_timed(const effort_desc* desc, const void* layout_dev, const f
 int dense_gemv(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_t out_dim,
                float* y_dev, void* stream);
 
-/* Bytes of the workspace dense_gemv_ws needs for this shape (host only). */
-int dense_workspace_bytes(int64_t in_dim, int64_t out_dim, uint64_t* bytes);
-
-/* dense_gemv in one kernel: its row splits add their partial sums through
-   ws_dev (caller-owned device memory, 256-byte aligned, at least
-   dense_workspace_bytes; zero-filled once before the first call, e.g. with
-   effort_workspace_init, and left zero by every call) instead of zero-filling
-   y and adding with atomics; y's sums are added in a fixed order.  Calls that
-   share a workspace must be stream-ordered.  ENOSPACE if ws_bytes is too
-   small; shapes the split kernel does not serve (out_dim not a multiple of 8,
-   W not 16-byte aligned) run dense_gemv. */
-int dense_gemv_ws(const uint16_t* w_dev, const float* v_dev, int64_t in_dim, int64_t out_dim,
-                  float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
-
 /* Dense y_dev[batch][out_dim] = v_dev[batch][in_dim] . W, 1 <= batch <= EFFORT_MAX_BATCH. */
 int dense_gemm_small(const uint16_t* w_dev, const float* v_dev, int32_t batch, int64_t in_dim,
                      int64_t out_dim, float* y_dev, void* stream);

@@ -182,54 +182,6 @@ def test_dense_gemv(m, n):
     assert rel_l2(y.cpu().numpy(), oracle.dense(W, v)) <= 1e-5
 
 
-@pytest.mark.parametrize("m,n", [(256, 256), (4096, 1024), (300, 1001), (1, 8), (77, 4100),
-                                 (4096, 14336), (14336, 4096), (4096, 32000), (513, 2048), (5, 16384)])
-def test_dense_gemv_ws(m, n):
-    """The one-kernel dense GEMV: the oracle's dense product; for widths the
-    split kernel serves, the same bits on a second and third call through the
-    same workspace (the partial sums are added in a fixed order); the calls
-    leave its counters at zero; and a smaller shape after a larger one on that
-    workspace."""
-    d = dev()
-    W, v = case(m, n, seed=7, tag="dense")
-    Wt = torch.from_numpy(W.view(np.int16)).to(d)
-    vt = torch.from_numpy(v).to(d)
-    m2, n2 = max(m // 2, 1), n // 2 // 8 * 8
-    # one workspace for both shapes (fewer columns can mean more row splits)
-    nb = max(E.dense_workspace_bytes(m, n), E.dense_workspace_bytes(m2, max(n2, 8)))
-    ws = torch.zeros(nb, dtype=torch.uint8, device=d)
-    ys = []
-    for _ in range(3):
-        y = torch.full((n,), float("nan"), dtype=torch.float32, device=d)
-        E.dense_gemv_ws(Wt, vt, m, n, y, ws, nb)
-        torch.cuda.synchronize()
-        ys.append(y.cpu().numpy())
-    assert rel_l2(ys[0], oracle.dense(W, v)) <= 1e-5
-    if n % 8 == 0:  # the split kernel (other widths take dense_gemv, whose atomics add in any order)
-        assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
-        assert np.array_equal(ys[0].view(np.uint32), ys[2].view(np.uint32))
-    assert not ws[:256].any().item()  # the strips' counters are back at zero
-    if m > 1 and n2 >= 8:
-        W2, v2 = case(m2, n2, seed=8, tag="dense2")
-        y2 = torch.empty(n2, dtype=torch.float32, device=d)
-        E.dense_gemv_ws(torch.from_numpy(W2.view(np.int16)).to(d), torch.from_numpy(v2).to(d), m2, n2, y2,
-                        ws, nb)
-        torch.cuda.synchronize()
-        assert rel_l2(y2.cpu().numpy(), oracle.dense(W2, v2)) <= 1e-5
-
-
-def test_dense_gemv_ws_rejects():
-    d = dev()
-    W, v = case(64, 512, seed=9, tag="dense3")
-    Wt = torch.from_numpy(W.view(np.int16)).to(d)
-    y = torch.empty(512, dtype=torch.float32, device=d)
-    nb = E.dense_workspace_bytes(64, 512)
-    ws = torch.zeros(nb, dtype=torch.uint8, device=d)
-    with pytest.raises(E.EffortError) as ei:
-        E.dense_gemv_ws(Wt, torch.from_numpy(v).to(d), 64, 512, y, ws, nb - 4)
-    assert ei.value.code == E.EFFORT_ENOSPACE
-
-
 @pytest.mark.parametrize("b", [1, 2, 3, 5, 16])
 def test_dense_gemm_small(b):
     d = dev()

@@ -19,9 +19,9 @@ LAYER_ROLES = ("wq", "wk", "wv", "wo", "w1", "w3", "w2")
 
 class EffortSchedule:
     """An effort for every matrix of a chain instead of one for all: the
-    author's reply about setting effort layer by layer, token by token and
-    matrix by matrix ("an equalizer, not a volume control"; the reply to uhlo
-    counts about 32 * 6 independent settings in a decode step).
+    author's reply in the HN thread likens effort to an equalizer with a
+    setting per layer, token and matrix rather than one knob; the reply to
+    uhlo counts roughly 32 * 6 separate knobs per decode step.
 
     Keys are (layer, role) in a decode step (the head is (None, "head")) and
     (expert, role) in an expert block.  Lookup order: (unit, role), then

@@ -11,8 +11,8 @@
 //
 // Options:
 //  * crop c < P stores only segments 0..c-1 of every row, the largest
-//    magnitudes (the post text: the data format lets one skip a share of the
-//    least important weights when loading; the author's reply about running
+//    magnitudes (the post text: with this format part of the smallest-magnitude
+//    weights need not be loaded; the author's reply about running
 //    Mixtral from the top ~70 % of its weights).  Probes and rowmax still come
 //    from the whole row, so the cutoff is the uncropped one; per row the
 //    largest magnitude left out is kept ("floor") so that a call can tell when

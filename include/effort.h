@@ -17,7 +17,7 @@
  *   probes per row, P magnitudes at ranks ceil((k+1) out_dim / P) of the row
  *          sorted by |w| descending.
  *   K      min(N, max(1, ceil(effort * N))) in double, N = in_dim * P.
- *   cutoff K-th largest of fl32(|v_i| * probe_i[k]) ("topK(cutoff_chart, effort)").
+ *   cutoff K-th largest of fl32(|v_i| * probe_i[k]) (the pseudocode's top-K step over the chart).
  *   kept   (i, j) with fl32(|v_i| * |W_ij|) >= cutoff.
  *   y_j    sum of v_i * W_ij over kept (i, j), accumulated in fp32.
  *
@@ -168,8 +168,8 @@ int effort_prepare_host_ex(const uint16_t* w_fp16, int64_t in_dim, int64_t out_d
                   bits 2-0 column in the cell).
    crop_segments  0 or P: every segment is stored.  c in [1, P): only the rank
                   segments 0..c-1 of each row (the largest magnitudes) are stored
-                  ([HN] post text: the format lets one skip a share of the least
-                  important weights; the reply about running Mixtral from its top
+                  ([HN] post text: with this format part of the smallest-magnitude
+                  weights need not be loaded; the reply about running Mixtral from its top
                   ~70 %).  Probes and rowmax still describe the whole row, so the
                   cutoff is the uncropped one; a call keeps exactly the uncropped
                   kept set whenever none of its kept products lies in a dropped

@@ -98,7 +98,7 @@ int oracle_chart(const float* v, const float* probes, int64_t m, int32_t P, floa
   return 0;
 }
 
-/* "cutoff = topK(cutoff_chart, effort)" in the [HN] pseudocode: effort is the
+/* The top-K step over the chart in the [HN] pseudocode: effort is the
    fraction of the chart that lies at or above the cutoff.  K rounds up so the
    kept fraction never falls below effort; the cutoff is the K-th largest chart
    value (a value, so ties need no rule).  A full descending sort stands in for
@@ -160,8 +160,8 @@ int oracle_keep_sum(const uint16_t* W, int64_t m, int64_t n, const float* v, flo
 }
 
 /* The stored part of a cropped layout (the [HN] post text: the data format
-   lets one load only part of the model, skipping a share of the least
-   important weights; the author runs Mixtral from its top ~70 %).  Reading
+   lets one load only part of the model, leaving out a share of the
+   smallest-magnitude weights; the author runs Mixtral from its top ~70 %).  Reading
    used here: rows are cut into the same P rank segments as the probes, and
    segments 0..crop-1 -- the ceil(crop n / P) largest magnitudes of the row,
    ties going to the lower column -- are stored.  stored[i*n+j] = 1 for those. */

@@ -93,6 +93,25 @@ def test_ragged_shapes(m, n, P, G, effort):
     run_pair(W, v, P, effort, groups=G, where="ragged")
 
 
+@pytest.mark.parametrize("m,n,G", [(4097, 512, 0), (5000, 700, 3), (9000, 1024, 8), (14336, 300, 2),
+                                   (40000, 256, 0), (70000, 128, 0)])
+def test_tall_matrices(m, n, G):
+    """Tall matrices, whose dispatch blocks (more than 64) put the cutoff's
+    candidates in one list instead of per-block regions: single and batched
+    calls against the oracle, from just past 4096 rows to 70000."""
+    W, v = case(m, n, seed=m + n, tag="tall")
+    for effort in (0.01, 0.25, 1.0):
+        say("tall m=%d n=%d G=%d effort=%g" % (m, n, G, effort))
+        run_pair(W, v, 16, effort, groups=G, with_mask=m * n <= (1 << 22), where=("tall", m, n, effort))
+    d = dev()
+    M = E.EffortMatrix(W, P=16, groups=G, device=d, batch=6)
+    V = np.stack([case(m, n, seed=m + n + 1 + k, tag="tallv")[1] for k in range(6)])
+    pr = oracle.probes(W, 16)
+    got = M.matvec_batched_debug(torch.from_numpy(V).to(d), 0.25)
+    for k in range(6):
+        check(got[k], oracle.run(W, pr, V[k], 0.25), where=("tall batched", m, n, k))
+
+
 def test_degenerate_inputs():
     d = dev()
     # zero vector: cutoff 0 keeps everything, y = 0

@@ -260,7 +260,10 @@ def main():
                           "bucketmul": mul_us},
             "roofline": {"bound": "hbm", "kernel": "k_bucketmul", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "traffic": traffic, "alg_bytes": alg_mul, "kernel_us": mul_us},
+                         "traffic": traffic, "alg_bytes": alg_mul, "kernel_us": mul_us,
+                         "traffic_source": (os.path.relpath(COUNTERS, ROOT) + ": rocprofv3 FETCH_SIZE + "
+                                            "WRITE_SIZE per dispatch of this kernels.hip and entry format, "
+                                            "scaled by a 1 GiB copy") if traffic else None},
             "rotation": R, "groups": M.groups,
         })
         for e in sum(evs, []):
@@ -326,6 +329,23 @@ def main():
                          "products) on %d seeded vectors of the same workload, probes precomputed; "
                          "median" % (m, n, len(times))}
         cpu.update(host_info())
+        # context: a plain dense fp32 matvec on one host core (numpy, one BLAS thread)
+        try:
+            from threadpoolctl import threadpool_limits
+            Wf = W.view(np.float16).astype(np.float32)
+            vf = synth.vector("config1", m, seed=0)
+            dts = []
+            with threadpool_limits(limits=1):
+                for _ in range(5):
+                    t = time.perf_counter()
+                    vf @ Wf
+                    dts.append(time.perf_counter() - t)
+            cpu["dense_context"] = {"value": statistics.median(dts) * 1e6, "unit": "µs/matvec", "cores": 1,
+                                    "kind": "numpy float32 v @ W (W widened from fp16 beforehand), "
+                                            "one BLAS thread, median of 5"}
+            del Wf
+        except ImportError:
+            pass
 
     if args.mode == "full":
         out = {

@@ -3,8 +3,9 @@ effort_matvec with the workspace in the library's static device array.  Its
 output is compared with effort_matvec's on the same inputs (the same cutoff and
 kept set; only the order of the fp32 atomics of the flush differs, so rel-L2
 <= 1e-5 is asked) and with the oracle (rel-L2 1e-3), on calls in a row whose
-second input is smaller than the first, and the size limit is checked on the
-host."""
+second input is smaller than the first, in the three entry formats (the
+oracle of a q8 layout runs on the quantized matrix), and the size limit is
+checked on the host."""
 import sys
 
 import numpy as np
@@ -27,11 +28,13 @@ def test_noalloc_matches_matvec_on_calls_in_a_row():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     d = torch.device("cuda:0")
-    cases = [(4096, 14336, 0.25, 0), (513, 2049, 0.3, 1), (4096, 14336, 0.125, 2), (300, 1000, 1.0, 3)]
-    for m, n, effort, seed in cases:
+    U32, R12, Q8 = E.EFFORT_ENTRY_U32, E.EFFORT_ENTRY_R12, E.EFFORT_ENTRY_Q8
+    cases = [(4096, 14336, 0.25, 0, R12), (513, 2049, 0.3, 1, U32), (4096, 14336, 0.125, 2, U32),
+             (300, 1000, 1.0, 3, Q8), (1000, 3000, 0.2, 4, R12)]
+    for m, n, effort, seed, fmt in cases:
         W = synth.weights(m, n, seed=seed, stream=synth.stream_id("noalloc", "W", m, n))
         v = synth.activations(m, seed=seed, stream=synth.stream_id("noalloc", "v", m))
-        M = E.EffortMatrix(W, P=16, device=d)
+        M = E.EffortMatrix(W, P=16, device=d, entry_format=fmt)
         vt = torch.from_numpy(v).to(d)
         y_ref = M.matvec(vt, effort)
         y = torch.full((n,), float("nan"), dtype=torch.float32, device=d)
@@ -39,11 +42,12 @@ def test_noalloc_matches_matvec_on_calls_in_a_row():
         torch.cuda.synchronize()
         y, y_ref = y.cpu().numpy(), y_ref.cpu().numpy()
         assert rel_l2(y, y_ref) <= 1e-5, (m, n, rel_l2(y, y_ref))
-        ref = oracle.run(W, oracle.probes(W, 16), v, effort)
+        Wr = oracle.quantize_q8(W, 16) if fmt == Q8 else W
+        ref = oracle.run(Wr, oracle.probes(Wr, 16), v, effort)
         err = rel_l2(y, ref["y"])
-        assert err <= 1e-3, (m, n, err)
-        say("noalloc %dx%d effort %g: rel-L2 %.2e against effort_matvec, %.2e against the oracle" % (
-            m, n, effort, rel_l2(y, y_ref), err))
+        assert err <= 1e-3, (m, n, fmt, err)
+        say("noalloc %dx%d effort %g format %d: rel-L2 %.2e against effort_matvec, %.2e against the oracle" % (
+            m, n, effort, fmt, rel_l2(y, y_ref), err))
 
 
 def test_noalloc_rejects_matrices_beyond_its_workspace():

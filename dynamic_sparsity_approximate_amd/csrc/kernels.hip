@@ -1146,7 +1146,7 @@ __device__ __forceinline__ uint32_t share_cum(uint32_t j) {
 //   (3) the share's first chunks of entries, in flight while each row's fp16
 //       key threshold is derived from the cutoff.
 // One vector: wave 0 only computes the cutoff, while the other waves run the
-// three rounds; each waits for the cutoff (an LDS flag) only after round 3.
+// three rounds; each waits for the cutoff (an LDS flag) only after load round 3.
 // Batched: waves 0..nv-1 compute the cutoffs and wave PW the partition sums
 // before a barrier, then every wave runs rounds 2 and 3.
 //
@@ -1207,7 +1207,7 @@ __device__ __forceinline__ void bucketmul_body(
     for (int b = (int)bid * MUL_T + tid; b < HIST_BINS; b += (int)nblk * MUL_T)
       a.hist[(size_t)p * a.vec_ws + b] = 0u;
 
-  // ---- round 1
+  // ---- load round 1
   // wave p < nv: the exact cutoff of vector p (batched: and its fixed-point scale)
   auto cutoff_wave = [&]() {
     const uint64_t vo = (uint64_t)wid * a.vec_ws;
@@ -1251,9 +1251,9 @@ __device__ __forceinline__ void bucketmul_body(
   uint32_t sp[4] = {0u, 0u, 0u, 0u};
   uint32_t T = 0u;  // the group's entry count
   int S1 = 0;       // one vector: the fixed-point scale, computed by every share wave
-  // One vector: round 1 also loads the run lengths and activations of two
+  // One vector: load round 1 also loads the run lengths and activations of two
   // 256-row blocks from w0, around the row where the wave's share would start
-  // if the group's entries were spread evenly over its rows; round 2 loads
+  // if the group's entries were spread evenly over its rows; load round 2 loads
   // only when the share starts outside them.
   uint32_t w0 = nbd;
   uint32_t slr[8];
@@ -1419,7 +1419,7 @@ __device__ __forceinline__ void bucketmul_body(
   const uint32_t r0 = bstar < nbd ? bstar * DSP_ROWS : m;
   const uint32_t nr = r0 < m ? (m - r0 < (uint32_t)DSP_ROWS ? m - r0 : (uint32_t)DSP_ROWS) : 0u;
 
-  // ---- round 2 (one vector: unless the window of round 1 holds the block);
+  // ---- load round 2 (one vector: unless the window of load round 1 holds the block);
   // lane l holds rows r0 + 4l .. r0 + 4l + 3
   uint32_t lr[4];
   float lv[4];
@@ -1441,7 +1441,7 @@ __device__ __forceinline__ void bucketmul_body(
     }
   }
 
-  // ---- round 3: the share's first rows, their chunks in flight
+  // ---- load round 3: the share's first rows, their chunks in flight
   uint32_t remaining = end - start;
   uint32_t rowb = m, offb = 0;
   if (active) {

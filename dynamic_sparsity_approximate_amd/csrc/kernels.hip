@@ -781,22 +781,31 @@ constexpr int mul_threads() {
   return BP == 1 ? 576 : 1024;
 }
 constexpr int CH = 256;  // u32 format: entries per chunk, one 16-byte quad per lane
-// Units per chunk: a quad of 4 entries per lane (u32), one 12-byte record of 4
-// entries per lane (r12).
+// Units per chunk: a quad of 4 entries per lane (u32), two 12-byte records of 4
+// entries per lane (r12), one 8-byte record per lane (q8).
+// Loads per lane of one chunk (records, u32: quads of 4 entries).  An r12
+// chunk is two: 128 records, 1536 contiguous bytes per wave, loaded as two
+// 768-byte halves; the larger pieces of a run in flight measured 0.2 us
+// faster at 4096x14336 than one record per lane (three or four per lane, and
+// two quads per lane for u32, were slower or no faster).
+template <int FMT>
+constexpr int records_per_lane() {
+  return FMT == EFFORT_ENTRY_R12 ? 2 : 1;
+}
 template <int FMT>
 constexpr uint32_t chunk_units() {
-  return FMT == EFFORT_ENTRY_U32 ? (uint32_t)CH : 64u;
+  return (FMT == EFFORT_ENTRY_U32 ? (uint32_t)CH : 64u) * (uint32_t)records_per_lane<FMT>();
 }
 
 // Chunks in flight per wave: a ring of loads, a slot processed and then
-// refilled, so RING - 1 loads stay outstanding while one is used.  4-byte
-// entries: 4 (measured faster than 2, 6 or 8).  12-byte records carry 3/4 of
-// the bytes per chunk, so their ring is deeper for the same bytes in flight.
+// refilled, so RING - 1 chunks stay outstanding while one is used.  4-byte
+// entries: 4 (measured faster than 2, 6 or 8).  r12: 3 chunks of 1536 bytes
+// (2 was slower, 4 the same).
 #ifndef EFFORT_RING_U32
 #define EFFORT_RING_U32 4
 #endif
 #ifndef EFFORT_RING_R12
-#define EFFORT_RING_R12 5
+#define EFFORT_RING_R12 3
 #endif
 #ifndef EFFORT_RING_Q8
 #define EFFORT_RING_Q8 6
@@ -1564,23 +1573,31 @@ __device__ __forceinline__ void bucketmul_body(
   // without a memory access (the range is checked per 4-byte word), so every
   // lane issues the load and the wait counters stay exact; an empty chunk
   // accesses no memory.
-  auto issue = [&](const Chunk& c, uint4& buf) {
+  constexpr int RPL = records_per_lane<FMT>();
+  auto issue = [&](const Chunk& c, uint4* buf) {
     const uint32_t units = c.valid ? c.s1 - c.s0 : 0u;
     const uint32_t* p0 = c.run + (size_t)c.s0 * UW;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)p0, (short)0, (int)(units * UW * 4u), kBufferDword3);
     if constexpr (FMT == EFFORT_ENTRY_R12) {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b96(rs, lane * 12, 0, 0);
-      buf = make_uint4(q[0], q[1], q[2], 0u);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b96(rs, (64 * r + lane) * 12, 0, 0);
+        buf[r] = make_uint4(q[0], q[1], q[2], 0u);
+      }
     } else if constexpr (FMT == EFFORT_ENTRY_Q8) {
       const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0);
-      buf = make_uint4(q[0], q[1], 0u, 0u);
+      buf[0] = make_uint4(q[0], q[1], 0u, 0u);
     } else {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, 0, 0);
-      buf = make_uint4(q[0], q[1], q[2], q[3]);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs, (64 * r + lane) * 16, 0, 0);
+        buf[r] = make_uint4(q[0], q[1], q[2], q[3]);
+      }
     }
   };
-  auto process = [&](const Chunk& c, const uint4& buf) {
+  // sub: which load of the lane (unit 64 sub + lane of the chunk, u32: quad)
+  auto process = [&](const Chunk& c, const uint4& buf, int sub) {
     if (!c.valid) return;
     float tf[BP], vf[BP];
     if constexpr (BP == 1) {
@@ -1609,7 +1626,7 @@ __device__ __forceinline__ void bucketmul_body(
       col[1] = col[0] + ((buf.z >> 12) & 0x7Fu);
       col[2] = col[1] + ((buf.z >> 19) & 0x7Fu);
       col[3] = col[2] + (buf.z >> 26);
-      const bool in = (uint32_t)lane < c.s1 - c.s0;
+      const bool in = (uint32_t)lane + 64u * (uint32_t)sub < c.s1 - c.s0;
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
         unit[k2] = in;
@@ -1648,7 +1665,7 @@ __device__ __forceinline__ void bucketmul_body(
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
         col[k2] = ev[k2] >> 16;
-        entry[k2] = 4u * (uint32_t)lane + (uint32_t)k2 < c.s1 - c.s0;
+        entry[k2] = 4u * ((uint32_t)lane + 64u * (uint32_t)sub) + (uint32_t)k2 < c.s1 - c.s0;
         unit[k2] = entry[k2];
       }
     }
@@ -1742,7 +1759,7 @@ __device__ __forceinline__ void bucketmul_body(
   // The ring of chunks in flight (ring_depth).
   constexpr int RING = ring_depth<FMT>();
   Chunk d[RING];
-  uint4 q[RING];
+  uint4 q[RING][RPL];
   auto fill = [&]() {
 #pragma unroll
     for (int k = 0; k < RING; ++k) {
@@ -1783,7 +1800,8 @@ __device__ __forceinline__ void bucketmul_body(
       bool any = false;
 #pragma unroll
       for (int k = 0; k < RING; ++k) {
-        process(d[k], q[k]);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) process(d[k], q[k][r], r);
         take(d[k]);
         issue(d[k], q[k]);
         any = any || d[k].valid;

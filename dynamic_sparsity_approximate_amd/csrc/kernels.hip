@@ -1562,17 +1562,17 @@ __device__ __forceinline__ void bucketmul_body(
     c.tf = stf;
     c.vf = svf;
     // u32: chunk ends on quad boundaries of the run (a share's first chunk
-    // in a row may start inside a quad); r12, q8: one record per lane
+    // in a row may start inside a quad); r12, q8: whole records
     const uint32_t cs = FMT == EFFORT_ENTRY_U32 ? (ss & ~3u) : ss;
     c.s1 = c.valid ? min(se, cs + chunk_units<FMT>()) : 0u;
     ss = c.valid ? c.s1 : ss;
   };
   // Loads the chunk for this lane through a buffer descriptor that starts at
-  // unit s0 and ends at s1: lane l reads units from s0 + l (r12, q8: one
-  // record) or words from s0 + 4l (u32: four entries).  Words past s1 read as zero
-  // without a memory access (the range is checked per 4-byte word), so every
-  // lane issues the load and the wait counters stay exact; an empty chunk
-  // accesses no memory.
+  // unit s0 and ends at s1: lane l reads unit s0 + l (q8: one record; r12:
+  // and s0 + 64 + l, a second) or words from s0 + 4l (u32: four entries).
+  // Words past s1 read as zero without a memory access (the range is checked
+  // per 4-byte word), so every lane issues the load and the wait counters
+  // stay exact; an empty chunk accesses no memory.
   constexpr int RPL = records_per_lane<FMT>();
   auto issue = [&](const Chunk& c, uint4* buf) {
     const uint32_t units = c.valid ? c.s1 - c.s0 : 0u;

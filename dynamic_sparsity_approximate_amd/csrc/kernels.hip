@@ -133,14 +133,39 @@ __device__ __forceinline__ void load_row_keys(const uint16_t* probes, int32_t P,
   }
 }
 
+// Keys pr[0 .. count) of a row, count <= PM, two per word (zero past count):
+// 16-byte loads when vec (pr 16-byte aligned and the row's P a multiple of
+// 8), else one load per key.  Used for rows with more than PM probes, a
+// chunk of PM keys at a time.
+template <int PM>
+__device__ __forceinline__ void load_keys(const uint16_t* pr, int count, bool vec, uint32_t* kw) {
+  if (vec) {
+#pragma unroll
+    for (int c = 0; c < PM / 8; ++c) {
+      uint4 q = make_uint4(0u, 0u, 0u, 0u);
+      if (c * 8 < count) q = *reinterpret_cast<const uint4*>(pr + c * 8);
+      kw[4 * c] = q.x;
+      kw[4 * c + 1] = q.y;
+      kw[4 * c + 2] = q.z;
+      kw[4 * c + 3] = q.w;
+    }
+  } else {
+    uint32_t h[PM];
+#pragma unroll
+    for (int k = 0; k < PM; ++k) h[k] = k < count ? (uint32_t)pr[k] : 0u;
+#pragma unroll
+    for (int t = 0; t < PM / 2; ++t) kw[t] = h[2 * t] | (h[2 * t + 1] << 16);
+  }
+}
+
 __device__ __forceinline__ uint32_t key_at(const uint32_t* kw, int k) {
   return (kw[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
 }
 
 constexpr int CH_T = 256;  // rows per block of the histogram kernel
 
-// PM: probes per row held in registers (16 or 32); rows with more take a
-// slower loop over memory.
+// PM: probes per row held in registers (16 or 32); rows with more are read
+// PM keys at a time.
 template <int PM>
 __device__ __forceinline__ void chart_hist_body(const SelectArgs& a) {
   __shared__ uint32_t hist[HIST_BINS + 1];  // + a slot for the keys past P
@@ -166,9 +191,17 @@ __device__ __forceinline__ void chart_hist_body(const SelectArgs& a) {
         atomicAdd(&hist[k < a.P ? bin : (uint32_t)HIST_BINS], 1u);
       }
     } else {
+      // PM keys at a time; the keys past P go to the spare slot
       const uint16_t* pr = a.probes + i * a.P;
-      for (int k = 0; k < a.P; ++k)
-        atomicAdd(&hist[__float_as_uint(__fmul_rn(av, h2f(pr[k]))) >> HIST_SHIFT], 1u);
+      const bool vec = (a.P & 7) == 0;
+      for (int k0 = 0; k0 < a.P; k0 += PM) {
+        load_keys<PM>(pr + k0, min(PM, a.P - k0), vec, kw);
+#pragma unroll
+        for (int k = 0; k < PM; ++k) {
+          const uint32_t bin = __float_as_uint(__fmul_rn(av, h2f(key_at(kw, k)))) >> HIST_SHIFT;
+          atomicAdd(&hist[k0 + k < a.P ? bin : (uint32_t)HIST_BINS], 1u);
+        }
+      }
     }
   }
   __syncthreads();
@@ -270,8 +303,9 @@ static_assert(HIST_BINS == 16 * DSP_T, "each dispatch thread holds 16 histogram 
 // the cutoff), a row keeps whole the probe segments whose chart value is >= lo
 // (probes are descending, so these are segments 0..q-1), and the read length
 // of (row, group) covers segments 0..min(q, P-1) through the counts table.
-// PM: probes per row held in registers (16 or 32); rows with more take a
-// slower loop over memory.
+// PM: probes per row held in registers (16 or 32); rows with more are read
+// PM keys at a time (one round trip per chunk), their candidates' slots
+// reserved once per wave as for the others.
 template <int PM>
 __device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
   __shared__ uint32_t tmp[DSP_T / 64 + 1];
@@ -339,6 +373,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
   const uint32_t hi_bits = (b1 + 1u) << HIST_SHIFT;
   int32_t q = 0;
   uint32_t hits = 0u;  // chart entries of this row in bin b1 (P <= PM)
+  uint32_t rlo = 0u, rhi = 0u;  // P > PM: those entries are keys rhi .. rlo - 1
   if (valid) {
     if (a.P <= PM) {
       // A row's probes do not increase with k, so neither do its chart
@@ -358,24 +393,33 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
       // bits chi .. clo - 1 (clo <= 32; shifts of 32 go through 64 bits)
       hits = (uint32_t)((1ull << clo) - (1ull << chi));
     } else {
+      // more probes than registers: the same prefix counts, PM keys at a
+      // time (the chunks' loads wait one round trip each)
       const uint16_t* pr = a.probes + i * a.P;
-      for (int k = 0; k < a.P; ++k) {
-        const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pr[k])));
-        q += bits >= lo_bits ? 1 : 0;
-        if ((bits >> HIST_SHIFT) == b1) {
-          atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
-          const uint32_t slot = atomicAdd(&a.result[RES_NCAND], 1u);
-          if ((uint64_t)slot < capc) a.cand[slot] = bits;
+      const bool vec = (a.P & 7) == 0;
+      uint32_t clo = 0u, chi = 0u;
+      for (int k0 = 0; k0 < a.P; k0 += PM) {
+        uint32_t kw[PM / 2];
+        load_keys<PM>(pr + k0, min(PM, a.P - k0), vec, kw);
+#pragma unroll
+        for (int k = 0; k < PM; ++k) {
+          const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(key_at(kw, k))));
+          const bool in = k0 + k < a.P;
+          clo += in && bits >= lo_bits ? 1u : 0u;
+          chi += in && bits >= hi_bits ? 1u : 0u;
         }
       }
+      q = (int32_t)clo;
+      rlo = clo;
+      rhi = chi;
     }
   }
   // The chart values in bin b1, for the exact cutoff: their slots are
   // reserved here, so that the reservation's round trip overlaps the work on
   // the read lengths; the values are stored at the end.
   uint32_t cnt = 0u, cpos = 0u, cret = 0u;
-  if (a.P <= PM) {
-    cnt = (uint32_t)__popc(hits);
+  {
+    cnt = a.P <= PM ? (uint32_t)__popc(hits) : rlo - rhi;
     const uint32_t incl = wave_incl_scan(cnt);
     cpos = incl - cnt;
     if (lane == 63 && incl) cret = atomicAdd(&a.result[RES_NCAND], incl);
@@ -423,8 +467,8 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
   // Last, the chart values in bin b1: into the candidate list and the
   // refinement histogram of their bits 18..9 (memory instructions inside the
   // keep loop above, even rarely taken ones, made it 0.4 us slower).
+  uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cret, 63) + cpos;
   if (a.P <= PM) {
-    uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)cret, 63) + cpos;
 #pragma unroll
     for (int k = 0; k < PM; ++k) {
       if ((hits >> k) & 1u) {
@@ -433,6 +477,14 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs& a) {
         ++base;
         atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
       }
+    }
+  } else if (valid) {
+    const uint16_t* pr = a.probes + i * a.P;
+    for (uint32_t k = rhi; k < rlo; ++k) {
+      const uint32_t bits = __float_as_uint(__fmul_rn(av, h2f(pr[k])));
+      if ((uint64_t)base < capc) a.cand[base] = bits;
+      ++base;
+      atomicAdd(&a.hist2[(bits >> 9) & 1023u], 1u);
     }
   }
 }

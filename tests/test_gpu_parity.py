@@ -93,6 +93,17 @@ def test_ragged_shapes(m, n, P, G, effort):
     run_pair(W, v, P, effort, groups=G, where="ragged")
 
 
+@pytest.mark.parametrize("P", [33, 40, 64, 100, 300])
+@pytest.mark.parametrize("effort", [0.02, 0.25, 1.0])
+def test_many_probes(P, effort):
+    """More probes per row than the kernels hold in registers (32): the chart
+    and dispatch read them in chunks of 32 keys (16-byte loads when P is a
+    multiple of 8), with a partial last chunk."""
+    W, v = case(700, 3000, seed=P, tag="manyp")
+    say("many probes P=%d effort=%g" % (P, effort))
+    run_pair(W, v, P, effort, where=("many probes", P, effort))
+
+
 @pytest.mark.parametrize("m,n,G", [(4097, 512, 0), (5000, 700, 3), (9000, 1024, 8), (14336, 300, 2),
                                    (40000, 256, 0), (70000, 128, 0)])
 def test_tall_matrices(m, n, G):

@@ -463,13 +463,14 @@ int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
 // Batches from kUnionMinBatch vectors at an effort of at least
 // kUnionMinEffort read the union of the vectors' read lengths once
 // (run_batched); other batches run each vector's own multiply, up to four in
-// one launch of each kernel.  At 4096x14336: b = 2 / 4 at effort 0.25 take
-// 40.6 / 62.3 us against 46.7 / 70.9 us for the union pass; b = 8 in two
-// launches of four against one union pass takes 301 / 121 / 86 us against
-// 168 / 123 / 106 us at effort 1 / 0.25 / 0.125 (the union of low-effort
-// prefixes is long compared with each one).
+// one launch of each kernel.  At 4096x14336 (r12), b = 8 in two launches of
+// four against one union pass takes 193 / 167 / 128 / 108 / 92 us against
+// 155 / 155 / 144 / 136 / 127 us at effort 1 / 0.75 / 0.5 / 0.35 / 0.25: the
+// union pass does every vector's keep test and LDS add for each entry it
+// reads, which costs about the same at any effort, so it wins only where
+// the vectors' prefixes are long.
 constexpr int32_t kUnionMinBatch = 5;
-constexpr float kUnionMinEffort = 0.25f;
+constexpr float kUnionMinEffort = 0.625f;
 
 int matvec_common(const effort_desc* desc, const void* layout_dev, const float* v_dev, int32_t batch,
                   float effort, float* y_dev, void* ws_dev, uint64_t ws_bytes, void* stream,

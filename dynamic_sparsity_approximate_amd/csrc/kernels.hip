@@ -1662,8 +1662,8 @@ __device__ __forceinline__ void bucketmul_body(
         vf[p] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vfj[p]), c.j));
       }
     }
-    // The chunk's 4 entries of this lane: fp16 value bits (low half) and the
-    // column inside the group; `in` whether they are units of the chunk
+    // The 4 entries of this lane's load `sub`: fp16 value bits (low half) and
+    // the column inside the group; `in` whether they are units of the chunk
     // (words past s1 read as zero).
     uint32_t ev[4], col[4];
     bool entry[4], unit[4];  // an entry of the chunk; a unit of the chunk (pads included)

@@ -360,15 +360,17 @@ def test_many_rows_few_columns(m, n):
 
 
 @pytest.mark.parametrize("m,n,G,b,P,effort", [(4096, 14336, 0, 2, 16, 0.25), (4096, 14336, 0, 9, 16, 0.25),
-                                              (4096, 14336, 0, 16, 16, 0.25), (513, 2049, 3, 3, 16, 0.25),
-                                              (300, 1000, 0, 16, 5, 0.25), (64, 8192, 1, 4, 8, 0.25),
-                                              (513, 2049, 3, 7, 16, 0.1), (300, 1000, 0, 16, 5, 0.5)])
+                                              (4096, 14336, 0, 16, 16, 0.75), (4096, 14336, 0, 9, 16, 1.0),
+                                              (513, 2049, 3, 3, 16, 0.25), (300, 1000, 0, 16, 5, 0.25),
+                                              (300, 1000, 0, 16, 5, 0.8), (64, 8192, 1, 4, 8, 0.25),
+                                              (513, 2049, 3, 7, 16, 0.1), (300, 1000, 0, 16, 5, 0.5),
+                                              (513, 2049, 3, 6, 16, 1.0)])
 def test_batched_fused_matches_oracle(m, n, G, b, P, effort):
-    """Batched calls (up to 4 vectors, or any number below effort 0.25: launches
-    of up to 4 vectors, each with its own multiply; from 5 vectors at effort
-    0.25 and above: passes of up to 8 vectors over the union of their read
-    lengths): every vector's exact cutoff bits, K and K' and y against the
-    oracle."""
+    """Batched calls (up to 4 vectors, or any number below effort 0.625:
+    launches of up to 4 vectors, each with its own multiply; from 5 vectors at
+    effort 0.625 and above: passes of up to 8 vectors over the union of their
+    read lengths): every vector's exact cutoff bits, K and K' and y against
+    the oracle."""
     d = dev()
     W, _ = case(m, n, seed=m + b, tag="fused")
     M = E.EffortMatrix(W, P=P, groups=G, device=d, batch=b)

@@ -128,7 +128,8 @@ def test_q8_batched_multi_and_crop():
     Wq = oracle.quantize_q8(W, 16)
     pr = oracle.probes(Wq, 16)
     V = np.stack([synth.activations(m, seed=s, stream=synth.stream_id("q8b", "v")) for s in range(9)])
-    for effort, b in ((0.25, 9), (0.25, 3), (0.1, 6)):
+    # 9 vectors at effort 0.8: two union passes; the others: launches of up to 4
+    for effort, b in ((0.25, 9), (0.8, 9), (0.25, 3), (0.1, 6)):
         got = M.matvec_batched_debug(torch.from_numpy(V[:b]).to(d), effort)
         for k in range(b):
             check(got[k], oracle.run(Wq, pr, V[k], effort), where=("batched", effort, b, k))

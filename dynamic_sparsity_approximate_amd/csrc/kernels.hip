@@ -833,16 +833,17 @@ constexpr int mul_threads() {
   return BP == 1 ? 576 : 1024;
 }
 constexpr int CH = 256;  // u32 format: entries per chunk, one 16-byte quad per lane
-// Units per chunk: a quad of 4 entries per lane (u32), two 12-byte records of 4
-// entries per lane (r12), one 8-byte record per lane (q8).
-// Loads per lane of one chunk (records, u32: quads of 4 entries).  An r12
-// chunk is two: 128 records, 1536 contiguous bytes per wave, loaded as two
-// 768-byte halves; the larger pieces of a run in flight measured 0.2 us
-// faster at 4096x14336 than one record per lane (three or four per lane, and
-// two quads per lane for u32, were slower or no faster).
+// Units per chunk: a quad of 4 entries per lane (u32), two records of 4
+// entries per lane (r12: 12 bytes each, q8: 8 bytes).
+// Loads per lane of one chunk (records, u32: quads of 4 entries).  r12 and
+// q8 chunks are two: 128 records, 1536 (r12) or 1024 (q8) contiguous bytes
+// per wave, loaded as two halves; the larger pieces of a run in flight
+// measured 0.2 us (r12) and 0.6 us (q8) faster at 4096x14336 than one record
+// per lane (three or four per lane, and two quads per lane for u32, were
+// slower or no faster).
 template <int FMT>
 constexpr int records_per_lane() {
-  return FMT == EFFORT_ENTRY_R12 ? 2 : 1;
+  return FMT == EFFORT_ENTRY_U32 ? 1 : 2;
 }
 template <int FMT>
 constexpr uint32_t chunk_units() {
@@ -852,7 +853,7 @@ constexpr uint32_t chunk_units() {
 // Chunks in flight per wave: a ring of loads, a slot processed and then
 // refilled, so RING - 1 chunks stay outstanding while one is used.  4-byte
 // entries: 4 (measured faster than 2, 6 or 8).  r12: 3 chunks of 1536 bytes
-// (2 was slower, 4 the same).
+// (2 was slower, 4 the same); q8: 3 of 1024 (4 the same).
 #ifndef EFFORT_RING_U32
 #define EFFORT_RING_U32 4
 #endif
@@ -860,7 +861,7 @@ constexpr uint32_t chunk_units() {
 #define EFFORT_RING_R12 3
 #endif
 #ifndef EFFORT_RING_Q8
-#define EFFORT_RING_Q8 6
+#define EFFORT_RING_Q8 3
 #endif
 template <int FMT>
 constexpr int ring_depth() {
@@ -1620,8 +1621,8 @@ __device__ __forceinline__ void bucketmul_body(
     ss = c.valid ? c.s1 : ss;
   };
   // Loads the chunk for this lane through a buffer descriptor that starts at
-  // unit s0 and ends at s1: lane l reads unit s0 + l (q8: one record; r12:
-  // and s0 + 64 + l, a second) or words from s0 + 4l (u32: four entries).
+  // unit s0 and ends at s1: lane l reads records s0 + l and s0 + 64 + l
+  // (r12, q8) or words from s0 + 4l (u32: four entries).
   // Words past s1 read as zero without a memory access (the range is checked
   // per 4-byte word), so every lane issues the load and the wait counters
   // stay exact; an empty chunk accesses no memory.
@@ -1638,8 +1639,11 @@ __device__ __forceinline__ void bucketmul_body(
         buf[r] = make_uint4(q[0], q[1], q[2], 0u);
       }
     } else if constexpr (FMT == EFFORT_ENTRY_Q8) {
-      const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0);
-      buf[0] = make_uint4(q[0], q[1], 0u, 0u);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const auto q = __builtin_amdgcn_raw_buffer_load_b64(rs, (64 * r + lane) * 8, 0, 0);
+        buf[r] = make_uint4(q[0], q[1], 0u, 0u);
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
@@ -1691,7 +1695,7 @@ __device__ __forceinline__ void bucketmul_body(
       // bucket of the record's segment.  Unused slots and words past the
       // chunk are not entries: the keep test below excludes them.
       const uint32_t H = buf.x, E = buf.y;
-      const bool in = (uint32_t)lane < c.s1 - c.s0;
+      const bool in = (uint32_t)lane + 64u * (uint32_t)sub < c.s1 - c.s0;
       uint32_t lo, hi, sh;
       const uint32_t trow = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.j) * (uint32_t)Q8_ROW_SLOTS;
       q8_bounds(qtab[wid][trow + (H & 15u)], lo, hi, sh);

@@ -232,14 +232,14 @@ int effort_matvec_noalloc(const effort_desc* desc, const void* layout_dev, const
 
 /* `batch` independent vectors v_dev[batch][in_dim] -> y_dev[batch][out_dim],
    each with its own K, cutoff and kept set (the same result as `batch` calls
-   of effort_matvec).  Up to 4 vectors, or any number at effort below 0.25:
-   launches of up to 4 vectors, one of each kernel, every vector with its own
-   multiply over its own read lengths.  From 5 vectors at effort 0.25 and
-   above: the vectors' cutoffs and read lengths come from one launch each;
-   then, per pass
-   of up to 8 vectors (fewer for wide column groups: their LDS tiles must
-   fit), every row's entries are read once up to the longest of the pass's
-   read lengths and each entry is tested against every vector's threshold.
+   of effort_matvec).  Up to 4 vectors, or any number at effort below
+   0.625: launches of up to 4 vectors, one of each kernel, every vector with
+   its own multiply over its own read lengths.  From 5 vectors at effort
+   0.625 and above: the vectors' cutoffs and read lengths come from one
+   launch each; then, per pass of up to 8 vectors (fewer for wide column
+   groups: their LDS tiles must fit), every row's entries are read once up to
+   the longest of the pass's read lengths and each entry is tested against
+   every vector's threshold.
    ws >= effort_workspace_bytes(desc, batch). */
 int effort_matvec_batched(const effort_desc* desc, const void* layout_dev, const float* v_dev,
                           int32_t batch, float effort, float* y_dev, void* ws_dev,

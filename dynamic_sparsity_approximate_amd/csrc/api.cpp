@@ -192,6 +192,7 @@ void build_args(const Geometry& g, const uint8_t* layout, const float* v, float 
   ma.floor = floor;
   ma.probes = probes;
   ma.rowmax = rowmax;
+  ma.regions = cand_regions(g.P, g.G, g.m) ? 1 : 0;  // launch_dispatch's choice for one matrix
   ma.runlen = runlen;
   ma.bsum = bsum;
   ma.hist = hist;
@@ -350,6 +351,7 @@ int run_batched(const Geometry& g, const uint8_t* layout, const float* v, int32_
     ma.floor = g.off_floor ? reinterpret_cast<const uint16_t*>(layout + g.off_floor) : nullptr;
     ma.probes = probes;
     ma.rowmax = rowmax;
+    ma.regions = cand_regions(g.P, g.G, g.m) ? 1 : 0;
     ma.runlen = urunlen;
     ma.bsum = ubsum;
     ma.hist = u32(b0, w.hist);
@@ -449,6 +451,10 @@ int run_multi(const Geometry* g, int32_t count, const uint8_t* const* layouts,
     bpg[j] = (int)(share / g[j].G);
     if (bpg[j] < 1) bpg[j] = 1;
   }
+  // a pair the quad dispatch cannot serve sends every pair to the
+  // row-per-thread dispatch, whose candidates form one list
+  if (!dispatch_multi_quad(dm, count))
+    for (int32_t j = 0; j < count; ++j) mm.a[j].regions = 0;
   if (hip_failed(launch_select_multi(sm, count, s))) return fail();
   if (hip_failed(launch_dispatch_multi(dm, count, s))) return fail();
   if (hip_failed(launch_bucketmul_multi(mm, count, bpg, record, s))) return fail();

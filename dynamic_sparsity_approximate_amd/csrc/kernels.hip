@@ -747,6 +747,12 @@ hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) 
   return hipGetLastError();
 }
 
+bool dispatch_multi_quad(const DispatchMulti& mm, int count) {
+  bool quad = true;
+  for (int j = 0; j < count; ++j) quad = quad && quad_dispatch(mm.a[j]);
+  return quad;
+}
+
 hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t s) {
   if (count < 1 || count > EFFORT_MAX_MULTI) return hipErrorInvalidValue;
   int P = 0;
@@ -755,9 +761,7 @@ hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t
     P = mm.a[j].P > P ? mm.a[j].P : P;
     m = mm.a[j].m > m ? mm.a[j].m : m;
   }
-  bool quad = true;
-  for (int j = 0; j < count; ++j) quad = quad && quad_dispatch(mm.a[j]);
-  if (quad) {
+  if (dispatch_multi_quad(mm, count)) {
     const dim3 gq((unsigned)((m + QR - 1) / QR), (unsigned)count);
     hipLaunchKernelGGL(k_dispatch_quad_multi, gq, dim3(DSP_T), 0, s, mm);
     return hipGetLastError();
@@ -1277,7 +1281,7 @@ __device__ __forceinline__ void bucketmul_body(
     const uint32_t b1 = res[RES_BIN], above1 = res[RES_ABOVE];
     const uint64_t cap = cand_capacity(a.m, a.P);
     uint32_t kp, cut;
-    if (cand_regions(a.P, a.G, a.m)) {  // the same test the dispatch made
+    if (a.regions) {  // where the dispatch put them
       const uint32_t nreg = (uint32_t)((a.m + QUAD_ROWS - 1) / QUAD_ROWS);
       cut = wave_exact_cutoff_regions(a.hist2 + vo, a.cand + vo, (uint32_t)cap, res + RES_RCOUNT,
                                       nreg, b1, above1, a.K, h3w[wid], &kp);

@@ -110,6 +110,8 @@ struct MulArgs {
   const uint16_t* floor;    // cropped layouts: [m] largest magnitude key not stored (else null)
   const uint16_t* probes;   // [m][P] probe keys, rowmax [m]: the q8 format's bucket bounds
   const uint16_t* rowmax;
+  int32_t regions;          // the dispatch put the candidates in per-block regions (quad
+                            // dispatch with cand_regions), else in one list
   const uint32_t* runlen;   // [G][m]
   const uint32_t* bsum;     // [nbd][G + 1]
   uint32_t* hist;           // [HIST_BINS], cleared here for the next call
@@ -163,6 +165,9 @@ struct MulMulti {
 };
 hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s);
 hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t s);
+// whether launch_dispatch_multi runs the quad-lane dispatch for these pairs
+// (all of them qualify); otherwise every pair gets the row-per-thread one
+bool dispatch_multi_quad(const DispatchMulti& mm, int count);
 // blocks_per_group[j]: matrix j's blocks per column group (its grid is G_j times that)
 hipError_t launch_bucketmul_multi(const MulMulti& mm, int count, const int* blocks_per_group,
                                   bool record, hipStream_t s);

@@ -128,3 +128,30 @@ def test_multi_own_inputs_and_heights():
             ref = oracle.run(W, oracle.probes(W, 16), v, e)
             check(got[j], ref, where=(rep, j), y=ys[j])
         print("multi own inputs rep %d ok" % rep, flush=True)
+
+
+def test_multi_and_batched_many_probes():
+    """Pairs with more probes per row than the kernels hold in registers (and
+    a mix of probe counts in one call), and batched calls at P = 64 on both
+    batch routes (launches of up to 4 vectors; the union pass)."""
+    d = dev()
+    m = 600
+    Ps, ns, efforts = (16, 64, 40), (900, 1300, 700), (0.25, 0.3, 0.6)
+    Ws = [synth.weights(m, n, seed=60 + j, stream=synth.stream_id("multiP", "W", m, n))
+          for j, n in enumerate(ns)]
+    v = synth.activations(m, seed=61, stream=synth.stream_id("multiP", "v", m))
+    mats = [E.EffortMatrix(W, P=P, device=d) for W, P in zip(Ws, Ps)]
+    group = E.EffortGroup(mats)
+    vt = torch.from_numpy(v).to(d)
+    ys, got = recorded(group, vt, efforts)
+    for j, (W, P, e) in enumerate(zip(Ws, Ps, efforts)):
+        check(got[j], oracle.run(W, oracle.probes(W, P), v, e), where=("multi P", P), y=ys[j])
+    W = Ws[1]
+    M = E.EffortMatrix(W, P=64, device=d, batch=6)
+    pr = oracle.probes(W, 64)
+    V = np.stack([synth.activations(m, seed=70 + s, stream=synth.stream_id("multiP", "v")) for s in range(6)])
+    for effort, b in ((0.25, 3), (0.8, 6)):
+        res = M.matvec_batched_debug(torch.from_numpy(V[:b]).to(d), effort)
+        for k in range(b):
+            check(res[k], oracle.run(W, pr, V[k], effort), where=("batched P=64", effort, b, k))
+    print("multi and batched with many probes ok", flush=True)

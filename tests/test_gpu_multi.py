@@ -155,3 +155,30 @@ def test_multi_and_batched_many_probes():
         for k in range(b):
             check(res[k], oracle.run(W, pr, V[k], effort), where=("batched P=64", effort, b, k))
     print("multi and batched with many probes ok", flush=True)
+
+
+def test_multi_and_batched_thirty_two_probes():
+    """P = 32 pairs in one multi-matrix call (the 8-lane dispatch for all), a
+    call mixing P = 32 with P = 16 (the row-per-thread dispatch for all), and
+    batched P = 32 calls on both batch routes."""
+    d = dev()
+    m = 1500
+    Ws = [synth.weights(m, n, seed=80 + j, stream=synth.stream_id("multi32", "W", m, n))
+          for j, n in enumerate((900, 2100, 700))]
+    v = synth.activations(m, seed=81, stream=synth.stream_id("multi32", "v", m))
+    vt = torch.from_numpy(v).to(d)
+    for Ps, efforts in (((32, 32, 32), (0.25, 0.1, 0.7)), ((32, 16, 32), (0.3, 0.3, 0.05))):
+        mats = [E.EffortMatrix(W, P=P, device=d) for W, P in zip(Ws, Ps)]
+        group = E.EffortGroup(mats)
+        ys, got = recorded(group, vt, efforts)
+        for j, (W, P, e) in enumerate(zip(Ws, Ps, efforts)):
+            check(got[j], oracle.run(W, oracle.probes(W, P), v, e), where=("multi", Ps, j), y=ys[j])
+    W = Ws[1]
+    M = E.EffortMatrix(W, P=32, device=d, batch=6)
+    pr = oracle.probes(W, 32)
+    V = np.stack([synth.activations(m, seed=90 + s, stream=synth.stream_id("multi32", "v")) for s in range(6)])
+    for effort, b in ((0.25, 3), (0.25, 6), (0.8, 6)):
+        res = M.matvec_batched_debug(torch.from_numpy(V[:b]).to(d), effort)
+        for k in range(b):
+            check(res[k], oracle.run(W, pr, V[k], effort), where=("batched P=32", effort, b, k))
+    print("multi and batched with 32 probes ok", flush=True)

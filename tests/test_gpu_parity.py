@@ -93,6 +93,26 @@ def test_ragged_shapes(m, n, P, G, effort):
     run_pair(W, v, P, effort, groups=G, where="ragged")
 
 
+@pytest.mark.parametrize("m,n,G,fmt", [(700, 3000, 0, 0), (2048, 1100, 3, 1), (2049, 4100, 8, 0),
+                                        (3000, 5000, 0, 1), (33, 70, 1, 0)])
+@pytest.mark.parametrize("effort", [0.02, 0.25, 1.0])
+def test_thirty_two_probes(m, n, G, fmt, effort):
+    """P = 32 takes the dispatch with 8 lanes per row (32 rows per block): its
+    candidates in per-block regions up to 2048 rows (64 blocks), in one list
+    beyond; every group count up to 8 and a ragged last block."""
+    d = dev()
+    W, v = case(m, n, seed=m + n + 32, tag="p32")
+    M = E.EffortMatrix(W, P=32, groups=G, device=d, entry_format=fmt)
+    vt = torch.from_numpy(v).to(d)
+    got = M.matvec_debug(vt, effort, with_mask=m * n <= (1 << 24))
+    ref = oracle.run(W, oracle.probes(W, 32), v, effort, mask=got["mask"] is not None)
+    check(got, ref, got["mask"] is not None, where=("P=32", m, n, G, fmt, effort))
+    y = M.matvec(vt, effort)
+    torch.cuda.synchronize()
+    assert rel_l2(y.cpu().numpy(), got["y"]) < 1e-6
+    say("P=32 %dx%d G=%d format %d effort %g ok" % (m, n, M.groups, fmt, effort))
+
+
 @pytest.mark.parametrize("P", [33, 40, 64, 100, 300])
 @pytest.mark.parametrize("effort", [0.02, 0.25, 1.0])
 def test_many_probes(P, effort):

@@ -10,8 +10,10 @@ Timing:
   * every timed loop cycles over R distinct device copies of the layout (and R
     vectors), R chosen so a cycle touches >= 1 GiB, so the 256 MB last-level
     cache cannot serve repeats; the dense comparator cycles over its own copies;
-  * the calls of one cycle are captured once in a HIP graph and the graph is
-    replayed; hipEvents on the replay stream bracket the timed region;
+  * C calls (at least 64, and at least one whole cycle) are captured once in a
+    HIP graph and the graph is replayed; the dense comparator's graph holds the
+    same C calls, so the per-replay launch cost weighs on both paths alike;
+    hipEvents on the replay stream bracket the timed region;
   * each kernel's own duration comes from a hipEvent pair that the runtime
     stamps with that kernel's begin and end (effort_matvec_timed, launched with
     hipExtLaunchKernelGGL), in eager calls queued behind graph replays.
@@ -55,6 +57,9 @@ def parse():
                          "quantized matrix)")
     ap.add_argument("--crop", type=int, default=0, help="stored segments per row (0: all)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--graph-calls", type=int, default=64,
+                    help="calls captured per graph, the same for the effort path and the dense "
+                         "GEMV, so that the per-replay launch cost weighs on both alike")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["full", "effort", "dense", "copy", "sweep", "batched",
@@ -196,7 +201,10 @@ def main():
     call_bytes = ebytes * kept0
     R = max(2, int(math.ceil(args.rotate_gib * GiB / call_bytes)))
     Rd = max(2, int(math.ceil(args.rotate_gib * GiB / (2.0 * m * n))))
-    log("rotation: %d layouts (%.0f MB read per call), %d dense copies" % (R, call_bytes / 1e6, Rd))
+    # both graphs hold C calls, cycling over their own copies
+    C = max(R, Rd, args.graph_calls)
+    log("rotation: %d layouts (%.0f MB read per call), %d dense copies, %d calls per graph"
+        % (R, call_bytes / 1e6, Rd, C))
 
     result = {}
     if args.mode in ("full", "effort"):
@@ -211,17 +219,18 @@ def main():
         ws, wsb = M.ws, M.ws_bytes
 
         def cycle():
-            for r in range(R):
+            for i in range(C):
+                r = i % R
                 E.effort_matvec(M.desc, layouts[r], vs[r], effort, ys[r], ws, wsb)
 
         for _ in range(3):  # eager warm-up (and JIT of code objects)
             cycle()
         torch.cuda.synchronize()
         g = capture(torch, cycle)
-        wreps = max(1, args.warmup // R)
+        wreps = max(1, args.warmup // C)
         time_replays(torch, g, wreps)
-        reps = max(1, int(math.ceil(args.steps / R)))
-        steps = reps * R
+        reps = max(1, int(math.ceil(args.steps / C)))
+        steps = reps * C
         log("timing %d steps" % steps)
         ms, host_ms = time_replays(torch, g, reps)
         us_per = ms * 1e3 / steps
@@ -264,7 +273,7 @@ def main():
                          "traffic_source": (os.path.relpath(COUNTERS, ROOT) + ": rocprofv3 FETCH_SIZE + "
                                             "WRITE_SIZE per dispatch of this kernels.hip and entry format, "
                                             "scaled by a 1 GiB copy") if traffic else None},
-            "rotation": R, "groups": M.groups,
+            "rotation": R, "graph_calls": C, "groups": M.groups,
         })
         for e in sum(evs, []):
             E.effort_event_destroy(e)
@@ -277,16 +286,17 @@ def main():
         yds = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(Rd)]
 
         def dcycle():
-            for r in range(Rd):
+            for i in range(C):
+                r = i % Rd
                 E.dense_gemv(Wds[r], vds[r], m, n, yds[r])
 
         for _ in range(3):
             dcycle()
         gd = capture(torch, dcycle)
-        time_replays(torch, gd, max(1, args.warmup // Rd))
-        dreps = max(1, int(math.ceil(args.steps / Rd)))
+        time_replays(torch, gd, max(1, args.warmup // C))
+        dreps = max(1, int(math.ceil(args.steps / C)))
         dms, _ = time_replays(torch, gd, dreps)
-        dense_us = dms * 1e3 / (dreps * Rd)
+        dense_us = dms * 1e3 / (dreps * C)
         result["dense_us"] = dense_us
         result["dense_gbs"] = 2.0 * m * n / (dense_us * 1e-6) / 1e9
         # library sanity reference: torch's fp16 matmul (hipBLASLt / rocBLAS) on the
@@ -296,7 +306,8 @@ def main():
         yhs = [torch.empty((1, n), dtype=torch.float16, device=dev) for _ in range(Rd)]
 
         def lcycle():
-            for r in range(Rd):
+            for i in range(C):
+                r = i % Rd
                 torch.matmul(vhs[r], Whs[r], out=yhs[r])
 
         for _ in range(3):
@@ -304,7 +315,7 @@ def main():
         gl = capture(torch, lcycle)
         time_replays(torch, gl, max(1, args.warmup // Rd))
         lms, _ = time_replays(torch, gl, dreps)
-        result["library_dense_us"] = lms * 1e3 / (dreps * Rd)
+        result["library_dense_us"] = lms * 1e3 / (dreps * C)
         if "us_per_matvec" in result:
             result["speedup_vs_dense"] = dense_us / result["us_per_matvec"]
 
@@ -356,6 +367,7 @@ def main():
             "config": {"workload": "effort matvec %dx%d fp16, effort %g, batch 1" % (m, n, effort),
                        "in_dim": m, "out_dim": n, "effort": effort, "P": P,
                        "groups": result["groups"], "rotation_copies": result["rotation"],
+                       "graph_calls": result["graph_calls"],
                        "entry_format": args.format, "crop_segments": args.crop or P},
             "hbm_gbs": result["hbm_gbs"], "kept_fraction": result["kept_fraction"],
             "dense_us": result["dense_us"], "dense_gbs": result["dense_gbs"],

@@ -411,7 +411,9 @@ def run_sweep(args, torch, np, E, synth, dev):
         Wds = [Wd] + [Wd.clone() for _ in range(Rd - 1)]
         vd = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
         yd = torch.empty(n, dtype=torch.float32, device=dev)
-        dense_us = graph_time_us(torch, lambda: [E.dense_gemv(w, vd, m, n, yd) for w in Wds], 50) / Rd
+        Cd = max(Rd, args.graph_calls)
+        dense_us = graph_time_us(torch, lambda: [E.dense_gemv(Wds[i % Rd], vd, m, n, yd) for i in range(Cd)],
+                                 max(5, 2000 // Cd)) / Cd
         del Wds
         for effort in (1.0, 0.5, 0.25, 0.125):
             v0 = torch.from_numpy(synth.vector("config1", m, seed=0)).to(dev)
@@ -421,11 +423,14 @@ def run_sweep(args, torch, np, E, synth, dev):
             vs = [torch.from_numpy(synth.vector("config1", m, seed=r)).to(dev) for r in range(R)]
             ys = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(R)]
 
+            C = max(R, args.graph_calls)
+
             def cyc():
-                for r in range(R):
+                for i in range(C):
+                    r = i % R
                     E.effort_matvec(M.desc, layouts[r], vs[r], effort, ys[r], M.ws, M.ws_bytes)
 
-            us = graph_time_us(torch, cyc, max(5, 2000 // R)) / R
+            us = graph_time_us(torch, cyc, max(5, 2000 // C)) / C
             rows.append({"in": m, "out": n, "effort": effort, "us": round(us, 2),
                          "kept_fraction": round(kept / (m * n), 4),
                          "alg_GBps": round((entry_bytes(args.format) * kept + 2.0 * m * args.P
@@ -455,13 +460,16 @@ def run_batched(args, torch, np, E, synth, dev):
         V = torch.from_numpy(np.stack([synth.vector("config4", m, seed=s) for s in range(b)])).to(dev)
         Y = torch.empty((b, n), dtype=torch.float32, device=dev)
 
-        def cyc():
-            for r in range(R):
-                E.effort_matvec_batched(M.desc, layouts[r], V, b, effort, Y, M.ws, M.ws_bytes)
+        C = max(R, args.graph_calls)
+        Cd = max(Rd, args.graph_calls)
 
-        us = graph_time_us(torch, cyc, max(5, 400 // R)) / R
-        dense_us = graph_time_us(torch, lambda: [E.dense_gemm_small(w, V, b, m, n, Y) for w in Wds],
-                                 20) / Rd
+        def cyc():
+            for i in range(C):
+                E.effort_matvec_batched(M.desc, layouts[i % R], V, b, effort, Y, M.ws, M.ws_bytes)
+
+        us = graph_time_us(torch, cyc, max(5, 400 // C)) / C
+        dense_us = graph_time_us(torch, lambda: [E.dense_gemm_small(Wds[i % Rd], V, b, m, n, Y)
+                                                 for i in range(Cd)], max(5, 400 // Cd)) / Cd
         rows.append({"batch": b, "effort_us": round(us, 2), "dense_gemm_us": round(dense_us, 2),
                      "effort_faster": us < dense_us})
         log(json.dumps(rows[-1]))

@@ -270,6 +270,8 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "k_bucketmul", "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "traffic": traffic, "alg_bytes": alg_mul, "kernel_us": mul_us,
+                         # the same kernel time over the bytes it actually moved
+                         "traffic_frac": (traffic / (mul_us * 1e-6) / 1e9 / HBM_PEAK_GBS) if traffic else None,
                          "traffic_source": (os.path.relpath(COUNTERS, ROOT) + ": rocprofv3 FETCH_SIZE + "
                                             "WRITE_SIZE per dispatch of this kernels.hip and entry format, "
                                             "scaled by a 1 GiB copy") if traffic else None},
